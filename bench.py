@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the mHC fused post->pre pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: repack the next layer's projection (mhc_pack_phi)
+and run the fused post -> coefficients -> pre pass
+(mhc_post_pre_fused_prepacked).  W untimed steps, then K timed steps between
+two device synchronisations; HIP events around every fused launch give the
+dominant kernel's average duration for the roofline figure.  Rank 0 prints
+one JSON line.  The default workload is prefill-shaped: T = 8192 tokens,
+C = 7168, 4 routes, 1% of the rows scaled by 100.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+METRIC = "mHC fused post+pre tokens/s and % peak HBM GB/s at C=7168, T=8192"
+
+
+def algorithmic_bytes(T: int, C: int, mxfp8: bool, with_h: bool = True) -> int:
+    """Bytes the fused pass must move: per token x (8C) + y (2C) + incoming
+    post/res (80) + x' (8C) + outgoing coefficients (96) + h (2C bf16 and/or
+    C + C/32 MXFP8); per call the projection (fp32, 384C), gamma (4C) and
+    bias (96), each read once."""
+    per_tok = 8 * C + 2 * C + 80 + 8 * C + 96
+    if with_h:
+        per_tok += 2 * C
+    if mxfp8:
+        per_tok += C + C // 32
+    return T * per_tok + 384 * C + 4 * C + 96
+
+
+def cpu_baseline(inp_host: dict, coeffs_host, params, budget_s: float = 10.0, chunk: int = 128) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle as O
+
+    f64 = lambda t: t.to("cpu").double().numpy()  # noqa: E731
+    x, y = f64(inp_host["x"]), f64(inp_host["y"])
+    cf = f64(coeffs_host)
+    phi, b, g = f64(inp_host["phi_next"]), f64(inp_host["bias_next"]), f64(inp_host["gamma_next"])
+    n = x.shape[0]
+    done = 0
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < budget_s:
+        s = (k * chunk) % n
+        rows = slice(s, min(s + chunk, n))
+        O.post_pre_fused(x[rows], y[rows], cf[rows], phi, b, g, hc_norm_eps=params.hc_norm_eps,
+                         rmsnorm_eps=params.rmsnorm_eps, hc_post_scale=params.hc_post_scale,
+                         sinkhorn_eps=params.sinkhorn_eps, sinkhorn_iters=params.sinkhorn_iters)
+        done += rows.stop - rows.start
+        k += 1
+    dt = time.perf_counter() - t0
+    threads = 1
+    for pool in threadpoolctl.threadpool_info():
+        threads = max(threads, int(pool.get("num_threads", 1)))
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} tokens of the same workload in chunks of {chunk} ({dt:.1f} s), "
+                      f"fp64 numpy oracle fused post->pre"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "mxfp8", "long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path is not built "
+                                   "(every token is independent: see DESIGN.md for how it would shard)",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import manifold_constrained_hyper_mhc_amd as mhc
+    from manifold_constrained_hyper_mhc_amd.params import Params
+    from manifold_constrained_hyper_mhc_amd.synthetic import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    T, C = w.T, w.C
+    mx = args.workload == "mxfp8"
+    params = Params()
+    print(f"[bench] workload={w.name} T={T} C={C} mxfp8={mx} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    inp = make_inputs(T, C, seed=0, rows=w.rows, device=dev)
+    # incoming coefficients of this layer: computed by the library itself
+    coeffs_in = mhc.coeffs(inp["x"], inp["phi"], inp["bias"], params)
+    ws = mhc.workspace(T, C, dev)
+    packed = torch.empty(int(mhc.lib().mhc_phi_packed_bytes(C)), dtype=torch.uint8, device=dev)
+    outs = {"x_out": torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev),
+            "coeffs_next": torch.empty((T, 24), dtype=torch.float32, device=dev)}
+    with_h = not mx
+    if with_h:
+        outs["h"] = torch.empty((T, C), dtype=torch.bfloat16, device=dev)
+    if mx:
+        outs["h_fp8"] = torch.empty((T, C), dtype=torch.uint8, device=dev)
+        outs["h_scale"] = torch.empty((T, C // 32), dtype=torch.uint8, device=dev)
+    L = mhc.lib()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        rc = L.mhc_pack_phi(mhc.binding._ptr(inp["phi_next"]), C, mhc.binding._ptr(packed),
+                            mhc.binding._stream(dev))
+        if rc:
+            raise mhc.MhcError(rc, "mhc_pack_phi")
+        if ev is not None:
+            ev[0].record(stream)
+        mhc.post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, packed, inp["bias_next"], inp["gamma_next"],
+                                     params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    kern_sorted = sorted(kern_ms)
+    err_word = int(ws[:4].view(torch.int32).item())
+    if err_word != 0:
+        print(f"[bench] WARNING: workspace error word {err_word} (a bounded wait expired)", file=sys.stderr)
+
+    nbytes = algorithmic_bytes(T, C, mx, with_h)
+    achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us, fused kernel avg {kern_avg_ms * 1e3:.1f} us "
+          f"(p10 {kern_sorted[len(kern_sorted) // 10] * 1e3:.1f}, p90 {kern_sorted[9 * len(kern_sorted) // 10] * 1e3:.1f}),"
+          f" {achieved:.0f} GB/s algorithmic = {achieved / HBM_PEAK_GBS:.3f} of peak; wall {wall:.3f} s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_s = min(T, 1024)
+        host = {k: inp[k][:n_s].cpu() for k in ("x", "y")}
+        host.update({k: inp[k].cpu() for k in ("phi_next", "bias_next", "gamma_next")})
+        cpu = cpu_baseline(host, coeffs_in[:n_s].cpu(), params)
+        print(f"[bench] cpu oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
+
+    rows = {"normal": "N(0,1)", "outliers": "N(0,1), 1% of rows x100", "decades": "N(0,1) x 10^U(-2,3) per row"}[w.rows]
+    line = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: fused post->pre (projection repack + fused pass per step)",
+                   "tokens": T, "hidden": C, "routes": 4, "mxfp8": mx, "bf16_h": with_h, "rows": rows,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_split (fused post->pre)", "kernel_avg_us": kern_avg_ms * 1e3,
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

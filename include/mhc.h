@@ -1,0 +1,197 @@
+/*
+ * libmhc — the mHC hyper-connection hot path on AMD Instinct MI355X (gfx950).
+ *
+ * mHC wraps every transformer sublayer with a residual stream of 4 routes
+ * ("hc_mult = 4"; hidden size a multiple of 1024), per-token mixing
+ * coefficients computed from the RMS-scaled, route-flattened row, a post
+ * step that writes the sublayer output back into the stream, and a pre step
+ * (combine + RMSNorm) that feeds the next sublayer.  Sources, by page and
+ * section:
+ *   [P1] "[SM80] Backport mHC fused post + int8 all-reduce; fixes #28, #29",
+ *        "What this fixes": post with a fused sum of squares feeding the
+ *        prenorm GEMM.
+ *   [P2] "[DSv4.1] Integrate Mega-mHC from DeepGEMM", review "Correctness
+ *        findings" (route count, hidden % 1024, token limit, scalar names,
+ *        the capture contract) and the SM12x comment (the projection takes
+ *        the flattened row of width hc_mult * hidden).
+ *   [P3] "[DSV4.1] Four BS=1 critical-path fixes for DSpark decode",
+ *        "What changed" item 3 and "Correctness" (combine+RMSNorm written in
+ *        BF16, MXFP8 epilogue with UE8M0 scales, bitwise equal to the
+ *        unfused pair); "Measured and deliberately left out" (per-token mHC
+ *        statistics and Sinkhorn; the fused post->pre kernel at T = 6).
+ *
+ * Conventions for every entry point
+ *   - Tensors are device pointers owned by the caller, row-major and
+ *     contiguous, 16-byte aligned.  bf16 tensors are passed as raw bits
+ *     (uint16_t).  Layouts:
+ *       x, x_out  [T][4][C] bf16     residual stream, route-major rows
+ *       y         [T][C]    bf16     sublayer output
+ *       h         [T][C]    bf16     normalised pre output
+ *       coeffs    [T][24]   fp32     {pre[4], post[4] (already times
+ *                                     hc_post_scale), res[4][4] row-major,
+ *                                     row j = output route}
+ *       phi       [4*C][24] fp32     projection, row k = route*C + channel
+ *       bias      [24] fp32, gamma [C] fp32
+ *       h_fp8     [T][C]    uint8    OCP e4m3fn codes
+ *       h_scale   [T][C/32] uint8    UE8M0 exponent bytes (bias 127),
+ *                                     linear (not swizzled) layout
+ *   - T is the token count, 0 <= T <= MHC_MAX_TOKENS; T == 0 validates the
+ *     scalars and returns MHC_OK without touching memory (pointers may then
+ *     be NULL).  C is the hidden size, a positive multiple of 1024 and at
+ *     most MHC_MAX_HIDDEN.  The route count is fixed at 4.
+ *   - Every argument is validated before any HIP call, so a rejected call
+ *     has no effect on the device.  Outputs must not overlap inputs or each
+ *     other.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     The library never allocates, frees or synchronises on the call path
+ *     and keeps no per-stream state, so calls may be captured in a HIP
+ *     graph from the first call on.  Errors of the device work itself
+ *     surface at the caller's next synchronisation.
+ *   - No exception crosses this interface.  Return values are mhc_status
+ *     codes; mhc_strerror() names them and mhc_last_hip_error() gives the
+ *     hipError_t behind the last MHC_ERR_HIP of the calling thread.
+ */
+#ifndef MHC_H_
+#define MHC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+#define MHC_NUM_ROUTES 4
+#define MHC_NUM_COEFFS 24
+#define MHC_MAX_TOKENS (1 << 20)  /* [P2] review: the kernel's token limit 2^20 */
+#define MHC_MAX_HIDDEN 65536
+#define MHC_MXFP8_BLOCK 32
+
+/* Scalars of the method, passed by name ([P2] review warns against a
+ * positional float tail whose order differs between two paths). */
+typedef struct mhc_params {
+  float hc_norm_eps;    /* eps of the RMS scale of the flattened 4C row */
+  float rmsnorm_eps;    /* eps of the RMSNorm in pre */
+  float hc_post_scale;  /* post = hc_post_scale * sigmoid(logit) */
+  float sinkhorn_eps;   /* each Sinkhorn normalisation divides by (sum + eps) */
+  int32_t sinkhorn_iters; /* iterations of (rows, then columns); 0..1024 */
+} mhc_params;
+
+typedef enum mhc_status {
+  MHC_OK = 0,
+  MHC_ERR_NULL = 1,       /* a required pointer is NULL */
+  MHC_ERR_SHAPE = 2,      /* T or C out of range, C % 1024 != 0 */
+  MHC_ERR_ALIGN = 3,      /* a tensor is not 16-byte aligned */
+  MHC_ERR_ALIAS = 4,      /* an output overlaps an input or another output */
+  MHC_ERR_FLAGS = 5,      /* unknown flag, or outputs inconsistent with flags */
+  MHC_ERR_WORKSPACE = 6,  /* workspace NULL, too small or misaligned */
+  MHC_ERR_PARAM = 7,      /* a scalar is negative, not finite or out of range */
+  MHC_ERR_HIP = 8         /* a HIP runtime call failed (see mhc_last_hip_error) */
+} mhc_status;
+
+/* Flags of mhc_post_pre_fused. */
+#define MHC_FLAG_MXFP8 1u /* also write h as MXFP8: e4m3fn codes + UE8M0 scale per 32 channels */
+
+/* ---------------------------------------------------------------------------
+ * Library information
+ * ------------------------------------------------------------------------- */
+int mhc_abi_version(void);
+const char* mhc_strerror(int status);
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int mhc_last_hip_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Workspace.  mhc_coeffs and mhc_post_pre_fused reduce each token's row
+ * across several workgroups and need a caller-owned device workspace of
+ * mhc_workspace_bytes(T, C, flags) bytes (256-byte aligned).  Before its
+ * first use a workspace must be cleared with mhc_workspace_init (a kernel on
+ * `stream`, no memset node); every call leaves it cleared again, so it can
+ * be reused by any later call with any T and C whose size it covers.  One
+ * workspace must not be used by two calls that may run concurrently.
+ * ------------------------------------------------------------------------- */
+size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags);
+int mhc_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Coefficients ([P1] "What this fixes": the sum of squares feeding the
+ * prenorm GEMM; [P2] SM12x comment: the projection takes the flattened row;
+ * [P3] "Measured and deliberately left out": mHC statistics and Sinkhorn).
+ * Per token t:
+ *   r      = 1 / sqrt(sum_{i,c} x[t][i][c]^2 / (4C) + hc_norm_eps)
+ *   l[m]   = r * sum_{k} x_flat[t][k] * phi[k][m] + bias[m],  k = i*C + c
+ *   pre    = sigmoid(l[0..3]); post = hc_post_scale * sigmoid(l[4..7])
+ *   res    = sinkhorn_iters x (rows then columns, each divided by its
+ *            sum + sinkhorn_eps) applied to exp(l[8..23]) as 4x4, row j =
+ *            output route
+ * Writes coeffs [T][24].  Uses the workspace (see above).
+ * ------------------------------------------------------------------------- */
+int mhc_coeffs(const uint16_t* x, int64_t T, int64_t C, const float* phi, const float* bias,
+               const mhc_params* p, float* coeffs, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Pre: combine + RMSNorm ([P3] "What changed" item 3: the combine+norm
+ * output is written in BF16 and feeds the sublayer's first projection).
+ *   g[c] = sum_i pre[t][i] * x[t][i][c]
+ *   h[t][c] = bf16_rne(g[c] / sqrt(mean_c g^2 + rmsnorm_eps) * gamma[c])
+ * pre is read from coeffs[t][0..3] (stride 24).
+ * ------------------------------------------------------------------------- */
+int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t T, int64_t C,
+            const mhc_params* p, uint16_t* h, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Post ([P2] "Purpose"/review: the mHC post kernel).
+ *   x_out[t][j][c] = bf16_rne(sum_i res[t][j][i] * x[t][i][c] + post[t][j] * y[t][c])
+ * post and res are read from coeffs[t][4..23].  The value that is rounded is
+ * the binary32 chain  a = post_j * y;  a = fma(res[j][i], x_i, a) for
+ * i = 0..3  (a fixed order, so the bf16 result is reproducible).
+ * ------------------------------------------------------------------------- */
+int mhc_post(const uint16_t* x, const uint16_t* y, const float* coeffs, int64_t T, int64_t C,
+             uint16_t* x_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused post -> next pre ([P2] "Purpose"/review: the fused post->pre kernel
+ * and Mega-mHC; [P1]: the shared sum of squares; [P3] item 3: the MXFP8
+ * epilogue).  In one pass over the stream:
+ *   x_out       = mhc_post(x, y, coeffs)
+ *   coeffs_next = mhc_coeffs(x_out; phi_next, bias_next)   (from the bf16 x_out)
+ *   h           = mhc_pre(x_out, coeffs_next, gamma_next)
+ * and with MHC_FLAG_MXFP8, per 32-channel block of the bf16 h: amax = max|h|,
+ * e = the smallest integer with amax <= 448 * 2^e (clamped to [-127, 127],
+ * -127 for an all-zero block), h_scale = e + 127, h_fp8 = e4m3fn_rne(h * 2^-e).
+ * h may be NULL when MHC_FLAG_MXFP8 is set; h_fp8 and h_scale are required
+ * with the flag and must be NULL without it.
+ * ------------------------------------------------------------------------- */
+int mhc_post_pre_fused(const uint16_t* x, const uint16_t* y, const float* coeffs,
+                       const float* phi_next, const float* bias_next, const float* gamma_next,
+                       int64_t T, int64_t C, const mhc_params* p, unsigned flags,
+                       uint16_t* x_out, float* coeffs_next, uint16_t* h, uint8_t* h_fp8,
+                       uint8_t* h_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Pre-packed projection.  The two calls above first repack phi (fp32) into
+ * the layout the matrix cores read: three bf16 terms per element (hi + mid +
+ * lo == phi exactly for |phi| >= 2^-100), in 1 KiB fragments.  A caller
+ * whose phi is a fixed weight can pack it once with mhc_pack_phi into a
+ * buffer of mhc_phi_packed_bytes(C) bytes (256-byte aligned) and call the
+ * _prepacked variants, which skip that step; results are bitwise identical.
+ * ------------------------------------------------------------------------- */
+size_t mhc_phi_packed_bytes(int64_t C);
+int mhc_pack_phi(const float* phi, int64_t C, void* phi_packed, void* stream);
+int mhc_coeffs_prepacked(const uint16_t* x, int64_t T, int64_t C, const void* phi_packed,
+                         const float* bias, const mhc_params* p, float* coeffs, void* workspace,
+                         size_t workspace_bytes, void* stream);
+int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const float* coeffs,
+                                 const void* phi_next_packed, const float* bias_next,
+                                 const float* gamma_next, int64_t T, int64_t C,
+                                 const mhc_params* p, unsigned flags, uint16_t* x_out,
+                                 float* coeffs_next, uint16_t* h, uint8_t* h_fp8,
+                                 uint8_t* h_scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H_ */

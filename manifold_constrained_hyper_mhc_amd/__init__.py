@@ -1,6 +1,16 @@
 """libmhc: the mHC hyper-connection hot path on MI355X (gfx950).
 
 The compute lives in the HIP shared library ``libmhc.so`` built from
-``csrc/``; this package loads it lazily (importing the package never needs a
-GPU) and exposes thin bindings with the library's names.
+``csrc/`` (``python -m manifold_constrained_hyper_mhc_amd.build``).  This
+package only marshals torch tensors into the C ABI of ``include/mhc.h``:
+it checks dtypes, shapes and devices, allocates outputs and the workspace
+with torch, and passes raw device pointers and torch's current stream.
+Importing it never needs a GPU; the library is loaded on first use and a
+missing library is an error, never a fallback.
 """
+from .params import Params
+from .binding import (MhcError, coeffs, coeffs_prepacked, lib, pack_phi, post,
+                      post_pre_fused, post_pre_fused_prepacked, pre, workspace)
+
+__all__ = ["Params", "MhcError", "lib", "coeffs", "coeffs_prepacked", "pre", "post",
+           "post_pre_fused", "post_pre_fused_prepacked", "pack_phi", "workspace"]

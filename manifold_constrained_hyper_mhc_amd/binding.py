@@ -1,0 +1,278 @@
+"""ctypes binding of libmhc.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls (without the
+``mhc_`` prefix).  Tensors must be CUDA (HIP) tensors, contiguous, with the
+dtypes of ``include/mhc.h``; bf16 tensors are passed as their raw bits.  Work
+is enqueued on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .params import Params
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmhc.so")
+
+FLAG_MXFP8 = 1
+_STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_ALIGN", 4: "MHC_ERR_ALIAS",
+           5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP"}
+
+
+class MhcParams(ctypes.Structure):
+    _fields_ = [("hc_norm_eps", ctypes.c_float), ("rmsnorm_eps", ctypes.c_float),
+                ("hc_post_scale", ctypes.c_float), ("sinkhorn_eps", ctypes.c_float),
+                ("sinkhorn_iters", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, p: Params) -> "MhcParams":
+        return cls(p.hc_norm_eps, p.rmsnorm_eps, p.hc_post_scale, p.sinkhorn_eps, p.sinkhorn_iters)
+
+
+class MhcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        msg = f"{what}: {self.name}"
+        if _LIB is not None:
+            msg += " (" + _LIB.mhc_strerror(status).decode() + ")"
+            if status == 8:
+                msg += f", hipError {_LIB.mhc_last_hip_error()}"
+        super().__init__(msg)
+
+
+_LIB = None
+_LOCK = threading.Lock()
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIG = {
+    "mhc_abi_version": ([], ctypes.c_int),
+    "mhc_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "mhc_last_hip_error": ([], ctypes.c_int),
+    "mhc_workspace_bytes": ([_I64, _I64, ctypes.c_uint], ctypes.c_size_t),
+    "mhc_workspace_init": ([_P, ctypes.c_size_t, _P], ctypes.c_int),
+    "mhc_phi_packed_bytes": ([_I64], ctypes.c_size_t),
+    "mhc_pack_phi": ([_P, _I64, _P, _P], ctypes.c_int),
+    "mhc_coeffs": ([_P, _I64, _I64, _P, _P, ctypes.POINTER(MhcParams), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "mhc_coeffs_prepacked": ([_P, _I64, _I64, _P, _P, ctypes.POINTER(MhcParams), _P, _P, ctypes.c_size_t, _P],
+                             ctypes.c_int),
+    "mhc_pre": ([_P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams), _P, _P], ctypes.c_int),
+    "mhc_post": ([_P, _P, _P, _I64, _I64, _P, _P], ctypes.c_int),
+    "mhc_post_pre_fused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams), ctypes.c_uint,
+                            _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "mhc_post_pre_fused_prepacked": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams),
+                                      ctypes.c_uint, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmhc.so (once).  Raises if it has not been built."""
+    global _LIB
+    with _LOCK:
+        if _LIB is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m manifold_constrained_hyper_mhc_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIG.items():
+                fn = getattr(L, name)
+                fn.argtypes = args
+                fn.restype = res
+            _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MhcError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(x):
+    if not isinstance(x, torch.Tensor) or x.dim() != 3 or x.shape[1] != 4:
+        raise ValueError("x must have shape [T, 4, C]")
+    return int(x.shape[0]), int(x.shape[2])
+
+
+# workspaces cached per (device, stream): a workspace must not be shared by
+# calls that can run concurrently
+_WS = {}
+
+
+def workspace(T: int, C: int, device=None, *, fresh: bool = False) -> torch.Tensor:
+    """A cleared workspace of at least mhc_workspace_bytes(T, C) bytes."""
+    L = lib()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    need = int(L.mhc_workspace_bytes(T, C, 0))
+    if need == 0:
+        raise MhcError(2, "mhc_workspace_bytes")
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    ws = None if fresh else _WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _check(L.mhc_workspace_init(_ptr(ws), ws.numel(), _stream(dev)), "mhc_workspace_init")
+        if not fresh:
+            _WS[key] = ws
+    return ws
+
+
+def pack_phi(phi: torch.Tensor) -> torch.Tensor:
+    L = lib()
+    C = phi.shape[0] // 4
+    _need(phi, "phi", torch.float32, (4 * C, 24))
+    out = torch.empty(int(L.mhc_phi_packed_bytes(C)), dtype=torch.uint8, device=phi.device)
+    _check(L.mhc_pack_phi(_ptr(phi), C, _ptr(out), _stream(phi.device)), "mhc_pack_phi")
+    return out
+
+
+def coeffs(x, phi, bias, params: Params = Params(), *, ws=None, out=None) -> torch.Tensor:
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(phi, "phi", torch.float32, (4 * C, 24), dev)
+    _need(bias, "bias", torch.float32, (24,), dev)
+    out = torch.empty((T, 24), dtype=torch.float32, device=dev) if out is None else out
+    _need(out, "coeffs", torch.float32, (T, 24), dev)
+    ws = workspace(T, C, dev) if ws is None else ws
+    p = MhcParams.of(params)
+    _check(L.mhc_coeffs(_ptr(x), T, C, _ptr(phi), _ptr(bias), ctypes.byref(p), _ptr(out), _ptr(ws), ws.numel(),
+                        _stream(dev)), "mhc_coeffs")
+    return out
+
+
+def coeffs_prepacked(x, phi_packed, bias, params: Params = Params(), *, ws=None, out=None) -> torch.Tensor:
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(phi_packed, "phi_packed", torch.uint8, (int(L.mhc_phi_packed_bytes(C)),), dev)
+    _need(bias, "bias", torch.float32, (24,), dev)
+    out = torch.empty((T, 24), dtype=torch.float32, device=dev) if out is None else out
+    _need(out, "coeffs", torch.float32, (T, 24), dev)
+    ws = workspace(T, C, dev) if ws is None else ws
+    p = MhcParams.of(params)
+    _check(L.mhc_coeffs_prepacked(_ptr(x), T, C, _ptr(phi_packed), _ptr(bias), ctypes.byref(p), _ptr(out),
+                                  _ptr(ws), ws.numel(), _stream(dev)), "mhc_coeffs_prepacked")
+    return out
+
+
+def pre(x, coeffs_t, gamma, params: Params = Params(), *, out=None) -> torch.Tensor:
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24), dev)
+    _need(gamma, "gamma", torch.float32, (C,), dev)
+    out = torch.empty((T, C), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "h", torch.bfloat16, (T, C), dev)
+    p = MhcParams.of(params)
+    _check(L.mhc_pre(_ptr(x), _ptr(coeffs_t), _ptr(gamma), T, C, ctypes.byref(p), _ptr(out), _stream(dev)),
+           "mhc_pre")
+    return out
+
+
+def post(x, y, coeffs_t, *, out=None) -> torch.Tensor:
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(y, "y", torch.bfloat16, (T, C), dev)
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24), dev)
+    out = torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "x_out", torch.bfloat16, (T, 4, C), dev)
+    _check(L.mhc_post(_ptr(x), _ptr(y), _ptr(coeffs_t), T, C, _ptr(out), _stream(dev)), "mhc_post")
+    return out
+
+
+def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
+    o = dict(outs or {})
+    o.setdefault("x_out", torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev))
+    o.setdefault("coeffs_next", torch.empty((T, 24), dtype=torch.float32, device=dev))
+    if want_h:
+        o.setdefault("h", torch.empty((T, C), dtype=torch.bfloat16, device=dev))
+    else:
+        o["h"] = None
+    if mxfp8:
+        o.setdefault("h_fp8", torch.empty((T, C), dtype=torch.uint8, device=dev))
+        o.setdefault("h_scale", torch.empty((T, C // 32), dtype=torch.uint8, device=dev))
+    else:
+        o["h_fp8"] = o["h_scale"] = None
+    _need(o["x_out"], "x_out", torch.bfloat16, (T, 4, C), dev)
+    _need(o["coeffs_next"], "coeffs_next", torch.float32, (T, 24), dev)
+    if o["h"] is not None:
+        _need(o["h"], "h", torch.bfloat16, (T, C), dev)
+    if mxfp8:
+        _need(o["h_fp8"], "h_fp8", torch.uint8, (T, C), dev)
+        _need(o["h_scale"], "h_scale", torch.uint8, (T, C // 32), dev)
+    return o
+
+
+def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Params = Params(), *,
+                   mxfp8: bool = False, want_h: bool = True, ws=None, outs=None) -> dict:
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(y, "y", torch.bfloat16, (T, C), dev)
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24), dev)
+    _need(phi_next, "phi_next", torch.float32, (4 * C, 24), dev)
+    _need(bias_next, "bias_next", torch.float32, (24,), dev)
+    _need(gamma_next, "gamma_next", torch.float32, (C,), dev)
+    o = _fused_outputs(T, C, dev, mxfp8, want_h, outs)
+    ws = workspace(T, C, dev) if ws is None else ws
+    p = MhcParams.of(params)
+    _check(L.mhc_post_pre_fused(_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next), _ptr(bias_next), _ptr(gamma_next),
+                                T, C, ctypes.byref(p), FLAG_MXFP8 if mxfp8 else 0, _ptr(o["x_out"]),
+                                _ptr(o["coeffs_next"]), _ptr(o["h"]), _ptr(o["h_fp8"]), _ptr(o["h_scale"]),
+                                _ptr(ws), ws.numel(), _stream(dev)), "mhc_post_pre_fused")
+    return o
+
+
+def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(), *,
+                             mxfp8: bool = False, want_h: bool = True, ws=None, outs=None) -> dict:
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(y, "y", torch.bfloat16, (T, C), dev)
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24), dev)
+    _need(phi_next_packed, "phi_next_packed", torch.uint8, (int(L.mhc_phi_packed_bytes(C)),), dev)
+    _need(bias_next, "bias_next", torch.float32, (24,), dev)
+    _need(gamma_next, "gamma_next", torch.float32, (C,), dev)
+    o = _fused_outputs(T, C, dev, mxfp8, want_h, outs)
+    ws = workspace(T, C, dev) if ws is None else ws
+    p = MhcParams.of(params)
+    _check(L.mhc_post_pre_fused_prepacked(_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next_packed), _ptr(bias_next),
+                                          _ptr(gamma_next), T, C, ctypes.byref(p), FLAG_MXFP8 if mxfp8 else 0,
+                                          _ptr(o["x_out"]), _ptr(o["coeffs_next"]), _ptr(o["h"]), _ptr(o["h_fp8"]),
+                                          _ptr(o["h_scale"]), _ptr(ws), ws.numel(), _stream(dev)),
+           "mhc_post_pre_fused_prepacked")
+    return o

@@ -1,0 +1,338 @@
+// The libmhc C ABI: argument validation, workspace layout and launches.
+// Every check runs before the first HIP call, so a rejected call has no
+// effect on the device (and the checks can be exercised without a GPU).
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mhc.h"
+#include "mhc_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MHC_OK;
+  g_last_hip_error = (int)e;
+  return MHC_ERR_HIP;
+}
+
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int64_t T, int64_t C) {
+  if (T < 0 || T > MHC_MAX_TOKENS) return MHC_ERR_SHAPE;
+  if (C <= 0 || C % 1024 != 0 || C > MHC_MAX_HIDDEN) return MHC_ERR_SHAPE;
+  return MHC_OK;
+}
+
+int check_params(const mhc_params* p, bool needs_coeff_scalars) {
+  if (p == nullptr) return MHC_ERR_NULL;
+  auto ok_eps = [](float v) { return isfinite(v) && v >= 0.0f; };
+  if (!ok_eps(p->rmsnorm_eps)) return MHC_ERR_PARAM;
+  if (needs_coeff_scalars) {
+    if (!ok_eps(p->hc_norm_eps) || !ok_eps(p->sinkhorn_eps)) return MHC_ERR_PARAM;
+    if (!isfinite(p->hc_post_scale)) return MHC_ERR_PARAM;
+    if (p->sinkhorn_iters < 0 || p->sinkhorn_iters > 1024) return MHC_ERR_PARAM;
+  }
+  return MHC_OK;
+}
+
+mhc::Scalars scalars(const mhc_params* p) {
+  mhc::Scalars s;
+  s.hc_norm_eps = p->hc_norm_eps;
+  s.rmsnorm_eps = p->rmsnorm_eps;
+  s.hc_post_scale = p->hc_post_scale;
+  s.sinkhorn_eps = p->sinkhorn_eps;
+  s.sinkhorn_iters = p->sinkhorn_iters;
+  return s;
+}
+
+// All listed tensors non-null and 16-byte aligned; no output overlaps an
+// input or another output.
+int check_tensors(const Span* in, int nin, const Span* out, int nout) {
+  for (int k = 0; k < nin; ++k)
+    if (in[k].p == nullptr) return MHC_ERR_NULL;
+  for (int k = 0; k < nout; ++k)
+    if (out[k].p == nullptr) return MHC_ERR_NULL;
+  for (int k = 0; k < nin; ++k)
+    if (!aligned16(in[k].p)) return MHC_ERR_ALIGN;
+  for (int k = 0; k < nout; ++k)
+    if (!aligned16(out[k].p)) return MHC_ERR_ALIGN;
+  for (int o = 0; o < nout; ++o) {
+    for (int k = 0; k < nin; ++k)
+      if (overlaps(out[o], in[k])) return MHC_ERR_ALIAS;
+    for (int k = o + 1; k < nout; ++k)
+      if (overlaps(out[o], out[k])) return MHC_ERR_ALIAS;
+  }
+  return MHC_OK;
+}
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
+  if (ws == nullptr) return MHC_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return MHC_ERR_WORKSPACE;
+  if (bytes < plan.total) return MHC_ERR_WORKSPACE;
+  return MHC_OK;
+}
+
+}  // namespace
+
+namespace mhc {
+
+// Tile shape: 16 tokens x 512 channels per workgroup (RB = 1, CW = 128).
+Plan make_plan(int64_t T, int64_t C) {
+  Plan p;
+  p.rb = 1;
+  p.cw = 128;
+  p.m = 16 * p.rb;
+  p.cc = 4 * p.cw;
+  p.s = (int)(C / p.cc);
+  p.tiles = (T + p.m - 1) / p.m;
+  size_t off = 0;
+  p.off_err = off;
+  off += 256;
+  p.off_cnt = off;
+  off = round256(off + (size_t)p.tiles * 4);
+  p.off_flag = off;
+  off = round256(off + (size_t)p.tiles * 4);
+  p.off_pub = off;
+  off = round256(off + (size_t)p.tiles * p.m * 4 * sizeof(float));
+  p.off_part = off;
+  off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(float));
+  p.off_phi = off;
+  off = round256(off + phi_packed_bytes(C));
+  p.total = off;
+  return p;
+}
+
+}  // namespace mhc
+
+namespace {
+
+mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C, const mhc_params* p) {
+  mhc::SplitArgs a;
+  memset(&a, 0, sizeof(a));
+  char* base = static_cast<char*>(ws);
+  a.err = reinterpret_cast<uint32_t*>(base + plan.off_err);
+  a.cnt = reinterpret_cast<uint32_t*>(base + plan.off_cnt);
+  a.flag = reinterpret_cast<uint32_t*>(base + plan.off_flag);
+  a.publish = reinterpret_cast<float*>(base + plan.off_pub);
+  a.partials = reinterpret_cast<float*>(base + plan.off_part);
+  a.T = T;
+  a.C = (int)C;
+  a.S = plan.s;
+  a.sc = scalars(p);
+  return a;
+}
+
+int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const void* phi_packed,
+                const float* bias, const mhc_params* p, float* coeffs, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_shape(T, C);
+  if (rc) return rc;
+  if ((rc = check_params(p, true))) return rc;
+  if (T == 0) return MHC_OK;
+  const size_t xb = (size_t)T * 4 * C * 2, cb = (size_t)T * 24 * 4;
+  const Span phi_span = phi ? Span{phi, (size_t)4 * C * 24 * 4} : Span{phi_packed, mhc::phi_packed_bytes(C)};
+  const Span in[] = {{x, xb}, phi_span, {bias, 96}};
+  const Span out[] = {{coeffs, cb}};
+  if ((rc = check_tensors(in, 3, out, 1))) return rc;
+  const mhc::Plan plan = mhc::make_plan(T, C);
+  if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
+  const Span wsp{ws, plan.total};
+  if (overlaps(wsp, out[0])) return MHC_ERR_ALIAS;
+  for (const Span& s : in)
+    if (overlaps(wsp, s)) return MHC_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mhc::SplitArgs a = split_args(plan, ws, T, C, p);
+  const void* packed = phi_packed;
+  if (phi != nullptr) {
+    void* dst = static_cast<char*>(ws) + plan.off_phi;
+    if ((rc = hip_status(mhc::launch_pack_phi(phi, (int)C, dst, s)))) return rc;
+    packed = dst;
+  }
+  a.x = x;
+  a.phi_packed = static_cast<const uint32_t*>(packed);
+  a.bias = bias;
+  a.coeffs_out = coeffs;
+  return hip_status(mhc::launch_split(plan, mhc::kModeCoeffs, a, s));
+}
+
+int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const float* phi,
+               const void* phi_packed, const float* bias, const float* gamma, int64_t T, int64_t C,
+               const mhc_params* p, unsigned flags, uint16_t* x_out, float* coeffs_next, uint16_t* h,
+               uint8_t* h_fp8, uint8_t* h_scale, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(T, C);
+  if (rc) return rc;
+  if ((rc = check_params(p, true))) return rc;
+  if (flags & ~MHC_FLAG_MXFP8) return MHC_ERR_FLAGS;
+  const bool mx = (flags & MHC_FLAG_MXFP8) != 0;
+  if (mx) {
+    if (T > 0 && (h_fp8 == nullptr || h_scale == nullptr)) return MHC_ERR_NULL;
+  } else if (h_fp8 != nullptr || h_scale != nullptr) {
+    return MHC_ERR_FLAGS;
+  }
+  if (T == 0) return MHC_OK;
+  if (!mx && h == nullptr) return MHC_ERR_NULL;
+  const size_t xb = (size_t)T * 4 * C * 2, yb = (size_t)T * C * 2, cb = (size_t)T * 24 * 4;
+  const Span phi_span = phi ? Span{phi, (size_t)4 * C * 24 * 4} : Span{phi_packed, mhc::phi_packed_bytes(C)};
+  const Span in[] = {{x, xb}, {y, yb}, {coeffs, cb}, phi_span, {bias, 96}, {gamma, (size_t)C * 4}};
+  Span out[5];
+  int nout = 0;
+  out[nout++] = {x_out, xb};
+  out[nout++] = {coeffs_next, cb};
+  if (h) out[nout++] = {h, yb};
+  if (mx) {
+    out[nout++] = {h_fp8, (size_t)T * C};
+    out[nout++] = {h_scale, (size_t)T * (C / 32)};
+  }
+  if ((rc = check_tensors(in, 6, out, nout))) return rc;
+  const mhc::Plan plan = mhc::make_plan(T, C);
+  if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
+  const Span wsp{ws, plan.total};
+  for (const Span& s : in)
+    if (overlaps(wsp, s)) return MHC_ERR_ALIAS;
+  for (int k = 0; k < nout; ++k)
+    if (overlaps(wsp, out[k])) return MHC_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mhc::SplitArgs a = split_args(plan, ws, T, C, p);
+  const void* packed = phi_packed;
+  if (phi != nullptr) {
+    void* dst = static_cast<char*>(ws) + plan.off_phi;
+    if ((rc = hip_status(mhc::launch_pack_phi(phi, (int)C, dst, s)))) return rc;
+    packed = dst;
+  }
+  a.x = x;
+  a.y = y;
+  a.coeffs_in = coeffs;
+  a.phi_packed = static_cast<const uint32_t*>(packed);
+  a.bias = bias;
+  a.gamma = gamma;
+  a.x_out = x_out;
+  a.coeffs_out = coeffs_next;
+  a.h = h;
+  a.h_fp8 = h_fp8;
+  a.h_scale = h_scale;
+  return hip_status(mhc::launch_split(plan, mx ? mhc::kModeFusedMx : mhc::kModeFused, a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+const char* mhc_strerror(int status) {
+  switch (status) {
+    case MHC_OK: return "success";
+    case MHC_ERR_NULL: return "a required pointer is NULL";
+    case MHC_ERR_SHAPE: return "T or C out of range (C must be a positive multiple of 1024)";
+    case MHC_ERR_ALIGN: return "a tensor is not 16-byte aligned";
+    case MHC_ERR_ALIAS: return "an output overlaps an input or another output";
+    case MHC_ERR_FLAGS: return "unknown flag, or outputs inconsistent with the flags";
+    case MHC_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MHC_ERR_PARAM: return "a scalar parameter is out of range";
+    case MHC_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int mhc_last_hip_error(void) { return g_last_hip_error; }
+
+size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags) {
+  if (check_shape(T, C) != MHC_OK || (flags & ~MHC_FLAG_MXFP8)) return 0;
+  return mhc::make_plan(T, C).total;
+}
+
+int mhc_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return MHC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0 || (workspace_bytes & 3u) != 0) return MHC_ERR_WORKSPACE;
+  return hip_status(mhc::launch_fill_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+size_t mhc_phi_packed_bytes(int64_t C) {
+  if (check_shape(0, C) != MHC_OK) return 0;
+  return mhc::phi_packed_bytes(C);
+}
+
+int mhc_pack_phi(const float* phi, int64_t C, void* phi_packed, void* stream) {
+  int rc = check_shape(0, C);
+  if (rc) return rc;
+  if (phi == nullptr || phi_packed == nullptr) return MHC_ERR_NULL;
+  if (!aligned16(phi) || ((uintptr_t)phi_packed & 255u) != 0) return MHC_ERR_ALIGN;
+  if (overlaps(Span{phi, (size_t)4 * C * 24 * 4}, Span{phi_packed, mhc::phi_packed_bytes(C)})) return MHC_ERR_ALIAS;
+  return hip_status(mhc::launch_pack_phi(phi, (int)C, phi_packed, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_coeffs(const uint16_t* x, int64_t T, int64_t C, const float* phi, const float* bias,
+               const mhc_params* p, float* coeffs, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  return coeffs_impl(x, T, C, phi, nullptr, bias, p, coeffs, workspace, workspace_bytes, stream);
+}
+
+int mhc_coeffs_prepacked(const uint16_t* x, int64_t T, int64_t C, const void* phi_packed,
+                         const float* bias, const mhc_params* p, float* coeffs, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return coeffs_impl(x, T, C, nullptr, phi_packed, bias, p, coeffs, workspace, workspace_bytes, stream);
+}
+
+int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t T, int64_t C,
+            const mhc_params* p, uint16_t* h, void* stream) {
+  int rc = check_shape(T, C);
+  if (rc) return rc;
+  if ((rc = check_params(p, false))) return rc;
+  if (T == 0) return MHC_OK;
+  const Span in[] = {{x, (size_t)T * 4 * C * 2}, {coeffs, (size_t)T * 24 * 4}, {gamma, (size_t)C * 4}};
+  const Span out[] = {{h, (size_t)T * C * 2}};
+  if ((rc = check_tensors(in, 3, out, 1))) return rc;
+  return hip_status(mhc::launch_pre(x, coeffs, gamma, T, (int)C, p->rmsnorm_eps, h, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_post(const uint16_t* x, const uint16_t* y, const float* coeffs, int64_t T, int64_t C,
+             uint16_t* x_out, void* stream) {
+  int rc = check_shape(T, C);
+  if (rc) return rc;
+  if (T == 0) return MHC_OK;
+  const size_t xb = (size_t)T * 4 * C * 2;
+  const Span in[] = {{x, xb}, {y, (size_t)T * C * 2}, {coeffs, (size_t)T * 24 * 4}};
+  const Span out[] = {{x_out, xb}};
+  if ((rc = check_tensors(in, 3, out, 1))) return rc;
+  return hip_status(mhc::launch_post(x, y, coeffs, T, (int)C, x_out, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_post_pre_fused(const uint16_t* x, const uint16_t* y, const float* coeffs,
+                       const float* phi_next, const float* bias_next, const float* gamma_next,
+                       int64_t T, int64_t C, const mhc_params* p, unsigned flags, uint16_t* x_out,
+                       float* coeffs_next, uint16_t* h, uint8_t* h_fp8, uint8_t* h_scale,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_impl(x, y, coeffs, phi_next, nullptr, bias_next, gamma_next, T, C, p, flags, x_out,
+                    coeffs_next, h, h_fp8, h_scale, workspace, workspace_bytes, stream);
+}
+
+int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const float* coeffs,
+                                 const void* phi_next_packed, const float* bias_next,
+                                 const float* gamma_next, int64_t T, int64_t C,
+                                 const mhc_params* p, unsigned flags, uint16_t* x_out,
+                                 float* coeffs_next, uint16_t* h, uint8_t* h_fp8,
+                                 uint8_t* h_scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return fused_impl(x, y, coeffs, nullptr, phi_next_packed, bias_next, gamma_next, T, C, p, flags,
+                    x_out, coeffs_next, h, h_fp8, h_scale, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

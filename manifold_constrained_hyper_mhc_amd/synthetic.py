@@ -19,21 +19,10 @@ import dataclasses
 
 import torch
 
+from .params import Params  # noqa: F401  (re-exported for the tests)
+
 N_ROUTES = 4
 N_LOGITS = 24
-
-
-@dataclasses.dataclass(frozen=True)
-class Params:
-    """The method's scalars, by name (the pages' vocabulary)."""
-    hc_norm_eps: float = 1e-6
-    rmsnorm_eps: float = 1e-6
-    hc_post_scale: float = 2.0
-    sinkhorn_eps: float = 1e-6
-    sinkhorn_iters: int = 20
-
-    def as_kwargs(self) -> dict:
-        return dataclasses.asdict(self)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -17,3 +17,11 @@ def pytest_configure(config):
 def params():
     from manifold_constrained_hyper_mhc_amd.synthetic import Params
     return Params()
+
+
+@pytest.fixture(autouse=True)
+def _name_gpu_case(request):
+    # name the case before any GPU work, so a run that ends abruptly says which
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[case] {request.node.nodeid}", flush=True)
+    yield

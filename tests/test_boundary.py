@@ -1,0 +1,184 @@
+"""The C ABI without a GPU: symbols, sizes and argument validation.
+
+Every entry point validates its arguments before its first HIP call, so the
+rejected calls below never touch a device.  The fake device addresses are
+never dereferenced; these tests are skipped where a GPU is visible, so that
+no call with a fake pointer can ever reach a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import manifold_constrained_hyper_mhc_amd as mhc
+from manifold_constrained_hyper_mhc_amd.binding import MhcParams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, FLAGS, WORKSPACE, PARAM, HIP = range(9)
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake-pointer validation tests run without a GPU")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mhc.lib()
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_strerror():
+    L = mhc.lib()
+    assert L.mhc_abi_version() == 1
+    for code in range(9):
+        assert L.mhc_strerror(code)
+    assert L.mhc_strerror(99) == b"unknown status"
+
+
+def test_sizes():
+    L = mhc.lib()
+    assert L.mhc_phi_packed_bytes(7168) == 4 * 7168 * 160
+    assert L.mhc_phi_packed_bytes(1000) == 0          # not a multiple of 1024
+    assert L.mhc_workspace_bytes(8192, 7168, 0) >= 4 * 7168 * 160
+    assert L.mhc_workspace_bytes(8192, 7168, 2) == 0  # unknown flag
+    assert L.mhc_workspace_bytes(-1, 7168, 0) == 0
+    w1, w2 = L.mhc_workspace_bytes(16, 1024, 0), L.mhc_workspace_bytes(17, 1024, 0)
+    assert 0 < w1 <= w2
+    assert L.mhc_workspace_bytes(0, 1024, 0) > 0
+    assert L.mhc_workspace_bytes(1 << 20, 65536, 1) % 256 == 0
+
+
+# ---------------------------------------------------------------------------
+# validation with fake device addresses (never dereferenced)
+# ---------------------------------------------------------------------------
+BASE = 0x7F0000000000
+SPACING = 1 << 36
+
+
+def fake(k, off=0):
+    return ctypes.c_void_p(BASE + k * SPACING + off)
+
+
+P = MhcParams(1e-6, 1e-6, 2.0, 1e-6, 20)
+
+
+def post_call(L, T=16, C=1024, x=None, y=None, cf=None, out=None):
+    return L.mhc_post(x or fake(0), y or fake(1), cf or fake(2), T, C, out or fake(3), None)
+
+
+@no_gpu
+def test_post_validation():
+    L = mhc.lib()
+    assert post_call(L, C=1000) == SHAPE
+    assert post_call(L, C=0) == SHAPE
+    assert post_call(L, T=-1) == SHAPE
+    assert post_call(L, T=(1 << 20) + 1) == SHAPE
+    assert post_call(L, C=65536 + 1024) == SHAPE
+    assert L.mhc_post(None, fake(1), fake(2), 16, 1024, fake(3), None) == NULL
+    assert L.mhc_post(fake(0), fake(1), fake(2), 16, 1024, None, None) == NULL
+    assert post_call(L, y=fake(1, 8)) == ALIGN
+    assert post_call(L, out=fake(0, 1024)) == ALIAS       # output inside x
+    assert post_call(L, out=fake(1, 16)) == ALIAS         # output overlapping y
+    # T == 0: nothing to do, pointers may be NULL
+    assert L.mhc_post(None, None, None, 0, 1024, None, None) == OK
+
+
+@no_gpu
+def test_pre_validation():
+    L = mhc.lib()
+    bad = MhcParams(1e-6, float("nan"), 2.0, 1e-6, 20)
+    assert L.mhc_pre(fake(0), fake(1), fake(2), 4, 1024, ctypes.byref(bad), fake(3), None) == PARAM
+    neg = MhcParams(1e-6, -1.0, 2.0, 1e-6, 20)
+    assert L.mhc_pre(fake(0), fake(1), fake(2), 4, 1024, ctypes.byref(neg), fake(3), None) == PARAM
+    assert L.mhc_pre(fake(0), fake(1), fake(2), 4, 1024, None, fake(3), None) == NULL
+    assert L.mhc_pre(fake(0), fake(1), fake(2), 4, 3000, ctypes.byref(P), fake(3), None) == SHAPE
+    assert L.mhc_pre(fake(0), fake(1), fake(2), 4, 1024, ctypes.byref(P), fake(0, 4096), None) == ALIAS
+    assert L.mhc_pre(fake(0), fake(1, 4), fake(2), 4, 1024, ctypes.byref(P), fake(3), None) == ALIGN
+    assert L.mhc_pre(None, None, None, 0, 1024, ctypes.byref(P), None, None) == OK
+
+
+def fused_call(L, T=16, C=1024, flags=0, p=P, ws=None, ws_bytes=None, h=True, fp8=None, sc=None,
+               x_out=None, cf_next=None, phi=None, gamma=None):
+    if ws_bytes is None:
+        ws_bytes = L.mhc_workspace_bytes(T, C, flags) if T >= 0 else 0
+    return L.mhc_post_pre_fused(fake(0), fake(1), fake(2), phi or fake(3), fake(4), gamma or fake(5), T, C,
+                                ctypes.byref(p) if p is not None else None, flags, x_out or fake(6),
+                                cf_next or fake(7), fake(8) if h else None, fp8, sc, ws or fake(11),
+                                ws_bytes, None)
+
+
+@no_gpu
+def test_fused_validation():
+    L = mhc.lib()
+    assert fused_call(L, C=1536) == SHAPE
+    assert fused_call(L, flags=4) == FLAGS
+    assert fused_call(L, fp8=fake(9)) == FLAGS                      # fp8 output without the flag
+    assert fused_call(L, flags=1, fp8=fake(9)) == NULL              # flag without the scale output
+    assert fused_call(L, h=False) == NULL                           # bf16 h required without the flag
+    assert fused_call(L, p=None) == NULL
+    assert fused_call(L, p=MhcParams(1e-6, 1e-6, float("inf"), 1e-6, 20)) == PARAM
+    assert fused_call(L, p=MhcParams(1e-6, 1e-6, 2.0, 1e-6, -1)) == PARAM
+    assert fused_call(L, p=MhcParams(1e-6, 1e-6, 2.0, 1e-6, 5000)) == PARAM
+    assert fused_call(L, p=MhcParams(-1e-6, 1e-6, 2.0, 1e-6, 20)) == PARAM
+    assert fused_call(L, ws_bytes=100) == WORKSPACE
+    assert fused_call(L, ws=fake(11, 16)) == WORKSPACE             # not 256-byte aligned
+    assert fused_call(L, x_out=fake(0, 2048)) == ALIAS
+    assert fused_call(L, cf_next=fake(6, 32)) == ALIAS              # two outputs overlap
+    assert fused_call(L, ws=fake(6, 0)) == ALIAS                    # workspace over an output
+    assert fused_call(L, phi=fake(3, 4)) == ALIGN
+    assert fused_call(L, T=0, h=False, flags=1) == OK
+
+
+@no_gpu
+def test_coeffs_validation():
+    L = mhc.lib()
+    ws_bytes = L.mhc_workspace_bytes(16, 1024, 0)
+
+    def call(T=16, C=1024, x=None, phi=None, out=None, ws=None, wsb=ws_bytes, p=P):
+        return L.mhc_coeffs(x or fake(0), T, C, phi or fake(1), fake(2), ctypes.byref(p), out or fake(3),
+                            ws or fake(4), wsb, None)
+    assert call(C=512) == SHAPE
+    assert call(wsb=ws_bytes - 256) == WORKSPACE
+    assert call(out=fake(0, 64)) == ALIAS
+    assert call(x=fake(0, 2)) == ALIGN
+    assert call(p=MhcParams(float("nan"), 1e-6, 2.0, 1e-6, 20)) == PARAM
+    assert L.mhc_coeffs(fake(0), 16, 1024, None, fake(2), ctypes.byref(P), fake(3), fake(4), ws_bytes, None) == NULL
+    assert call(T=0) == OK
+
+
+@no_gpu
+def test_pack_phi_validation():
+    L = mhc.lib()
+    assert L.mhc_pack_phi(None, 1024, fake(1), None) == NULL
+    assert L.mhc_pack_phi(fake(0), 1000, fake(1), None) == SHAPE
+    assert L.mhc_pack_phi(fake(0), 1024, fake(1, 16), None) == ALIGN
+    assert L.mhc_pack_phi(fake(0), 1024, fake(0, 256), None) == ALIAS
+
+
+@no_gpu
+def test_hip_failure_is_an_error_code_without_a_gpu():
+    # a valid call reaches the HIP runtime, which has no device here
+    L = mhc.lib()
+    assert L.mhc_workspace_init(fake(0), 4096, None) == HIP
+    assert L.mhc_last_hip_error() != 0
+    assert L.mhc_workspace_init(None, 4096, None) == WORKSPACE
+    assert L.mhc_workspace_init(fake(0, 8), 4096, None) == WORKSPACE
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    x = torch.zeros((2, 4, 1024), dtype=torch.float32)
+    with pytest.raises((TypeError, ValueError)):
+        mhc.post(x, torch.zeros((2, 1024), dtype=torch.bfloat16), torch.zeros((2, 24)))
+    xb = torch.zeros((2, 4, 1024), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):      # CPU tensors are refused
+        mhc.post(xb, torch.zeros((2, 1024), dtype=torch.bfloat16), torch.zeros((2, 24)))

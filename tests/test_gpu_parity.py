@@ -1,0 +1,362 @@
+"""Parity of the HIP library against the fp64 oracle, through the C ABI.
+
+Every input comes from the seeded generator (manifold_constrained_hyper_mhc_amd.synthetic);
+the incoming coefficients of post and the fused pass are the oracle's own
+Coeffs of the generated stream, stored as fp32.  Nothing the oracle sees
+comes from the HIP path.
+
+Bars (tests/_compare.py): coefficients within 1e-4 relative, elementwise;
+bf16 outputs within 1e-2 of max(|oracle|, row RMS); x_out bit-exact (its bf16
+rounding is decided by the same binary32 chain on both sides); MXFP8 codes
+and scales bit-exact on every block whose bf16 h equals the oracle's.
+Small cases compare every element; the full-size workloads (the launch
+configuration the benchmark times) compare a sample of tokens, which the
+oracle computes one row at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import manifold_constrained_hyper_mhc_amd as mhc
+import oracle as O
+from manifold_constrained_hyper_mhc_amd.params import Params
+from manifold_constrained_hyper_mhc_amd.synthetic import WORKLOADS, make_inputs
+from tests._compare import assert_bf16_close, assert_coeffs_close, f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+P = Params()
+
+
+def kw(p=P):
+    return dict(hc_norm_eps=p.hc_norm_eps, hc_post_scale=p.hc_post_scale, sinkhorn_eps=p.sinkhorn_eps,
+                sinkhorn_iters=p.sinkhorn_iters)
+
+
+def fkw(p=P):
+    return dict(kw(p), rmsnorm_eps=p.rmsnorm_eps)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mhc.lib()
+
+
+def oracle_coeffs_in(x, phi, bias, p=P, n_max=2048):
+    """fp32 incoming coefficients: the oracle's Coeffs of the first n_max
+    tokens, tiled over T (tokens are independent, so any realistic
+    coefficient row is a valid input for any token)."""
+    T = x.shape[0]
+    n = min(T, n_max)
+    cf = O.coeffs(f64(x[:n]), f64(phi), f64(bias), **kw(p))
+    cf = O.f32_round(cf)
+    reps = (T + n - 1) // n
+    return torch.from_numpy(np.tile(cf, (reps, 1))[:T].astype(np.float32))
+
+
+def small_inputs(T, C, rows="normal", seed=0):
+    inp = make_inputs(T, C, seed=seed, rows=rows, device="cpu")
+    inp["coeffs"] = oracle_coeffs_in(inp["x"], inp["phi"], inp["bias"])
+    return inp
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048)]
+
+
+# ---------------------------------------------------------------------------
+# standalone ops, every element
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,C", SMALL)
+def test_post_bit_exact(T, C):
+    inp = small_inputs(T, C)
+    d = to_dev(inp)
+    out = mhc.post(d["x"], d["y"], d["coeffs"])
+    torch.cuda.synchronize()
+    _, pw, res = O.split_coeffs(f64(inp["coeffs"]))
+    ref = O.post(f64(inp["x"]), f64(inp["y"]), pw, res)
+    assert np.array_equal(f64(out), ref)
+
+
+@pytest.mark.parametrize("T,C", SMALL)
+def test_coeffs(T, C):
+    inp = small_inputs(T, C)
+    d = to_dev(inp)
+    cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
+    torch.cuda.synchronize()
+    ref = O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw())
+    assert_coeffs_close(f64(cf), ref)
+
+
+@pytest.mark.parametrize("T,C", SMALL + [(5, 9216), (2, 65536)])
+def test_pre(T, C):
+    inp = small_inputs(T, C)
+    d = to_dev(inp)
+    h = mhc.pre(d["x"], d["coeffs"], d["gamma"])
+    torch.cuda.synchronize()
+    ref = O.pre(f64(inp["x"]), f64(inp["coeffs"])[:, 0:4], f64(inp["gamma"]), rmsnorm_eps=P.rmsnorm_eps)
+    assert_bf16_close(f64(h), ref)
+
+
+# ---------------------------------------------------------------------------
+# fused pass, every element
+# ---------------------------------------------------------------------------
+def check_fused(inp, out, p=P, mx=False, rows=None):
+    sel = slice(None) if rows is None else rows
+    ref = O.post_pre_fused(f64(inp["x"][sel]), f64(inp["y"][sel]), f64(inp["coeffs"][sel]), f64(inp["phi_next"]),
+                           f64(inp["bias_next"]), f64(inp["gamma_next"]), with_mxfp8=mx, **fkw(p))
+    g = {k: (v[sel] if v is not None and rows is not None else v) for k, v in out.items()}
+    assert np.array_equal(f64(g["x_out"]), ref["x_out"]), "x_out differs from the oracle"
+    assert_coeffs_close(f64(g["coeffs_next"]), ref["coeffs_next"], what="coeffs_next")
+    if g["h"] is not None:
+        assert_bf16_close(f64(g["h"]), ref["h"], what="h")
+    if mx:
+        check_mxfp8(g, ref)
+    return ref
+
+
+def check_mxfp8(g, ref):
+    T, C = ref["h"].shape
+    q = g["h_fp8"].cpu().numpy()
+    sc = g["h_scale"].cpu().numpy()
+    hg = f64(g["h"]).reshape(T, C // 32, 32)
+    same = np.all(hg == ref["h"].reshape(T, C // 32, 32), axis=2) & \
+        np.all(np.signbit(hg) == np.signbit(ref["h"].reshape(T, C // 32, 32)), axis=2)
+    assert same.mean() > 0.95, f"only {same.mean():.3f} of the blocks have identical bf16 h"
+    assert np.array_equal(sc[same], ref["h_scale"][same])
+    qb, rb = q.reshape(T, C // 32, 32), ref["h_fp8"].reshape(T, C // 32, 32)
+    assert np.array_equal(qb[same], rb[same])
+    # every block: the codes decode to the oracle's h within half an e4m3 step
+    # plus the bf16 tolerance of h
+    e = sc.astype(np.int64) - 127
+    dec = O.e4m3_decode(q).reshape(T, C // 32, 32) * np.ldexp(1.0, e)[:, :, None]
+    ho = ref["h"].reshape(T, C // 32, 32)
+    rms = np.sqrt(np.mean(ref["h"] ** 2, axis=1))[:, None, None]
+    bound = np.ldexp(1.0, e)[:, :, None] * 16.0 + 1e-2 * np.maximum(np.abs(ho), rms)
+    assert np.all(np.abs(dec - ho) <= bound)
+
+
+@pytest.mark.parametrize("T,C", SMALL)
+def test_fused(T, C):
+    inp = small_inputs(T, C)
+    d = to_dev(inp)
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"])
+    torch.cuda.synchronize()
+    check_fused(inp, out)
+
+
+@pytest.mark.parametrize("T,C", [(16, 1024), (37, 4096), (3, 7168)])
+def test_fused_mxfp8(T, C):
+    inp = small_inputs(T, C, rows="decades")
+    d = to_dev(inp)
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
+    torch.cuda.synchronize()
+    check_fused(inp, out, mx=True)
+    # the same bytes without the bf16 output
+    out2 = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"],
+                              mxfp8=True, want_h=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out2["h_fp8"], out["h_fp8"]) and torch.equal(out2["h_scale"], out["h_scale"])
+    assert torch.equal(out2["coeffs_next"], out["coeffs_next"]) and torch.equal(out2["x_out"], out["x_out"])
+
+
+def test_distinct_scalars_catch_swaps():
+    # distinct values for every scalar: a swapped argument shows up
+    p = Params(hc_norm_eps=2e-5, rmsnorm_eps=3e-4, hc_post_scale=1.25, sinkhorn_eps=2e-6, sinkhorn_iters=20)
+    inp = small_inputs(24, 2048)
+    inp["coeffs"] = oracle_coeffs_in(inp["x"], inp["phi"], inp["bias"], p)
+    d = to_dev(inp)
+    cf = mhc.coeffs(d["x"], d["phi"], d["bias"], p)
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], p)
+    h = mhc.pre(d["x"], d["coeffs"], d["gamma"], p)
+    torch.cuda.synchronize()
+    assert_coeffs_close(f64(cf), O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw(p)))
+    check_fused(inp, out, p)
+    assert_bf16_close(f64(h), O.pre(f64(inp["x"]), f64(inp["coeffs"])[:, 0:4], f64(inp["gamma"]),
+                                    rmsnorm_eps=p.rmsnorm_eps))
+
+
+@pytest.mark.parametrize("iters", [0, 1, 7])
+def test_sinkhorn_iteration_counts(iters):
+    p = Params(sinkhorn_iters=iters)
+    inp = small_inputs(16, 1024)
+    d = to_dev(inp)
+    cf = mhc.coeffs(d["x"], d["phi"], d["bias"], p)
+    torch.cuda.synchronize()
+    assert_coeffs_close(f64(cf), O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw(p)))
+
+
+def test_identity_post_is_exact():
+    # res = I and post = 0 give x' = x bitwise, in post and in the fused pass
+    inp = small_inputs(20, 2048)
+    cf = inp["coeffs"].clone()
+    cf[:, 4:8] = 0.0
+    cf[:, 8:] = torch.eye(4).reshape(16)
+    inp["coeffs"] = cf
+    d = to_dev(inp)
+    xo = mhc.post(d["x"], d["y"], d["coeffs"])
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"])
+    torch.cuda.synchronize()
+    assert torch.equal(xo, d["x"]) and torch.equal(out["x_out"], d["x"])
+    check_fused(inp, out)
+
+
+# ---------------------------------------------------------------------------
+# library behaviour
+# ---------------------------------------------------------------------------
+def test_prepacked_is_bitwise_identical():
+    inp = small_inputs(45, 3072)
+    d = to_dev(inp)
+    pk = mhc.pack_phi(d["phi_next"])
+    a = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
+    b = mhc.post_pre_fused_prepacked(d["x"], d["y"], d["coeffs"], pk, d["bias_next"], d["gamma_next"], mxfp8=True)
+    c1 = mhc.coeffs(d["x"], d["phi_next"], d["bias_next"])
+    c2 = mhc.coeffs_prepacked(d["x"], pk, d["bias_next"])
+    torch.cuda.synchronize()
+    for k in ("x_out", "coeffs_next", "h", "h_fp8", "h_scale"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(c1, c2)
+
+
+def test_deterministic_and_workspace_reuse():
+    ws = mhc.workspace(300, 7168, DEV, fresh=True)
+    runs = []
+    for T, C in [(40, 2048), (300, 7168), (7, 1024), (40, 2048)]:
+        inp = small_inputs(T, C, seed=T)
+        d = to_dev(inp)
+        out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], ws=ws)
+        torch.cuda.synchronize()
+        runs.append(out)
+        if T == 7:
+            check_fused(inp, out)
+    for k in ("x_out", "coeffs_next", "h"):
+        assert torch.equal(runs[0][k], runs[3][k])
+    assert int(ws[:4].view(torch.int32).item()) == 0, "workspace error word set (a bounded wait expired)"
+
+
+def test_outputs_stay_in_bounds():
+    T, C = 19, 2048
+    inp = small_inputs(T, C)
+    d = to_dev(inp)
+    pad = 4096
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * pad,), 77, dtype=dtype, device=DEV)
+        return buf, buf[pad:pad + n]
+
+    bx, x_out = guarded(T * 4 * C, torch.bfloat16)
+    bc, cn = guarded(T * 24, torch.float32)
+    bh, h = guarded(T * C, torch.bfloat16)
+    bq, q = guarded(T * C, torch.uint8)
+    bs, s = guarded(T * C // 32, torch.uint8)
+    outs = {"x_out": x_out.view(T, 4, C), "coeffs_next": cn.view(T, 24), "h": h.view(T, C),
+            "h_fp8": q.view(T, C), "h_scale": s.view(T, C // 32)}
+    mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True,
+                       outs=outs)
+    bx2, xo2 = guarded(T * 4 * C, torch.bfloat16)
+    mhc.post(d["x"], d["y"], d["coeffs"], out=xo2.view(T, 4, C))
+    bh2, h2 = guarded(T * C, torch.bfloat16)
+    mhc.pre(d["x"], d["coeffs"], d["gamma"], out=h2.view(T, C))
+    bc2, c2 = guarded(T * 24, torch.float32)
+    mhc.coeffs(d["x"], d["phi"], d["bias"], out=c2.view(T, 24))
+    torch.cuda.synchronize()
+    for buf in (bx, bc, bh, bq, bs, bx2, bh2, bc2):
+        assert torch.all(buf[:pad] == 77) and torch.all(buf[-pad:] == 77)
+    check_fused(inp, {k: v for k, v in outs.items()}, mx=True)
+
+
+def test_zero_tokens():
+    C = 1024
+    x = torch.empty((0, 4, C), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((0, C), dtype=torch.bfloat16, device=DEV)
+    cf = torch.empty((0, 24), dtype=torch.float32, device=DEV)
+    phi = torch.zeros((4 * C, 24), dtype=torch.float32, device=DEV)
+    b = torch.zeros(24, dtype=torch.float32, device=DEV)
+    g = torch.ones(C, dtype=torch.float32, device=DEV)
+    assert mhc.post(x, y, cf).shape == (0, 4, C)
+    assert mhc.pre(x, cf, g).shape == (0, C)
+    assert mhc.coeffs(x, phi, b).shape == (0, 24)
+    out = mhc.post_pre_fused(x, y, cf, phi, b, g, mxfp8=True)
+    torch.cuda.synchronize()
+    assert out["h_fp8"].shape == (0, C)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled tokens
+# ---------------------------------------------------------------------------
+def full_inputs(name, seed=0):
+    w = WORKLOADS[name]
+    d = make_inputs(w.T, w.C, seed=seed, rows=w.rows, device=DEV)
+    d["coeffs"] = oracle_coeffs_in(d["x"][:1024], d["phi"], d["bias"]).to(DEV)
+    d["coeffs"] = d["coeffs"].repeat((w.T + 1023) // 1024, 1)[:w.T].contiguous()
+    return d
+
+
+def sample_rows(T, extra=(), n=24, seed=1):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, size=n, replace=False).tolist()) | {0, T - 1, T - 2} | set(int(v) for v in extra)
+    return np.array(sorted(rows))
+
+
+def host_rows(d, rows):
+    idx = torch.from_numpy(rows).to(DEV)
+    return {k: (v.index_select(0, idx).cpu() if k in ("x", "y", "coeffs") else v.cpu())
+            for k, v in d.items() if isinstance(v, torch.Tensor)}
+
+
+def test_prefill_workload_sampled():
+    d = full_inputs("prefill")
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"])
+    torch.cuda.synchronize()
+    rows = sample_rows(8192, extra=d["outlier_rows"][:8].tolist())
+    inp = host_rows(d, rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    g = {k: (v.index_select(0, idx) if v is not None else None) for k, v in out.items()}
+    check_fused(inp, g)
+
+
+def test_mxfp8_workload_sampled():
+    d = full_inputs("mxfp8")
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(8192)
+    inp = host_rows(d, rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    g = {k: (v.index_select(0, idx) if v is not None else None) for k, v in out.items()}
+    check_fused(inp, g, mx=True)
+
+
+def test_decode_workload():
+    d = full_inputs("decode")
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"])
+    torch.cuda.synchronize()
+    check_fused({k: v.cpu() for k, v in d.items() if isinstance(v, torch.Tensor)}, out)
+
+
+def test_long_workload_sampled():
+    d = full_inputs("long")
+    T = d["x"].shape[0]
+    cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
+    h = mhc.pre(d["x"], d["coeffs"], d["gamma"])
+    xo = mhc.post(d["x"], d["y"], d["coeffs"])
+    torch.cuda.synchronize()
+    rows = sample_rows(T, n=16)
+    inp = host_rows(d, rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    assert_coeffs_close(f64(cf.index_select(0, idx)),
+                        O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw()))
+    assert_bf16_close(f64(h.index_select(0, idx)),
+                      O.pre(f64(inp["x"]), f64(inp["coeffs"])[:, 0:4], f64(inp["gamma"]), rmsnorm_eps=P.rmsnorm_eps))
+    _, pw, res = O.split_coeffs(f64(inp["coeffs"]))
+    assert np.array_equal(f64(xo.index_select(0, idx)), O.post(f64(inp["x"]), f64(inp["y"]), pw, res))
+    del xo, h
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"])
+    torch.cuda.synchronize()
+    g = {k: (v.index_select(0, idx) if v is not None else None) for k, v in out.items()}
+    check_fused(inp, g)
