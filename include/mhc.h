@@ -65,7 +65,7 @@ extern "C" {
 #define MHC_NUM_ROUTES 4
 #define MHC_NUM_COEFFS 24
 #define MHC_MAX_TOKENS (1 << 20)  /* [P2] review: the kernel's token limit 2^20 */
-#define MHC_MAX_HIDDEN 65536
+#define MHC_MAX_HIDDEN 16384 /* keeps a row within 128 co-resident workgroups */
 #define MHC_MXFP8_BLOCK 32
 
 /* Scalars of the method, passed by name ([P2] review warns against a

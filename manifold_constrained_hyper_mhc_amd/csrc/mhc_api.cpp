@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/mhc.h"
+#include "mhc.h"
 #include "mhc_internal.h"
 
 namespace {
@@ -81,7 +81,15 @@ int check_tensors(const Span* in, int nin, const Span* out, int nout) {
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The split kernel's reduce-scatter stages at most ceil(M/S) * S * 34 words
+// per workgroup (18 per thread) for at most 8 tokens; every plan must fit.
+bool plan_fits(const mhc::Plan& p) {
+  const int64_t ntok = (p.m + p.s - 1) / p.s;
+  return ntok <= 8 && ntok * p.s * mhc::kPartVals <= 18 * 256;
+}
+
 int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
+  if (!plan_fits(plan)) return MHC_ERR_SHAPE;
   if (ws == nullptr) return MHC_ERR_WORKSPACE;
   if (((uintptr_t)ws & 255u) != 0) return MHC_ERR_WORKSPACE;
   if (bytes < plan.total) return MHC_ERR_WORKSPACE;
@@ -92,11 +100,11 @@ int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
 
 namespace mhc {
 
-// Tile shape: 16 tokens x 512 channels per workgroup (RB = 1, CW = 128).
+// Tile shape: 64 tokens x 128 channels per workgroup (RB = 4, CW = 32).
 Plan make_plan(int64_t T, int64_t C) {
   Plan p;
-  p.rb = 1;
-  p.cw = 128;
+  p.rb = 4;
+  p.cw = 32;
   p.m = 16 * p.rb;
   p.cc = 4 * p.cw;
   p.s = (int)(C / p.cc);
@@ -104,14 +112,14 @@ Plan make_plan(int64_t T, int64_t C) {
   size_t off = 0;
   p.off_err = off;
   off += 256;
-  p.off_cnt = off;
+  p.off_epoch = off;
   off = round256(off + (size_t)p.tiles * 4);
-  p.off_flag = off;
+  p.off_dep = off;
   off = round256(off + (size_t)p.tiles * 4);
   p.off_pub = off;
-  off = round256(off + (size_t)p.tiles * p.m * 4 * sizeof(float));
+  off = round256(off + (size_t)p.tiles * p.m * 4 * sizeof(uint64_t));
   p.off_part = off;
-  off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(float));
+  off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(uint64_t));
   p.off_phi = off;
   off = round256(off + phi_packed_bytes(C));
   p.total = off;
@@ -127,10 +135,10 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   memset(&a, 0, sizeof(a));
   char* base = static_cast<char*>(ws);
   a.err = reinterpret_cast<uint32_t*>(base + plan.off_err);
-  a.cnt = reinterpret_cast<uint32_t*>(base + plan.off_cnt);
-  a.flag = reinterpret_cast<uint32_t*>(base + plan.off_flag);
-  a.publish = reinterpret_cast<float*>(base + plan.off_pub);
-  a.partials = reinterpret_cast<float*>(base + plan.off_part);
+  a.epoch = reinterpret_cast<uint32_t*>(base + plan.off_epoch);
+  a.dep = reinterpret_cast<uint32_t*>(base + plan.off_dep);
+  a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
+  a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.T = T;
   a.C = (int)C;
   a.S = plan.s;

@@ -21,14 +21,14 @@ struct Scalars {
 // channels of every route per workgroup; a token's row is spread over
 // S = C / CC workgroups whose partial sums meet in the workspace.
 struct Plan {
-  int rb = 2;      // 16-token MFMA row blocks per workgroup
-  int cw = 64;     // channels per wave
-  int m = 32;      // tokens per tile
-  int cc = 256;    // channels per workgroup
+  int rb = 4;      // 16-token MFMA row blocks per workgroup
+  int cw = 32;     // channels per wave
+  int m = 64;      // tokens per tile
+  int cc = 128;    // channels per workgroup
   int s = 1;       // workgroups per row
   int64_t tiles = 0;
   // workspace layout (byte offsets)
-  size_t off_err = 0, off_cnt = 0, off_flag = 0, off_pub = 0, off_part = 0, off_phi = 0, total = 0;
+  size_t off_err = 0, off_epoch = 0, off_dep = 0, off_pub = 0, off_part = 0, off_phi = 0, total = 0;
 };
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
@@ -50,10 +50,10 @@ struct SplitArgs {
   uint16_t* h;
   uint8_t* h_fp8;
   uint8_t* h_scale;
-  float* partials;
-  uint32_t* cnt;
-  uint32_t* flag;
-  float* publish;
+  uint64_t* partials;  // [tiles][S][M][34] tagged words
+  uint32_t* epoch;     // [tiles]
+  uint32_t* dep;       // [tiles]
+  uint64_t* publish;   // [tiles][M][4] tagged words
   uint32_t* err;
   int64_t T;
   int C;

@@ -15,11 +15,14 @@ namespace mhc {
 // Projection packing.  The flattened row index k = route*C + c runs over 4C
 // rows of phi [4C][24].  Each fp32 element is split into three bf16 terms
 // (hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid); the sum is v
-// exactly for |v| >= 2^-100), giving 72 columns, padded to 80 = five MFMA
-// column blocks:
+// exactly for |v| >= 2^-100).  Five MFMA column blocks of 16 per 32 rows:
 //   block 0: hi  of logits 0..15        block 3: hi  of 16..23 | mid of 16..23
 //   block 1: mid of logits 0..15        block 4: lo  of 16..23 | zero
 //   block 2: lo  of logits 0..15
+// Blocks 0-2 accumulate into one MFMA accumulator (x'*hi + x'*mid + x'*lo:
+// every product is exact, the sum is an fp32 accumulation) and blocks 3-4
+// into a second one whose columns 0..7 hold hi+lo and 8..15 mid of logits
+// 16..23.
 // Packed layout: [k/32][block][lane 0..63][8 bf16]; lane l of a fragment
 // holds rows k = 32q + 8*(l/16) + e, e = 0..7, of column 16*block + l%16,
 // which is the B-operand layout of v_mfma_f32_16x16x32_bf16.
@@ -64,46 +67,123 @@ __global__ __launch_bounds__(256) void k_pack_phi(const float* __restrict__ phi,
 // ===========================================================================
 // Split-row kernel.
 //
-// Workgroup = 4 waves; blockIdx = tile * S + split.  The tile holds
+// Workgroup = 4 waves; blockIdx = tile * S + split.  A tile holds
 // M = 16*RB tokens; the workgroup owns channels [split*CC, split*CC + CC) of
-// all 4 routes, wave w the CW channels starting at split*CC + w*CW.
-// Lane l serves token 16*r + l%16 of row block r and, in each 32-channel
-// step, channels 8*(l/16) .. +8: this is the A-operand layout of the MFMA,
-// so the bf16 stream chunk a lane loads (or the x' it computes) is its MFMA
-// operand without any shuffle.
+// all 4 routes and wave w the CW channels from split*CC + w*CW.  Lane l
+// serves token 16*r + l%16 of row block r (r < RB) and, in each 32-channel
+// step, channels 8*(l/16) .. +8.  That is the A-operand layout of
+// v_mfma_f32_16x16x32_bf16, so the bf16 chunk a lane loads (or the x' it
+// computes) is its MFMA operand as is, and one projection fragment serves
+// RB row blocks.
 //
-// Phase A  load x (and y, post/res), compute x' = post chain (bf16), store
-//          x', accumulate the route Gram matrix (fused) or the sum of
-//          squares (coeffs) and the 24 projections on the matrix cores.
-// Reduce   fold hi+mid+lo, sum the 4 waves in LDS, write the tile's partial
-//          [M][34] to the workspace and arrive on the tile counter.  The
-//          last workgroup to arrive sums the S partials in split order
-//          (deterministic), finalises the coefficients of the M tokens and,
-//          in the fused modes, publishes pre'_i * r_h (the RMSNorm scale of
-//          g = sum_i pre'_i x'_i, taken from the Gram matrix:
-//          sum_c g_c^2 = pre'^T G pre') and raises the tile flag.
-// Phase C  (fused) the other workgroups wait for the flag, then every
-//          workgroup writes h = (sum_i q_i x'_i) * gamma from the x' still in
-//          registers, as bf16 and/or MXFP8.
+// Phase A  load x (and y; post/res staged in LDS), compute x' with the post
+//          chain, round to bf16, store it and keep it in registers;
+//          accumulate the route Gram matrix of x' (fused; its trace is the
+//          sum of squares) or the sum of squares of x (coeffs), and the 24
+//          projections on the matrix cores.
+// Reduce   fold hi+mid+lo, sum the 4 waves in LDS and write the tile's
+//          partial [M][34] to the workspace.  Barrier 1 over the tile's S
+//          workgroups; then workgroup `split` reduces tokens
+//          split, split+S, ... (split order, so the sums are deterministic),
+//          finalises their coefficients with one wave per token (Sinkhorn on
+//          16 lanes) and, in the fused modes, publishes pre'_i * r_h, where
+//          r_h is the RMSNorm scale of g = sum_i pre'_i x'_i obtained from
+//          the Gram matrix: sum_c g_c^2 = pre'^T G pre'.  Barrier 2 (fused).
+// Phase C  (fused) h = (sum_i q_i x'_i) * gamma from the registers, as bf16
+//          and/or MXFP8.
 //
-// Progress: workgroups are dispatched in blockIdx order, so a waiting
-// workgroup's partners are either running or will be dispatched once earlier
-// (complete) tiles retire.  The wait is bounded anyway; on expiry it sets the
-// workspace error word and continues.
+// Communication between workgroups uses agent-coherent 64-bit words that
+// carry a value and a tag: (float bits) | (tag << 32).  The tag of a launch
+// is the tile's epoch + 1, read when the workgroup starts; a reader polls
+// the words it needs until their tags match, so no counter sits on the
+// critical path and no cache write-back or invalidation is needed (agent
+// scope accesses bypass the per-XCD caches, and an aligned 64-bit access is
+// single-copy atomic, so a value is never seen with the wrong tag).  The
+// last workgroup of a tile to leave (a counter off the critical path) bumps
+// the epoch, so every launch uses a fresh tag and a zero-filled workspace
+// is a valid start.  Every word a launch reads is written in that launch.
+// Workgroups are dispatched in blockIdx order, so every workgroup a waiting
+// one depends on is running or will run once earlier tiles retire; the waits
+// are bounded anyway and set the workspace error word on expiry.
 // ===========================================================================
-constexpr uint32_t kSpinLimit = 1u << 24;
+constexpr uint32_t kSpinLimit = 1u << 22;
+// Reduce-scatter bounds: a workgroup owns at most ceil(M/S) <= 8 tokens
+// (M = 64, S >= 8) and gathers at most (M + S - 1) * 34 <= 18 * 256 words.
+constexpr int kMaxTileTokensPerGroup = 8;
+constexpr int kGatherPerThread = 18;
+
+__device__ __forceinline__ void tagged_store(uint64_t* p, float v, uint32_t tag) {
+  const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tagged_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// Wait until the word at p carries `tag`; returns its value.
+__device__ __forceinline__ float tagged_wait(const uint64_t* p, uint32_t tag, uint32_t* err) {
+  uint64_t w = tagged_load(p);
+  uint32_t it = 0;
+  while ((uint32_t)(w >> 32) != tag) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++it > kSpinLimit) {
+      __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    w = tagged_load(p);
+  }
+  return tagged_value(w);
+}
+
+// Coefficients of one token on one wave.  sums: 24 projections, then the
+// Gram matrix (fused) or the sum of squares (coeffs).  Lanes 0..15 carry
+// res[j][i] (j = lane/4, i = lane%4), lanes 16..23 pre/post.  Returns in
+// every lane the value of coefficient `slot(lane)`; q gets pre_i * r_h.
+template <bool FUSED>
+__device__ __forceinline__ float finalize_wave(const float* sums, const float* bias, int C, const Scalars& sc,
+                                               int lane, float* q) {
+  const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
+  const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
+  const int li = lane < 16 ? 8 + lane : (lane < 24 ? lane - 16 : 0);
+  const float l = r * sums[li] + bias[li];
+  const float sg = 1.0f / (1.0f + expf(-l));
+  const float pp = (lane >= 20 && lane < 24) ? sc.hc_post_scale * sg : sg;
+  float v = expf(l);
+  const float eps = sc.sinkhorn_eps;
+  for (int it = 0; it < sc.sinkhorn_iters; ++it) {
+    float rs = v + __shfl_xor(v, 1);
+    rs += __shfl_xor(rs, 2);
+    v = v / (rs + eps);
+    float cs = v + __shfl_xor(v, 4);
+    cs += __shfl_xor(cs, 8);
+    v = v / (cs + eps);
+  }
+  if constexpr (FUSED) {
+    const float p[4] = {__shfl(pp, 16), __shfl(pp, 17), __shfl(pp, 18), __shfl(pp, 19)};
+    const float gq = gram_quadratic(sums + 24, p);
+    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
+    q[0] = p[0] * rh;
+    q[1] = p[1] * rh;
+    q[2] = p[2] * rh;
+    q[3] = p[3] * rh;
+  }
+  return lane < 16 ? v : pp;
+}
 
 template <int MODE, int RB, int CW>
-__global__ __launch_bounds__(256) void k_split(const SplitArgs a) {
+__global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
   constexpr bool FUSED = MODE != kModeCoeffs;
   constexpr bool MX = MODE == kModeFusedMx;
   constexpr int W = 4, M = 16 * RB, NS = CW / 32, CC = W * CW;
   constexpr int NV = kPartVals;
+  constexpr int NG = FUSED ? kGram : 1;
 
   __shared__ float red[W][M][NV];
-  __shared__ float fin[M][NV];
-  __shared__ float qs[M][4];
-  __shared__ uint32_t s_last, s_f0;
+  __shared__ float cfs[FUSED ? M : 1][20];
+  __shared__ float fin[kMaxTileTokensPerGroup][NV];
+  __shared__ float qs[FUSED ? M : 1][4];
+  __shared__ uint32_t s_tag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
@@ -113,10 +193,24 @@ __global__ __launch_bounds__(256) void k_split(const SplitArgs a) {
   const int C = a.C;
   const int cw0 = split * CC + wave * CW;
 
+  if (tid == 0)
+    s_tag = __hip_atomic_load(a.epoch + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+
   // ---------------- phase A: loads ----------------
+  if constexpr (FUSED) {
+    for (int idx = tid; idx < M * 5; idx += 256) {
+      const int m = idx / 5, k = idx % 5;
+      const int64_t t = tok0 + m;
+      const float4 v = t < a.T ? reinterpret_cast<const float4*>(a.coeffs_in + t * kCoeffs)[1 + k]
+                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      cfs[m][4 * k] = v.x;
+      cfs[m][4 * k + 1] = v.y;
+      cfs[m][4 * k + 2] = v.z;
+      cfs[m][4 * k + 3] = v.w;
+    }
+  }
   u32x4_t xf[RB][NS][4];
   u32x4_t yv[RB][NS];
-  float pw[RB][4], rs[RB][16];
   bool valid[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
@@ -132,94 +226,7 @@ __global__ __launch_bounds__(256) void k_split(const SplitArgs a) {
       if constexpr (FUSED)
         yv[r][s] = valid[r] ? ld16_stream(a.y + t * (int64_t)C + c) : u32x4_t{0, 0, 0, 0};
     }
-    if constexpr (FUSED) {
-      const float* cf = a.coeffs_in + (valid[r] ? t : 0) * kCoeffs + 4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pw[r][k] = valid[r] ? cf[k] : 0.0f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) rs[r][k] = valid[r] ? cf[4 + k] : 0.0f;
-    }
   }
-
-  // ---------------- phase A: post, statistics, projection ----------------
-  constexpr int NG = FUSED ? kGram : 1;
-  float st[RB][NG];
-  f32x4_t acc[RB][kPackBlocks];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-#pragma unroll
-    for (int k = 0; k < NG; ++k) st[r][k] = 0.0f;
-#pragma unroll
-    for (int b = 0; b < kPackBlocks; ++b) acc[r][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      float xv[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) unpack8(xf[r][s][i], xv[i]);
-      if constexpr (FUSED) {
-        float yy[8];
-        unpack8(yv[r][s], yy);
-        float o[4][8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            o[j][e] = post_chain(pw[r][j], yy[e], &rs[r][4 * j], xv[0][e], xv[1][e], xv[2][e], xv[3][e]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xf[r][s][j] = pack8(o[j]);
-        if (valid[r]) {
-          const int64_t t = tok0 + r * 16 + n16;
-          uint16_t* xo = a.x_out + t * (int64_t)(4 * C) + cw0 + s * 32 + g * 8;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, xf[r][s][j]);
-        }
-        // statistics of the bf16 x'
-#pragma unroll
-        for (int j = 0; j < 4; ++j) unpack8(xf[r][s][j], xv[j]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          st[r][0] = __builtin_fmaf(xv[0][e], xv[0][e], st[r][0]);
-          st[r][1] = __builtin_fmaf(xv[1][e], xv[1][e], st[r][1]);
-          st[r][2] = __builtin_fmaf(xv[2][e], xv[2][e], st[r][2]);
-          st[r][3] = __builtin_fmaf(xv[3][e], xv[3][e], st[r][3]);
-          st[r][4] = __builtin_fmaf(xv[0][e], xv[1][e], st[r][4]);
-          st[r][5] = __builtin_fmaf(xv[0][e], xv[2][e], st[r][5]);
-          st[r][6] = __builtin_fmaf(xv[0][e], xv[3][e], st[r][6]);
-          st[r][7] = __builtin_fmaf(xv[1][e], xv[2][e], st[r][7]);
-          st[r][8] = __builtin_fmaf(xv[1][e], xv[3][e], st[r][8]);
-          st[r][9] = __builtin_fmaf(xv[2][e], xv[3][e], st[r][9]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st[r][0] = __builtin_fmaf(xv[i][e], xv[i][e], st[r][0]);
-      }
-    }
-    // projection: 4 routes x 5 column blocks per 32-channel step
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t kstep = ((int64_t)j * C + cw0 + s * 32) >> 5;
-      const u32x4_t* bp = reinterpret_cast<const u32x4_t*>(a.phi_packed) + kstep * (kPackBlocks * kWave) + lane;
-      u32x4_t bfrag[kPackBlocks];
-#pragma unroll
-      for (int b = 0; b < kPackBlocks; ++b) bfrag[b] = bp[b * kWave];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xf[r][s][j]);
-#pragma unroll
-        for (int b = 0; b < kPackBlocks; ++b)
-          acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bfrag[b]),
-                                                             acc[r][b], 0, 0, 0);
-      }
-    }
-  }
-
-  // gamma for phase C, fetched while the reduction runs
   float gm[NS][8];
   if constexpr (FUSED) {
 #pragma unroll
@@ -230,161 +237,257 @@ __global__ __launch_bounds__(256) void k_split(const SplitArgs a) {
       gm[s][4] = g1.x; gm[s][5] = g1.y; gm[s][6] = g1.z; gm[s][7] = g1.w;
     }
   }
+  __syncthreads();  // cfs, s_tag
+  const uint32_t tag = s_tag;
 
-  // ---------------- reduce within the workgroup ----------------
+  // ---------------- phase A: post and statistics ----------------
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    float st[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) st[k] = 0.0f;
+    float pw[4], rs[16];
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pw[k] = cfs[r * 16 + n16][k];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) rs[k] = cfs[r * 16 + n16][4 + k];
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (FUSED) {
+        // two channels at a time: unpack, post chain, round, statistics
+        u32x4_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float xl[4] = {bf16_lo(xf[r][s][0][k]), bf16_lo(xf[r][s][1][k]), bf16_lo(xf[r][s][2][k]),
+                               bf16_lo(xf[r][s][3][k])};
+          const float xh[4] = {bf16_hi(xf[r][s][0][k]), bf16_hi(xf[r][s][1][k]), bf16_hi(xf[r][s][2][k]),
+                               bf16_hi(xf[r][s][3][k])};
+          const float yl = bf16_lo(yv[r][s][k]), yh = bf16_hi(yv[r][s][k]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j][k] = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
+                                  post_chain(pw[j], yh, &rs[4 * j], xh[0], xh[1], xh[2], xh[3]));
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const float v0 = h2 ? bf16_hi(o[0][k]) : bf16_lo(o[0][k]);
+            const float v1 = h2 ? bf16_hi(o[1][k]) : bf16_lo(o[1][k]);
+            const float v2 = h2 ? bf16_hi(o[2][k]) : bf16_lo(o[2][k]);
+            const float v3 = h2 ? bf16_hi(o[3][k]) : bf16_lo(o[3][k]);
+            st[0] = __builtin_fmaf(v0, v0, st[0]);
+            st[1] = __builtin_fmaf(v1, v1, st[1]);
+            st[2] = __builtin_fmaf(v2, v2, st[2]);
+            st[3] = __builtin_fmaf(v3, v3, st[3]);
+            st[4] = __builtin_fmaf(v0, v1, st[4]);
+            st[5] = __builtin_fmaf(v0, v2, st[5]);
+            st[6] = __builtin_fmaf(v0, v3, st[6]);
+            st[7] = __builtin_fmaf(v1, v2, st[7]);
+            st[8] = __builtin_fmaf(v1, v3, st[8]);
+            st[9] = __builtin_fmaf(v2, v3, st[9]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xf[r][s][j] = o[j];
+        if (valid[r]) {
+          const int64_t t = tok0 + r * 16 + n16;
+          uint16_t* xo = a.x_out + t * (int64_t)(4 * C) + cw0 + s * 32 + g * 8;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, xf[r][s][j]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float vl = bf16_lo(xf[r][s][i][k]), vh = bf16_hi(xf[r][s][i][k]);
+            st[0] = __builtin_fmaf(vl, vl, st[0]);
+            st[0] = __builtin_fmaf(vh, vh, st[0]);
+          }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const float v = sum_groups(st[k]);
+      if (g == 0) red[wave][r * 16 + n16][24 + k] = v;
+    }
+  }
+
+  // ---------------- phase A: projection on the matrix cores ----------------
+  f32x4_t acc[RB][2];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    acc[r][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    acc[r][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_barrier(0);  // keep one route's fragments live at a time
+      const int64_t kstep = ((int64_t)j * C + cw0 + s * 32) >> 5;
+      const u32x4_t* bp = reinterpret_cast<const u32x4_t*>(a.phi_packed) + kstep * (kPackBlocks * kWave) + lane;
+      u32x4_t bfrag[kPackBlocks];
+#pragma unroll
+      for (int b = 0; b < kPackBlocks; ++b) bfrag[b] = bp[b * kWave];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xf[r][s][j]);
+#pragma unroll
+        for (int b = 0; b < kPackBlocks; ++b)
+          acc[r][b < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              av, __builtin_bit_cast(bf16x8_t, bfrag[b]), acc[r][b < 3 ? 0 : 1], 0, 0, 0);
+      }
+    }
+  }
   // MFMA output: lane l holds column l%16 of rows 4*(l/16)+e, e = 0..3.
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float lo16 = (acc[r][0][e] + acc[r][1][e]) + acc[r][2][e];
-      const float v3 = acc[r][3][e], v4 = acc[r][4][e];
-      const float mid = __shfl_xor(v3, 8);
+      const float v1 = acc[r][1][e];
+      const float mid = __shfl_xor(v1, 8);
       const int row = r * 16 + 4 * g + e;
-      red[wave][row][n16] = lo16;
-      if (n16 < 8) red[wave][row][16 + n16] = (v3 + mid) + v4;
-    }
-#pragma unroll
-    for (int k = 0; k < NG; ++k) {
-      const float v = sum_groups(st[r][k]);
-      if (g == 0) red[wave][r * 16 + n16][24 + k] = v;
+      red[wave][row][n16] = acc[r][0][e];
+      if (n16 < 8) red[wave][row][16 + n16] = v1 + mid;
     }
   }
   __syncthreads();
-  float* flat_fin = &fin[0][0];
+
+  // ---------------- tile partial -> workspace ----------------
+  constexpr int NVU = FUSED ? NV : 25;
+  uint64_t* part = a.partials + (int64_t)blockIdx.x * (M * NV);
   const float* flat_red = &red[0][0][0];
-  constexpr int NVU = FUSED ? NV : 25;  // values in use per token
   for (int idx = tid; idx < M * NV; idx += 256) {
     if (idx % NV >= NVU) continue;
-    flat_fin[idx] = ((flat_red[idx] + flat_red[M * NV + idx]) + flat_red[2 * M * NV + idx]) +
-                    flat_red[3 * M * NV + idx];
+    tagged_store(part + idx, ((flat_red[idx] + flat_red[M * NV + idx]) + flat_red[2 * M * NV + idx]) +
+                                 flat_red[3 * M * NV + idx], tag);
   }
 
-  bool last = true;
-  uint32_t f0 = 0;
-  if (S > 1) {
-    float* part = a.partials + (int64_t)blockIdx.x * (M * NV);
-    for (int idx = tid; idx < M * NV; idx += 256) part[idx] = flat_fin[idx];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t fl = __hip_atomic_load(&a.flag[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t old = __hip_atomic_fetch_add(&a.cnt[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      s_f0 = fl;
-      s_last = (old == (uint32_t)(S - 1)) ? 1u : 0u;
+  // ---------------- reduce-scatter: tokens split, split+S, ... ----------------
+  // Token m of the tile is reduced by workgroup m % S, which owns
+  // ntok <= ceil(M/S) tokens.  Their ntok x S x 34 tagged words are
+  // gathered with every load in flight (<= kGatherPerThread per thread),
+  // the stale ones re-polled together, staged in LDS (over the per-wave
+  // partial buffer, no longer needed) and summed in split order.
+  const uint64_t* tp = a.partials + (int64_t)tile * S * (M * NV);
+  const int ntok = split < M ? (M - split + S - 1) / S : 0;
+  if (ntok > 0) {
+    float* stage = &red[0][0][0];
+    const int nwords = ntok * S * NV;
+    uint64_t w[kGatherPerThread];
+#pragma unroll
+    for (int q = 0; q < kGatherPerThread; ++q) {
+      const int u = tid + 256 * q;
+      const int v = u % NV, rr = u / NV;
+      const int sp = rr % S, kk = rr / S;
+      w[q] = (u < nwords && v < NVU) ? tagged_load(tp + ((int64_t)sp * M + split + kk * S) * NV + v)
+                                     : ((uint64_t)tag << 32);
     }
-    __syncthreads();
-    last = s_last != 0;
-    f0 = s_f0;
-    if (last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      const float* tp = a.partials + (int64_t)tile * S * (M * NV);
-      for (int idx = tid; idx < M * NV; idx += 256) {
-        if (idx % NV >= NVU) continue;
-        float v = 0.0f;
-        for (int sp = 0; sp < S; ++sp) v += tp[(int64_t)sp * (M * NV) + idx];
-        flat_fin[idx] = v;
+    uint32_t it = 0;
+    for (;;) {
+      bool stale = false;
+#pragma unroll
+      for (int q = 0; q < kGatherPerThread; ++q) stale |= (uint32_t)(w[q] >> 32) != tag;
+      if (!stale) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++it > kSpinLimit) {
+        __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+#pragma unroll
+      for (int q = 0; q < kGatherPerThread; ++q) {
+        const int u = tid + 256 * q;
+        const int v = u % NV, rr = u / NV;
+        const int sp = rr % S, kk = rr / S;
+        if ((uint32_t)(w[q] >> 32) != tag) w[q] = tagged_load(tp + ((int64_t)sp * M + split + kk * S) * NV + v);
       }
     }
-  }
-
-  if (last) {
+#pragma unroll
+    for (int q = 0; q < kGatherPerThread; ++q) {
+      const int u = tid + 256 * q;
+      if (u < nwords) stage[u] = tagged_value(w[q]);
+    }
     __syncthreads();
-    if (tid < M) {
-      const int64_t t = tok0 + tid;
-      float ss;
-      if constexpr (FUSED)
-        ss = ((fin[tid][24] + fin[tid][25]) + fin[tid][26]) + fin[tid][27];
-      else
-        ss = fin[tid][24];
-      float out[kCoeffs];
-      finalize_coeffs(&fin[tid][0], ss, a.bias, C, a.sc, out);
-      if (t < a.T) {
-        float4* co = reinterpret_cast<float4*>(a.coeffs_out + t * kCoeffs);
-#pragma unroll
-        for (int k = 0; k < 6; ++k) co[k] = make_float4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
-      }
-      if constexpr (FUSED) {
-        const float q = gram_quadratic(&fin[tid][24], out);
-        const float rh = 1.0f / sqrtf(q / (float)C + a.sc.rmsnorm_eps);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qs[tid][i] = out[i] * rh;
-          if (S > 1) a.publish[((int64_t)tile * M + tid) * 4 + i] = out[i] * rh;
+    for (int pidx = tid; pidx < ntok * NV; pidx += 256) {
+      const int kk = pidx / NV, v = pidx % NV;
+      float acc = 0.0f;
+      if (v < NVU)
+        for (int sp = 0; sp < S; ++sp) acc += stage[(kk * S + sp) * NV + v];
+      fin[kk][v] = acc;
+    }
+    __syncthreads();
+    for (int k0 = 0; k0 < ntok; k0 += W) {
+      const int kk = k0 + wave;
+      if (kk < ntok) {
+        const int m = split + kk * S;
+        float q[4];
+        const float cv = finalize_wave<FUSED>(fin[kk], a.bias, C, a.sc, lane, q);
+        const int64_t t = tok0 + m;
+        if (t < a.T && lane < 24) a.coeffs_out[t * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
+        if constexpr (FUSED) {
+          if (lane < 4) tagged_store(a.publish + ((int64_t)tile * M + m) * 4 + lane, q[lane], tag);
         }
       }
     }
-    if (S > 1) {
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) {
-        __hip_atomic_store(&a.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if constexpr (FUSED)
-          __hip_atomic_store(&a.flag[tile], f0 + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-  } else {
-    if constexpr (!FUSED) return;  // coeffs: only the last workgroup writes
-    if (tid == 0) {
-      uint32_t it = 0;
-      while (__hip_atomic_load(&a.flag[tile], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == f0) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++it > kSpinLimit) {
-          __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    for (int idx = tid; idx < M * 4; idx += 256) (&qs[0][0])[idx] = a.publish[(int64_t)tile * M * 4 + idx];
-    __syncthreads();
   }
+
+  if constexpr (FUSED) {
+    for (int idx = tid; idx < M * 4; idx += 256)
+      (&qs[0][0])[idx] = tagged_wait(a.publish + (int64_t)tile * M * 4 + idx, tag, a.err);
+  }
+  // leave: the last workgroup of the tile moves the epoch on
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(a.dep + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)S - 1u) {
+      __hip_atomic_store(a.dep + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.epoch + tile, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if constexpr (!FUSED) return;
 
   // ---------------- phase C: h = (sum_i q_i x'_i) * gamma ----------------
-  if constexpr (FUSED) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int64_t t = tok0 + r * 16 + n16;
-      const float q0 = qs[r * 16 + n16][0], q1 = qs[r * 16 + n16][1];
-      const float q2 = qs[r * 16 + n16][2], q3 = qs[r * 16 + n16][3];
+  for (int r = 0; r < RB; ++r) {
+    const int64_t t = tok0 + r * 16 + n16;
+    const float q0 = qs[r * 16 + n16][0], q1 = qs[r * 16 + n16][1];
+    const float q2 = qs[r * 16 + n16][2], q3 = qs[r * 16 + n16][3];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int c = cw0 + s * 32 + g * 8;
-        float xv[4][8];
+    for (int s = 0; s < NS; ++s) {
+      const int c = cw0 + s * 32 + g * 8;
+      float xv[4][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) unpack8(xf[r][s][i], xv[i]);
-        float hv[8];
+      for (int i = 0; i < 4; ++i) unpack8(xf[r][s][i], xv[i]);
+      float hv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float v = q0 * xv[0][e];
-          v = __builtin_fmaf(q1, xv[1][e], v);
-          v = __builtin_fmaf(q2, xv[2][e], v);
-          v = __builtin_fmaf(q3, xv[3][e], v);
-          hv[e] = v * gm[s][e];
+      for (int e = 0; e < 8; ++e) {
+        float v = q0 * xv[0][e];
+        v = __builtin_fmaf(q1, xv[1][e], v);
+        v = __builtin_fmaf(q2, xv[2][e], v);
+        v = __builtin_fmaf(q3, xv[3][e], v);
+        hv[e] = v * gm[s][e];
+      }
+      const u32x4_t hb = pack8(hv);
+      if (a.h != nullptr && valid[r]) st16_stream(a.h + t * (int64_t)C + c, hb);
+      if constexpr (MX) {
+        float hr[8];
+        unpack8(hb, hr);
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
+        amax = max_groups(amax);
+        const int ex = mx_scale_exponent(amax);
+        const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w0 |= e4m3_code(hr[e] * scale) << (8 * e);
+          w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
         }
-        const u32x4_t hb = pack8(hv);
-        if (a.h != nullptr && valid[r]) st16_stream(a.h + t * (int64_t)C + c, hb);
-        if constexpr (MX) {
-          float hr[8];
-          unpack8(hb, hr);
-          float amax = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
-          amax = max_groups(amax);
-          const int ex = mx_scale_exponent(amax);
-          const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
-          uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w0 |= e4m3_code(hr[e] * scale) << (8 * e);
-            w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
-          }
-          if (valid[r]) {
-            *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + c) = u32x2_t{w0, w1};
-            if (g == 0) a.h_scale[t * (int64_t)(C / 32) + ((cw0 + s * 32) >> 5)] = (uint8_t)(ex + 127);
-          }
+        if (valid[r]) {
+          *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + c) = u32x2_t{w0, w1};
+          if (g == 0) a.h_scale[t * (int64_t)(C / 32) + ((cw0 + s * 32) >> 5)] = (uint8_t)(ex + 127);
         }
       }
     }
@@ -532,7 +635,9 @@ hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s) {
 template <int MODE>
 static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(p.tiles * p.s)), block(256);
-  if (p.rb == 2 && p.cw == 64) {
+  if (p.rb == 4 && p.cw == 32) {
+    k_split<MODE, 4, 32><<<grid, block, 0, s>>>(a);
+  } else if (p.rb == 2 && p.cw == 64) {
     k_split<MODE, 2, 64><<<grid, block, 0, s>>>(a);
   } else if (p.rb == 1 && p.cw == 128) {
     k_split<MODE, 1, 128><<<grid, block, 0, s>>>(a);
