@@ -81,11 +81,13 @@ int check_tensors(const Span* in, int nin, const Span* out, int nout) {
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// The split kernel's reduce-scatter stages at most ceil(M/S) * S * 34 words
-// per workgroup (18 per thread) for at most 8 tokens; every plan must fit.
+// Bounds of the split kernel's reduce-scatter (ntok * 34 partial words per
+// workgroup, runs of at most kRunMax splits per thread); the tile count must
+// fit the fixed leave counters.
 bool plan_fits(const mhc::Plan& p) {
   const int64_t ntok = (p.m + p.s - 1) / p.s;
-  return ntok <= 8 && ntok * p.s * mhc::kPartVals <= 18 * 256;
+  if (ntok > 8 || ntok * mhc::kPartVals > 256) return false;
+  return mhc::plan_run_len(p) <= mhc::kRunMax && p.m == 32 && p.tiles <= mhc::kMaxTiles;
 }
 
 int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
@@ -100,22 +102,24 @@ int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
 
 namespace mhc {
 
-// Tile shape: 64 tokens x 128 channels per workgroup (RB = 4, CW = 32).
+// Tile shape: 32 tokens x 128 channels (of every route) per workgroup.
 Plan make_plan(int64_t T, int64_t C) {
   Plan p;
-  p.rb = 4;
-  p.cw = 32;
-  p.m = 16 * p.rb;
-  p.cc = 4 * p.cw;
+  p.m = 32;
+  p.cc = 128;
   p.s = (int)(C / p.cc);
   p.tiles = (T + p.m - 1) / p.m;
-  size_t off = 0;
-  p.off_err = off;
-  off += 256;
-  p.off_epoch = off;
-  off = round256(off + (size_t)p.tiles * 4);
-  p.off_dep = off;
-  off = round256(off + (size_t)p.tiles * 4);
+  // stage delays of the reduce (d1) and the pre step (d2) behind a tile's
+  // phase A: a few stages absorb the spread of workgroup progress; a short
+  // launch keeps them short so that its few tiles are not delayed
+  if (p.tiles >= 64) {
+    p.d1 = 12;
+    p.d2 = 16;
+  } else {
+    p.d1 = 1;
+    p.d2 = 2;
+  }
+  size_t off = kWsHeaderBytes;
   p.off_pub = off;
   off = round256(off + (size_t)p.tiles * p.m * 4 * sizeof(uint64_t));
   p.off_part = off;
@@ -134,14 +138,18 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   mhc::SplitArgs a;
   memset(&a, 0, sizeof(a));
   char* base = static_cast<char*>(ws);
-  a.err = reinterpret_cast<uint32_t*>(base + plan.off_err);
-  a.epoch = reinterpret_cast<uint32_t*>(base + plan.off_epoch);
-  a.dep = reinterpret_cast<uint32_t*>(base + plan.off_dep);
+  a.err = reinterpret_cast<uint32_t*>(base + mhc::kWsErr);
+  a.epoch = reinterpret_cast<uint32_t*>(base + mhc::kWsEpoch);
+  a.tiles_done = reinterpret_cast<uint32_t*>(base + mhc::kWsTilesDone);
+  a.dep = reinterpret_cast<uint32_t*>(base + mhc::kWsDep);
   a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.T = T;
+  a.tiles = (uint32_t)plan.tiles;
   a.C = (int)C;
   a.S = plan.s;
+  a.d1 = plan.d1;
+  a.d2 = plan.d2;
   a.sc = scalars(p);
   return a;
 }

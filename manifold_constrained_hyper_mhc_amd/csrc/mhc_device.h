@@ -51,6 +51,13 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cas
 __device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
+// LAST_USE: a non-temporal load (the line is not read again); otherwise a
+// plain load that leaves the line in the caches for a later reader.
+template <bool LAST_USE>
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  if constexpr (LAST_USE) return ld16_stream(p);
+  return ld16(p);
+}
 __device__ __forceinline__ void st16_stream(void* p, u32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
 }

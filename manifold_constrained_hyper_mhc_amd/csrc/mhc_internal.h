@@ -17,25 +17,46 @@ struct Scalars {
   int sinkhorn_iters;
 };
 
-// The split-row kernel covers a tile of M = 16*RB tokens and CC = 4*CW
-// channels of every route per workgroup; a token's row is spread over
-// S = C / CC workgroups whose partial sums meet in the workspace.
+// The split-row kernel covers a tile of m tokens and cc channels of every
+// route per workgroup; a token's row is spread over s = C / cc workgroups
+// whose partial sums meet in the workspace.
 struct Plan {
-  int rb = 4;      // 16-token MFMA row blocks per workgroup
-  int cw = 32;     // channels per wave
-  int m = 64;      // tokens per tile
+  int m = 32;      // tokens per tile
   int cc = 128;    // channels per workgroup
+  int d1 = 1;      // stage delay of the reduce after a tile's phase A
+  int d2 = 2;      // stage delay of the pre step (fused modes), > d1
   int s = 1;       // workgroups per row
   int64_t tiles = 0;
   // workspace layout (byte offsets)
-  size_t off_err = 0, off_epoch = 0, off_dep = 0, off_pub = 0, off_part = 0, off_phi = 0, total = 0;
+  size_t off_pub = 0, off_part = 0, off_phi = 0, total = 0;
 };
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
+
+// Workspace header at fixed offsets, whatever the shape of a call: the error
+// word, the launch epoch, the tiles-done counter, then one leave counter per
+// possible tile (2^20 tokens / 32 tokens per tile).
+constexpr size_t kWsErr = 0, kWsEpoch = 4, kWsTilesDone = 8;
+constexpr size_t kWsDep = 256;
+constexpr int64_t kMaxTiles = (int64_t)(1 << 20) / 32;
+constexpr size_t kWsHeaderBytes = kWsDep + (size_t)kMaxTiles * 4;
 constexpr int kPackBlocks = 5;          // 80 packed columns = 5 MFMA 16-column blocks
 constexpr size_t kPackBytesPerRow = 160;  // 80 bf16 per flattened row k
 
 Plan make_plan(int64_t T, int64_t C);
+
+// Reduce-scatter of the split kernel: a workgroup owns ntok = ceil(m/s)
+// tokens of a tile; each of their ntok*34 partial words is summed over the
+// s splits by r = clamp(256/(ntok*34), 1, 8) threads, each taking a run of
+// plan_run_len() splits (at most kRunMax).
+constexpr int kRunMax = 20;
+inline int plan_run_len(const Plan& p) {
+  const int64_t ntok = (p.m + p.s - 1) / p.s;
+  const int64_t npair = ntok * kPartVals;
+  int64_t r = npair > 0 ? 256 / npair : 1;
+  r = r < 1 ? 1 : (r > 8 ? 8 : r);
+  return (int)((p.s + r - 1) / r);
+}
 inline size_t phi_packed_bytes(int64_t C) { return (size_t)(4 * C) * kPackBytesPerRow; }
 
 struct SplitArgs {
@@ -51,13 +72,16 @@ struct SplitArgs {
   uint8_t* h_fp8;
   uint8_t* h_scale;
   uint64_t* partials;  // [tiles][S][M][34] tagged words
-  uint32_t* epoch;     // [tiles]
-  uint32_t* dep;       // [tiles]
+  uint32_t* epoch;     // launch epoch (fixed offset)
+  uint32_t* tiles_done;  // tiles completed in this launch (fixed offset)
+  uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
   uint64_t* publish;   // [tiles][M][4] tagged words
   uint32_t* err;
   int64_t T;
+  uint32_t tiles;
   int C;
   int S;
+  int d1, d2;
   Scalars sc;
 };
 

@@ -65,52 +65,74 @@ __global__ __launch_bounds__(256) void k_pack_phi(const float* __restrict__ phi,
 }
 
 // ===========================================================================
-// Split-row kernel.
+// Split-row kernel (a staggered pipeline over tiles).
 //
-// Workgroup = 4 waves; blockIdx = tile * S + split.  A tile holds
-// M = 16*RB tokens; the workgroup owns channels [split*CC, split*CC + CC) of
-// all 4 routes and wave w the CW channels from split*CC + w*CW.  Lane l
-// serves token 16*r + l%16 of row block r (r < RB) and, in each 32-channel
-// step, channels 8*(l/16) .. +8.  That is the A-operand layout of
-// v_mfma_f32_16x16x32_bf16, so the bf16 chunk a lane loads (or the x' it
-// computes) is its MFMA operand as is, and one projection fragment serves
-// RB row blocks.
+// A tile holds TM tokens.  A token's row is spread over S = C / 128
+// "splits", each owning 128 channels of all 4 routes.  Workgroup
+// (stage k, split s) does three jobs in this order, each on another tile:
 //
-// Phase A  load x (and y; post/res staged in LDS), compute x' with the post
-//          chain, round to bf16, store it and keep it in registers;
-//          accumulate the route Gram matrix of x' (fused; its trace is the
-//          sum of squares) or the sum of squares of x (coeffs), and the 24
-//          projections on the matrix cores.
-// Reduce   fold hi+mid+lo, sum the 4 waves in LDS and write the tile's
-//          partial [M][34] to the workspace.  Barrier 1 over the tile's S
-//          workgroups; then workgroup `split` reduces tokens
-//          split, split+S, ... (split order, so the sums are deterministic),
-//          finalises their coefficients with one wave per token (Sinkhorn on
-//          16 lanes) and, in the fused modes, publishes pre'_i * r_h, where
-//          r_h is the RMSNorm scale of g = sum_i pre'_i x'_i obtained from
-//          the Gram matrix: sum_c g_c^2 = pre'^T G pre'.  Barrier 2 (fused).
-// Phase C  (fused) h = (sum_i q_i x'_i) * gamma from the registers, as bf16
-//          and/or MXFP8.
+//   A  tile k: lane tid serves the 8 channels 8*(tid%16) of tokens
+//      16p + tid/16 (sixteen lanes cover one 256-byte row segment).  It
+//      computes x' with the post chain, stores it, stages it in LDS and on
+//      the matrix cores (wave w: the 32-channel step w) forms the 24
+//      projections of the flattened row (A = x' rows of 16 tokens, B =
+//      packed projection fragments, the three bf16 terms in one
+//      accumulator) and the route Gram matrix G_ij = sum_c x'_i x'_j
+//      (A = rows (token, route) of 4 tokens, D = A A^T; the trace of G is
+//      the sum of squares).  The 4 waves' partials are summed in LDS and the
+//      tile partial [TM][34] goes to the workspace as tagged words.
+//   R  tile k - D1: workgroup s reduces tokens m with m % S == s: it gathers
+//      their S partials, sums them in split order (deterministic),
+//      finalises the coefficients on one wave per token (Sinkhorn on 16
+//      lanes) and, in the fused modes, publishes q_i, where r_h is the
+//      RMSNorm scale of g = sum_i pre'_i x'_i from the Gram matrix:
+//      sum_c g^2 = pre'^T G pre'.
+//   C  (fused modes) tile k - D2: the pre step.  It loads x and y of its
+//      128 channels again (the loads of A left them in the caches) and
+//      recomputes x' with the post chain, bit for bit what A stored, waits
+//      for the tile's published q_i = pre'_i * r_h and writes
+//      h = (sum_i q_i x'_i) * gamma as bf16 and/or MXFP8 (a 32-channel
+//      block is 4 neighbouring lanes).
+//
+// R consumes what A of stage k - D1 produced and C what R of stage
+// k - (D2 - D1) produced, each at the same point of an older workgroup's
+// life, so with delays of a few stages (more than the spread of
+// workgroup progress) nothing waits in steady state, and the inputs that C
+// reads again are still in the caches.  The grid has tiles + D2 (fused) or
+// tiles + D1 stages of S workgroups; the last stages only do R and C.  Stages are dispatched in blockIdx
+// order and a job depends only on lower stages, so progress never depends
+// on a later workgroup; the waits are bounded anyway.
+//
+// LDS layout of x': row = 4*token + route, sixteen 16-byte chunks per row,
+// chunk k stored at k ^ ((token + 4*route) & 15).  The coalesced writes,
+// the projection reads (16 tokens, one route, one chunk) and the Gram reads
+// (4 tokens x 4 routes, one chunk) then each touch 16 distinct chunk
+// positions: no bank conflicts.
+//
+// blockIdx -> (stage, split): the S workgroups of a stage are consecutive;
+// when S is a multiple of 8 the split is interleaved over blockIdx mod 8, so
+// that with the round-robin dispatch of workgroups over the 8 XCDs each XCD
+// reads only 1/8 of the packed projection (which then stays in its L2).
 //
 // Communication between workgroups uses agent-coherent 64-bit words that
 // carry a value and a tag: (float bits) | (tag << 32).  The tag of a launch
-// is the tile's epoch + 1, read when the workgroup starts; a reader polls
-// the words it needs until their tags match, so no counter sits on the
-// critical path and no cache write-back or invalidation is needed (agent
-// scope accesses bypass the per-XCD caches, and an aligned 64-bit access is
-// single-copy atomic, so a value is never seen with the wrong tag).  The
-// last workgroup of a tile to leave (a counter off the critical path) bumps
-// the epoch, so every launch uses a fresh tag and a zero-filled workspace
-// is a valid start.  Every word a launch reads is written in that launch.
-// Workgroups are dispatched in blockIdx order, so every workgroup a waiting
-// one depends on is running or will run once earlier tiles retire; the waits
-// are bounded anyway and set the workspace error word on expiry.
+// is the workspace's launch epoch + 1, read by every workgroup when it
+// starts; a reader polls the words it needs until their tags match, so no
+// counter sits on the critical path and no cache write-back or invalidation
+// is needed (agent-scope accesses bypass the per-XCD caches, and an aligned
+// 64-bit access is single-copy atomic, so a value is never seen with a
+// wrong tag).  Stale words of earlier launches carry older tags whatever the
+// shapes of those launches were.  Off the critical path, the last of a
+// tile's final consumers counts the tile as done, and the one completing the
+// last tile advances the epoch and clears the counter, so the workspace
+// (counters at fixed offsets) is ready for the next launch of any shape.
 // ===========================================================================
 constexpr uint32_t kSpinLimit = 1u << 22;
-// Reduce-scatter bounds: a workgroup owns at most ceil(M/S) <= 8 tokens
-// (M = 64, S >= 8) and gathers at most (M + S - 1) * 34 <= 18 * 256 words.
+// Reduce-scatter bounds, checked by the host when it makes the plan: a
+// workgroup owns ntok = ceil(TM/S) <= 7 tokens (ntok * 34 <= 256 partial
+// words) and one thread sums a run of at most kRunMax splits of one word
+// (the kernel is instantiated for runs of up to 8 and up to kRunMax).
 constexpr int kMaxTileTokensPerGroup = 8;
-constexpr int kGatherPerThread = 18;
 
 __device__ __forceinline__ void tagged_store(uint64_t* p, float v, uint32_t tag) {
   const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
@@ -136,10 +158,21 @@ __device__ __forceinline__ float tagged_wait(const uint64_t* p, uint32_t tag, ui
   return tagged_value(w);
 }
 
+// DPP lane moves inside rows of 16 lanes (no LDS traffic): quad_perm swaps
+// within groups of 4 lanes, row_ror rotates the 16-lane row.
+#define MHC_DPP(v, ctrl) __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowRor4 = 0x124;   // row_ror:4
+constexpr int kDppRowRor8 = 0x128;   // row_ror:8
+
 // Coefficients of one token on one wave.  sums: 24 projections, then the
 // Gram matrix (fused) or the sum of squares (coeffs).  Lanes 0..15 carry
-// res[j][i] (j = lane/4, i = lane%4), lanes 16..23 pre/post.  Returns in
-// every lane the value of coefficient `slot(lane)`; q gets pre_i * r_h.
+// res[j][i] (j = lane/4, i = lane%4), lanes 16..23 pre/post.  Row sums of
+// the 4x4 matrix are sums over lane ^ {1, 2}, column sums over the 16-lane
+// row rotated by 4, 8, 12.  Each normalisation multiplies by the reciprocal
+// of (sum + eps).  Returns in every lane the value of coefficient
+// slot(lane); q gets pre_i * r_h.
 template <bool FUSED>
 __device__ __forceinline__ float finalize_wave(const float* sums, const float* bias, int C, const Scalars& sc,
                                                int lane, float* q) {
@@ -152,12 +185,12 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
   float v = expf(l);
   const float eps = sc.sinkhorn_eps;
   for (int it = 0; it < sc.sinkhorn_iters; ++it) {
-    float rs = v + __shfl_xor(v, 1);
-    rs += __shfl_xor(rs, 2);
-    v = v / (rs + eps);
-    float cs = v + __shfl_xor(v, 4);
-    cs += __shfl_xor(cs, 8);
-    v = v / (cs + eps);
+    float rs = v + MHC_DPP(v, kDppQuadSwap1);
+    rs = rs + MHC_DPP(rs, kDppQuadSwap2);
+    v = v * __builtin_amdgcn_rcpf(rs + eps);
+    float cs = v + MHC_DPP(v, kDppRowRor8);
+    cs = cs + MHC_DPP(cs, kDppRowRor4);
+    v = v * __builtin_amdgcn_rcpf(cs + eps);
   }
   if constexpr (FUSED) {
     const float p[4] = {__shfl(pp, 16), __shfl(pp, 17), __shfl(pp, 18), __shfl(pp, 19)};
@@ -171,224 +204,292 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
   return lane < 16 ? v : pp;
 }
 
-template <int MODE, int RB, int CW>
+constexpr int kCC = 128;  // channels per workgroup
+
+__device__ __forceinline__ int xs_offset(int token, int route, int chunk) {
+  // 16-byte units
+  return (token * 4 + route) * 16 + (chunk ^ ((token + 4 * route) & 15));
+}
+
+// Gram slot of (e, j), e <= j: 00,11,22,33 -> 0..3, 01,02,03,12,13,23 -> 4..9
+__device__ __forceinline__ int gram_slot(int e, int j) {
+  if (e == j) return e;
+  return e == 0 ? 3 + j : (e == 1 ? 5 + j : 9);
+}
+
+// Per-lane stream registers of one tile: x (then x') of 4 routes and y for
+// the tokens 16p + tid/16, p < TM/16.
+template <int NP>
+struct TileRegs {
+  u32x4_t x[NP][4];
+  u32x4_t y[NP];
+};
+
+template <bool WITH_Y, int TM, bool LAST_USE>
+__device__ __forceinline__ void load_stream(const SplitArgs& a, int64_t tok0, int cl, int tr, TileRegs<TM / 16>& R) {
+  constexpr int NP = TM / 16;
+  const int C = a.C;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t t = tok0 + p * 16 + tr;
+    const bool valid = t < a.T;
+    const uint16_t* xp = a.x + (valid ? t : 0) * (int64_t)(4 * C) + cl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R.x[p][i] = valid ? ld16<LAST_USE>(xp + (int64_t)i * C) : u32x4_t{0, 0, 0, 0};
+    if constexpr (WITH_Y) R.y[p] = valid ? ld16<LAST_USE>(a.y + t * (int64_t)C + cl) : u32x4_t{0, 0, 0, 0};
+  }
+}
+
+// post / res of the tile's tokens: thread tid < TM*5 fetches one float4
+// (token tid/5, part tid%5) into a register, stored to LDS [TM][20] later,
+// so that the fetch does not delay the issue of other loads.
+template <int TM>
+__device__ __forceinline__ float4 fetch_post_coeffs(const SplitArgs& a, int64_t tok0, int tid) {
+  const int64_t t = tok0 + tid / 5;
+  if (tid >= TM * 5 || t >= a.T) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  return reinterpret_cast<const float4*>(a.coeffs_in + t * kCoeffs)[1 + tid % 5];
+}
+template <int TM>
+__device__ __forceinline__ void store_post_coeffs(float4 v, int tid, float (*cfs)[20]) {
+  if (tid >= TM * 5) return;
+  float* d = &cfs[tid / 5][4 * (tid % 5)];
+  d[0] = v.x;
+  d[1] = v.y;
+  d[2] = v.z;
+  d[3] = v.w;
+}
+
+// x' = post chain of (x, y) in place, for the lane's tokens
+template <int TM>
+__device__ __forceinline__ void post_tile(TileRegs<TM / 16>& R, const float (*cfs)[20], int tr) {
+  constexpr int NP = TM / 16;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int m = p * 16 + tr;
+    float pw[4], rs[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pw[q] = cfs[m][q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) rs[q] = cfs[m][4 + q];
+    u32x4_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float xl[4] = {bf16_lo(R.x[p][0][q]), bf16_lo(R.x[p][1][q]), bf16_lo(R.x[p][2][q]), bf16_lo(R.x[p][3][q])};
+      const float xh[4] = {bf16_hi(R.x[p][0][q]), bf16_hi(R.x[p][1][q]), bf16_hi(R.x[p][2][q]), bf16_hi(R.x[p][3][q])};
+      const float yl = bf16_lo(R.y[p][q]), yh = bf16_hi(R.y[p][q]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j][q] = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
+                              post_chain(pw[j], yh, &rs[4 * j], xh[0], xh[1], xh[2], xh[3]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R.x[p][j] = o[j];
+  }
+}
+
+template <int MODE, int TM, int RUN>
 __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
   constexpr bool FUSED = MODE != kModeCoeffs;
   constexpr bool MX = MODE == kModeFusedMx;
-  constexpr int W = 4, M = 16 * RB, NS = CW / 32, CC = W * CW;
-  constexpr int NV = kPartVals;
-  constexpr int NG = FUSED ? kGram : 1;
-
-  __shared__ float red[W][M][NV];
-  __shared__ float cfs[FUSED ? M : 1][20];
+  constexpr int W = 4, NV = kPartVals, NP = TM / 16, RB = TM / 16, NQ = TM / 4;
+  constexpr int NVU = FUSED ? NV : 25;
+  // LDS: x' (TM*4 rows x 256 B), later reused for the wave partials and the
+  // reduce-scatter run sums
+  constexpr int XS_BYTES = TM * 4 * 256;
+  constexpr int RED_BYTES = W * TM * NV * 4;
+  constexpr int LDS_BYTES = XS_BYTES > RED_BYTES ? XS_BYTES : RED_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  __shared__ float cfs_a[FUSED ? TM : 1][20];
+  __shared__ float cfs_c[FUSED ? TM : 1][20];
   __shared__ float fin[kMaxTileTokensPerGroup][NV];
-  __shared__ float qs[FUSED ? M : 1][4];
+  __shared__ float qs[FUSED ? TM : 1][4];
   __shared__ uint32_t s_tag;
+  u32x4_t* xs = reinterpret_cast<u32x4_t*>(lds);
+  float* red = reinterpret_cast<float*>(lds);   // [W][TM][NV]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n16 = lane & 15, g = lane >> 4;
   const int S = a.S;
-  const int tile = (int)(blockIdx.x / S), split = (int)(blockIdx.x % S);
-  const int64_t tok0 = (int64_t)tile * M;
+  int stage, split;
+  if ((S & 7) == 0) {
+    const int per = S >> 3, b = (int)blockIdx.x, j = b >> 3;
+    stage = j / per;
+    split = (b & 7) * per + j % per;
+  } else {
+    stage = (int)(blockIdx.x / S);
+    split = (int)(blockIdx.x % S);
+  }
+  const int tiles = (int)a.tiles;
+  const int tA = stage < tiles ? stage : -1;
+  const int tR = (stage - a.d1 >= 0 && stage - a.d1 < tiles) ? stage - a.d1 : -1;
+  const int tC = (FUSED && stage - a.d2 >= 0 && stage - a.d2 < tiles) ? stage - a.d2 : -1;
   const int C = a.C;
-  const int cw0 = split * CC + wave * CW;
+  const int c0 = split * kCC;
+  const int c8 = tid & 15, tr = tid >> 4;
+  const int cl = c0 + c8 * 8;  // this lane's first channel in A and C
+  const int n16 = lane & 15, g = lane >> 4;
+  const int chunk = wave * 4 + g;  // MFMA: 32-channel step `wave`, 8 channels per lane group
 
-  if (tid == 0)
-    s_tag = __hip_atomic_load(a.epoch + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-
-  // ---------------- phase A: loads ----------------
+  // ---- issue the loads that do not depend on this workgroup's own work ----
+  // A's stream (x, y of tile tA), the post coefficients of tiles tA and tC,
+  // and R's gather of the partials of tile tR (written by workgroups of stage
+  // tR, D1 stages earlier, normally complete by now; stale words are polled
+  // again when R runs).
+  if (tid == 0) s_tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  TileRegs<NP> ra;
+  if (tA >= 0) load_stream<FUSED, TM, false>(a, (int64_t)tA * TM, cl, tr, ra);
+  float4 cfa = make_float4(0.0f, 0.0f, 0.0f, 0.0f), cfc = cfa;
   if constexpr (FUSED) {
-    for (int idx = tid; idx < M * 5; idx += 256) {
-      const int m = idx / 5, k = idx % 5;
-      const int64_t t = tok0 + m;
-      const float4 v = t < a.T ? reinterpret_cast<const float4*>(a.coeffs_in + t * kCoeffs)[1 + k]
-                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      cfs[m][4 * k] = v.x;
-      cfs[m][4 * k + 1] = v.y;
-      cfs[m][4 * k + 2] = v.z;
-      cfs[m][4 * k + 3] = v.w;
-    }
+    if (tA >= 0) cfa = fetch_post_coeffs<TM>(a, (int64_t)tA * TM, tid);
+    if (tC >= 0) cfc = fetch_post_coeffs<TM>(a, (int64_t)tC * TM, tid);
   }
-  u32x4_t xf[RB][NS][4];
-  u32x4_t yv[RB][NS];
-  bool valid[RB];
+  // R: workgroup `split` owns tokens split + kk*S, kk < ntok.  Each of its
+  // ntok*34 partial words is summed over the S splits by RT threads, thread
+  // r taking the run of splits [r*L, r*L + L); the RT run sums are added in
+  // run order, so the total is a fixed-order sum.
+  const int ntok = split < TM ? (TM - split + S - 1) / S : 0;
+  const bool doR = tR >= 0 && ntok > 0;
+  const int npair = ntok * NV;
+  const int RT = npair == 0 ? 1 : (256 / npair < 1 ? 1 : (256 / npair > 8 ? 8 : 256 / npair));
+  const int L = (S + RT - 1) / RT;
+  const int pidx = tid / RT, rr = tid % RT;
+  const int kk = pidx / NV, v = pidx % NV;
+  const bool active = doR && pidx < npair && v < NVU;
+  const int sp0 = rr * L, n = active ? (S - sp0 < L ? (S - sp0 > 0 ? S - sp0 : 0) : L) : 0;
+  const uint64_t* gbase =
+      a.partials + ((int64_t)(doR ? tR : 0) * S * TM + (int64_t)sp0 * TM + split + kk * S) * NV + v;
+  const int64_t gstride = (int64_t)TM * NV;
+  uint64_t w[RUN];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int64_t t = tok0 + r * 16 + n16;
-    valid[r] = t < a.T;
-    const uint16_t* xr = a.x + (valid[r] ? t : 0) * (int64_t)(4 * C);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int c = cw0 + s * 32 + g * 8;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xf[r][s][i] = valid[r] ? ld16_stream(xr + (int64_t)i * C + c) : u32x4_t{0, 0, 0, 0};
-      if constexpr (FUSED)
-        yv[r][s] = valid[r] ? ld16_stream(a.y + t * (int64_t)C + c) : u32x4_t{0, 0, 0, 0};
-    }
-  }
-  float gm[NS][8];
+  for (int q = 0; q < RUN; ++q) w[q] = q < n ? tagged_load(gbase + q * gstride) : 0;
   if constexpr (FUSED) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float4* gp = reinterpret_cast<const float4*>(a.gamma + cw0 + s * 32 + g * 8);
-      const float4 g0 = gp[0], g1 = gp[1];
-      gm[s][0] = g0.x; gm[s][1] = g0.y; gm[s][2] = g0.z; gm[s][3] = g0.w;
-      gm[s][4] = g1.x; gm[s][5] = g1.y; gm[s][6] = g1.z; gm[s][7] = g1.w;
-    }
+    store_post_coeffs<TM>(cfa, tid, cfs_a);
+    store_post_coeffs<TM>(cfc, tid, cfs_c);
   }
-  __syncthreads();  // cfs, s_tag
+  __syncthreads();  // s_tag, cfs
   const uint32_t tag = s_tag;
 
-  // ---------------- phase A: post and statistics ----------------
+  // ---------------- A: post, statistics and projection of tile tA ----------------
+  if (tA >= 0) {
+    const int64_t tok0 = (int64_t)tA * TM;
+    if constexpr (FUSED) post_tile<TM>(ra, cfs_a, tr);
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    float st[NG];
-#pragma unroll
-    for (int k = 0; k < NG; ++k) st[k] = 0.0f;
-    float pw[4], rs[16];
-    if constexpr (FUSED) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pw[k] = cfs[r * 16 + n16][k];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) rs[k] = cfs[r * 16 + n16][4 + k];
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int p = 0; p < NP; ++p) {
+      const int m = p * 16 + tr;
       if constexpr (FUSED) {
-        // two channels at a time: unpack, post chain, round, statistics
-        u32x4_t o[4];
+        if (tok0 + m < a.T) {
+          uint16_t* xo = a.x_out + (tok0 + m) * (int64_t)(4 * C) + cl;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float xl[4] = {bf16_lo(xf[r][s][0][k]), bf16_lo(xf[r][s][1][k]), bf16_lo(xf[r][s][2][k]),
-                               bf16_lo(xf[r][s][3][k])};
-          const float xh[4] = {bf16_hi(xf[r][s][0][k]), bf16_hi(xf[r][s][1][k]), bf16_hi(xf[r][s][2][k]),
-                               bf16_hi(xf[r][s][3][k])};
-          const float yl = bf16_lo(yv[r][s][k]), yh = bf16_hi(yv[r][s][k]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            o[j][k] = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
-                                  post_chain(pw[j], yh, &rs[4 * j], xh[0], xh[1], xh[2], xh[3]));
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const float v0 = h2 ? bf16_hi(o[0][k]) : bf16_lo(o[0][k]);
-            const float v1 = h2 ? bf16_hi(o[1][k]) : bf16_lo(o[1][k]);
-            const float v2 = h2 ? bf16_hi(o[2][k]) : bf16_lo(o[2][k]);
-            const float v3 = h2 ? bf16_hi(o[3][k]) : bf16_lo(o[3][k]);
-            st[0] = __builtin_fmaf(v0, v0, st[0]);
-            st[1] = __builtin_fmaf(v1, v1, st[1]);
-            st[2] = __builtin_fmaf(v2, v2, st[2]);
-            st[3] = __builtin_fmaf(v3, v3, st[3]);
-            st[4] = __builtin_fmaf(v0, v1, st[4]);
-            st[5] = __builtin_fmaf(v0, v2, st[5]);
-            st[6] = __builtin_fmaf(v0, v3, st[6]);
-            st[7] = __builtin_fmaf(v1, v2, st[7]);
-            st[8] = __builtin_fmaf(v1, v3, st[8]);
-            st[9] = __builtin_fmaf(v2, v3, st[9]);
-          }
+          for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, ra.x[p][j]);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xf[r][s][j] = o[j];
-        if (valid[r]) {
-          const int64_t t = tok0 + r * 16 + n16;
-          uint16_t* xo = a.x_out + t * (int64_t)(4 * C) + cw0 + s * 32 + g * 8;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, xf[r][s][j]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float vl = bf16_lo(xf[r][s][i][k]), vh = bf16_hi(xf[r][s][i][k]);
-            st[0] = __builtin_fmaf(vl, vl, st[0]);
-            st[0] = __builtin_fmaf(vh, vh, st[0]);
-          }
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xs[xs_offset(m, j, c8)] = ra.x[p][j];
     }
-#pragma unroll
-    for (int k = 0; k < NG; ++k) {
-      const float v = sum_groups(st[k]);
-      if (g == 0) red[wave][r * 16 + n16][24 + k] = v;
-    }
-  }
-
-  // ---------------- phase A: projection on the matrix cores ----------------
-  f32x4_t acc[RB][2];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    acc[r][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    acc[r][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
+    // projection fragments of the wave's 32-channel step, all four routes,
+    // in flight together while the workgroup meets at the barrier
+    u32x4_t bfrag[4][kPackBlocks];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_sched_barrier(0);  // keep one route's fragments live at a time
-      const int64_t kstep = ((int64_t)j * C + cw0 + s * 32) >> 5;
+      const int64_t kstep = ((int64_t)j * C + c0 + wave * 32) >> 5;
       const u32x4_t* bp = reinterpret_cast<const u32x4_t*>(a.phi_packed) + kstep * (kPackBlocks * kWave) + lane;
-      u32x4_t bfrag[kPackBlocks];
 #pragma unroll
-      for (int b = 0; b < kPackBlocks; ++b) bfrag[b] = bp[b * kWave];
+      for (int b = 0; b < kPackBlocks; ++b) bfrag[j][b] = bp[b * kWave];
+    }
+    __syncthreads();  // x' staged
+
+    f32x4_t acc[RB][2];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      acc[r][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      acc[r][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // Gram matrices: groups of 4 tokens; lane l reads row l%16 = (token 4q + (l%16)/4, route l%4)
+    float gv[NQ][4];
+#pragma unroll
+    for (int qg = 0; qg < NQ; ++qg) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(4 * qg + (n16 >> 2), n16 & 3, chunk)]);
+      const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, av, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gv[qg][e] = d[e];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xf[r][s][j]);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(r * 16 + n16, j, chunk)]);
 #pragma unroll
         for (int b = 0; b < kPackBlocks; ++b)
           acc[r][b < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              av, __builtin_bit_cast(bf16x8_t, bfrag[b]), acc[r][b < 3 ? 0 : 1], 0, 0, 0);
+              av, __builtin_bit_cast(bf16x8_t, bfrag[j][b]), acc[r][b < 3 ? 0 : 1], 0, 0, 0);
       }
     }
-  }
-  // MFMA output: lane l holds column l%16 of rows 4*(l/16)+e, e = 0..3.
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v1 = acc[r][1][e];
-      const float mid = __shfl_xor(v1, 8);
-      const int row = r * 16 + 4 * g + e;
-      red[wave][row][n16] = acc[r][0][e];
-      if (n16 < 8) red[wave][row][16 + n16] = v1 + mid;
-    }
-  }
-  __syncthreads();
+    __syncthreads();  // LDS x' no longer needed: reuse it for the wave partials
 
-  // ---------------- tile partial -> workspace ----------------
-  constexpr int NVU = FUSED ? NV : 25;
-  uint64_t* part = a.partials + (int64_t)blockIdx.x * (M * NV);
-  const float* flat_red = &red[0][0][0];
-  for (int idx = tid; idx < M * NV; idx += 256) {
-    if (idx % NV >= NVU) continue;
-    tagged_store(part + idx, ((flat_red[idx] + flat_red[M * NV + idx]) + flat_red[2 * M * NV + idx]) +
-                                 flat_red[3 * M * NV + idx], tag);
+    // MFMA output: lane l holds column l%16 of rows 4*(l/16)+e.
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v1 = acc[r][1][e];
+        const float mid = __shfl_xor(v1, 8);
+        const int row = r * 16 + 4 * g + e;
+        red[(wave * TM + row) * NV + n16] = acc[r][0][e];
+        if (n16 < 8) red[(wave * TM + row) * NV + 16 + n16] = v1 + mid;
+      }
+    }
+    // Gram: useful lanes have (l/16) == (l%16)/4: token 4q + l/16, column route j = l%4, rows e
+    if ((n16 >> 2) == g) {
+      const int jr = n16 & 3;
+#pragma unroll
+      for (int qg = 0; qg < NQ; ++qg) {
+        const int row = 4 * qg + g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e <= jr) red[(wave * TM + row) * NV + 24 + gram_slot(e, jr)] = gv[qg][e];
+      }
+    }
+    __syncthreads();
+
+    uint64_t* part = a.partials + ((int64_t)tA * S + split) * (TM * NV);
+    for (int idx = tid; idx < TM * NV; idx += 256) {
+      const int vv = idx % NV;
+      if (vv >= NVU) continue;
+      float sum = ((red[idx] + red[TM * NV + idx]) + red[2 * TM * NV + idx]) + red[3 * TM * NV + idx];
+      if constexpr (!FUSED) {
+        if (vv == 24) {  // coeffs: only the trace of the Gram matrix
+          const int b = idx - 24;
+          sum = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < W; ++ww)
+            sum += ((red[ww * TM * NV + b + 24] + red[ww * TM * NV + b + 25]) + red[ww * TM * NV + b + 26]) +
+                   red[ww * TM * NV + b + 27];
+        }
+      }
+      tagged_store(part + idx, sum, tag);
+    }
+    __syncthreads();  // LDS free for R
   }
 
-  // ---------------- reduce-scatter: tokens split, split+S, ... ----------------
-  // Token m of the tile is reduced by workgroup m % S, which owns
-  // ntok <= ceil(M/S) tokens.  Their ntok x S x 34 tagged words are
-  // gathered with every load in flight (<= kGatherPerThread per thread),
-  // the stale ones re-polled together, staged in LDS (over the per-wave
-  // partial buffer, no longer needed) and summed in split order.
-  const uint64_t* tp = a.partials + (int64_t)tile * S * (M * NV);
-  const int ntok = split < M ? (M - split + S - 1) / S : 0;
-  if (ntok > 0) {
-    float* stage = &red[0][0][0];
-    const int nwords = ntok * S * NV;
-    uint64_t w[kGatherPerThread];
-#pragma unroll
-    for (int q = 0; q < kGatherPerThread; ++q) {
-      const int u = tid + 256 * q;
-      const int v = u % NV, rr = u / NV;
-      const int sp = rr % S, kk = rr / S;
-      w[q] = (u < nwords && v < NVU) ? tagged_load(tp + ((int64_t)sp * M + split + kk * S) * NV + v)
-                                     : ((uint64_t)tag << 32);
-    }
+  // the loads of C (inputs only) are in flight while R runs
+  TileRegs<NP> rc;
+  float gm[8];
+  if (tC >= 0) {
+    load_stream<true, TM, true>(a, (int64_t)tC * TM, cl, tr, rc);
+    const float4* gp = reinterpret_cast<const float4*>(a.gamma + cl);
+    const float4 g0 = gp[0], g1 = gp[1];
+    gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
+    gm[4] = g1.x; gm[5] = g1.y; gm[6] = g1.z; gm[7] = g1.w;
+  }
+
+  // ---------------- R: reduce-scatter of tile tR ----------------
+  if (doR) {
+    const int64_t tok0 = (int64_t)tR * TM;
+    float* runs = reinterpret_cast<float*>(lds);  // [npair][RT]
     uint32_t it = 0;
     for (;;) {
       bool stale = false;
 #pragma unroll
-      for (int q = 0; q < kGatherPerThread; ++q) stale |= (uint32_t)(w[q] >> 32) != tag;
+      for (int q = 0; q < RUN; ++q) stale |= q < n && (uint32_t)(w[q] >> 32) != tag;
       if (!stale) break;
       __builtin_amdgcn_s_sleep(1);
       if (++it > kSpinLimit) {
@@ -396,98 +497,117 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
         break;
       }
 #pragma unroll
-      for (int q = 0; q < kGatherPerThread; ++q) {
-        const int u = tid + 256 * q;
-        const int v = u % NV, rr = u / NV;
-        const int sp = rr % S, kk = rr / S;
-        if ((uint32_t)(w[q] >> 32) != tag) w[q] = tagged_load(tp + ((int64_t)sp * M + split + kk * S) * NV + v);
-      }
+      for (int q = 0; q < RUN; ++q)
+        if (q < n && (uint32_t)(w[q] >> 32) != tag) w[q] = tagged_load(gbase + q * gstride);
     }
+    float sum = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kGatherPerThread; ++q) {
-      const int u = tid + 256 * q;
-      if (u < nwords) stage[u] = tagged_value(w[q]);
-    }
+    for (int q = 0; q < RUN; ++q)
+      if (q < n) sum += tagged_value(w[q]);
+    if (pidx < npair) runs[pidx * RT + rr] = sum;
     __syncthreads();
-    for (int pidx = tid; pidx < ntok * NV; pidx += 256) {
-      const int kk = pidx / NV, v = pidx % NV;
-      float acc = 0.0f;
-      if (v < NVU)
-        for (int sp = 0; sp < S; ++sp) acc += stage[(kk * S + sp) * NV + v];
-      fin[kk][v] = acc;
+    for (int p2 = tid; p2 < npair; p2 += 256) {
+      float t2 = 0.0f;
+      for (int q = 0; q < RT; ++q) t2 += runs[p2 * RT + q];
+      fin[p2 / NV][p2 % NV] = t2;
     }
     __syncthreads();
     for (int k0 = 0; k0 < ntok; k0 += W) {
-      const int kk = k0 + wave;
-      if (kk < ntok) {
-        const int m = split + kk * S;
+      const int kq = k0 + wave;
+      if (kq < ntok) {
+        const int m = split + kq * S;
         float q[4];
-        const float cv = finalize_wave<FUSED>(fin[kk], a.bias, C, a.sc, lane, q);
+        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, C, a.sc, lane, q);
         const int64_t t = tok0 + m;
         if (t < a.T && lane < 24) a.coeffs_out[t * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
         if constexpr (FUSED) {
-          if (lane < 4) tagged_store(a.publish + ((int64_t)tile * M + m) * 4 + lane, q[lane], tag);
+          if (lane < 4) tagged_store(a.publish + ((int64_t)tR * TM + m) * 4 + lane, q[lane], tag);
         }
       }
     }
   }
 
+  // ---------------- C: pre of tile tC ----------------
   if constexpr (FUSED) {
-    for (int idx = tid; idx < M * 4; idx += 256)
-      (&qs[0][0])[idx] = tagged_wait(a.publish + (int64_t)tile * M * 4 + idx, tag, a.err);
-  }
-  // leave: the last workgroup of the tile moves the epoch on
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.dep + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint32_t)S - 1u) {
-      __hip_atomic_store(a.dep + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.epoch + tile, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tC >= 0) {
+      const int64_t tok0 = (int64_t)tC * TM;
+      if (tid < TM * 4) {
+        const uint64_t* qp = a.publish + tok0 * 4 + tid;
+        uint64_t qw = tagged_load(qp);
+        uint32_t it = 0;
+        while ((uint32_t)(qw >> 32) != tag) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++it > kSpinLimit) {
+            __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          qw = tagged_load(qp);
+        }
+        (&qs[0][0])[tid] = tagged_value(qw);
+      }
+      post_tile<TM>(rc, cfs_c, tr);
+      __syncthreads();  // qs
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int m = p * 16 + tr;
+        const int64_t t = tok0 + m;
+        const bool valid = t < a.T;
+        const float q0 = qs[m][0], q1 = qs[m][1], q2 = qs[m][2], q3 = qs[m][3];
+        float xv[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unpack8(rc.x[p][i], xv[i]);
+        float hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float vv = q0 * xv[0][e];
+          vv = __builtin_fmaf(q1, xv[1][e], vv);
+          vv = __builtin_fmaf(q2, xv[2][e], vv);
+          vv = __builtin_fmaf(q3, xv[3][e], vv);
+          hv[e] = vv * gm[e];
+        }
+        const u32x4_t hb = pack8(hv);
+        if (a.h != nullptr && valid) st16_stream(a.h + t * (int64_t)C + cl, hb);
+        if constexpr (MX) {
+          // a 32-channel block is the 4 lanes c8 = 4b .. 4b+3
+          float hr[8];
+          unpack8(hb, hr);
+          float amax = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
+          amax = __builtin_fmaxf(amax, MHC_DPP(amax, kDppQuadSwap1));
+          amax = __builtin_fmaxf(amax, MHC_DPP(amax, kDppQuadSwap2));
+          const int ex = mx_scale_exponent(amax);
+          const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w0 |= e4m3_code(hr[e] * scale) << (8 * e);
+            w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
+          }
+          if (valid) {
+            *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + cl) = u32x2_t{w0, w1};
+            if ((c8 & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
+          }
+        }
+      }
     }
   }
-  if constexpr (!FUSED) return;
 
-  // ---------------- phase C: h = (sum_i q_i x'_i) * gamma ----------------
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int64_t t = tok0 + r * 16 + n16;
-    const float q0 = qs[r * 16 + n16][0], q1 = qs[r * 16 + n16][1];
-    const float q2 = qs[r * 16 + n16][2], q3 = qs[r * 16 + n16][3];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int c = cw0 + s * 32 + g * 8;
-      float xv[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) unpack8(xf[r][s][i], xv[i]);
-      float hv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = q0 * xv[0][e];
-        v = __builtin_fmaf(q1, xv[1][e], v);
-        v = __builtin_fmaf(q2, xv[2][e], v);
-        v = __builtin_fmaf(q3, xv[3][e], v);
-        hv[e] = v * gm[s][e];
-      }
-      const u32x4_t hb = pack8(hv);
-      if (a.h != nullptr && valid[r]) st16_stream(a.h + t * (int64_t)C + c, hb);
-      if constexpr (MX) {
-        float hr[8];
-        unpack8(hb, hr);
-        float amax = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
-        amax = max_groups(amax);
-        const int ex = mx_scale_exponent(amax);
-        const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
-        uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w0 |= e4m3_code(hr[e] * scale) << (8 * e);
-          w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
-        }
-        if (valid[r]) {
-          *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + c) = u32x2_t{w0, w1};
-          if (g == 0) a.h_scale[t * (int64_t)(C / 32) + ((cw0 + s * 32) >> 5)] = (uint8_t)(ex + 127);
+  // ---------------- leave ----------------
+  // The last of a tile's S final consumers (C in the fused modes, R in the
+  // coeffs mode) counts the tile done; the one that completes the last tile
+  // advances the launch epoch.
+  const int tLeave = FUSED ? tC : tR;
+  if (tLeave >= 0) {
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(a.dep + tLeave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == (uint32_t)S - 1u) {
+        __hip_atomic_store(a.dep + tLeave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t done = __hip_atomic_fetch_add(a.tiles_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == a.tiles - 1u) {
+          __hip_atomic_store(a.tiles_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
@@ -634,15 +754,13 @@ hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s) {
 
 template <int MODE>
 static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(p.tiles * p.s)), block(256);
-  if (p.rb == 4 && p.cw == 32) {
-    k_split<MODE, 4, 32><<<grid, block, 0, s>>>(a);
-  } else if (p.rb == 2 && p.cw == 64) {
-    k_split<MODE, 2, 64><<<grid, block, 0, s>>>(a);
-  } else if (p.rb == 1 && p.cw == 128) {
-    k_split<MODE, 1, 128><<<grid, block, 0, s>>>(a);
+  const int64_t stages = p.tiles + (MODE == kModeCoeffs ? p.d1 : p.d2);
+  const dim3 grid((unsigned)(stages * p.s)), block(256);
+  if (p.m != 32 || p.cc != kCC) return hipErrorInvalidConfiguration;
+  if (plan_run_len(p) <= 8) {
+    k_split<MODE, 32, 8><<<grid, block, 0, s>>>(a);
   } else {
-    return hipErrorInvalidConfiguration;
+    k_split<MODE, 32, kRunMax><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
 }
