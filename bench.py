@@ -2,6 +2,8 @@
 """Benchmark of the mHC fused post->pre pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py --copy-probe           # copy kernel of known size (counter calibration)
+    python bench.py --pmc-summary FILE...  # per-kernel means of rocprofv3 counter output
 
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: repack the next layer's projection (mhc_pack_phi)
@@ -15,8 +17,12 @@ C = 7168, 4 routes, 1% of the rows scaled by 100.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
+import sqlite3
 import sys
 import time
 
@@ -27,6 +33,78 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 
 METRIC = "mHC fused post+pre tokens/s and % peak HBM GB/s at C=7168, T=8192"
+
+# Sources whose change invalidates the stored hardware counter figures.
+KERNEL_SOURCES = ["mhc_kernels.hip", "mhc_device.h", "mhc_internal.h", "mhc_api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_split_fused_prefill_traffic.txt")
+COPY_PROBE_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "manifold_constrained_hyper_mhc_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per fused launch measured with rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE, each scaled by the copy-kernel calibration), or None when the
+    kernel sources changed since the counters were taken."""
+    if workload != "prefill" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = re.match(r"^([a-z_0-9]+):\s*(.+)$", line.strip())
+            if m:
+                kv[m.group(1)] = m.group(2).strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["hbm_read_bytes"]) + int(kv["hbm_write_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pmc_summary(paths) -> int:
+    """Mean value per dispatch of each counter of each kernel, from rocprofv3
+    counter output (counter_collection.csv or a rocpd database)."""
+    import collections
+    agg = collections.defaultdict(list)
+    for path in paths:
+        if path.endswith(".db"):
+            con = sqlite3.connect(path)
+            rows = con.execute("select kernel_name, counter_name, value from counters_collection")
+            for name, cname, val in rows:
+                agg[(name, cname)].append(float(val))
+        else:
+            with open(path, newline="") as f:
+                for r in csv.DictReader(f):
+                    agg[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    for (name, cname), vals in sorted(agg.items(), key=lambda kv: -max(kv[1])):
+        short = re.sub(r"\(.*", "", name)[-70:]
+        print(f"{short:70s} {cname:11s} dispatches={len(vals):4d} mean={sum(vals) / len(vals):16.1f}")
+    return 0
+
+
+def copy_probe() -> int:
+    """A plain device-to-device copy of COPY_PROBE_BYTES, three times: the
+    counters it reads calibrate FETCH_SIZE and WRITE_SIZE against known bytes."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 3
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 3,
+                      "GB_per_s_read_plus_write": 2 * COPY_PROBE_BYTES / dt / 1e9}), flush=True)
+    return 0
 
 
 def algorithmic_bytes(T: int, C: int, mxfp8: bool, with_h: bool = True) -> int:
@@ -81,7 +159,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "mxfp8", "long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="FILE", help="summarise rocprofv3 counter output and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        return pmc_summary(args.pmc_summary)
+    if args.copy_probe:
+        return copy_probe()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path is not built "
                                    "(every token is independent: see DESIGN.md for how it would shard)",
@@ -188,7 +272,7 @@ def main() -> int:
                    "tokens": T, "hidden": C, "routes": 4, "mxfp8": mx, "bf16_h": with_h, "rows": rows,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(args.workload),
                      "kernel": "k_split (fused post->pre)", "kernel_avg_us": kern_avg_ms * 1e3,
                      "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,

@@ -92,6 +92,10 @@ typedef enum mhc_status {
 
 /* Flags of mhc_post_pre_fused. */
 #define MHC_FLAG_MXFP8 1u /* also write h as MXFP8: e4m3fn codes + UE8M0 scale per 32 channels */
+/* The pre step normally reads x_out back where the same XCD wrote it (its
+ * L2 holds the lines) and recomputes x' from x and y elsewhere; with this
+ * flag it always recomputes.  Results are bitwise identical either way. */
+#define MHC_FLAG_RECOMPUTE_X 2u
 
 /* ---------------------------------------------------------------------------
  * Library information

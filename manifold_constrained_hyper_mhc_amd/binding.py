@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmhc.so")
 
 FLAG_MXFP8 = 1
+FLAG_RECOMPUTE_X = 2
 _STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_ALIGN", 4: "MHC_ERR_ALIAS",
            5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP"}
 
@@ -212,6 +213,10 @@ def post(x, y, coeffs_t, *, out=None) -> torch.Tensor:
     return out
 
 
+def _flags(mxfp8: bool, recompute_x: bool) -> int:
+    return (FLAG_MXFP8 if mxfp8 else 0) | (FLAG_RECOMPUTE_X if recompute_x else 0)
+
+
 def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
     o = dict(outs or {})
     o.setdefault("x_out", torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev))
@@ -236,7 +241,8 @@ def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
 
 
 def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Params = Params(), *,
-                   mxfp8: bool = False, want_h: bool = True, ws=None, outs=None) -> dict:
+                   mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
+                  recompute_x: bool = False) -> dict:
     L = lib()
     T, C = _dims(x)
     dev = x.device
@@ -250,14 +256,15 @@ def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Para
     ws = workspace(T, C, dev) if ws is None else ws
     p = MhcParams.of(params)
     _check(L.mhc_post_pre_fused(_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next), _ptr(bias_next), _ptr(gamma_next),
-                                T, C, ctypes.byref(p), FLAG_MXFP8 if mxfp8 else 0, _ptr(o["x_out"]),
+                                T, C, ctypes.byref(p), _flags(mxfp8, recompute_x), _ptr(o["x_out"]),
                                 _ptr(o["coeffs_next"]), _ptr(o["h"]), _ptr(o["h_fp8"]), _ptr(o["h_scale"]),
                                 _ptr(ws), ws.numel(), _stream(dev)), "mhc_post_pre_fused")
     return o
 
 
 def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(), *,
-                             mxfp8: bool = False, want_h: bool = True, ws=None, outs=None) -> dict:
+                             mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
+                            recompute_x: bool = False) -> dict:
     L = lib()
     T, C = _dims(x)
     dev = x.device
@@ -271,7 +278,7 @@ def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_n
     ws = workspace(T, C, dev) if ws is None else ws
     p = MhcParams.of(params)
     _check(L.mhc_post_pre_fused_prepacked(_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next_packed), _ptr(bias_next),
-                                          _ptr(gamma_next), T, C, ctypes.byref(p), FLAG_MXFP8 if mxfp8 else 0,
+                                          _ptr(gamma_next), T, C, ctypes.byref(p), _flags(mxfp8, recompute_x),
                                           _ptr(o["x_out"]), _ptr(o["coeffs_next"]), _ptr(o["h"]), _ptr(o["h_fp8"]),
                                           _ptr(o["h_scale"]), _ptr(ws), ws.numel(), _stream(dev)),
            "mhc_post_pre_fused_prepacked")

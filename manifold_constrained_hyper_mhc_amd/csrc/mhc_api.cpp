@@ -124,6 +124,8 @@ Plan make_plan(int64_t T, int64_t C) {
   off = round256(off + (size_t)p.tiles * p.m * 4 * sizeof(uint64_t));
   p.off_part = off;
   off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(uint64_t));
+  p.off_own = off;
+  off = round256(off + (size_t)p.tiles * p.s * sizeof(uint64_t));
   p.off_phi = off;
   off = round256(off + phi_packed_bytes(C));
   p.total = off;
@@ -144,6 +146,7 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.dep = reinterpret_cast<uint32_t*>(base + mhc::kWsDep);
   a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
+  a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
   a.T = T;
   a.tiles = (uint32_t)plan.tiles;
   a.C = (int)C;
@@ -195,7 +198,7 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
   int rc = check_shape(T, C);
   if (rc) return rc;
   if ((rc = check_params(p, true))) return rc;
-  if (flags & ~MHC_FLAG_MXFP8) return MHC_ERR_FLAGS;
+  if (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X)) return MHC_ERR_FLAGS;
   const bool mx = (flags & MHC_FLAG_MXFP8) != 0;
   if (mx) {
     if (T > 0 && (h_fp8 == nullptr || h_scale == nullptr)) return MHC_ERR_NULL;
@@ -244,6 +247,7 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
   a.h = h;
   a.h_fp8 = h_fp8;
   a.h_scale = h_scale;
+  a.recompute_x = (flags & MHC_FLAG_RECOMPUTE_X) != 0;
   return hip_status(mhc::launch_split(plan, mx ? mhc::kModeFusedMx : mhc::kModeFused, a, s));
 }
 
@@ -271,7 +275,7 @@ const char* mhc_strerror(int status) {
 int mhc_last_hip_error(void) { return g_last_hip_error; }
 
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags) {
-  if (check_shape(T, C) != MHC_OK || (flags & ~MHC_FLAG_MXFP8)) return 0;
+  if (check_shape(T, C) != MHC_OK || (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X))) return 0;
   return mhc::make_plan(T, C).total;
 }
 

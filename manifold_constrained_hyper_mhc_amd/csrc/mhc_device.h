@@ -58,6 +58,7 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) {
   if constexpr (LAST_USE) return ld16_stream(p);
   return ld16(p);
 }
+__device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 __device__ __forceinline__ void st16_stream(void* p, u32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
 }

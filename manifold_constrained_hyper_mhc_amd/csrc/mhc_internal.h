@@ -28,7 +28,7 @@ struct Plan {
   int s = 1;       // workgroups per row
   int64_t tiles = 0;
   // workspace layout (byte offsets)
-  size_t off_pub = 0, off_part = 0, off_phi = 0, total = 0;
+  size_t off_pub = 0, off_part = 0, off_own = 0, off_phi = 0, total = 0;
 };
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
@@ -76,12 +76,14 @@ struct SplitArgs {
   uint32_t* tiles_done;  // tiles completed in this launch (fixed offset)
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
   uint64_t* publish;   // [tiles][M][4] tagged words
+  uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
   uint32_t* err;
   int64_t T;
   uint32_t tiles;
   int C;
   int S;
   int d1, d2;
+  int recompute_x;     // the pre step never reads x_out back
   Scalars sc;
 };
 

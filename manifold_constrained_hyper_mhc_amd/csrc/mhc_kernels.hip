@@ -138,6 +138,10 @@ __device__ __forceinline__ void tagged_store(uint64_t* p, float v, uint32_t tag)
   const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
   __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// XCD (accelerator complex die) the calling wave runs on: hardware register
+// XCC_ID, bits 3:0.
+__device__ __forceinline__ uint32_t xcd_id() { return (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u; }
+
 __device__ __forceinline__ uint64_t tagged_load(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -240,6 +244,21 @@ __device__ __forceinline__ void load_stream(const SplitArgs& a, int64_t tok0, in
   }
 }
 
+// x' of a tile, read back from x_out (last use)
+template <int TM>
+__device__ __forceinline__ void load_xprime(const SplitArgs& a, int64_t tok0, int cl, int tr, TileRegs<TM / 16>& R) {
+  constexpr int NP = TM / 16;
+  const int C = a.C;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t t = tok0 + p * 16 + tr;
+    const bool valid = t < a.T;
+    const uint16_t* xp = a.x_out + (valid ? t : 0) * (int64_t)(4 * C) + cl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R.x[p][i] = valid ? ld16_stream(xp + (int64_t)i * C) : u32x4_t{0, 0, 0, 0};
+  }
+}
+
 // post / res of the tile's tokens: thread tid < TM*5 fetches one float4
 // (token tid/5, part tid%5) into a register, stored to LDS [TM][20] later,
 // so that the fetch does not delay the issue of other loads.
@@ -303,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
   __shared__ float cfs_c[FUSED ? TM : 1][20];
   __shared__ float fin[kMaxTileTokensPerGroup][NV];
   __shared__ float qs[FUSED ? TM : 1][4];
-  __shared__ uint32_t s_tag;
+  __shared__ uint32_t s_tag, s_xdirect;
   u32x4_t* xs = reinterpret_cast<u32x4_t*>(lds);
   float* red = reinterpret_cast<float*>(lds);   // [W][TM][NV]
 
@@ -336,7 +355,9 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
   // again when R runs).
   if (tid == 0) s_tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   TileRegs<NP> ra;
-  if (tA >= 0) load_stream<FUSED, TM, false>(a, (int64_t)tA * TM, cl, tr, ra);
+  if (tA >= 0) load_stream<FUSED, TM, true>(a, (int64_t)tA * TM, cl, tr, ra);
+  uint64_t own = 0;
+  if (tid == 0 && tC >= 0) own = tagged_load(a.owner + (int64_t)tC * S + split);
   float4 cfa = make_float4(0.0f, 0.0f, 0.0f, 0.0f), cfc = cfa;
   if constexpr (FUSED) {
     if (tA >= 0) cfa = fetch_post_coeffs<TM>(a, (int64_t)tA * TM, tid);
@@ -365,8 +386,15 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
     store_post_coeffs<TM>(cfa, tid, cfs_a);
     store_post_coeffs<TM>(cfc, tid, cfs_c);
   }
-  __syncthreads();  // s_tag, cfs
+  // The pre step of tile tC reads back the x' that phase A of the same split
+  // stored, when that workgroup ran on this XCD (their shared L2 holds the
+  // stores); otherwise it recomputes x' from x and y.
+  if (tid == 0)
+    s_xdirect = tC >= 0 && !a.recompute_x && (uint32_t)(own >> 32) == s_tag &&
+                __float_as_uint(tagged_value(own)) == xcd_id();
+  __syncthreads();  // s_tag, cfs, s_xdirect
   const uint32_t tag = s_tag;
+  const bool xdirect = s_xdirect != 0;
 
   // ---------------- A: post, statistics and projection of tile tA ----------------
   if (tA >= 0) {
@@ -379,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
         if (tok0 + m < a.T) {
           uint16_t* xo = a.x_out + (tok0 + m) * (int64_t)(4 * C) + cl;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, ra.x[p][j]);
+          for (int j = 0; j < 4; ++j) st16(xo + (int64_t)j * C, ra.x[p][j]);
         }
       }
 #pragma unroll
@@ -448,6 +476,11 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
           if (e <= jr) red[(wave * TM + row) * NV + 24 + gram_slot(e, jr)] = gv[qg][e];
       }
     }
+    if constexpr (FUSED) {
+      // every wave's x' stores have reached the L2 before the owner word
+      // (stored after this barrier) announces them
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     __syncthreads();
 
     uint64_t* part = a.partials + ((int64_t)tA * S + split) * (TM * NV);
@@ -468,13 +501,18 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
       tagged_store(part + idx, sum, tag);
     }
     __syncthreads();  // LDS free for R
+    if (FUSED && tid == 0) tagged_store(a.owner + (int64_t)tA * S + split, __uint_as_float(xcd_id()), tag);
   }
 
   // the loads of C (inputs only) are in flight while R runs
   TileRegs<NP> rc;
   float gm[8];
   if (tC >= 0) {
-    load_stream<true, TM, true>(a, (int64_t)tC * TM, cl, tr, rc);
+    if (xdirect) {
+      load_xprime<TM>(a, (int64_t)tC * TM, cl, tr, rc);
+    } else {
+      load_stream<true, TM, true>(a, (int64_t)tC * TM, cl, tr, rc);
+    }
     const float4* gp = reinterpret_cast<const float4*>(a.gamma + cl);
     const float4 g0 = gp[0], g1 = gp[1];
     gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
@@ -545,7 +583,7 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
         }
         (&qs[0][0])[tid] = tagged_value(qw);
       }
-      post_tile<TM>(rc, cfs_c, tr);
+      if (!xdirect) post_tile<TM>(rc, cfs_c, tr);
       __syncthreads();  // qs
 #pragma unroll
       for (int p = 0; p < NP; ++p) {

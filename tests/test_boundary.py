@@ -50,7 +50,8 @@ def test_sizes():
     assert L.mhc_phi_packed_bytes(7168) == 4 * 7168 * 160
     assert L.mhc_phi_packed_bytes(1000) == 0          # not a multiple of 1024
     assert L.mhc_workspace_bytes(8192, 7168, 0) >= 4 * 7168 * 160
-    assert L.mhc_workspace_bytes(8192, 7168, 2) == 0  # unknown flag
+    assert L.mhc_workspace_bytes(8192, 7168, 2) == L.mhc_workspace_bytes(8192, 7168, 0)
+    assert L.mhc_workspace_bytes(8192, 7168, 4) == 0  # unknown flag
     assert L.mhc_workspace_bytes(-1, 7168, 0) == 0
     w1, w2 = L.mhc_workspace_bytes(16, 1024, 0), L.mhc_workspace_bytes(17, 1024, 0)
     assert 0 < w1 <= w2
@@ -122,6 +123,8 @@ def test_fused_validation():
     L = mhc.lib()
     assert fused_call(L, C=1536) == SHAPE
     assert fused_call(L, flags=4) == FLAGS
+    assert fused_call(L, flags=2 | 4) == FLAGS
+    assert fused_call(L, flags=2, fp8=fake(9)) == FLAGS             # fp8 output without the MXFP8 flag
     assert fused_call(L, fp8=fake(9)) == FLAGS                      # fp8 output without the flag
     assert fused_call(L, flags=1, fp8=fake(9)) == NULL              # flag without the scale output
     assert fused_call(L, h=False) == NULL                           # bf16 h required without the flag

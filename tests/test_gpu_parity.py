@@ -224,6 +224,22 @@ def test_prepacked_is_bitwise_identical():
     assert torch.equal(c1, c2)
 
 
+@pytest.mark.parametrize("mx", [False, True])
+def test_recompute_flag_is_bitwise_identical(mx):
+    # 65 tiles with a ragged last one: the pipelined launch, where the pre step
+    # reads x_out back on the XCD that wrote it unless told to recompute x'
+    inp = small_inputs(2070, 1024, seed=5)
+    d = to_dev(inp)
+    a = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=mx)
+    b = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=mx,
+                           recompute_x=True)
+    torch.cuda.synchronize()
+    keys = ("x_out", "coeffs_next", "h") + (("h_fp8", "h_scale") if mx else ())
+    for k in keys:
+        assert torch.equal(a[k], b[k]), k
+    check_fused(inp, b, mx=mx)
+
+
 def test_deterministic_and_workspace_reuse():
     ws = mhc.workspace(300, 7168, DEV, fresh=True)
     runs = []
