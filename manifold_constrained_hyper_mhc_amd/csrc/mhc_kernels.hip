@@ -306,8 +306,10 @@ __device__ __forceinline__ void post_tile(TileRegs<TM / 16>& R, const float (*cf
   }
 }
 
+// Four workgroups per CU (<= 128 VGPRs, 4 x 39.5 KB of LDS) when the reduce
+// runs are short; long runs (hidden sizes above 7168) need more registers.
 template <int MODE, int TM, int RUN>
-__global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
+__global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs a) {
   constexpr bool FUSED = MODE != kModeCoeffs;
   constexpr bool MX = MODE == kModeFusedMx;
   constexpr int W = 4, NV = kPartVals, NP = TM / 16, RB = TM / 16, NQ = TM / 4;
@@ -431,15 +433,6 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
       acc[r][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       acc[r][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    // Gram matrices: groups of 4 tokens; lane l reads row l%16 = (token 4q + (l%16)/4, route l%4)
-    float gv[NQ][4];
-#pragma unroll
-    for (int qg = 0; qg < NQ; ++qg) {
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(4 * qg + (n16 >> 2), n16 & 3, chunk)]);
-      const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, av, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gv[qg][e] = d[e];
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -450,6 +443,16 @@ __global__ __launch_bounds__(256, 2) void k_split(const SplitArgs a) {
           acc[r][b < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               av, __builtin_bit_cast(bf16x8_t, bfrag[j][b]), acc[r][b < 3 ? 0 : 1], 0, 0, 0);
       }
+    }
+    // (after the projection, so that the fragments are dead: fewer registers)
+    // Gram matrices: groups of 4 tokens; lane l reads row l%16 = (token 4q + (l%16)/4, route l%4)
+    float gv[NQ][4];
+#pragma unroll
+    for (int qg = 0; qg < NQ; ++qg) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(4 * qg + (n16 >> 2), n16 & 3, chunk)]);
+      const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, av, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gv[qg][e] = d[e];
     }
     __syncthreads();  // LDS x' no longer needed: reuse it for the wave partials
 
