@@ -113,6 +113,19 @@ int mhc_last_hip_error(void);
  * `stream`, no memset node); every call leaves it cleared again, so it can
  * be reused by any later call with any T and C whose size it covers.  One
  * workspace must not be used by two calls that may run concurrently.
+ * Its first 4 bytes are an error word (uint32): the kernels' waits on other
+ * workgroups are bounded, and one that expires sets it nonzero, after which
+ * that call's outputs are invalid.  Calls never clear it; mhc_workspace_init
+ * does.  The caller reads it after synchronising with `stream`.
+ *
+ * Schedule.  These two calls run a staged kernel whose workgroups wait only
+ * on work of lower-numbered workgroups.  With the environment variable
+ * MHC_SCHEDULE=persistent (read on every call) and 32 <= C/128 <= 64, a
+ * persistent kernel runs instead: one 512-thread workgroup per compute unit,
+ * every one of which must be resident at once, so nothing else may occupy
+ * the device while it runs (else its waits expire and set the error word).
+ * Results of the two schedules are equal to within the stated tolerances
+ * (x_out and the MXFP8 codes bitwise).
  * ------------------------------------------------------------------------- */
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags);
 int mhc_workspace_init(void* workspace, size_t workspace_bytes, void* stream);

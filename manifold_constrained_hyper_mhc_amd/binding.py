@@ -144,6 +144,12 @@ def workspace(T: int, C: int, device=None, *, fresh: bool = False) -> torch.Tens
     return ws
 
 
+def workspace_error(ws: torch.Tensor) -> int:
+    """The workspace's error word (its first 4 bytes): nonzero once a bounded
+    wait of a kernel that used it expired.  Synchronises with the device."""
+    return int(ws[:4].cpu().view(torch.int32).item())
+
+
 def pack_phi(phi: torch.Tensor) -> torch.Tensor:
     L = lib()
     C = phi.shape[0] // 4

@@ -3,6 +3,7 @@
 // effect on the device (and the checks can be exercised without a GPU).
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "mhc.h"
@@ -90,6 +91,39 @@ bool plan_fits(const mhc::Plan& p) {
   return mhc::plan_run_len(p) <= mhc::kRunMax && p.m == 32 && p.tiles <= mhc::kMaxTiles;
 }
 
+// Persistent kernel: one 512-thread workgroup per CU, S*L stream workgroups
+// plus 32 reduce workgroups, all resident.  Eligible when a tile's 32 tokens
+// map onto distinct splits for the level-1 reduce (32 <= S <= 64) and each
+// stream workgroup gets at least two tiles.  It runs only when the
+// environment variable MHC_SCHEDULE is "persistent" (read on every call);
+// otherwise, and for shapes it does not take, the staged kernel runs.
+bool persistent_requested() {
+  const char* v = getenv("MHC_SCHEDULE");
+  return v != nullptr && strcmp(v, "persistent") == 0;
+}
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+void choose_kernel(mhc::Plan& p) {
+  p.lanes = 0;
+  if (!persistent_requested()) return;
+  if (p.m != 32 || p.s < 32 || p.s > 64 || (p.s + 14) / 15 > 5) return;
+  const int cus = device_cus();
+  const int lanes = (cus - 32) / p.s;
+  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes) return;
+  p.lanes = lanes;
+}
+
 int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
   if (!plan_fits(plan)) return MHC_ERR_SHAPE;
   if (ws == nullptr) return MHC_ERR_WORKSPACE;
@@ -126,6 +160,8 @@ Plan make_plan(int64_t T, int64_t C) {
   off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(uint64_t));
   p.off_own = off;
   off = round256(off + (size_t)p.tiles * p.s * sizeof(uint64_t));
+  p.off_red = off;
+  off = round256(off + (size_t)p.tiles * p.m * kPartVals * sizeof(uint64_t));
   p.off_phi = off;
   off = round256(off + phi_packed_bytes(C));
   p.total = off;
@@ -147,12 +183,14 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
+  a.reduced = reinterpret_cast<uint64_t*>(base + plan.off_red);
   a.T = T;
   a.tiles = (uint32_t)plan.tiles;
   a.C = (int)C;
   a.S = plan.s;
   a.d1 = plan.d1;
   a.d2 = plan.d2;
+  a.lanes = plan.lanes;
   a.sc = scalars(p);
   return a;
 }
@@ -177,7 +215,9 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
     if (overlaps(wsp, s)) return MHC_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  mhc::SplitArgs a = split_args(plan, ws, T, C, p);
+  mhc::Plan run = plan;
+  choose_kernel(run);
+  mhc::SplitArgs a = split_args(run, ws, T, C, p);
   const void* packed = phi_packed;
   if (phi != nullptr) {
     void* dst = static_cast<char*>(ws) + plan.off_phi;
@@ -188,7 +228,7 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
   a.phi_packed = static_cast<const uint32_t*>(packed);
   a.bias = bias;
   a.coeffs_out = coeffs;
-  return hip_status(mhc::launch_split(plan, mhc::kModeCoeffs, a, s));
+  return hip_status(mhc::launch_split(run, mhc::kModeCoeffs, a, s));
 }
 
 int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const float* phi,
@@ -229,7 +269,9 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
     if (overlaps(wsp, out[k])) return MHC_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  mhc::SplitArgs a = split_args(plan, ws, T, C, p);
+  mhc::Plan run = plan;
+  choose_kernel(run);
+  mhc::SplitArgs a = split_args(run, ws, T, C, p);
   const void* packed = phi_packed;
   if (phi != nullptr) {
     void* dst = static_cast<char*>(ws) + plan.off_phi;
@@ -248,7 +290,7 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
   a.h_fp8 = h_fp8;
   a.h_scale = h_scale;
   a.recompute_x = (flags & MHC_FLAG_RECOMPUTE_X) != 0;
-  return hip_status(mhc::launch_split(plan, mx ? mhc::kModeFusedMx : mhc::kModeFused, a, s));
+  return hip_status(mhc::launch_split(run, mx ? mhc::kModeFusedMx : mhc::kModeFused, a, s));
 }
 
 }  // namespace

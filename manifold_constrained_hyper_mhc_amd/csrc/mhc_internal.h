@@ -26,9 +26,10 @@ struct Plan {
   int d1 = 1;      // stage delay of the reduce after a tile's phase A
   int d2 = 2;      // stage delay of the pre step (fused modes), > d1
   int s = 1;       // workgroups per row
+  int lanes = 0;   // persistent kernel: stream workgroups per split (0: staged kernel)
   int64_t tiles = 0;
   // workspace layout (byte offsets)
-  size_t off_pub = 0, off_part = 0, off_own = 0, off_phi = 0, total = 0;
+  size_t off_pub = 0, off_part = 0, off_own = 0, off_red = 0, off_phi = 0, total = 0;
 };
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
@@ -77,12 +78,14 @@ struct SplitArgs {
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
   uint64_t* publish;   // [tiles][M][4] tagged words
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
+  uint64_t* reduced;   // [tiles][M][34] tagged split sums of each token (persistent kernel)
   uint32_t* err;
   int64_t T;
   uint32_t tiles;
   int C;
   int S;
   int d1, d2;
+  int lanes;           // persistent kernel: stream workgroups per split
   int recompute_x;     // the pre step never reads x_out back
   Scalars sc;
 };

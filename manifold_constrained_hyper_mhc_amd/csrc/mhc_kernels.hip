@@ -656,6 +656,534 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 }
 
 // ===========================================================================
+// Persistent split-row kernel (fused modes and coeffs, long launches).
+//
+// One workgroup of 512 threads per CU, all resident at once:
+//   * S*L "stream" workgroups: workgroup (split s, lane r) owns the 128
+//     channels of split s and the tiles t = r, r + L, r + 2L, ...  Its slice
+//     of the packed projection (80 KB) is copied to LDS once.  Iteration i
+//     handles tile t_i: the pre step of tile t_{i-D} (x' of that tile kept
+//     in registers since its own phase A, D iterations earlier), then phase
+//     A of t_i (post, x' out, projection and Gram on the matrix cores from
+//     LDS, tile partial to the workspace), while the loads of t_{i+1} are in
+//     flight.
+//   * 32 "reduce" workgroups: workgroup m owns token m of every tile; wave w
+//     handles tiles t = w, w + 8, ...: it gathers the S partials of its token
+//     (lane = split), sums them with a fixed butterfly, finalises the
+//     coefficients on 16 lanes and publishes q_i = pre'_i * r_h.
+// Stream workgroups wait for q words published by reduce workgroups, which
+// wait for partials of stream workgroups, so the launch needs all S*L + 32
+// workgroups resident together (the host sizes L from the CU count; every
+// wait is bounded and sets the workspace error word on expiry).  Nothing is
+// read back from x_out: the pre step uses the x' registers, so the HBM
+// traffic is the algorithmic one plus the partial and q words.
+// ===========================================================================
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+constexpr int kPersistThreads = 512;
+constexpr int kPersistTM = 32;
+constexpr int kPersistDepth = 3;  // iterations between phase A and the pre step of a tile
+constexpr int kPersistR1 = 1;     // iterations between phase A and the level-1 reduce of a tile
+constexpr int kR1Run = 5;         // splits summed by one thread in the level-1 reduce (S <= 75)
+constexpr uint32_t kPersistSpinLimit = 1u << 18;
+constexpr int kPersistMaxS = 64;  // splits per row the reduce threads can gather
+
+// Coefficients of one token in one thread (the reduce workgroups finalise
+// eight tokens side by side): sums = 24 projections, then the Gram matrix
+// (fused) or the sum of squares (coeffs).  The same formulas as
+// finalize_wave: RMS scale, sigmoids, exp, and sinkhorn_iters rounds of row
+// then column normalisation, each multiplying by the reciprocal of
+// (sum + sinkhorn_eps); q_i = pre_i * r_h from the Gram quadratic form.
+template <bool FUSED>
+__device__ __forceinline__ void finalize_token(const float* sums, const float* bias, int C, const Scalars& sc,
+                                               float* cf, float* q) {
+  const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
+  const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = 1.0f / (1.0f + expf(-(r * sums[i] + bias[i])));
+    cf[i] = p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cf[4 + i] = sc.hc_post_scale * (1.0f / (1.0f + expf(-(r * sums[4 + i] + bias[4 + i]))));
+  float mres[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) mres[k] = expf(r * sums[8 + k] + bias[8 + k]);
+  const float eps = sc.sinkhorn_eps;
+  for (int it = 0; it < sc.sinkhorn_iters; ++it) {
+#pragma unroll
+    for (int jr = 0; jr < 4; ++jr) {
+      const float rs = __builtin_amdgcn_rcpf(((mres[4 * jr] + mres[4 * jr + 1]) + (mres[4 * jr + 2] + mres[4 * jr + 3])) + eps);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mres[4 * jr + i] *= rs;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float cs = __builtin_amdgcn_rcpf(((mres[i] + mres[4 + i]) + (mres[8 + i] + mres[12 + i])) + eps);
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) mres[4 * jr + i] *= cs;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cf[8 + k] = mres[k];
+  if constexpr (FUSED) {
+    const float gq = gram_quadratic(sums + 24, p);
+    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = p[i] * rh;
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs a) {
+  constexpr bool FUSED = MODE != kModeCoeffs;
+  constexpr bool MX = MODE == kModeFusedMx;
+  constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
+  constexpr int NVU = FUSED ? NV : 25;
+  // LDS: projection slice [4 routes][4 k-steps][5 blocks][64 lanes] x 16 B,
+  // x' staging (aliased by the wave partials), post coefficients, q words.
+  __shared__ __attribute__((aligned(16))) u32x4_t phi_lds[4 * 4 * kPackBlocks * kWave];
+  __shared__ __attribute__((aligned(16))) u32x4_t xs[TM * 4 * 16];
+  __shared__ float cfs[FUSED ? TM : 1][20];
+  __shared__ float qs[FUSED ? TM : 1][4];
+  __shared__ float r1runs[NVU][kPersistThreads / NVU];  // level-1 reduce: run sums of each word
+  __shared__ float gam[FUSED ? kCC : 1];                  // gamma of this split
+  float* redP = reinterpret_cast<float*>(xs);      // [8 waves][TM][24]
+  float* redG = redP + 8 * TM * 24;                // [4 k-steps][TM][10]
+  float* finw = reinterpret_cast<float*>(phi_lds);  // reduce workgroups: [8 tokens][NV]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.S, C = a.C, L = a.lanes;
+  const int tiles = (int)a.tiles;
+  const uint32_t tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  const int nstream = S * L;
+
+  if ((int)blockIdx.x >= nstream) {
+    // ------------------------- reduce workgroup -------------------------
+    // Reduce workgroup j owns tokens 8*(j%4) .. +7 of the tiles t = j/4 + 8k.
+    // The split sums of each token were already added up by the stream
+    // workgroup of split = token (reduced words); thread (token k, word v)
+    // loads one of them, and after a barrier eight threads finalise one
+    // token each, with the whole 4x4 Sinkhorn in registers.
+    const int j = (int)blockIdx.x - nstream;
+    const int grp = j & 3, ph = j >> 2;
+    float* fin = finw;  // [8 tokens][NV]
+    const int kt = tid / NVU, v = tid % NVU;
+    const bool act = tid < 8 * NVU;
+    auto rload = [&](int t) {
+      return tagged_load(a.reduced + ((int64_t)(t < tiles ? t : 0) * TM + 8 * grp + (act ? kt : 0)) * NV + (act ? v : 0));
+    };
+    uint64_t wn = ph < tiles ? rload(ph) : 0;
+    for (int t = ph; t < tiles; t += 8) {
+      uint64_t w = wn;
+      wn = rload(t + 8);
+      const uint64_t* wp = a.reduced + ((int64_t)t * TM + 8 * grp + (act ? kt : 0)) * NV + (act ? v : 0);
+      uint32_t it = 0;
+      while (__syncthreads_or(act && (uint32_t)(w >> 32) != tag) != 0) {
+        __builtin_amdgcn_s_sleep(2);
+        // bounded: a wait that expires sets the error word, and every other
+        // wait of the launch gives up as soon as it sees it
+        if (++it > kPersistSpinLimit ||
+            __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+          if (tid == 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        if (act && (uint32_t)(w >> 32) != tag) w = tagged_load(wp);
+      }
+      if (act) fin[kt * NV + v] = tagged_value(w);
+      __syncthreads();  // fin
+      if (tid < 8) {
+        const int64_t tok = (int64_t)t * TM + 8 * grp + tid;
+        float cf[kCoeffs], q[4];
+        finalize_token<FUSED>(fin + tid * NV, a.bias, C, a.sc, cf, q);
+        if (tok < a.T) {
+          float4* o = reinterpret_cast<float4*>(a.coeffs_out + tok * kCoeffs);
+#pragma unroll
+          for (int k = 0; k < 6; ++k) o[k] = make_float4(cf[4 * k], cf[4 * k + 1], cf[4 * k + 2], cf[4 * k + 3]);
+        }
+        if constexpr (FUSED) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tagged_store(a.publish + tok * 4 + i, q[i], tag);
+        }
+      }
+      __syncthreads();  // fin is rewritten by the next tile
+    }
+  } else {
+    // ------------------------- stream workgroup -------------------------
+    const int split = (int)blockIdx.x % S, r = (int)blockIdx.x / S;
+    const int c0 = split * kCC;
+    const int c8 = tid & 15, tr = tid >> 4;  // token tr of the tile, channels c0 + 8*c8 .. +8
+    const int cl = c0 + c8 * 8;
+    const int n16 = lane & 15, g = lane >> 4;
+    const int niter = r < tiles ? (tiles - r + L - 1) / L : 0;
+    // Level-1 reduce: workgroup `split` (< 32) sums token `split` of tile
+    // t_{i-R1} over the S splits.  Word v takes RT threads, thread rr the
+    // splits [rr*LR, rr*LR + LR); run sums are added in run order.
+    constexpr int RT = kPersistThreads / NVU;
+    const bool r1own = split < TM;
+    const int LR = (S + RT - 1) / RT;
+    const int pv = tid / RT, rr = tid % RT;
+    const bool r1act = r1own && pv < NVU;
+    const int nr = r1act ? max(0, min(LR, S - rr * LR)) : 0;
+    uint64_t w1[kR1Run];
+    auto issue_r1 = [&](int i1) {
+      const int t1 = i1 >= 0 && i1 < niter ? r + L * i1 : 0;
+      const uint64_t* b1 = a.partials + (((int64_t)t1 * S + rr * LR) * TM + (r1own ? split : 0)) * NV + (r1act ? pv : 0);
+#pragma unroll
+      for (int q = 0; q < kR1Run; ++q) w1[q] = tagged_load(b1 + (q < nr ? q : 0) * (int64_t)(TM * NV));
+    };
+
+    // projection slice -> LDS
+    for (int idx = tid; idx < 4 * 4 * kPackBlocks * kWave; idx += kPersistThreads) {
+      const int ln = idx & 63, b = (idx >> 6) % kPackBlocks, jq = (idx >> 6) / kPackBlocks;
+      const int j = jq >> 2, kq = jq & 3;
+      const int64_t kstep = ((int64_t)j * C + c0 + kq * 32) >> 5;
+      phi_lds[idx] = reinterpret_cast<const u32x4_t*>(a.phi_packed)[(kstep * kPackBlocks + b) * kWave + ln];
+    }
+    if constexpr (FUSED) {
+      if (tid < kCC) gam[tid] = a.gamma[c0 + tid];
+    }
+
+    // Stream registers of the next tile (x of 4 routes, y) and its post
+    // coefficients: loaded once the current tile's have been used (after its
+    // post step), so one set suffices.  Rows past T load row 0 and are
+    // zeroed after use.
+    u32x4_t nx[4], ny = u32x4_t{0, 0, 0, 0};
+    float4 ncf = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto issue = [&](int i) {
+      const int t = r + L * (i < niter ? i : 0);
+      const int64_t tok = (int64_t)t * TM + tr;
+      const int64_t tc = tok < a.T ? tok : 0;
+      const uint16_t* xp = a.x + tc * (int64_t)(4 * C) + cl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nx[j] = ld16_stream(xp + (int64_t)j * C);
+      if constexpr (FUSED) {
+        ny = ld16_stream(a.y + tc * (int64_t)C + cl);
+        const int64_t ct = (int64_t)t * TM + tid / 5;
+        const bool cv = tid < TM * 5 && ct < a.T;
+        ncf = reinterpret_cast<const float4*>(a.coeffs_in + (cv ? ct : 0) * kCoeffs)[1 + (cv ? tid % 5 : 0)];
+      }
+    };
+    // q words of the tile whose pre step runs in iteration i
+    uint64_t nq = 0;
+    auto issue_q = [&](int i) {
+      const int ic = i - D;
+      const int t = ic >= 0 && ic < niter ? r + L * ic : 0;
+      nq = tagged_load(a.publish + (int64_t)t * TM * 4 + (tid & (TM * 4 - 1)));
+    };
+
+    u32x4_t ring[D][4];  // x' of the last D tiles (packed bf16, 4 routes)
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ring[k][j] = u32x4_t{0, 0, 0, 0};
+
+    // Iteration i: pre step of tile t_{i-D} (x' from the ring), then phase
+    // A of tile t_i.  The steady-state iterations have no data-dependent
+    // branch around memory operations, so the compiler's wait counts stay
+    // exact across the loop: the next tile's loads, issued first, are waited
+    // for without waiting for this iteration's stores.
+    auto body = [&](int i, auto kA, auto kC) {
+      constexpr bool doA = decltype(kA)::value;
+      constexpr bool doC = FUSED && decltype(kC)::value;
+      const int t = r + L * i;
+      // this tile's data (loaded during the previous iteration)
+      u32x4_t* cx = nx;
+      u32x4_t& cy = ny;
+      const float4 ccf = ncf;
+      const uint64_t cq = nq;
+      const int i1 = i - kPersistR1;
+      const bool doR1 = r1own && i1 >= 0 && i1 < niter;
+      issue_r1(i1);  // clamped addresses; used only when doR1
+      if constexpr (FUSED) issue_q(i + 1);
+
+      if constexpr (FUSED) {
+        if (doA && tid < TM * 5) {
+          const bool ok = (int64_t)t * TM + tid / 5 < a.T;
+          float* d = &cfs[tid / 5][4 * (tid % 5)];
+          d[0] = ok ? ccf.x : 0.0f;
+          d[1] = ok ? ccf.y : 0.0f;
+          d[2] = ok ? ccf.z : 0.0f;
+          d[3] = ok ? ccf.w : 0.0f;
+        }
+        if (doC && tid < TM * 4) {
+          const uint64_t* qp = a.publish + (int64_t)(r + L * (i - D)) * TM * 4 + tid;
+          uint64_t qw = cq;
+          uint32_t it = 0;
+          while ((uint32_t)(qw >> 32) != tag) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++it > kPersistSpinLimit ||
+                __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            qw = tagged_load(qp);
+          }
+          (&qs[0][0])[tid] = tagged_value(qw);
+        }
+      }
+      __syncthreads();  // cfs, qs; the previous iteration's readers of xs are done
+
+      // ---- pre step of tile t_{i-D} from the x' registers ----
+      if constexpr (FUSED) {
+        if (doC) {
+          const int64_t tok = (int64_t)(r + L * (i - D)) * TM + tr;
+          const bool valid = tok < a.T;
+          const float q0 = qs[tr][0], q1 = qs[tr][1], q2 = qs[tr][2], q3 = qs[tr][3];
+          float xv[4][8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) unpack8(ring[0][j], xv[j]);
+          float hv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float vv = q0 * xv[0][e];
+            vv = __builtin_fmaf(q1, xv[1][e], vv);
+            vv = __builtin_fmaf(q2, xv[2][e], vv);
+            vv = __builtin_fmaf(q3, xv[3][e], vv);
+            hv[e] = vv * gam[c8 * 8 + e];
+          }
+          const u32x4_t hb = pack8(hv);
+          if (a.h != nullptr && valid) st16_stream(a.h + tok * (int64_t)C + cl, hb);
+          if constexpr (MX) {
+            float hr[8];
+            unpack8(hb, hr);
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
+            amax = __builtin_fmaxf(amax, MHC_DPP(amax, kDppQuadSwap1));
+            amax = __builtin_fmaxf(amax, MHC_DPP(amax, kDppQuadSwap2));
+            const int ex = mx_scale_exponent(amax);
+            const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w0 |= e4m3_code(hr[e] * scale) << (8 * e);
+              w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
+            }
+            if (valid) {
+              *reinterpret_cast<u32x2_t*>(a.h_fp8 + tok * (int64_t)C + cl) = u32x2_t{w0, w1};
+              if ((c8 & 3) == 0) a.h_scale[tok * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
+            }
+          }
+        }
+        // shift the x' ring: slot 0 is consumed
+#pragma unroll
+        for (int k = 0; k + 1 < D; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ring[k][j] = ring[k + 1][j];
+      }
+
+      if (doA) {
+        // ---- phase A of tile t_i ----
+        const int64_t tok = (int64_t)t * TM + tr;
+        const bool valid = tok < a.T;
+        if (!valid) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cx[j] = u32x4_t{0, 0, 0, 0};
+          cy = u32x4_t{0, 0, 0, 0};
+        }
+        if constexpr (FUSED) {
+          float pw[4], rs[16];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pw[k] = cfs[tr][k];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) rs[k] = cfs[tr][4 + k];
+          u32x4_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float xl[4] = {bf16_lo(cx[0][q]), bf16_lo(cx[1][q]), bf16_lo(cx[2][q]), bf16_lo(cx[3][q])};
+            const float xh[4] = {bf16_hi(cx[0][q]), bf16_hi(cx[1][q]), bf16_hi(cx[2][q]), bf16_hi(cx[3][q])};
+            const float yl = bf16_lo(cy[q]), yh = bf16_hi(cy[q]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              o[j][q] = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
+                                    post_chain(pw[j], yh, &rs[4 * j], xh[0], xh[1], xh[2], xh[3]));
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cx[j] = o[j];
+          if (valid) {
+            uint16_t* xo = a.x_out + tok * (int64_t)(4 * C) + cl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, cx[j]);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ring[D - 1][j] = cx[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[xs_offset(tr, j, c8)] = cx[j];
+        // the stream registers are free: load the next tile
+        issue(i + 1);
+      }
+      __syncthreads();  // x' staged
+
+      if (doA) {
+        // projection: wave w covers route w/2, k-steps 2(w%2) and 2(w%2)+1,
+        // both 16-token row blocks; Gram: k-step w%4, token groups 4(w/4)..+3
+        const int jr = wave >> 1;
+        f32x4_t acc[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          acc[rb][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          acc[rb][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int kq = 2 * (wave & 1) + kk;
+          const u32x4_t* bp = phi_lds + ((jr * 4 + kq) * kPackBlocks) * kWave + lane;
+          u32x4_t bf[kPackBlocks];
+#pragma unroll
+          for (int b = 0; b < kPackBlocks; ++b) bf[b] = bp[b * kWave];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(rb * 16 + n16, jr, kq * 4 + g)]);
+#pragma unroll
+            for (int b = 0; b < kPackBlocks; ++b)
+              acc[rb][b < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  av, __builtin_bit_cast(bf16x8_t, bf[b]), acc[rb][b < 3 ? 0 : 1], 0, 0, 0);
+          }
+        }
+        const int kg = wave & 3;
+        float gv[4][4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int qg = 4 * (wave >> 2) + qq;
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(4 * qg + (n16 >> 2), n16 & 3, kg * 4 + g)]);
+          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, av, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gv[qq][e] = d[e];
+        }
+        __syncthreads();  // x' staging no longer read: the partials reuse it
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v1 = acc[rb][1][e];
+            const float mid = __shfl_xor(v1, 8);
+            const int row = rb * 16 + 4 * g + e;
+            redP[(wave * TM + row) * 24 + n16] = acc[rb][0][e];
+            if (n16 < 8) redP[(wave * TM + row) * 24 + 16 + n16] = v1 + mid;
+          }
+        }
+        if ((n16 >> 2) == g) {
+          const int jj = n16 & 3;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int row = 4 * (4 * (wave >> 2) + qq) + g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (e <= jj) redG[(kg * TM + row) * 10 + gram_slot(e, jj)] = gv[qq][e];
+          }
+        }
+      }
+      __syncthreads();  // wave partials
+      // Wait here for every memory operation issued so far: the next
+      // tile's loads (issued at the top of this iteration), the x' and h
+      // stores, and the previous iteration's partial stores have all had
+      // most of an iteration to complete.  The partial stores below go
+      // out last and are waited for only one iteration later, so no wait
+      // inside an iteration depends on their write-through latency.
+      // (Exactly three stores per thread; threads past the tile's words
+      // store the last word again.)
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      // level-1 reduce: check the gathered words (loaded long ago) and
+      // write the run sums
+      {
+        const int t1 = doR1 ? r + L * i1 : 0;
+        const uint64_t* b1 = a.partials + (((int64_t)t1 * S + rr * LR) * TM + (r1own ? split : 0)) * NV + (r1act ? pv : 0);
+        uint32_t it = 0;
+        for (;;) {
+          bool stale = false;
+#pragma unroll
+          for (int q = 0; q < kR1Run; ++q) stale |= doR1 && q < nr && (uint32_t)(w1[q] >> 32) != tag;
+          if (!stale) break;
+          __builtin_amdgcn_s_sleep(1);
+          if (++it > kPersistSpinLimit ||
+              __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+            __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+#pragma unroll
+          for (int q = 0; q < kR1Run; ++q)
+            if (doR1 && q < nr && (uint32_t)(w1[q] >> 32) != tag) w1[q] = tagged_load(b1 + q * (int64_t)(TM * NV));
+        }
+        float rs = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kR1Run; ++q) rs += q < nr ? tagged_value(w1[q]) : 0.0f;
+        if (pv < NVU) r1runs[pv][rr] = rs;
+      }
+      if (doA) {
+        uint64_t* part = a.partials + ((int64_t)t * S + split) * (TM * NV);
+        static_assert(TM * NV <= 3 * kPersistThreads, "three partial words per thread");
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const int idx = min(tid + k * kPersistThreads, TM * NV - 1);
+          const int mm = idx / NV, v = idx % NV;
+          float sum;
+          if (v < 24) {
+            sum = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < 8; ++ww) sum += redP[(ww * TM + mm) * 24 + v];
+          } else if constexpr (FUSED) {
+            sum = ((redG[(0 * TM + mm) * 10 + v - 24] + redG[(1 * TM + mm) * 10 + v - 24]) +
+                   redG[(2 * TM + mm) * 10 + v - 24]) + redG[(3 * TM + mm) * 10 + v - 24];
+          } else {
+            sum = 0.0f;  // coeffs: trace of the Gram matrix
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+              sum += ((redG[(kq * TM + mm) * 10 + 0] + redG[(kq * TM + mm) * 10 + 1]) +
+                      redG[(kq * TM + mm) * 10 + 2]) + redG[(kq * TM + mm) * 10 + 3];
+          }
+          tagged_store(part + idx, sum, tag);
+        }
+      }
+      __syncthreads();  // level-1 run sums
+      if (doR1 && tid < NVU) {
+        float sum = 0.0f;
+        for (int q = 0; q < RT; ++q) sum += r1runs[tid][q];
+        tagged_store(a.reduced + ((int64_t)(r + L * i1) * TM + split) * NV + tid, sum, tag);
+      }
+    };
+    using Yes = BoolC<true>;
+    using No = BoolC<false>;
+    if (niter > 0) issue(0);
+    if constexpr (FUSED) issue_q(0);
+    int i = 0;
+    const int pro = niter < D ? niter : D;
+    for (; i < pro; ++i) body(i, Yes{}, No{});
+    // (an empty memory counter on entry keeps the loop's own wait counts exact)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+    for (; i < niter; ++i) body(i, Yes{}, Yes{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+    for (; i < niter + (FUSED ? D : kPersistR1); ++i) {
+      if (FUSED && i >= D) {
+        body(i, No{}, Yes{});
+      } else {
+        body(i, No{}, No{});
+      }
+    }
+  }
+
+  // ---- leave: the last workgroup to finish advances the launch epoch ----
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(a.tiles_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1u) {
+      __hip_atomic_store(a.tiles_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ===========================================================================
 // Post (standalone): one thread per (token, 8 channels); consecutive threads
 // read consecutive 16-byte chunks of each route.
 // ===========================================================================
@@ -806,7 +1334,22 @@ static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream
   return hipGetLastError();
 }
 
+template <int MODE>
+static hipError_t launch_persist_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(p.s * p.lanes + kPersistTM)), block(kPersistThreads);
+  k_persist<MODE><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStream_t s) {
+  if (plan.lanes > 0) {
+    switch (mode) {
+      case kModeCoeffs: return launch_persist_mode<kModeCoeffs>(plan, a, s);
+      case kModeFused: return launch_persist_mode<kModeFused>(plan, a, s);
+      case kModeFusedMx: return launch_persist_mode<kModeFusedMx>(plan, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (mode) {
     case kModeCoeffs: return launch_split_mode<kModeCoeffs>(plan, a, s);
     case kModeFused: return launch_split_mode<kModeFused>(plan, a, s);

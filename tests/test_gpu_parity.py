@@ -69,6 +69,21 @@ def to_dev(inp):
 
 SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048)]
 
+# shapes the persistent schedule takes (32 <= C/128 <= 64, enough tiles),
+# with a ragged last tile
+PERSISTENT = [(300, 7168), (500, 4096)]
+
+
+@pytest.fixture(params=["staged", "persistent"])
+def schedule(request, monkeypatch):
+    """Runs the test under each kernel schedule (MHC_SCHEDULE is read by the
+    library on every call); afterwards the workspace error word must be 0."""
+    monkeypatch.setenv("MHC_SCHEDULE", request.param)
+    yield request.param
+    torch.cuda.synchronize()
+    for ws in list(mhc.binding._WS.values()):
+        assert mhc.workspace_error(ws) == 0, "a bounded wait expired"
+
 
 # ---------------------------------------------------------------------------
 # standalone ops, every element
@@ -140,6 +155,26 @@ def check_mxfp8(g, ref):
     rms = np.sqrt(np.mean(ref["h"] ** 2, axis=1))[:, None, None]
     bound = np.ldexp(1.0, e)[:, :, None] * 16.0 + 1e-2 * np.maximum(np.abs(ho), rms)
     assert np.all(np.abs(dec - ho) <= bound)
+
+
+@pytest.mark.parametrize("T,C", PERSISTENT)
+def test_coeffs_schedules(T, C, schedule):
+    inp = small_inputs(T, C, seed=11)
+    d = to_dev(inp)
+    cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
+    torch.cuda.synchronize()
+    ref = O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw())
+    assert_coeffs_close(f64(cf), ref)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("T,C", PERSISTENT)
+def test_fused_schedules(T, C, mx, schedule):
+    inp = small_inputs(T, C, seed=12)
+    d = to_dev(inp)
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=mx)
+    torch.cuda.synchronize()
+    check_fused(inp, out, mx=mx)
 
 
 @pytest.mark.parametrize("T,C", SMALL)
@@ -326,7 +361,7 @@ def host_rows(d, rows):
             for k, v in d.items() if isinstance(v, torch.Tensor)}
 
 
-def test_prefill_workload_sampled():
+def test_prefill_workload_sampled(schedule):
     d = full_inputs("prefill")
     out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"])
     torch.cuda.synchronize()
@@ -337,7 +372,7 @@ def test_prefill_workload_sampled():
     check_fused(inp, g)
 
 
-def test_mxfp8_workload_sampled():
+def test_mxfp8_workload_sampled(schedule):
     d = full_inputs("mxfp8")
     out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
     torch.cuda.synchronize()
@@ -355,7 +390,7 @@ def test_decode_workload():
     check_fused({k: v.cpu() for k, v in d.items() if isinstance(v, torch.Tensor)}, out)
 
 
-def test_long_workload_sampled():
+def test_long_workload_sampled(schedule):
     d = full_inputs("long")
     T = d["x"].shape[0]
     cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
@@ -378,7 +413,7 @@ def test_long_workload_sampled():
     check_fused(inp, g)
 
 
-def test_fused_matches_gpu_composition_on_every_token():
+def test_fused_matches_gpu_composition_on_every_token(schedule):
     # every token of the prefill workload: the fused pass equals the GPU's own
     # post -> coeffs -> pre chain (summation orders differ, so within the
     # tolerances), which exercises the cross-workgroup reduction on all tiles
