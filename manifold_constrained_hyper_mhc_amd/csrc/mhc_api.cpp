@@ -120,7 +120,7 @@ void choose_kernel(mhc::Plan& p) {
   if (p.m != 32 || p.s < 32 || p.s > 64 || (p.s + 14) / 15 > 5) return;
   const int cus = device_cus();
   const int lanes = (cus - 32) / p.s;
-  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes) return;
+  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes || p.s * lanes + 32 > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;
 }
 
@@ -162,6 +162,8 @@ Plan make_plan(int64_t T, int64_t C) {
   off = round256(off + (size_t)p.tiles * p.s * sizeof(uint64_t));
   p.off_red = off;
   off = round256(off + (size_t)p.tiles * p.m * kPartVals * sizeof(uint64_t));
+  p.off_sink = off;
+  off = round256(off + kSinkBytes);
   p.off_phi = off;
   off = round256(off + phi_packed_bytes(C));
   p.total = off;
@@ -184,6 +186,7 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
   a.reduced = reinterpret_cast<uint64_t*>(base + plan.off_red);
+  a.sink = reinterpret_cast<uint32_t*>(base + plan.off_sink);
   a.T = T;
   a.tiles = (uint32_t)plan.tiles;
   a.C = (int)C;

@@ -134,16 +134,20 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // (the kernel is instantiated for runs of up to 8 and up to kRunMax).
 constexpr int kMaxTileTokensPerGroup = 8;
 
+// Tagged words are exchanged between workgroups on different XCDs, whose L2
+// caches are not kept coherent with each other: stores and loads use system
+// scope (sc0 sc1), which writes through to memory and reads from it, so a
+// poll never spins on a stale line of its own L2.
 __device__ __forceinline__ void tagged_store(uint64_t* p, float v, uint32_t tag) {
   const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
-  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 // XCD (accelerator complex die) the calling wave runs on: hardware register
 // XCC_ID, bits 3:0.
 __device__ __forceinline__ uint32_t xcd_id() { return (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u; }
 
 __device__ __forceinline__ uint64_t tagged_load(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 __device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
@@ -661,22 +665,33 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 // One workgroup of 512 threads per CU, all resident at once:
 //   * S*L "stream" workgroups: workgroup (split s, lane r) owns the 128
 //     channels of split s and the tiles t = r, r + L, r + 2L, ...  Its slice
-//     of the packed projection (80 KB) is copied to LDS once.  Iteration i
-//     handles tile t_i: the pre step of tile t_{i-D} (x' of that tile kept
-//     in registers since its own phase A, D iterations earlier), then phase
-//     A of t_i (post, x' out, projection and Gram on the matrix cores from
-//     LDS, tile partial to the workspace), while the loads of t_{i+1} are in
-//     flight.
-//   * 32 "reduce" workgroups: workgroup m owns token m of every tile; wave w
-//     handles tiles t = w, w + 8, ...: it gathers the S partials of its token
-//     (lane = split), sums them with a fixed butterfly, finalises the
-//     coefficients on 16 lanes and publishes q_i = pre'_i * r_h.
+//     of the packed projection (72 KB: block 4 keeps only its 32 used lanes)
+//     is copied to LDS once.  Iteration i handles tile t_i:
+//       - the pre step of tile t_{i-D}, from x' kept in registers since its
+//         own phase A, D iterations earlier;
+//       - phase A of t_i: post, x' out, projection and Gram on the matrix
+//         cores, tile partial to the workspace.
+//     The x slice of a tile (32 KB) is copied into one of two LDS slots by
+//     asynchronous global->LDS loads issued two iterations ahead; y and the
+//     post coefficients are loaded into registers one iteration ahead.
+//     Every lane works in the operand layout of v_mfma_f32_16x16x32_bf16:
+//     wave w takes tokens 16*(w%2) .. +15 and the 32-channel step w/2, lane
+//     l the token l%16 and channels 8*(l/16) .. +7 of that step, for all
+//     four routes.  Its x' registers are then directly the A operands of the
+//     projection (B = packed projection fragments from LDS) and of the Gram
+//     products x'_i x'_j^T, whose diagonals are the per-token route Gram
+//     entries; no x' staging through LDS.
+//   * Level-1 reduce: stream workgroup `split` (< 32) sums token `split` of
+//     a tile over the S splits, from words gathered one iteration after the
+//     tile's phase A and added up in the next.
+//   * 32 "reduce" workgroups finalise the coefficients of 8 tokens at a
+//     time from the level-1 sums and publish q_i = pre'_i * r_h.
 // Stream workgroups wait for q words published by reduce workgroups, which
-// wait for partials of stream workgroups, so the launch needs all S*L + 32
+// wait for sums of stream workgroups, so the launch needs all S*L + 32
 // workgroups resident together (the host sizes L from the CU count; every
 // wait is bounded and sets the workspace error word on expiry).  Nothing is
 // read back from x_out: the pre step uses the x' registers, so the HBM
-// traffic is the algorithmic one plus the partial and q words.
+// traffic is the algorithmic one plus the partial, level-1 and q words.
 // ===========================================================================
 template <bool B>
 struct BoolC {
@@ -684,57 +699,42 @@ struct BoolC {
 };
 constexpr int kPersistThreads = 512;
 constexpr int kPersistTM = 32;
-constexpr int kPersistDepth = 3;  // iterations between phase A and the pre step of a tile
-constexpr int kPersistR1 = 1;     // iterations between phase A and the level-1 reduce of a tile
-constexpr int kR1Run = 5;         // splits summed by one thread in the level-1 reduce (S <= 75)
+constexpr int kPersistDepth = 5;  // iterations between phase A and the pre step of a tile
+constexpr int kPersistR1 = 2;     // iterations between phase A and the level-1 reduce of a tile
+constexpr int kR1Run = 5;         // splits summed by one thread in the level-1 reduce (S <= 5 * 15)
 constexpr uint32_t kPersistSpinLimit = 1u << 18;
 constexpr int kPersistMaxS = 64;  // splits per row the reduce threads can gather
+// LDS projection fragments of one (route, 32-channel step): blocks 0-3 whole
+// (64 lanes each) and the 32 lanes of block 4 whose column is < 8 (the rest
+// of block 4 is zero), in 16-byte units.
+constexpr int kPhiFrag = 4 * kWave + kWave / 2;
+// Whether a bounded wait of the launch has expired (read from memory; the
+// polls look at it every 16th round only, so that a poll round costs one
+// load latency).
+__device__ __forceinline__ bool error_seen(uint32_t* err) {
+  return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u;
+}
+constexpr int kSlotChunks = kPersistTM * 4 * 16;  // 16-byte chunks of a tile's x slice
 
-// Coefficients of one token in one thread (the reduce workgroups finalise
-// eight tokens side by side): sums = 24 projections, then the Gram matrix
-// (fused) or the sum of squares (coeffs).  The same formulas as
-// finalize_wave: RMS scale, sigmoids, exp, and sinkhorn_iters rounds of row
-// then column normalisation, each multiplying by the reciprocal of
-// (sum + sinkhorn_eps); q_i = pre_i * r_h from the Gram quadratic form.
-template <bool FUSED>
-__device__ __forceinline__ void finalize_token(const float* sums, const float* bias, int C, const Scalars& sc,
-                                               float* cf, float* q) {
-  const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
-  const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = 1.0f / (1.0f + expf(-(r * sums[i] + bias[i])));
-    cf[i] = p[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) cf[4 + i] = sc.hc_post_scale * (1.0f / (1.0f + expf(-(r * sums[4 + i] + bias[4 + i]))));
-  float mres[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) mres[k] = expf(r * sums[8 + k] + bias[8 + k]);
-  const float eps = sc.sinkhorn_eps;
-  for (int it = 0; it < sc.sinkhorn_iters; ++it) {
-#pragma unroll
-    for (int jr = 0; jr < 4; ++jr) {
-      const float rs = __builtin_amdgcn_rcpf(((mres[4 * jr] + mres[4 * jr + 1]) + (mres[4 * jr + 2] + mres[4 * jr + 3])) + eps);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mres[4 * jr + i] *= rs;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float cs = __builtin_amdgcn_rcpf(((mres[i] + mres[4 + i]) + (mres[8 + i] + mres[12 + i])) + eps);
-#pragma unroll
-      for (int jr = 0; jr < 4; ++jr) mres[4 * jr + i] *= cs;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 16; ++k) cf[8 + k] = mres[k];
-  if constexpr (FUSED) {
-    const float gq = gram_quadratic(sums + 24, p);
-    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = p[i] * rh;
-  }
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Asynchronous copy of 16 bytes per lane from global memory into LDS: lane l
+// writes LDS bytes [base + 16 l, base + 16 l + 16), base uniform over the
+// wave.  Written as inline assembly so that the compiler neither counts nor
+// waits for it: callers wait with an explicit vmcnt, and the compiler's own
+// waits for other loads only get more conservative from the uncounted ops.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
 }
 
 template <int MODE>
@@ -743,16 +743,17 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   constexpr bool MX = MODE == kModeFusedMx;
   constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
   constexpr int NVU = FUSED ? NV : 25;
-  // LDS: projection slice [4 routes][4 k-steps][5 blocks][64 lanes] x 16 B,
-  // x' staging (aliased by the wave partials), post coefficients, q words.
-  __shared__ __attribute__((aligned(16))) u32x4_t phi_lds[4 * 4 * kPackBlocks * kWave];
-  __shared__ __attribute__((aligned(16))) u32x4_t xs[TM * 4 * 16];
+  // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B, two x
+  // slots [token][route][16 chunks] x 16 B (chunk c of token t at position
+  // c ^ (t % 16), so that the 16 tokens a wave reads at once hit distinct
+  // banks), the wave partials, post coefficients, q words, level-1 run sums.
+  __shared__ __attribute__((aligned(16))) u32x4_t phi_lds[16 * kPhiFrag];
+  __shared__ __attribute__((aligned(16))) u32x4_t xslot[2][kSlotChunks];
+  __shared__ float red[8][16][NV];  // [wave][token of its row block][projection, Gram]
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
-  __shared__ float r1runs[NVU][kPersistThreads / NVU];  // level-1 reduce: run sums of each word
-  __shared__ float gam[FUSED ? kCC : 1];                  // gamma of this split
-  float* redP = reinterpret_cast<float*>(xs);      // [8 waves][TM][24]
-  float* redG = redP + 8 * TM * 24;                // [4 k-steps][TM][10]
+  __shared__ float r1runs[NVU][kPersistThreads / NVU];
+  __shared__ float gam[FUSED ? kCC : 1];
   float* finw = reinterpret_cast<float*>(phi_lds);  // reduce workgroups: [8 tokens][NV]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -766,8 +767,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     // Reduce workgroup j owns tokens 8*(j%4) .. +7 of the tiles t = j/4 + 8k.
     // The split sums of each token were already added up by the stream
     // workgroup of split = token (reduced words); thread (token k, word v)
-    // loads one of them, and after a barrier eight threads finalise one
-    // token each, with the whole 4x4 Sinkhorn in registers.
+    // loads one of them, and after a barrier each of the eight waves
+    // finalises one token, the Sinkhorn matrix on 16 lanes.
     const int j = (int)blockIdx.x - nstream;
     const int grp = j & 3, ph = j >> 2;
     float* fin = finw;  // [8 tokens][NV]
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         // bounded: a wait that expires sets the error word, and every other
         // wait of the launch gives up as soon as it sees it
         if (++it > kPersistSpinLimit ||
-            __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+            ((it & 15u) == 0u && error_seen(a.err))) {
           if (tid == 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
@@ -795,18 +796,15 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       }
       if (act) fin[kt * NV + v] = tagged_value(w);
       __syncthreads();  // fin
-      if (tid < 8) {
-        const int64_t tok = (int64_t)t * TM + 8 * grp + tid;
-        float cf[kCoeffs], q[4];
-        finalize_token<FUSED>(fin + tid * NV, a.bias, C, a.sc, cf, q);
-        if (tok < a.T) {
-          float4* o = reinterpret_cast<float4*>(a.coeffs_out + tok * kCoeffs);
-#pragma unroll
-          for (int k = 0; k < 6; ++k) o[k] = make_float4(cf[4 * k], cf[4 * k + 1], cf[4 * k + 2], cf[4 * k + 3]);
-        }
+      {
+        // wave w finalises token w of the group (lanes 0-15: Sinkhorn
+        // matrix, 16-23: pre and post)
+        const int64_t tok = (int64_t)t * TM + 8 * grp + wave;
+        float q[4];
+        const float cv = finalize_wave<FUSED>(fin + wave * NV, a.bias, C, a.sc, lane, q);
+        if (tok < a.T && lane < 24) a.coeffs_out[tok * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
         if constexpr (FUSED) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tagged_store(a.publish + tok * 4 + i, q[i], tag);
+          if (lane < 4) tagged_store(a.publish + tok * 4 + lane, q[lane], tag);
         }
       }
       __syncthreads();  // fin is rewritten by the next tile
@@ -815,57 +813,83 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     // ------------------------- stream workgroup -------------------------
     const int split = (int)blockIdx.x % S, r = (int)blockIdx.x / S;
     const int c0 = split * kCC;
-    const int c8 = tid & 15, tr = tid >> 4;  // token tr of the tile, channels c0 + 8*c8 .. +8
-    const int cl = c0 + c8 * 8;
     const int n16 = lane & 15, g = lane >> 4;
+    const int rbk = wave & 1, ks = wave >> 1;
+    const int m = rbk * 16 + n16;  // this lane's token in the tile
+    const int ch = 32 * ks + 8 * g;  // this lane's first channel in the split
+    const int cl = c0 + ch;
+    const int xpos = (4 * ks + g) ^ n16;  // LDS position of this lane's chunk in a row
     const int niter = r < tiles ? (tiles - r + L - 1) / L : 0;
-    // Level-1 reduce: workgroup `split` (< 32) sums token `split` of tile
-    // t_{i-R1} over the S splits.  Word v takes RT threads, thread rr the
-    // splits [rr*LR, rr*LR + LR); run sums are added in run order.
+    // Level-1 reduce: workgroup `split` (< 32) sums token `split` of
+    // tile t_{i-R1} over the S splits.  Thread (word v = tid % NVU, first
+    // split s0 = tid / NVU < RT) adds the splits s0, s0 + RT, ... in that
+    // order; the RT sums of a word are then added in the order of s0.  A
+    // wave's gather touches two splits' 34 contiguous words at a time.
     constexpr int RT = kPersistThreads / NVU;
     const bool r1own = split < TM;
-    const int LR = (S + RT - 1) / RT;
-    const int pv = tid / RT, rr = tid % RT;
-    const bool r1act = r1own && pv < NVU;
-    const int nr = r1act ? max(0, min(LR, S - rr * LR)) : 0;
+    const int pv = tid % NVU, s0 = tid / NVU;
+    const bool r1act = r1own && s0 < RT;
+    const int nr = r1act ? (S - s0 + RT - 1) / RT : 0;
     uint64_t w1[kR1Run];
-    auto issue_r1 = [&](int i1) {
+    auto r1_base = [&](int i1) {
       const int t1 = i1 >= 0 && i1 < niter ? r + L * i1 : 0;
-      const uint64_t* b1 = a.partials + (((int64_t)t1 * S + rr * LR) * TM + (r1own ? split : 0)) * NV + (r1act ? pv : 0);
+      return a.partials + (((int64_t)t1 * S + (r1act ? s0 : 0)) * TM + (r1own ? split : 0)) * NV + pv;
+    };
+    auto issue_r1 = [&](int i1) {
+      const uint64_t* b1 = r1_base(i1);
 #pragma unroll
-      for (int q = 0; q < kR1Run; ++q) w1[q] = tagged_load(b1 + (q < nr ? q : 0) * (int64_t)(TM * NV));
+      for (int q = 0; q < kR1Run; ++q) w1[q] = tagged_load(b1 + (q < nr ? q : 0) * (int64_t)(RT * TM * NV));
     };
 
     // projection slice -> LDS
-    for (int idx = tid; idx < 4 * 4 * kPackBlocks * kWave; idx += kPersistThreads) {
-      const int ln = idx & 63, b = (idx >> 6) % kPackBlocks, jq = (idx >> 6) / kPackBlocks;
-      const int j = jq >> 2, kq = jq & 3;
-      const int64_t kstep = ((int64_t)j * C + c0 + kq * 32) >> 5;
-      phi_lds[idx] = reinterpret_cast<const u32x4_t*>(a.phi_packed)[(kstep * kPackBlocks + b) * kWave + ln];
+    {
+      const u32x4_t* pk = reinterpret_cast<const u32x4_t*>(a.phi_packed);
+      for (int idx = tid; idx < 16 * kPhiFrag; idx += kPersistThreads) {
+        const int jk = idx / kPhiFrag, o = idx % kPhiFrag;
+        const int j = jk >> 2, kq = jk & 3;
+        const int64_t kstep = ((int64_t)j * C + c0 + kq * 32) >> 5;
+        int b, ln;
+        if (o < 4 * kWave) {
+          b = o >> 6;
+          ln = o & 63;
+        } else {
+          b = 4;
+          ln = ((o - 4 * kWave) >> 3) * 16 + ((o - 4 * kWave) & 7);
+        }
+        phi_lds[idx] = pk[(kstep * kPackBlocks + b) * kWave + ln];
+      }
     }
     if constexpr (FUSED) {
       if (tid < kCC) gam[tid] = a.gamma[c0 + tid];
     }
 
-    // Stream registers of the next tile (x of 4 routes, y) and its post
-    // coefficients: loaded once the current tile's have been used (after its
-    // post step), so one set suffices.  Rows past T load row 0 and are
-    // zeroed after use.
-    u32x4_t nx[4], ny = u32x4_t{0, 0, 0, 0};
-    float4 ncf = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    auto issue = [&](int i) {
+    // x slice of tile t_i -> slot i%2: wave-instruction k covers the four
+    // routes of token wave + 8k (1 KB of LDS, 4 x 256 contiguous bytes of x).
+    const uint32_t slot0 = lds_address(&xslot[0][0]), slot1 = lds_address(&xslot[1][0]);
+    auto issue_x = [&](int i) {
       const int t = r + L * (i < niter ? i : 0);
-      const int64_t tok = (int64_t)t * TM + tr;
-      const int64_t tc = tok < a.T ? tok : 0;
-      const uint16_t* xp = a.x + tc * (int64_t)(4 * C) + cl;
+      const uint32_t sb = (i & 1) ? slot1 : slot0;
+      const int jr = lane >> 4, p = lane & 15;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) nx[j] = ld16_stream(xp + (int64_t)j * C);
-      if constexpr (FUSED) {
-        ny = ld16_stream(a.y + tc * (int64_t)C + cl);
-        const int64_t ct = (int64_t)t * TM + tid / 5;
-        const bool cv = tid < TM * 5 && ct < a.T;
-        ncf = reinterpret_cast<const float4*>(a.coeffs_in + (cv ? ct : 0) * kCoeffs)[1 + (cv ? tid % 5 : 0)];
+      for (int k = 0; k < 4; ++k) {
+        const int q = wave + 8 * k;
+        const int64_t tok = (int64_t)t * TM + q;
+        const int64_t tc = tok < a.T ? tok : 0;
+        const uint16_t* src = a.x + tc * (int64_t)(4 * C) + (int64_t)jr * C + c0 + 8 * (p ^ (q & 15));
+        lds_dma16(src, __builtin_amdgcn_readfirstlane(sb + (uint32_t)q * 1024u));
       }
+    };
+    // y and the post coefficients of tile t_i (registers, one iteration ahead)
+    u32x4_t ny = u32x4_t{0, 0, 0, 0};
+    float4 ncf = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto issue_y = [&](int i) {
+      const int t = r + L * (i < niter ? i : 0);
+      const int64_t tok = (int64_t)t * TM + m;
+      const int64_t tc = tok < a.T ? tok : 0;
+      ny = ld16_stream(a.y + tc * (int64_t)C + cl);
+      const int64_t ct = (int64_t)t * TM + tid / 5;
+      const bool cv = tid < TM * 5 && ct < a.T;
+      ncf = reinterpret_cast<const float4*>(a.coeffs_in + (cv ? ct : 0) * kCoeffs)[1 + (cv ? tid % 5 : 0)];
     };
     // q words of the tile whose pre step runs in iteration i
     uint64_t nq = 0;
@@ -874,31 +898,55 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       const int t = ic >= 0 && ic < niter ? r + L * ic : 0;
       nq = tagged_load(a.publish + (int64_t)t * TM * 4 + (tid & (TM * 4 - 1)));
     };
+    // Memory-operation order of an iteration (vmcnt counts them in issue
+    // order; the x slot loads are invisible to the compiler's own counting):
+    //   top:  y, coefficients and q of the next tile (FUSED: 3 loads)
+    //         -- explicit wait: all but the last 4 + 3 + kTopOps ops done --
+    //   B1 .. h and x_out stores (conditional) .. B2
+    //   gathers of the level-1 reduce (5 loads, only in the workgroups of
+    //   splits < 32; used next iteration)
+    //   4 sink stores, so that every load consumed before the next explicit
+    //   wait has at least 4 counted operations between it and the x slot
+    //   loads that follow: a compiler wait for it never covers those
+    //   x slot loads of tile t_{i+2} (4, invisible)
+    //   .. B3 .. partial stores (3)
+    constexpr int kTopOps = FUSED ? 3 : 0;
+    constexpr int kTopWait = 4 + 3 + kTopOps;
+    uint32_t* sinkw = a.sink + (int64_t)blockIdx.x * 16;
 
     u32x4_t ring[D][4];  // x' of the last D tiles (packed bf16, 4 routes)
 #pragma unroll
     for (int k = 0; k < D; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) ring[k][j] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < kR1Run; ++q) w1[q] = 0;
 
-    // Iteration i: pre step of tile t_{i-D} (x' from the ring), then phase
-    // A of tile t_i.  The steady-state iterations have no data-dependent
-    // branch around memory operations, so the compiler's wait counts stay
-    // exact across the loop: the next tile's loads, issued first, are waited
-    // for without waiting for this iteration's stores.
     auto body = [&](int i, auto kA, auto kC) {
       constexpr bool doA = decltype(kA)::value;
       constexpr bool doC = FUSED && decltype(kC)::value;
       const int t = r + L * i;
-      // this tile's data (loaded during the previous iteration)
-      u32x4_t* cx = nx;
-      u32x4_t& cy = ny;
+      const u32x4_t cy = ny;
       const float4 ccf = ncf;
       const uint64_t cq = nq;
-      const int i1 = i - kPersistR1;
+      uint64_t cw[kR1Run];
+#pragma unroll
+      for (int q = 0; q < kR1Run; ++q) cw[q] = w1[q];
+      const int i1 = i - kPersistR1;  // tile whose level-1 sums are formed in this iteration
       const bool doR1 = r1own && i1 >= 0 && i1 < niter;
-      issue_r1(i1);  // clamped addresses; used only when doR1
-      if constexpr (FUSED) issue_q(i + 1);
+      if constexpr (FUSED) {
+        issue_y(i + 1);
+        issue_q(i + 1);
+      }
+      // The slot of tile t_i was filled by loads issued two iterations ago;
+      // since then at least the previous iteration's loads, sink stores, x
+      // slot loads (t_{i+1}) and partial stores and this iteration's loads
+      // were issued: waiting until only the last 4 + 3 + kTopOps are pending
+      // completes the slot, the gathers and the loads of the previous top,
+      // and leaves the loads of t_{i+1} in flight.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTopWait));
+      __builtin_amdgcn_sched_barrier(0);
 
       if constexpr (FUSED) {
         if (doA && tid < TM * 5) {
@@ -910,65 +958,104 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           d[3] = ok ? ccf.w : 0.0f;
         }
         if (doC && tid < TM * 4) {
-          const uint64_t* qp = a.publish + (int64_t)(r + L * (i - D)) * TM * 4 + tid;
+          // (the polling loop is a separate branch, so that the common path
+          // has no loop whose reloads the compiler would wait for)
           uint64_t qw = cq;
-          uint32_t it = 0;
-          while ((uint32_t)(qw >> 32) != tag) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++it > kPersistSpinLimit ||
-                __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            qw = tagged_load(qp);
+          if ((uint32_t)(qw >> 32) != tag) {
+            const uint64_t* qp = a.publish + (int64_t)(r + L * (i - D)) * TM * 4 + tid;
+            uint32_t it = 0;
+            do {
+              __builtin_amdgcn_s_sleep(1);
+              if (++it > kPersistSpinLimit ||
+                  ((it & 15u) == 0u && error_seen(a.err))) {
+                __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+              }
+              qw = tagged_load(qp);
+            } while ((uint32_t)(qw >> 32) != tag);
           }
           (&qs[0][0])[tid] = tagged_value(qw);
         }
       }
-      __syncthreads();  // cfs, qs; the previous iteration's readers of xs are done
+      // level-1 reduce of tile t_{i1}: check the words gathered during the
+      // previous iteration and write the run sums
+      {
+        const uint64_t* b1 = r1_base(i1);
+        auto stale = [&]() {
+          bool st = false;
+#pragma unroll
+          for (int q = 0; q < kR1Run; ++q) st |= doR1 && q < nr && (uint32_t)(cw[q] >> 32) != tag;
+          return st;
+        };
+        if (stale()) {
+          uint32_t it = 0;
+          do {
+            __builtin_amdgcn_s_sleep(1);
+            if (++it > kPersistSpinLimit ||
+                ((it & 15u) == 0u && error_seen(a.err))) {
+              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+#pragma unroll
+            for (int q = 0; q < kR1Run; ++q)
+              if (doR1 && q < nr && (uint32_t)(cw[q] >> 32) != tag) cw[q] = tagged_load(b1 + q * (int64_t)(RT * TM * NV));
+          } while (stale());
+        }
+        float rs = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kR1Run; ++q) rs += q < nr ? tagged_value(cw[q]) : 0.0f;
+        if (s0 < RT) r1runs[pv][s0] = rs;
+      }
+      __syncthreads();  // B1: x slot, cfs, qs, run sums
+      if (doR1 && tid < NVU) {
+        float sum = 0.0f;
+        for (int q = 0; q < RT; ++q) sum += r1runs[tid][q];
+        tagged_store(a.reduced + ((int64_t)(r + L * i1) * TM + split) * NV + tid, sum, tag);
+      }
 
       // ---- pre step of tile t_{i-D} from the x' registers ----
-      if constexpr (FUSED) {
-        if (doC) {
-          const int64_t tok = (int64_t)(r + L * (i - D)) * TM + tr;
-          const bool valid = tok < a.T;
-          const float q0 = qs[tr][0], q1 = qs[tr][1], q2 = qs[tr][2], q3 = qs[tr][3];
-          float xv[4][8];
+      if constexpr (doC) {
+        const int64_t tok = (int64_t)(r + L * (i - D)) * TM + m;
+        const bool valid = tok < a.T;
+        const float q0 = qs[m][0], q1 = qs[m][1], q2 = qs[m][2], q3 = qs[m][3];
+        float xv[4][8];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) unpack8(ring[0][j], xv[j]);
-          float hv[8];
+        for (int j = 0; j < 4; ++j) unpack8(ring[0][j], xv[j]);
+        float hv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float vv = q0 * xv[0][e];
-            vv = __builtin_fmaf(q1, xv[1][e], vv);
-            vv = __builtin_fmaf(q2, xv[2][e], vv);
-            vv = __builtin_fmaf(q3, xv[3][e], vv);
-            hv[e] = vv * gam[c8 * 8 + e];
+        for (int e = 0; e < 8; ++e) {
+          float vv = q0 * xv[0][e];
+          vv = __builtin_fmaf(q1, xv[1][e], vv);
+          vv = __builtin_fmaf(q2, xv[2][e], vv);
+          vv = __builtin_fmaf(q3, xv[3][e], vv);
+          hv[e] = vv * gam[ch + e];
+        }
+        const u32x4_t hb = pack8(hv);
+        if (a.h != nullptr && valid) st16_stream(a.h + tok * (int64_t)C + cl, hb);
+        if constexpr (MX) {
+          // a 32-channel block is the 4 lanes n16, n16 + 16, n16 + 32, n16 + 48
+          float hr[8];
+          unpack8(hb, hr);
+          float amax = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
+          amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+          amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+          const int ex = mx_scale_exponent(amax);
+          const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
+          uint32_t w0 = 0, w1c = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w0 |= e4m3_code(hr[e] * scale) << (8 * e);
+            w1c |= e4m3_code(hr[4 + e] * scale) << (8 * e);
           }
-          const u32x4_t hb = pack8(hv);
-          if (a.h != nullptr && valid) st16_stream(a.h + tok * (int64_t)C + cl, hb);
-          if constexpr (MX) {
-            float hr[8];
-            unpack8(hb, hr);
-            float amax = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
-            amax = __builtin_fmaxf(amax, MHC_DPP(amax, kDppQuadSwap1));
-            amax = __builtin_fmaxf(amax, MHC_DPP(amax, kDppQuadSwap2));
-            const int ex = mx_scale_exponent(amax);
-            const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              w0 |= e4m3_code(hr[e] * scale) << (8 * e);
-              w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
-            }
-            if (valid) {
-              *reinterpret_cast<u32x2_t*>(a.h_fp8 + tok * (int64_t)C + cl) = u32x2_t{w0, w1};
-              if ((c8 & 3) == 0) a.h_scale[tok * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
-            }
+          if (valid) {
+            *reinterpret_cast<u32x2_t*>(a.h_fp8 + tok * (int64_t)C + cl) = u32x2_t{w0, w1c};
+            if (g == 0) a.h_scale[tok * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
           }
         }
+      }
+      if constexpr (FUSED) {
         // shift the x' ring: slot 0 is consumed
 #pragma unroll
         for (int k = 0; k + 1 < D; ++k)
@@ -976,199 +1063,172 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           for (int j = 0; j < 4; ++j) ring[k][j] = ring[k + 1][j];
       }
 
-      if (doA) {
-        // ---- phase A of tile t_i ----
-        const int64_t tok = (int64_t)t * TM + tr;
+      // ---- phase A of tile t_i: x (and y) -> x' in the MFMA A layout ----
+      u32x4_t o[4];
+      if constexpr (doA) {
+        const int64_t tok = (int64_t)t * TM + m;
         const bool valid = tok < a.T;
-        if (!valid) {
+        const u32x4_t* sp = (i & 1) ? &xslot[1][0] : &xslot[0][0];
+        u32x4_t xin[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) cx[j] = u32x4_t{0, 0, 0, 0};
-          cy = u32x4_t{0, 0, 0, 0};
-        }
+        for (int j = 0; j < 4; ++j) xin[j] = sp[(m * 4 + j) * 16 + xpos];
         if constexpr (FUSED) {
           float pw[4], rs[16];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) pw[k] = cfs[tr][k];
+          for (int k = 0; k < 4; ++k) pw[k] = cfs[m][k];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) rs[k] = cfs[tr][4 + k];
-          u32x4_t o[4];
+          for (int k = 0; k < 16; ++k) rs[k] = cfs[m][4 + k];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float xl[4] = {bf16_lo(cx[0][q]), bf16_lo(cx[1][q]), bf16_lo(cx[2][q]), bf16_lo(cx[3][q])};
-            const float xh[4] = {bf16_hi(cx[0][q]), bf16_hi(cx[1][q]), bf16_hi(cx[2][q]), bf16_hi(cx[3][q])};
+            const float xl[4] = {bf16_lo(xin[0][q]), bf16_lo(xin[1][q]), bf16_lo(xin[2][q]), bf16_lo(xin[3][q])};
+            const float xh[4] = {bf16_hi(xin[0][q]), bf16_hi(xin[1][q]), bf16_hi(xin[2][q]), bf16_hi(xin[3][q])};
             const float yl = bf16_lo(cy[q]), yh = bf16_hi(cy[q]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               o[j][q] = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
                                     post_chain(pw[j], yh, &rs[4 * j], xh[0], xh[1], xh[2], xh[3]));
           }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) cx[j] = o[j];
           if (valid) {
             uint16_t* xo = a.x_out + tok * (int64_t)(4 * C) + cl;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, cx[j]);
+            for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, o[j]);
           }
+        } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ring[D - 1][j] = cx[j];
+          for (int j = 0; j < 4; ++j) o[j] = xin[j];
         }
+        if (!valid) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xs[xs_offset(tr, j, c8)] = cx[j];
-        // the stream registers are free: load the next tile
-        issue(i + 1);
+          for (int j = 0; j < 4; ++j) o[j] = u32x4_t{0, 0, 0, 0};
+        }
+        if constexpr (FUSED) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ring[D - 1][j] = o[j];
+        }
       }
-      __syncthreads();  // x' staged
+      __syncthreads();  // B2: every wave has read the slot
+      // gathers of tile t_{i-1} (its partials were stored during the
+      // previous iteration), sink stores, x slice of t_{i+2} into the slot
+      // just read; all unconditional with clamped addresses
+      if (r1own) issue_r1(i - 1);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sinkw[4 * k] = 0u;
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      issue_x(i + 2);
 
-      if (doA) {
-        // projection: wave w covers route w/2, k-steps 2(w%2) and 2(w%2)+1,
-        // both 16-token row blocks; Gram: k-step w%4, token groups 4(w/4)..+3
-        const int jr = wave >> 1;
-        f32x4_t acc[2][2];
+      if constexpr (doA) {
+        // projection: A = x' of route j (16 tokens x 32 channels), B = the
+        // five packed blocks of (route j, step ks); blocks 0-2 accumulate
+        // logits 0..15, blocks 3-4 logits 16..23 (hi+lo | mid)
+        f32x4_t acc0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          acc[rb][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          acc[rb][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int kq = 2 * (wave & 1) + kk;
-          const u32x4_t* bp = phi_lds + ((jr * 4 + kq) * kPackBlocks) * kWave + lane;
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t* bp = phi_lds + (j * 4 + ks) * kPhiFrag;
           u32x4_t bf[kPackBlocks];
 #pragma unroll
-          for (int b = 0; b < kPackBlocks; ++b) bf[b] = bp[b * kWave];
+          for (int b = 0; b < 4; ++b) bf[b] = bp[b * kWave + lane];
+          const u32x4_t b4 = bp[4 * kWave + g * 8 + (n16 & 7)];
+          bf[4] = n16 < 8 ? b4 : u32x4_t{0, 0, 0, 0};
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, o[j]);
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(rb * 16 + n16, jr, kq * 4 + g)]);
-#pragma unroll
-            for (int b = 0; b < kPackBlocks; ++b)
-              acc[rb][b < 3 ? 0 : 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  av, __builtin_bit_cast(bf16x8_t, bf[b]), acc[rb][b < 3 ? 0 : 1], 0, 0, 0);
+          for (int b = 0; b < kPackBlocks; ++b) {
+            if (b < 3) {
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc0, 0, 0, 0);
+            } else {
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc1, 0, 0, 0);
+            }
           }
         }
-        const int kg = wave & 3;
-        float gv[4][4];
+        // Gram: D = x'_a x'_b^T over the 32 channels; its diagonal entry for
+        // token n sits in lane n + 16*(n/4), element n%4 (picked with
+        // selects after all products are issued: no branch waits on a result)
+        const bool holds = (n16 >> 2) == g;
+        constexpr int NG = FUSED ? 10 : 4;
+        constexpr int ga[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
+        constexpr int gb[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+        f32x4_t gm[NG];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int qg = 4 * (wave >> 2) + qq;
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xs[xs_offset(4 * qg + (n16 >> 2), n16 & 3, kg * 4 + g)]);
-          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, av, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        for (int s2 = 0; s2 < NG; ++s2)
+          gm[s2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, o[ga[s2]]),
+                                                          __builtin_bit_cast(bf16x8_t, o[gb[s2]]),
+                                                          f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        bool em[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) gv[qq][e] = d[e];
+        for (int e = 0; e < 4; ++e) em[e] = (n16 & 3) == e;
+        float gd[NG];
+#pragma unroll
+        for (int s2 = 0; s2 < NG; ++s2) {
+          float v = gm[s2][0];
+          v = em[1] ? gm[s2][1] : v;
+          v = em[2] ? gm[s2][2] : v;
+          gd[s2] = em[3] ? gm[s2][3] : v;
         }
-        __syncthreads();  // x' staging no longer read: the partials reuse it
+        // MFMA output: lane l holds column l%16 of rows 4*(l/16)+e
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v1 = acc[rb][1][e];
-            const float mid = __shfl_xor(v1, 8);
-            const int row = rb * 16 + 4 * g + e;
-            redP[(wave * TM + row) * 24 + n16] = acc[rb][0][e];
-            if (n16 < 8) redP[(wave * TM + row) * 24 + 16 + n16] = v1 + mid;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float v1 = acc1[e];
+          const float mid = __shfl_xor(v1, 8);
+          red[wave][4 * g + e][n16] = acc0[e];
+          if (n16 < 8) red[wave][4 * g + e][16 + n16] = v1 + mid;
         }
-        if ((n16 >> 2) == g) {
-          const int jj = n16 & 3;
+        if (holds) {
+          if constexpr (FUSED) {
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int row = 4 * (4 * (wave >> 2) + qq) + g;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (e <= jj) redG[(kg * TM + row) * 10 + gram_slot(e, jj)] = gv[qq][e];
+            for (int s2 = 0; s2 < 10; ++s2) red[wave][n16][24 + s2] = gd[s2];
+          } else {
+            red[wave][n16][24] = ((gd[0] + gd[1]) + gd[2]) + gd[3];
           }
         }
       }
-      __syncthreads();  // wave partials
-      // Wait here for every memory operation issued so far: the next
-      // tile's loads (issued at the top of this iteration), the x' and h
-      // stores, and the previous iteration's partial stores have all had
-      // most of an iteration to complete.  The partial stores below go
-      // out last and are waited for only one iteration later, so no wait
-      // inside an iteration depends on their write-through latency.
-      // (Exactly three stores per thread; threads past the tile's words
-      // store the last word again.)
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __builtin_amdgcn_sched_barrier(0);
-      // level-1 reduce: check the gathered words (loaded long ago) and
-      // write the run sums
-      {
-        const int t1 = doR1 ? r + L * i1 : 0;
-        const uint64_t* b1 = a.partials + (((int64_t)t1 * S + rr * LR) * TM + (r1own ? split : 0)) * NV + (r1act ? pv : 0);
-        uint32_t it = 0;
-        for (;;) {
-          bool stale = false;
-#pragma unroll
-          for (int q = 0; q < kR1Run; ++q) stale |= doR1 && q < nr && (uint32_t)(w1[q] >> 32) != tag;
-          if (!stale) break;
-          __builtin_amdgcn_s_sleep(1);
-          if (++it > kPersistSpinLimit ||
-              __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-            __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-#pragma unroll
-          for (int q = 0; q < kR1Run; ++q)
-            if (doR1 && q < nr && (uint32_t)(w1[q] >> 32) != tag) w1[q] = tagged_load(b1 + q * (int64_t)(TM * NV));
-        }
-        float rs = 0.0f;
-#pragma unroll
-        for (int q = 0; q < kR1Run; ++q) rs += q < nr ? tagged_value(w1[q]) : 0.0f;
-        if (pv < NVU) r1runs[pv][rr] = rs;
-      }
-      if (doA) {
+      __syncthreads();  // B3: wave partials
+      if constexpr (doA) {
+        // tile partial: the four 32-channel steps of each token, in order
         uint64_t* part = a.partials + ((int64_t)t * S + split) * (TM * NV);
         static_assert(TM * NV <= 3 * kPersistThreads, "three partial words per thread");
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           const int idx = min(tid + k * kPersistThreads, TM * NV - 1);
           const int mm = idx / NV, v = idx % NV;
-          float sum;
-          if (v < 24) {
-            sum = 0.0f;
-#pragma unroll
-            for (int ww = 0; ww < 8; ++ww) sum += redP[(ww * TM + mm) * 24 + v];
-          } else if constexpr (FUSED) {
-            sum = ((redG[(0 * TM + mm) * 10 + v - 24] + redG[(1 * TM + mm) * 10 + v - 24]) +
-                   redG[(2 * TM + mm) * 10 + v - 24]) + redG[(3 * TM + mm) * 10 + v - 24];
-          } else {
-            sum = 0.0f;  // coeffs: trace of the Gram matrix
-#pragma unroll
-            for (int kq = 0; kq < 4; ++kq)
-              sum += ((redG[(kq * TM + mm) * 10 + 0] + redG[(kq * TM + mm) * 10 + 1]) +
-                      redG[(kq * TM + mm) * 10 + 2]) + redG[(kq * TM + mm) * 10 + 3];
-          }
+          const int rb = mm >> 4, tm = mm & 15;
+          const float sum = v < NVU ? ((red[rb][tm][v] + red[2 + rb][tm][v]) + red[4 + rb][tm][v]) + red[6 + rb][tm][v]
+                                    : 0.0f;
           tagged_store(part + idx, sum, tag);
         }
-      }
-      __syncthreads();  // level-1 run sums
-      if (doR1 && tid < NVU) {
-        float sum = 0.0f;
-        for (int q = 0; q < RT; ++q) sum += r1runs[tid][q];
-        tagged_store(a.reduced + ((int64_t)(r + L * i1) * TM + split) * NV + tid, sum, tag);
       }
     };
     using Yes = BoolC<true>;
     using No = BoolC<false>;
-    if (niter > 0) issue(0);
-    if constexpr (FUSED) issue_q(0);
-    int i = 0;
-    const int pro = niter < D ? niter : D;
-    for (; i < pro; ++i) body(i, Yes{}, No{});
-    // (an empty memory counter on entry keeps the loop's own wait counts exact)
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __builtin_amdgcn_sched_barrier(0);
-    for (; i < niter; ++i) body(i, Yes{}, Yes{});
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __builtin_amdgcn_sched_barrier(0);
-    for (; i < niter + (FUSED ? D : kPersistR1); ++i) {
-      if (FUSED && i >= D) {
-        body(i, No{}, Yes{});
-      } else {
-        body(i, No{}, No{});
+    if (niter > 0) {
+      // prologue: the x slices of the first two tiles, y, coefficients and q
+      // of the first; the loop starts with nothing pending, so that the
+      // compiler's counts inside it hold from the first iteration
+      issue_x(0);
+      if constexpr (FUSED) {
+        issue_y(0);
+        issue_q(0);
       }
+      issue_x(1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_sched_barrier(0);
+      int i = 0;
+      const int pro = niter < D ? niter : D;
+      for (; i < pro; ++i) body(i, Yes{}, No{});
+      for (; i < niter; ++i) body(i, Yes{}, Yes{});
+      for (; i < niter + (FUSED ? D : kPersistR1); ++i) {
+        if (FUSED && i >= D) {
+          body(i, No{}, Yes{});
+        } else {
+          body(i, No{}, No{});
+        }
+      }
+      // the last slot loads land before the workgroup's LDS is released
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
