@@ -117,7 +117,11 @@ int device_cus() {
 void choose_kernel(mhc::Plan& p) {
   p.lanes = 0;
   if (!persistent_requested()) return;
-  if (p.m != 32 || p.s < 32 || p.s > 64 || (p.s + 14) / 15 > 5) return;
+  if (p.m != 32 || p.s < 32 || p.s > 64) return;
+  // level-1 reduce: a split's share of a tile's 32*34 partial words, summed
+  // by runs of at most three splits per thread
+  const int ch = (32 * mhc::kPartVals + p.s - 1) / p.s, rt = 512 / ch;
+  if ((p.s + rt - 1) / rt > 3) return;
   const int cus = device_cus();
   const int lanes = (cus - 32) / p.s;
   if (lanes < 1 || p.tiles < 2 * (int64_t)lanes || p.s * lanes + 32 > mhc::kPersistMaxBlocks) return;

@@ -681,9 +681,9 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 //     projection (B = packed projection fragments from LDS) and of the Gram
 //     products x'_i x'_j^T, whose diagonals are the per-token route Gram
 //     entries; no x' staging through LDS.
-//   * Level-1 reduce: stream workgroup `split` (< 32) sums token `split` of
-//     a tile over the S splits, from words gathered one iteration after the
-//     tile's phase A and added up in the next.
+//   * Level-1 reduce: stream workgroup `split` sums its share of a tile's
+//     partial words over the S splits, from words gathered one iteration
+//     after the tile's phase A and added up in the next.
 //   * 32 "reduce" workgroups finalise the coefficients of 8 tokens at a
 //     time from the level-1 sums and publish q_i = pre'_i * r_h.
 // Stream workgroups wait for q words published by reduce workgroups, which
@@ -701,7 +701,7 @@ constexpr int kPersistThreads = 512;
 constexpr int kPersistTM = 32;
 constexpr int kPersistDepth = 5;  // iterations between phase A and the pre step of a tile
 constexpr int kPersistR1 = 2;     // iterations between phase A and the level-1 reduce of a tile
-constexpr int kR1Run = 5;         // splits summed by one thread in the level-1 reduce (S <= 5 * 15)
+constexpr int kR1Run = 3;         // splits summed by one thread in the level-1 reduce (32 <= S <= 64)
 constexpr uint32_t kPersistSpinLimit = 1u << 18;
 constexpr int kPersistMaxS = 64;  // splits per row the reduce threads can gather
 // LDS projection fragments of one (route, 32-channel step): blocks 0-3 whole
@@ -752,7 +752,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   __shared__ float red[8][16][NV];  // [wave][token of its row block][projection, Gram]
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
-  __shared__ float r1runs[NVU][kPersistThreads / NVU];
+  __shared__ float r1runs[kPersistThreads];  // level-1 run sums [word of the chunk][first split]
   __shared__ float gam[FUSED ? kCC : 1];
   float* finw = reinterpret_cast<float*>(phi_lds);  // reduce workgroups: [8 tokens][NV]
 
@@ -820,20 +820,21 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     const int cl = c0 + ch;
     const int xpos = (4 * ks + g) ^ n16;  // LDS position of this lane's chunk in a row
     const int niter = r < tiles ? (tiles - r + L - 1) / L : 0;
-    // Level-1 reduce: workgroup `split` (< 32) sums token `split` of
-    // tile t_{i-R1} over the S splits.  Thread (word v = tid % NVU, first
-    // split s0 = tid / NVU < RT) adds the splits s0, s0 + RT, ... in that
-    // order; the RT sums of a word are then added in the order of s0.  A
-    // wave's gather touches two splits' 34 contiguous words at a time.
-    constexpr int RT = kPersistThreads / NVU;
-    const bool r1own = split < TM;
-    const int pv = tid % NVU, s0 = tid / NVU;
-    const bool r1act = r1own && s0 < RT;
+    // Level-1 reduce of tile t_{i-R1}: its partials are TM*NV words per
+    // split; workgroup `split` owns the CH = ceil(TM*NV / S) consecutive
+    // words from split*CH and sums them over the S splits.  Thread (word
+    // v = tid % CH, first split s0 = tid / CH < RT) adds the splits s0,
+    // s0 + RT, ... in that order; the RT sums of a word are then added in
+    // the order of s0.  A wave's gather reads runs of CH contiguous words.
+    const int CH = (TM * NV + S - 1) / S, RT = kPersistThreads / CH;
+    const int w0 = split * CH, nw = max(0, min(CH, TM * NV - w0));
+    const int pv = tid % CH, s0 = tid / CH;
+    const bool r1act = s0 < RT && pv < nw;
     const int nr = r1act ? (S - s0 + RT - 1) / RT : 0;
     uint64_t w1[kR1Run];
     auto r1_base = [&](int i1) {
       const int t1 = i1 >= 0 && i1 < niter ? r + L * i1 : 0;
-      return a.partials + (((int64_t)t1 * S + (r1act ? s0 : 0)) * TM + (r1own ? split : 0)) * NV + pv;
+      return a.partials + ((int64_t)t1 * S + (r1act ? s0 : 0)) * (TM * NV) + (r1act ? w0 + pv : 0);
     };
     auto issue_r1 = [&](int i1) {
       const uint64_t* b1 = r1_base(i1);
@@ -903,8 +904,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     //   top:  y, coefficients and q of the next tile (FUSED: 3 loads)
     //         -- explicit wait: all but the last 4 + 3 + kTopOps ops done --
     //   B1 .. h and x_out stores (conditional) .. B2
-    //   gathers of the level-1 reduce (5 loads, only in the workgroups of
-    //   splits < 32; used next iteration)
+    //   gathers of the level-1 reduce (kR1Run loads, used next iteration)
     //   4 sink stores, so that every load consumed before the next explicit
     //   wait has at least 4 counted operations between it and the x slot
     //   loads that follow: a compiler wait for it never covers those
@@ -933,7 +933,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
       for (int q = 0; q < kR1Run; ++q) cw[q] = w1[q];
       const int i1 = i - kPersistR1;  // tile whose level-1 sums are formed in this iteration
-      const bool doR1 = r1own && i1 >= 0 && i1 < niter;
+      const bool doR1 = i1 >= 0 && i1 < niter;
       if constexpr (FUSED) {
         issue_y(i + 1);
         issue_q(i + 1);
@@ -1004,13 +1004,13 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         float rs = 0.0f;
 #pragma unroll
         for (int q = 0; q < kR1Run; ++q) rs += q < nr ? tagged_value(cw[q]) : 0.0f;
-        if (s0 < RT) r1runs[pv][s0] = rs;
+        if (r1act) r1runs[pv * RT + s0] = rs;
       }
       __syncthreads();  // B1: x slot, cfs, qs, run sums
-      if (doR1 && tid < NVU) {
+      if (doR1 && tid < nw) {
         float sum = 0.0f;
-        for (int q = 0; q < RT; ++q) sum += r1runs[tid][q];
-        tagged_store(a.reduced + ((int64_t)(r + L * i1) * TM + split) * NV + tid, sum, tag);
+        for (int q = 0; q < RT; ++q) sum += r1runs[tid * RT + q];
+        tagged_store(a.reduced + (int64_t)(r + L * i1) * (TM * NV) + w0 + tid, sum, tag);
       }
 
       // ---- pre step of tile t_{i-D} from the x' registers ----
@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // gathers of tile t_{i-1} (its partials were stored during the
       // previous iteration), sink stores, x slice of t_{i+2} into the slot
       // just read; all unconditional with clamped addresses
-      if (r1own) issue_r1(i - 1);
+      issue_r1(i - 1);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1184,6 +1184,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
       }
       __syncthreads();  // B3: wave partials
+
       if constexpr (doA) {
         // tile partial: the four 32-channel steps of each token, in order
         uint64_t* part = a.partials + ((int64_t)t * S + split) * (TM * NV);
