@@ -1007,10 +1007,17 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         if (r1act) r1runs[pv * RT + s0] = rs;
       }
       __syncthreads();  // B1: x slot, cfs, qs, run sums
-      if (doR1 && tid < nw) {
+      if (doR1 && tid < 8 * CH) {
+        // word v's RT run sums: lane p of its 8 adds runs p, p + 8, ...;
+        // the 8 partial sums meet in a fixed tree (lane xor 1, 2, then 4)
+        const int v = tid >> 3, pq = tid & 7;
         float sum = 0.0f;
-        for (int q = 0; q < RT; ++q) sum += r1runs[tid * RT + q];
-        tagged_store(a.reduced + (int64_t)(r + L * i1) * (TM * NV) + w0 + tid, sum, tag);
+        if (v < nw)
+          for (int q = pq; q < RT; q += 8) sum += r1runs[v * RT + q];
+        sum += MHC_DPP(sum, kDppQuadSwap1);
+        sum += MHC_DPP(sum, kDppQuadSwap2);
+        sum += __shfl_xor(sum, 4);
+        if (v < nw && pq == 0) tagged_store(a.reduced + (int64_t)(r + L * i1) * (TM * NV) + w0 + v, sum, tag);
       }
 
       // ---- pre step of tile t_{i-D} from the x' registers ----
