@@ -201,7 +201,10 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
     v = v * __builtin_amdgcn_rcpf(cs + eps);
   }
   if constexpr (FUSED) {
-    const float p[4] = {__shfl(pp, 16), __shfl(pp, 17), __shfl(pp, 18), __shfl(pp, 19)};
+    const float p[4] = {__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 16)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 17)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 18)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 19))};
     const float gq = gram_quadratic(sums + 24, p);
     const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
     q[0] = p[0] * rh;
@@ -210,6 +213,44 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
     q[3] = p[3] * rh;
   }
   return lane < 16 ? v : pp;
+}
+
+// Coefficients of four tokens on one wave, one token per 16-lane row, with
+// the arithmetic of finalize_wave: lane k of a row carries res[k/4][k%4]
+// of the row's token and, for k < 8, its pre (k < 4) or post (4 <= k < 8)
+// weight.  The Sinkhorn row and column sums are the same row-local DPP
+// moves, so the four rows run side by side.  sums: this lane's token.
+template <bool FUSED>
+__device__ __forceinline__ void finalize_rows(const float* sums, const float* bias, int C, const Scalars& sc,
+                                              int lane, float& res, float& pp, float* q) {
+  const int k = lane & 15, kp = lane & 7;
+  const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
+  const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
+  const float lp = r * sums[kp] + bias[kp];
+  const float sg = 1.0f / (1.0f + expf(-lp));
+  pp = kp >= 4 ? sc.hc_post_scale * sg : sg;
+  const float l = r * sums[8 + k] + bias[8 + k];
+  float v = expf(l);
+  const float eps = sc.sinkhorn_eps;
+  for (int it = 0; it < sc.sinkhorn_iters; ++it) {
+    float rs = v + MHC_DPP(v, kDppQuadSwap1);
+    rs = rs + MHC_DPP(rs, kDppQuadSwap2);
+    v = v * __builtin_amdgcn_rcpf(rs + eps);
+    float cs = v + MHC_DPP(v, kDppRowRor8);
+    cs = cs + MHC_DPP(cs, kDppRowRor4);
+    v = v * __builtin_amdgcn_rcpf(cs + eps);
+  }
+  res = v;
+  if constexpr (FUSED) {
+    const int row0 = lane & 48;
+    const float p[4] = {__shfl(pp, row0), __shfl(pp, row0 + 1), __shfl(pp, row0 + 2), __shfl(pp, row0 + 3)};
+    const float gq = gram_quadratic(sums + 24, p);
+    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
+    q[0] = p[0] * rh;
+    q[1] = p[1] * rh;
+    q[2] = p[2] * rh;
+    q[3] = p[3] * rh;
+  }
 }
 
 constexpr int kCC = 128;  // channels per workgroup
@@ -666,32 +707,35 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 //   * S*L "stream" workgroups: workgroup (split s, lane r) owns the 128
 //     channels of split s and the tiles t = r, r + L, r + 2L, ...  Its slice
 //     of the packed projection (72 KB: block 4 keeps only its 32 used lanes)
-//     is copied to LDS once.  Iteration i handles tile t_i:
-//       - the pre step of tile t_{i-D}, from x' kept in registers since its
-//         own phase A, D iterations earlier;
-//       - phase A of t_i: post, x' out, projection and Gram on the matrix
-//         cores, tile partial to the workspace.
-//     The x slice of a tile (32 KB) is copied into one of two LDS slots by
-//     asynchronous global->LDS loads issued two iterations ahead; y and the
-//     post coefficients are loaded into registers one iteration ahead.
-//     Every lane works in the operand layout of v_mfma_f32_16x16x32_bf16:
-//     wave w takes tokens 16*(w%2) .. +15 and the 32-channel step w/2, lane
-//     l the token l%16 and channels 8*(l/16) .. +7 of that step, for all
-//     four routes.  Its x' registers are then directly the A operands of the
+//     is copied to LDS once.  A tile's 32 tokens form two row blocks of 16;
+//     the four waves of row block b (waves 4b .. 4b+3, one per SIMD) take
+//     the four 32-channel steps of the split.  Every lane works in the
+//     operand layout of v_mfma_f32_16x16x32_bf16: lane l holds token l%16
+//     of its row block and channels 8*(l/16) .. +7 of its step, for all four
+//     routes, so its x' registers are directly the A operands of the
 //     projection (B = packed projection fragments from LDS) and of the Gram
-//     products x'_i x'_j^T, whose diagonals are the per-token route Gram
-//     entries; no x' staging through LDS.
-//   * Level-1 reduce: stream workgroup `split` sums its share of a tile's
-//     partial words over the S splits, from words gathered one iteration
-//     after the tile's phase A and added up in the next.
-//   * 32 "reduce" workgroups finalise the coefficients of 8 tokens at a
-//     time from the level-1 sums and publish q_i = pre'_i * r_h.
+//     products x'_a x'_b^T, whose diagonals are the route Gram entries.
+//     Per tile and row block there are two phases:
+//       P (vector ALU): partial sums of the previous tile, loads of the next
+//         tile's y and coefficients, the pre step of tile t_{i-D} from x'
+//         kept in registers since its own phase P, the post of tile t_i,
+//         x' and h out;
+//       M (matrix cores): asynchronous global->LDS copy of tile t_{i+2}'s x
+//         slice, projection and Gram of tile t_i, fold of the four steps
+//         through LDS, then the post coefficients and q words of the next
+//         tile to LDS.
+//     The two row blocks run half an iteration apart: while one runs P,
+//     the other runs M, so each SIMD has one wave on its vector ALU and one
+//     on its matrix core between the two barriers of an iteration.
+//   * 32 "reduce" workgroups gather the S partial rows of 8 tokens at a
+//     time, finalise their coefficients (one wave per token) and publish
+//     q_i = pre'_i * r_h.
 // Stream workgroups wait for q words published by reduce workgroups, which
-// wait for sums of stream workgroups, so the launch needs all S*L + 32
+// wait for partials of stream workgroups, so the launch needs all S*L + 32
 // workgroups resident together (the host sizes L from the CU count; every
 // wait is bounded and sets the workspace error word on expiry).  Nothing is
 // read back from x_out: the pre step uses the x' registers, so the HBM
-// traffic is the algorithmic one plus the partial, level-1 and q words.
+// traffic is the algorithmic one plus the partial and q words.
 // ===========================================================================
 template <bool B>
 struct BoolC {
@@ -699,28 +743,33 @@ struct BoolC {
 };
 constexpr int kPersistThreads = 512;
 constexpr int kPersistTM = 32;
-constexpr int kPersistDepth = 5;  // iterations between phase A and the pre step of a tile
-constexpr int kPersistR1 = 2;     // iterations between phase A and the level-1 reduce of a tile
-constexpr int kR1Run = 3;         // splits summed by one thread in the level-1 reduce (32 <= S <= 64)
+constexpr int kPersistDepth = 6;  // iterations between the post and the pre step of a tile
 constexpr uint32_t kPersistSpinLimit = 1u << 18;
 constexpr int kPersistMaxS = 64;  // splits per row the reduce threads can gather
 // LDS projection fragments of one (route, 32-channel step): blocks 0-3 whole
 // (64 lanes each) and the 32 lanes of block 4 whose column is < 8 (the rest
 // of block 4 is zero), in 16-byte units.
 constexpr int kPhiFrag = 4 * kWave + kWave / 2;
+// 16-byte chunks of one row block's x slice: 16 tokens x 4 routes x 16
+constexpr int kHalfChunks = 16 * 4 * 16;
+
 // Whether a bounded wait of the launch has expired (read from memory; the
 // polls look at it every 16th round only, so that a poll round costs one
 // load latency).
 __device__ __forceinline__ bool error_seen(uint32_t* err) {
   return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u;
 }
-constexpr int kSlotChunks = kPersistTM * 4 * 16;  // 16-byte chunks of a tile's x slice
 
 // s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // LDS byte address of a __shared__ object.
+// Workgroup barrier for the persistent loop: waits for this wave's LDS
+// operations, then s_barrier.  The text argument only keeps two otherwise
+// identical barriers apart in the compiled code.
+#define MHC_GROUP_BARRIER(where) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier ; " where ::: "memory")
+
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -737,24 +786,31 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
                : "memory", "m0");
 }
 
+// Buffer resource over [base, base + bytes): the hardware drops stores at
+// offsets past the end, so a store to a row past T needs no branch (raw
+// buffer, gfx9 resource word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kBufNT = 2;  // buffer store cache policy: non-temporal
+
 template <int MODE>
 __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs a) {
   constexpr bool FUSED = MODE != kModeCoeffs;
   constexpr bool MX = MODE == kModeFusedMx;
   constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
   constexpr int NVU = FUSED ? NV : 25;
-  // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B, two x
-  // slots [token][route][16 chunks] x 16 B (chunk c of token t at position
-  // c ^ (t % 16), so that the 16 tokens a wave reads at once hit distinct
-  // banks), the wave partials, post coefficients, q words, level-1 run sums.
-  __shared__ __attribute__((aligned(16))) u32x4_t phi_lds[16 * kPhiFrag];
-  __shared__ __attribute__((aligned(16))) u32x4_t xslot[2][kSlotChunks];
+  // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
+  // [2][row block][token][route][16 chunks] x 16 B (chunk c of token t at
+  // position c ^ (t % 16), so that the 16 tokens a wave reads at once hit
+  // distinct banks); wave partials; post coefficients; q words; gamma.
+  __shared__ __attribute__((aligned(16))) u32x4_t phi_lds[16 * kPhiFrag + 1];
+  __shared__ __attribute__((aligned(16))) u32x4_t xslot[2][2][kHalfChunks];
   __shared__ float red[8][16][NV];  // [wave][token of its row block][projection, Gram]
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
-  __shared__ float r1runs[kPersistThreads];  // level-1 run sums [word of the chunk][first split]
   __shared__ float gam[FUSED ? kCC : 1];
-  float* finw = reinterpret_cast<float*>(phi_lds);  // reduce workgroups: [8 tokens][NV]
+  float* finw = reinterpret_cast<float*>(&xslot[0][0][0]);  // reduce workgroups: [TM][NV]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, C = a.C, L = a.lanes;
@@ -764,91 +820,107 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 
   if ((int)blockIdx.x >= nstream) {
     // ------------------------- reduce workgroup -------------------------
-    // Reduce workgroup j owns tokens 8*(j%4) .. +7 of the tiles t = j/4 + 8k.
-    // The split sums of each token were already added up by the stream
-    // workgroup of split = token (reduced words); thread (token k, word v)
-    // loads one of them, and after a barrier each of the eight waves
-    // finalises one token, the Sinkhorn matrix on 16 lanes.
+    // Reduce workgroup j owns the tiles t = j, j + R, ... (R reduce
+    // workgroups).  Thread v sums partial words v, v + 512, ... of the tile
+    // ([TM][NV] words per split) over the S splits in split order,
+    // reloading words whose tag is stale; then each wave finalises four
+    // tokens, one per 16-lane row.
     const int j = (int)blockIdx.x - nstream;
-    const int grp = j & 3, ph = j >> 2;
-    float* fin = finw;  // [8 tokens][NV]
-    const int kt = tid / NVU, v = tid % NVU;
-    const bool act = tid < 8 * NVU;
-    auto rload = [&](int t) {
-      return tagged_load(a.reduced + ((int64_t)(t < tiles ? t : 0) * TM + 8 * grp + (act ? kt : 0)) * NV + (act ? v : 0));
+    const int nred = (int)gridDim.x - nstream;
+    const int64_t pstride = (int64_t)TM * NV;  // one split's partial tile
+    uint64_t wa[16], wb[16], wc[16], wd[16];
+    const uint64_t* pb = a.partials;
+    bool act = false;
+    float sum = 0.0f;
+    auto load_chunk = [&](uint64_t* w, int sc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w[k] = act && sc + k < S ? tagged_load(pb + (sc + k) * pstride) : 0;
     };
-    uint64_t wn = ph < tiles ? rload(ph) : 0;
-    for (int t = ph; t < tiles; t += 8) {
-      uint64_t w = wn;
-      wn = rload(t + 8);
-      const uint64_t* wp = a.reduced + ((int64_t)t * TM + 8 * grp + (act ? kt : 0)) * NV + (act ? v : 0);
-      uint32_t it = 0;
-      while (__syncthreads_or(act && (uint32_t)(w >> 32) != tag) != 0) {
-        __builtin_amdgcn_s_sleep(2);
-        // bounded: a wait that expires sets the error word, and every other
-        // wait of the launch gives up as soon as it sees it
-        if (++it > kPersistSpinLimit ||
-            ((it & 15u) == 0u && error_seen(a.err))) {
-          if (tid == 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        if (act && (uint32_t)(w >> 32) != tag) w = tagged_load(wp);
+    auto add_chunk = [&](uint64_t* w, int sc) __attribute__((always_inline)) {
+      auto stale = [&]() __attribute__((always_inline)) {
+        bool st = false;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) st |= act && sc + k < S && (uint32_t)(w[k] >> 32) != tag;
+        return st;
+      };
+      if (stale()) {
+        uint32_t it = 0;
+        do {
+          __builtin_amdgcn_s_sleep(2);
+          // bounded: a wait that expires sets the error word, and every
+          // other wait of the launch gives up as soon as it sees it
+          if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
+            __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            if (act && sc + k < S && (uint32_t)(w[k] >> 32) != tag) w[k] = tagged_load(pb + (sc + k) * pstride);
+        } while (stale());
       }
-      if (act) fin[kt * NV + v] = tagged_value(w);
-      __syncthreads();  // fin
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sum += sc + k < S ? tagged_value(w[k]) : 0.0f;
+    };
+    static_assert(kPersistMaxS == 64, "four chunks of 16 splits");
+    float* fin = finw;  // [TM][NV] sums of the current tile
+    for (int t = j; t < tiles; t += nred) {
+      for (int v = tid; v < TM * NV; v += kPersistThreads) {
+        act = (v % NV) < NVU;
+        pb = a.partials + (int64_t)t * S * pstride + v;
+        sum = 0.0f;
+        load_chunk(wa, 0);
+        load_chunk(wb, 16);
+        load_chunk(wc, 32);
+        load_chunk(wd, 48);
+        add_chunk(wa, 0);
+        add_chunk(wb, 16);
+        add_chunk(wc, 32);
+        add_chunk(wd, 48);
+        fin[v] = act ? sum : 0.0f;
+      }
+      __syncthreads();  // the tile's sums
       {
-        // wave w finalises token w of the group (lanes 0-15: Sinkhorn
-        // matrix, 16-23: pre and post)
-        const int64_t tok = (int64_t)t * TM + 8 * grp + wave;
-        float q[4];
-        const float cv = finalize_wave<FUSED>(fin + wave * NV, a.bias, C, a.sc, lane, q);
-        if (tok < a.T && lane < 24) a.coeffs_out[tok * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
+        // wave w finalises tokens 4w .. 4w + 3, token 4w + r on lanes
+        // 16r .. 16r + 15
+        const int m = 4 * wave + (lane >> 4), k = lane & 15;
+        const int64_t tok = (int64_t)t * TM + m;
+        float res, pp, q[4];
+        finalize_rows<FUSED>(fin + m * NV, a.bias, C, a.sc, lane, res, pp, q);
+        if (tok < a.T) {
+          a.coeffs_out[tok * kCoeffs + 8 + k] = res;
+          if (k < 8) a.coeffs_out[tok * kCoeffs + k] = pp;
+        }
         if constexpr (FUSED) {
-          if (lane < 4) tagged_store(a.publish + tok * 4 + lane, q[lane], tag);
+          // every row of the tile is published ([tiles][TM][4] words): the
+          // stream workgroups poll whole row blocks, padding rows included
+          if (k < 4) tagged_store(a.publish + tok * 4 + k, k == 0 ? q[0] : k == 1 ? q[1] : k == 2 ? q[2] : q[3], tag);
         }
       }
-      __syncthreads();  // fin is rewritten by the next tile
+      __syncthreads();  // this tile's sums are read
     }
   } else {
     // ------------------------- stream workgroup -------------------------
     const int split = (int)blockIdx.x % S, r = (int)blockIdx.x / S;
     const int c0 = split * kCC;
     const int n16 = lane & 15, g = lane >> 4;
-    const int rbk = wave & 1, ks = wave >> 1;
-    const int m = rbk * 16 + n16;  // this lane's token in the tile
-    const int ch = 32 * ks + 8 * g;  // this lane's first channel in the split
+    // (wave index made provably uniform, so that branches on the row block
+    // are scalar and buffer resources stay in scalar registers)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int rb = wv >> 2, ks = wv & 3;  // row block (pipeline group), 32-channel step
+    const int gt = tid & 255;                 // thread of the row block's group
+    const int m = rb * 16 + n16;              // this lane's token in the tile
+    const int ch = 32 * ks + 8 * g;           // this lane's first channel in the split
     const int cl = c0 + ch;
     const int xpos = (4 * ks + g) ^ n16;  // LDS position of this lane's chunk in a row
     const int niter = r < tiles ? (tiles - r + L - 1) / L : 0;
-    // Level-1 reduce of tile t_{i-R1}: its partials are TM*NV words per
-    // split; workgroup `split` owns the CH = ceil(TM*NV / S) consecutive
-    // words from split*CH and sums them over the S splits.  Thread (word
-    // v = tid % CH, first split s0 = tid / CH < RT) adds the splits s0,
-    // s0 + RT, ... in that order; the RT sums of a word are then added in
-    // the order of s0.  A wave's gather reads runs of CH contiguous words.
-    const int CH = (TM * NV + S - 1) / S, RT = kPersistThreads / CH;
-    const int w0 = split * CH, nw = max(0, min(CH, TM * NV - w0));
-    const int pv = tid % CH, s0 = tid / CH;
-    const bool r1act = s0 < RT && pv < nw;
-    const int nr = r1act ? (S - s0 + RT - 1) / RT : 0;
-    uint64_t w1[kR1Run];
-    auto r1_base = [&](int i1) {
-      const int t1 = i1 >= 0 && i1 < niter ? r + L * i1 : 0;
-      return a.partials + ((int64_t)t1 * S + (r1act ? s0 : 0)) * (TM * NV) + (r1act ? w0 + pv : 0);
-    };
-    auto issue_r1 = [&](int i1) {
-      const uint64_t* b1 = r1_base(i1);
-#pragma unroll
-      for (int q = 0; q < kR1Run; ++q) w1[q] = tagged_load(b1 + (q < nr ? q : 0) * (int64_t)(RT * TM * NV));
-    };
 
-    // projection slice -> LDS
+    // projection slice -> LDS (and one zero fragment for block 4's unused lanes)
     {
       const u32x4_t* pk = reinterpret_cast<const u32x4_t*>(a.phi_packed);
       for (int idx = tid; idx < 16 * kPhiFrag; idx += kPersistThreads) {
         const int jk = idx / kPhiFrag, o = idx % kPhiFrag;
-        const int j = jk >> 2, kq = jk & 3;
-        const int64_t kstep = ((int64_t)j * C + c0 + kq * 32) >> 5;
+        const int jr = jk >> 2, kq = jk & 3;
+        const int64_t kstep = ((int64_t)jr * C + c0 + kq * 32) >> 5;
         int b, ln;
         if (o < 4 * kWave) {
           b = o >> 6;
@@ -859,186 +931,127 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
         phi_lds[idx] = pk[(kstep * kPackBlocks + b) * kWave + ln];
       }
+      if (tid == 0) phi_lds[16 * kPhiFrag] = u32x4_t{0, 0, 0, 0};
     }
     if constexpr (FUSED) {
       if (tid < kCC) gam[tid] = a.gamma[c0 + tid];
     }
+    // block 4 fragment of this lane: its own column if < 8, else the zero fragment
+    const int b4off = n16 < 8 ? 4 * kWave + g * 8 + n16 : -1;
 
-    // x slice of tile t_i -> slot i%2: wave-instruction k covers the four
-    // routes of token wave + 8k (1 KB of LDS, 4 x 256 contiguous bytes of x).
-    const uint32_t slot0 = lds_address(&xslot[0][0]), slot1 = lds_address(&xslot[1][0]);
-    auto issue_x = [&](int i) {
+    // x slice of this row block of tile t_i -> slot i%2: wave-instruction k
+    // covers the four routes of token ks + 4k of the row block (1 KB of LDS,
+    // 4 x 256 contiguous bytes of x).
+    const uint32_t slot0 = lds_address(&xslot[0][rb][0]);
+    constexpr uint32_t kSlotStride = 2u * kHalfChunks * 16u;  // bytes from xslot[0][b] to xslot[1][b]
+    auto issue_x = [&](int i) __attribute__((always_inline)) {
       const int t = r + L * (i < niter ? i : 0);
-      const uint32_t sb = (i & 1) ? slot1 : slot0;
+      const uint32_t sb = slot0 + (uint32_t)(i & 1) * kSlotStride;
       const int jr = lane >> 4, p = lane & 15;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int q = wave + 8 * k;
-        const int64_t tok = (int64_t)t * TM + q;
+        const int q = ks + 4 * k;
+        const int64_t tok = (int64_t)t * TM + rb * 16 + q;
         const int64_t tc = tok < a.T ? tok : 0;
-        const uint16_t* src = a.x + tc * (int64_t)(4 * C) + (int64_t)jr * C + c0 + 8 * (p ^ (q & 15));
+        const uint16_t* src = a.x + tc * (int64_t)(4 * C) + (int64_t)jr * C + c0 + 8 * (p ^ q);
         lds_dma16(src, __builtin_amdgcn_readfirstlane(sb + (uint32_t)q * 1024u));
       }
     };
-    // y and the post coefficients of tile t_i (registers, one iteration ahead)
+    // y and post coefficients of this row block of tile t_i (registers)
     u32x4_t ny = u32x4_t{0, 0, 0, 0};
     float4 ncf = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    auto issue_y = [&](int i) {
+    uint64_t nq = 0;
+    auto issue_y = [&](int i) __attribute__((always_inline)) {
       const int t = r + L * (i < niter ? i : 0);
       const int64_t tok = (int64_t)t * TM + m;
       const int64_t tc = tok < a.T ? tok : 0;
       ny = ld16_stream(a.y + tc * (int64_t)C + cl);
-      const int64_t ct = (int64_t)t * TM + tid / 5;
-      const bool cv = tid < TM * 5 && ct < a.T;
-      ncf = reinterpret_cast<const float4*>(a.coeffs_in + (cv ? ct : 0) * kCoeffs)[1 + (cv ? tid % 5 : 0)];
+      const int64_t ct = (int64_t)t * TM + rb * 16 + gt / 5;
+      const bool cv = gt < 16 * 5 && ct < a.T;
+      ncf = reinterpret_cast<const float4*>(a.coeffs_in + (cv ? ct : 0) * kCoeffs)[1 + (cv ? gt % 5 : 0)];
     };
-    // q words of the tile whose pre step runs in iteration i
-    uint64_t nq = 0;
-    auto issue_q = [&](int i) {
+    // q words (this row block) of the tile whose pre step runs in phase P of
+    // iteration i
+    auto issue_q = [&](int i) __attribute__((always_inline)) {
       const int ic = i - D;
       const int t = ic >= 0 && ic < niter ? r + L * ic : 0;
-      nq = tagged_load(a.publish + (int64_t)t * TM * 4 + (tid & (TM * 4 - 1)));
+      nq = tagged_load(a.publish + ((int64_t)t * TM + rb * 16) * 4 + (gt & 63));
     };
-    // Memory-operation order of an iteration (vmcnt counts them in issue
-    // order; the x slot loads are invisible to the compiler's own counting):
-    //   top:  y, coefficients and q of the next tile (FUSED: 3 loads)
-    //         -- explicit wait: all but the last 4 + 3 + kTopOps ops done --
-    //   B1 .. h and x_out stores (conditional) .. B2
-    //   gathers of the level-1 reduce (kR1Run loads, used next iteration)
-    //   4 sink stores, so that every load consumed before the next explicit
-    //   wait has at least 4 counted operations between it and the x slot
-    //   loads that follow: a compiler wait for it never covers those
-    //   x slot loads of tile t_{i+2} (4, invisible)
-    //   .. B3 .. partial stores (3)
-    constexpr int kTopOps = FUSED ? 3 : 0;
-    constexpr int kTopWait = 4 + 3 + kTopOps;
-    uint32_t* sinkw = a.sink + (int64_t)blockIdx.x * 16;
 
     u32x4_t ring[D][4];  // x' of the last D tiles (packed bf16, 4 routes)
 #pragma unroll
     for (int k = 0; k < D; ++k)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ring[k][j] = u32x4_t{0, 0, 0, 0};
+      for (int jr = 0; jr < 4; ++jr) ring[k][jr] = u32x4_t{0, 0, 0, 0};
+    u32x4_t o[4];  // x' of the current tile, from phase P to phase M
 #pragma unroll
-    for (int q = 0; q < kR1Run; ++q) w1[q] = 0;
+    for (int jr = 0; jr < 4; ++jr) o[jr] = u32x4_t{0, 0, 0, 0};
 
-    auto body = [&](int i, auto kA, auto kC) {
+    // Memory-operation order of one row block (vmcnt counts them in issue
+    // order; the x slot copies are invisible to the compiler's counting):
+    //   P(i): partial stores of tile t_{i-1} (3), loads of tile t_{i+1}
+    //         (FUSED: y, coefficients, q), h and x_out buffer stores
+    //         (unconditional: rows past T are dropped by the bounds check)
+    //   M(i): x slot copies of tile t_{i+2} (4, invisible), MFMAs, fold,
+    //         explicit wait for all but those 4, then the next tile's post
+    //         coefficients and q words to LDS.
+    // The loads M(i) and P(i+1) consume are followed by at least 4 counted
+    // stores before the copies, so a compiler wait for them never reaches
+    // the copies, and the explicit wait leaves exactly the copies pending.
+
+    // ---- phase P of tile t_i ----
+    auto phaseP = [&](int i, auto kA, auto kC, auto kPrev) __attribute__((always_inline)) {
       constexpr bool doA = decltype(kA)::value;
       constexpr bool doC = FUSED && decltype(kC)::value;
+      constexpr bool doPrev = decltype(kPrev)::value;
       const int t = r + L * i;
-      const u32x4_t cy = ny;
-      const float4 ccf = ncf;
-      const uint64_t cq = nq;
-      uint64_t cw[kR1Run];
+      // partial row of tile t_{i-1}: this row block's 16 tokens x NV words,
+      // the four 32-channel steps added in order
+      if constexpr (doPrev) {
+        uint64_t* part = a.partials + ((int64_t)(t - L) * S + split) * (TM * NV) + rb * 16 * NV;
 #pragma unroll
-      for (int q = 0; q < kR1Run; ++q) cw[q] = w1[q];
-      const int i1 = i - kPersistR1;  // tile whose level-1 sums are formed in this iteration
-      const bool doR1 = i1 >= 0 && i1 < niter;
+        for (int k = 0; k < 3; ++k) {
+          const int idx = min(gt + k * 256, 16 * NV - 1);
+          const int tm = idx / NV, vv = idx % NV;
+          const float sum = vv < NVU ? ((red[rb * 4][tm][vv] + red[rb * 4 + 1][tm][vv]) + red[rb * 4 + 2][tm][vv]) +
+                                           red[rb * 4 + 3][tm][vv]
+                                     : 0.0f;
+          tagged_store(part + idx, sum, tag);
+        }
+      }
+      const u32x4_t cy = ny;
       if constexpr (FUSED) {
         issue_y(i + 1);
         issue_q(i + 1);
       }
-      // The slot of tile t_i was filled by loads issued two iterations ago;
-      // since then at least the previous iteration's loads, sink stores, x
-      // slot loads (t_{i+1}) and partial stores and this iteration's loads
-      // were issued: waiting until only the last 4 + 3 + kTopOps are pending
-      // completes the slot, the gathers and the loads of the previous top,
-      // and leaves the loads of t_{i+1} in flight.
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTopWait));
-      __builtin_amdgcn_sched_barrier(0);
-
-      if constexpr (FUSED) {
-        if (doA && tid < TM * 5) {
-          const bool ok = (int64_t)t * TM + tid / 5 < a.T;
-          float* d = &cfs[tid / 5][4 * (tid % 5)];
-          d[0] = ok ? ccf.x : 0.0f;
-          d[1] = ok ? ccf.y : 0.0f;
-          d[2] = ok ? ccf.z : 0.0f;
-          d[3] = ok ? ccf.w : 0.0f;
-        }
-        if (doC && tid < TM * 4) {
-          // (the polling loop is a separate branch, so that the common path
-          // has no loop whose reloads the compiler would wait for)
-          uint64_t qw = cq;
-          if ((uint32_t)(qw >> 32) != tag) {
-            const uint64_t* qp = a.publish + (int64_t)(r + L * (i - D)) * TM * 4 + tid;
-            uint32_t it = 0;
-            do {
-              __builtin_amdgcn_s_sleep(1);
-              if (++it > kPersistSpinLimit ||
-                  ((it & 15u) == 0u && error_seen(a.err))) {
-                __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-              }
-              qw = tagged_load(qp);
-            } while ((uint32_t)(qw >> 32) != tag);
-          }
-          (&qs[0][0])[tid] = tagged_value(qw);
-        }
-      }
-      // level-1 reduce of tile t_{i1}: check the words gathered during the
-      // previous iteration and write the run sums
-      {
-        const uint64_t* b1 = r1_base(i1);
-        auto stale = [&]() {
-          bool st = false;
-#pragma unroll
-          for (int q = 0; q < kR1Run; ++q) st |= doR1 && q < nr && (uint32_t)(cw[q] >> 32) != tag;
-          return st;
-        };
-        if (stale()) {
-          uint32_t it = 0;
-          do {
-            __builtin_amdgcn_s_sleep(1);
-            if (++it > kPersistSpinLimit ||
-                ((it & 15u) == 0u && error_seen(a.err))) {
-              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-#pragma unroll
-            for (int q = 0; q < kR1Run; ++q)
-              if (doR1 && q < nr && (uint32_t)(cw[q] >> 32) != tag) cw[q] = tagged_load(b1 + q * (int64_t)(RT * TM * NV));
-          } while (stale());
-        }
-        float rs = 0.0f;
-#pragma unroll
-        for (int q = 0; q < kR1Run; ++q) rs += q < nr ? tagged_value(cw[q]) : 0.0f;
-        if (r1act) r1runs[pv * RT + s0] = rs;
-      }
-      __syncthreads();  // B1: x slot, cfs, qs, run sums
-      if (doR1 && tid < 8 * CH) {
-        // word v's RT run sums: lane p of its 8 adds runs p, p + 8, ...;
-        // the 8 partial sums meet in a fixed tree (lane xor 1, 2, then 4)
-        const int v = tid >> 3, pq = tid & 7;
-        float sum = 0.0f;
-        if (v < nw)
-          for (int q = pq; q < RT; q += 8) sum += r1runs[v * RT + q];
-        sum += MHC_DPP(sum, kDppQuadSwap1);
-        sum += MHC_DPP(sum, kDppQuadSwap2);
-        sum += __shfl_xor(sum, 4);
-        if (v < nw && pq == 0) tagged_store(a.reduced + (int64_t)(r + L * i1) * (TM * NV) + w0 + v, sum, tag);
-      }
-
-      // ---- pre step of tile t_{i-D} from the x' registers ----
+      // pre step of tile t_{i-D}
       if constexpr (doC) {
-        const int64_t tok = (int64_t)(r + L * (i - D)) * TM + m;
-        const bool valid = tok < a.T;
+        const int64_t tokC0 = (int64_t)(r + L * (i - D)) * TM + rb * 16;
+        const uint32_t nC = (uint32_t)max((int64_t)0, min((int64_t)16, a.T - tokC0));
         const float q0 = qs[m][0], q1 = qs[m][1], q2 = qs[m][2], q3 = qs[m][3];
-        float xv[4][8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) unpack8(ring[0][j], xv[j]);
         float hv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float vv = q0 * xv[0][e];
-          vv = __builtin_fmaf(q1, xv[1][e], vv);
-          vv = __builtin_fmaf(q2, xv[2][e], vv);
-          vv = __builtin_fmaf(q3, xv[3][e], vv);
-          hv[e] = vv * gam[ch + e];
+        for (int qd = 0; qd < 4; ++qd) {
+          float xl[4], xh[4];
+#pragma unroll
+          for (int jr = 0; jr < 4; ++jr) {
+            xl[jr] = bf16_lo(ring[0][jr][qd]);
+            xh[jr] = bf16_hi(ring[0][jr][qd]);
+          }
+          float vl = q0 * xl[0], vh = q0 * xh[0];
+          vl = __builtin_fmaf(q1, xl[1], vl);
+          vh = __builtin_fmaf(q1, xh[1], vh);
+          vl = __builtin_fmaf(q2, xl[2], vl);
+          vh = __builtin_fmaf(q2, xh[2], vh);
+          vl = __builtin_fmaf(q3, xl[3], vl);
+          vh = __builtin_fmaf(q3, xh[3], vh);
+          hv[2 * qd] = vl * gam[ch + 2 * qd];
+          hv[2 * qd + 1] = vh * gam[ch + 2 * qd + 1];
         }
         const u32x4_t hb = pack8(hv);
-        if (a.h != nullptr && valid) st16_stream(a.h + tok * (int64_t)C + cl, hb);
+        if (!MX || a.h != nullptr)
+          __builtin_amdgcn_raw_buffer_store_b128(hb, buffer_rsrc(a.h + tokC0 * C, nC * (uint32_t)(2 * C)),
+                                                 (n16 * C + cl) * 2, 0, kBufNT);
         if constexpr (MX) {
           // a 32-channel block is the 4 lanes n16, n16 + 16, n16 + 32, n16 + 48
           float hr[8];
@@ -1050,16 +1063,18 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
           const int ex = mx_scale_exponent(amax);
           const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
-          uint32_t w0 = 0, w1c = 0;
+          uint32_t w0 = 0, w1 = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             w0 |= e4m3_code(hr[e] * scale) << (8 * e);
-            w1c |= e4m3_code(hr[4 + e] * scale) << (8 * e);
+            w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
           }
-          if (valid) {
-            *reinterpret_cast<u32x2_t*>(a.h_fp8 + tok * (int64_t)C + cl) = u32x2_t{w0, w1c};
-            if (g == 0) a.h_scale[tok * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
-          }
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, buffer_rsrc(a.h_fp8 + tokC0 * C, nC * (uint32_t)C),
+                                                n16 * C + cl, 0, 0);
+          // the block's four lanes store the same scale byte
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(ex + 127),
+                                               buffer_rsrc(a.h_scale + tokC0 * (C / 32), nC * (uint32_t)(C / 32)),
+                                               n16 * (C / 32) + (cl >> 5), 0, 0);
         }
       }
       if constexpr (FUSED) {
@@ -1067,18 +1082,16 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k + 1 < D; ++k)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ring[k][j] = ring[k + 1][j];
+          for (int jr = 0; jr < 4; ++jr) ring[k][jr] = ring[k + 1][jr];
       }
-
-      // ---- phase A of tile t_i: x (and y) -> x' in the MFMA A layout ----
-      u32x4_t o[4];
+      // post of tile t_i: x (slot) and y -> x' in the MFMA A layout
       if constexpr (doA) {
-        const int64_t tok = (int64_t)t * TM + m;
-        const bool valid = tok < a.T;
-        const u32x4_t* sp = (i & 1) ? &xslot[1][0] : &xslot[0][0];
+        const int64_t tokA0 = (int64_t)t * TM + rb * 16;
+        const uint32_t nA = (uint32_t)max((int64_t)0, min((int64_t)16, a.T - tokA0));
+        const u32x4_t* sp = &xslot[i & 1][rb][0];
         u32x4_t xin[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xin[j] = sp[(m * 4 + j) * 16 + xpos];
+        for (int jr = 0; jr < 4; ++jr) xin[jr] = sp[(n16 * 4 + jr) * 16 + xpos];
         if constexpr (FUSED) {
           float pw[4], rs[16];
 #pragma unroll
@@ -1091,128 +1104,150 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
             const float xh[4] = {bf16_hi(xin[0][q]), bf16_hi(xin[1][q]), bf16_hi(xin[2][q]), bf16_hi(xin[3][q])};
             const float yl = bf16_lo(cy[q]), yh = bf16_hi(cy[q]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              o[j][q] = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
-                                    post_chain(pw[j], yh, &rs[4 * j], xh[0], xh[1], xh[2], xh[3]));
+            for (int jr = 0; jr < 4; ++jr)
+              o[jr][q] = pack_bf16x2(post_chain(pw[jr], yl, &rs[4 * jr], xl[0], xl[1], xl[2], xl[3]),
+                                     post_chain(pw[jr], yh, &rs[4 * jr], xh[0], xh[1], xh[2], xh[3]));
           }
-          if (valid) {
-            uint16_t* xo = a.x_out + tok * (int64_t)(4 * C) + cl;
+          const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x_out + tokA0 * (4 * C), nA * (uint32_t)(8 * C));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st16_stream(xo + (int64_t)j * C, o[j]);
-          }
+          for (int jr = 0; jr < 4; ++jr)
+            __builtin_amdgcn_raw_buffer_store_b128(o[jr], rx, ((n16 * 4 + jr) * C + cl) * 2, 0, kBufNT);
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = xin[j];
+          for (int jr = 0; jr < 4; ++jr) o[jr] = xin[jr];
         }
-        if (!valid) {
+        if ((uint32_t)n16 >= nA) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = u32x4_t{0, 0, 0, 0};
+          for (int jr = 0; jr < 4; ++jr) o[jr] = u32x4_t{0, 0, 0, 0};
         }
         if constexpr (FUSED) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ring[D - 1][j] = o[j];
-        }
-      }
-      __syncthreads();  // B2: every wave has read the slot
-      // gathers of tile t_{i-1} (its partials were stored during the
-      // previous iteration), sink stores, x slice of t_{i+2} into the slot
-      // just read; all unconditional with clamped addresses
-      issue_r1(i - 1);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sinkw[4 * k] = 0u;
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      issue_x(i + 2);
-
-      if constexpr (doA) {
-        // projection: A = x' of route j (16 tokens x 32 channels), B = the
-        // five packed blocks of (route j, step ks); blocks 0-2 accumulate
-        // logits 0..15, blocks 3-4 logits 16..23 (hi+lo | mid)
-        f32x4_t acc0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4_t* bp = phi_lds + (j * 4 + ks) * kPhiFrag;
-          u32x4_t bf[kPackBlocks];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) bf[b] = bp[b * kWave + lane];
-          const u32x4_t b4 = bp[4 * kWave + g * 8 + (n16 & 7)];
-          bf[4] = n16 < 8 ? b4 : u32x4_t{0, 0, 0, 0};
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, o[j]);
-#pragma unroll
-          for (int b = 0; b < kPackBlocks; ++b) {
-            if (b < 3) {
-              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc0, 0, 0, 0);
-            } else {
-              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc1, 0, 0, 0);
-            }
-          }
-        }
-        // Gram: D = x'_a x'_b^T over the 32 channels; its diagonal entry for
-        // token n sits in lane n + 16*(n/4), element n%4 (picked with
-        // selects after all products are issued: no branch waits on a result)
-        const bool holds = (n16 >> 2) == g;
-        constexpr int NG = FUSED ? 10 : 4;
-        constexpr int ga[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
-        constexpr int gb[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
-        f32x4_t gm[NG];
-#pragma unroll
-        for (int s2 = 0; s2 < NG; ++s2)
-          gm[s2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, o[ga[s2]]),
-                                                          __builtin_bit_cast(bf16x8_t, o[gb[s2]]),
-                                                          f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        bool em[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) em[e] = (n16 & 3) == e;
-        float gd[NG];
-#pragma unroll
-        for (int s2 = 0; s2 < NG; ++s2) {
-          float v = gm[s2][0];
-          v = em[1] ? gm[s2][1] : v;
-          v = em[2] ? gm[s2][2] : v;
-          gd[s2] = em[3] ? gm[s2][3] : v;
-        }
-        // MFMA output: lane l holds column l%16 of rows 4*(l/16)+e
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v1 = acc1[e];
-          const float mid = __shfl_xor(v1, 8);
-          red[wave][4 * g + e][n16] = acc0[e];
-          if (n16 < 8) red[wave][4 * g + e][16 + n16] = v1 + mid;
-        }
-        if (holds) {
-          if constexpr (FUSED) {
-#pragma unroll
-            for (int s2 = 0; s2 < 10; ++s2) red[wave][n16][24 + s2] = gd[s2];
-          } else {
-            red[wave][n16][24] = ((gd[0] + gd[1]) + gd[2]) + gd[3];
-          }
-        }
-      }
-      __syncthreads();  // B3: wave partials
-
-      if constexpr (doA) {
-        // tile partial: the four 32-channel steps of each token, in order
-        uint64_t* part = a.partials + ((int64_t)t * S + split) * (TM * NV);
-        static_assert(TM * NV <= 3 * kPersistThreads, "three partial words per thread");
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          const int idx = min(tid + k * kPersistThreads, TM * NV - 1);
-          const int mm = idx / NV, v = idx % NV;
-          const int rb = mm >> 4, tm = mm & 15;
-          const float sum = v < NVU ? ((red[rb][tm][v] + red[2 + rb][tm][v]) + red[4 + rb][tm][v]) + red[6 + rb][tm][v]
-                                    : 0.0f;
-          tagged_store(part + idx, sum, tag);
+          for (int jr = 0; jr < 4; ++jr) ring[D - 1][jr] = o[jr];
         }
       }
     };
+
+    // ---- phase M of tile t_i: slot copy of t_{i+2}, projection, Gram, fold ----
+    auto phaseM = [&](int i) __attribute__((always_inline)) {
+      issue_x(i + 2);
+      // projection: A = x' of route jr (16 tokens x 32 channels), B = the
+      // five packed blocks of (route jr, step ks); blocks 0-2 accumulate
+      // logits 0..15, blocks 3-4 logits 16..23 (hi+lo | mid)
+      u32x4_t xa[4];
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) xa[jr] = FUSED ? ring[D - 1][jr] : o[jr];
+      f32x4_t acc0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) {
+        const u32x4_t* bp = phi_lds + (jr * 4 + ks) * kPhiFrag;
+        u32x4_t bf[kPackBlocks];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bf[b] = bp[b * kWave + lane];
+        bf[4] = b4off >= 0 ? bp[b4off] : phi_lds[16 * kPhiFrag];
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[jr]);
+#pragma unroll
+        for (int b = 0; b < kPackBlocks; ++b) {
+          if (b < 3) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc0, 0, 0, 0);
+          } else {
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc1, 0, 0, 0);
+          }
+        }
+      }
+      // Gram: D = x'_a x'_b^T over the 32 channels; its diagonal entry for
+      // token n sits in lane n + 16*(n/4), element n%4 (picked with
+      // selects after all products are issued: no branch waits on a result)
+      const bool holds = (n16 >> 2) == g;
+      constexpr int NG = FUSED ? 10 : 4;
+      constexpr int ga[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
+      constexpr int gb[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+      f32x4_t gm[NG];
+#pragma unroll
+      for (int s2 = 0; s2 < NG; ++s2)
+        gm[s2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[ga[s2]]),
+                                                        __builtin_bit_cast(bf16x8_t, xa[gb[s2]]),
+                                                        f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      bool em[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) em[e] = (n16 & 3) == e;
+      float gd[NG];
+#pragma unroll
+      for (int s2 = 0; s2 < NG; ++s2) {
+        float vv = gm[s2][0];
+        vv = em[1] ? gm[s2][1] : vv;
+        vv = em[2] ? gm[s2][2] : vv;
+        gd[s2] = em[3] ? gm[s2][3] : vv;
+      }
+      // MFMA output: lane l holds column l%16 of rows 4*(l/16)+e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v1 = acc1[e];
+        const float mid = __shfl_xor(v1, 8);
+        red[wave][4 * g + e][n16] = acc0[e];
+        if (n16 < 8) red[wave][4 * g + e][16 + n16] = v1 + mid;
+      }
+      if (holds) {
+        if constexpr (FUSED) {
+#pragma unroll
+          for (int s2 = 0; s2 < 10; ++s2) red[wave][n16][24 + s2] = gd[s2];
+        } else {
+          red[wave][n16][24] = ((gd[0] + gd[1]) + gd[2]) + gd[3];
+        }
+      }
+    };
+
+    // ---- before phase P of tile t_i: its slot, post coefficients, q words ----
+    // copied: whether this slot's phase M issued slot copies (left pending)
+    auto prepP = [&](int i, auto kCopied) __attribute__((always_inline)) {
+      constexpr bool copied = decltype(kCopied)::value;
+      // Everything but the copies just issued has landed: the slot of t_i
+      // (copied during the phase M before), the loads and stores of the last
+      // phase P.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(copied ? 4 : 0));
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (FUSED) {
+        const int ti = r + L * i;
+        const float4 ccf = ncf;
+        if (gt < 16 * 5) {
+          const bool ok = (int64_t)ti * TM + rb * 16 + gt / 5 < a.T;
+          float* dd = &cfs[rb * 16 + gt / 5][4 * (gt % 5)];
+          dd[0] = ok ? ccf.x : 0.0f;
+          dd[1] = ok ? ccf.y : 0.0f;
+          dd[2] = ok ? ccf.z : 0.0f;
+          dd[3] = ok ? ccf.w : 0.0f;
+        }
+        // q words of the tile whose pre step runs in phase P(i)
+        const int ic = i - D;
+        if (ic >= 0 && ic < niter && gt < 64) {
+          uint64_t qw = nq;
+          if ((uint32_t)(qw >> 32) != tag) {
+            const uint64_t* qp = a.publish + ((int64_t)(r + L * ic) * TM + rb * 16) * 4 + gt;
+            uint32_t it = 0;
+            do {
+              __builtin_amdgcn_s_sleep(1);
+              if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
+                __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+              }
+              qw = tagged_load(qp);
+            } while ((uint32_t)(qw >> 32) != tag);
+          }
+          qs[rb * 16 + gt / 4][gt & 3] = tagged_value(qw);
+        }
+      }
+    };
+
     using Yes = BoolC<true>;
     using No = BoolC<false>;
+    // Iteration i: [row block 0: P(i) | row block 1: M(i-1)] barrier
+    //              [row block 0: M(i) | row block 1: P(i)]   barrier
+    // Phase P(i) has the post when i < niter, the pre step when
+    // D <= i < niter + D, the previous tile's partials when 1 <= i <= niter;
+    // phase M(i) runs for i < niter.
     if (niter > 0) {
-      // prologue: the x slices of the first two tiles, y, coefficients and q
-      // of the first; the loop starts with nothing pending, so that the
-      // compiler's counts inside it hold from the first iteration
+      // prologue: this row block's x slices of the first two tiles, y,
+      // coefficients and q of the first; nothing pending when the loop starts
       issue_x(0);
       if constexpr (FUSED) {
         issue_y(0);
@@ -1222,18 +1257,73 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_sched_barrier(0);
-      int i = 0;
-      const int pro = niter < D ? niter : D;
-      for (; i < pro; ++i) body(i, Yes{}, No{});
-      for (; i < niter; ++i) body(i, Yes{}, Yes{});
-      for (; i < niter + (FUSED ? D : kPersistR1); ++i) {
-        if (FUSED && i >= D) {
-          body(i, No{}, Yes{});
+      if (rb == 0) prepP(0, No{});
+      __syncthreads();
+      // step i: [row block 0: P(i)       | row block 1: M(i-1), prep P(i)]   barrier
+      //         [row block 0: M(i), prep P(i+1) | row block 1: P(i)]         barrier
+      // Each row block runs its own copy of the loop (the same barriers in
+      // the same order), so that the compiler's wait counting follows one
+      // row block's memory operations only: with one loop whose slots branch
+      // on the row block, the two paths merge between the slots and phase M
+      // would wait for the other path's loads and its own stores.  The
+      // barriers are written out with a distinct text per place (LDS
+      // operations drained, then s_barrier), so that the compiler cannot
+      // merge the two loops back into one at a shared barrier call.
+      auto stepA = [&](int i, auto kA, auto kC, auto kPrev, auto kMprev, auto kMcur) __attribute__((always_inline)) {
+        constexpr bool mCur = decltype(kMcur)::value;  // phase M(i) runs
+        phaseP(i, kA, kC, kPrev);
+        MHC_GROUP_BARRIER("row block 0, slot 1");
+        if constexpr (mCur) {
+          phaseM(i);
+          prepP(i + 1, Yes{});
         } else {
-          body(i, No{}, No{});
+          prepP(i + 1, No{});
         }
+        MHC_GROUP_BARRIER("row block 0, slot 2");
+      };
+      auto stepB = [&](int i, auto kA, auto kC, auto kPrev, auto kMprev, auto kMcur) __attribute__((always_inline)) {
+        constexpr bool mPrev = decltype(kMprev)::value;  // phase M(i-1) runs
+        if constexpr (mPrev) {
+          phaseM(i - 1);
+          prepP(i, Yes{});
+        } else {
+          prepP(i, No{});
+        }
+        MHC_GROUP_BARRIER("row block 1, slot 1");
+        phaseP(i, kA, kC, kPrev);
+        MHC_GROUP_BARRIER("row block 1, slot 2");
+      };
+      // Phase P(i) has the post when i < niter, the pre step when
+      // D <= i < niter + D, the previous tile's partials when 1 <= i <= niter;
+      // phase M(i) runs when i < niter.
+      auto run = [&](auto step) __attribute__((always_inline)) {
+        int i = 0;
+        step(0, Yes{}, No{}, No{}, No{}, Yes{});
+        ++i;
+        const int pro = niter < D ? niter : D;
+        for (; i < pro; ++i) step(i, Yes{}, No{}, Yes{}, Yes{}, Yes{});
+        for (; i < niter; ++i) step(i, Yes{}, Yes{}, Yes{}, Yes{}, Yes{});
+        // i = niter: the last tile's partials and row block 1's last phase M
+        if (i < D) {
+          step(i, No{}, No{}, Yes{}, Yes{}, No{});
+        } else {
+          step(i, No{}, Yes{}, Yes{}, Yes{}, No{});
+        }
+        ++i;
+        for (; i < niter + D; ++i) {
+          if (i >= D) {
+            step(i, No{}, Yes{}, No{}, No{}, No{});
+          } else {
+            step(i, No{}, No{}, No{}, No{}, No{});  // (only the next phase P's preparation)
+          }
+        }
+      };
+      if (rb == 0) {
+        run(stepA);
+      } else {
+        run(stepB);
       }
-      // the last slot loads land before the workgroup's LDS is released
+      // the last slot copies land before the workgroup's LDS is released
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_sched_barrier(0);
