@@ -36,7 +36,11 @@ METRIC = "mHC fused post+pre tokens/s and % peak HBM GB/s at C=7168, T=8192"
 
 # Sources whose change invalidates the stored hardware counter figures.
 KERNEL_SOURCES = ["mhc_kernels.hip", "mhc_device.h", "mhc_internal.h", "mhc_api.cpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_split_fused_prefill_traffic.txt")
+# counter figures of the fused kernel each schedule runs on the prefill workload
+TRAFFIC_FILES = {"persistent": os.path.join(ROOT, "profiles", "k_persist_fused_prefill_traffic.txt"),
+                 "staged": os.path.join(ROOT, "profiles", "k_split_fused_prefill_traffic.txt")}
+KERNEL_NAMES = {"persistent": "k_persist (fused post->pre, persistent schedule)",
+                "staged": "k_split (fused post->pre, staged schedule)"}
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -48,14 +52,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, schedule: str):
     """HBM bytes per fused launch measured with rocprofv3 counters (FETCH_SIZE,
     WRITE_SIZE, each scaled by the copy-kernel calibration), or None when the
     kernel sources changed since the counters were taken."""
-    if workload != "prefill" or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(schedule)
+    if workload != "prefill" or path is None or not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             m = re.match(r"^([a-z_0-9]+):\s*(.+)$", line.strip())
             if m:
@@ -187,8 +192,9 @@ def main() -> int:
     T, C = w.T, w.C
     mx = args.workload == "mxfp8"
     params = Params()
-    print(f"[bench] workload={w.name} T={T} C={C} mxfp8={mx} steps={args.steps} warmup={args.warmup}",
-          file=sys.stderr, flush=True)
+    sched = mhc.schedule(T, C)
+    print(f"[bench] workload={w.name} T={T} C={C} mxfp8={mx} steps={args.steps} warmup={args.warmup} "
+          f"schedule={sched}", file=sys.stderr, flush=True)
     inp = make_inputs(T, C, seed=0, rows=w.rows, device=dev)
     # incoming coefficients of this layer: computed by the library itself
     coeffs_in = mhc.coeffs(inp["x"], inp["phi"], inp["bias"], params)
@@ -270,10 +276,11 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name}: fused post->pre (projection repack + fused pass per step)",
                    "tokens": T, "hidden": C, "routes": 4, "mxfp8": mx, "bf16_h": with_h, "rows": rows,
+                   "schedule": sched,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(args.workload),
-                     "kernel": "k_split (fused post->pre)", "kernel_avg_us": kern_avg_ms * 1e3,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(args.workload, sched),
+                     "kernel": KERNEL_NAMES[sched], "kernel_avg_us": kern_avg_ms * 1e3,
                      "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
     }

@@ -118,16 +118,24 @@ int mhc_last_hip_error(void);
  * that call's outputs are invalid.  Calls never clear it; mhc_workspace_init
  * does.  The caller reads it after synchronising with `stream`.
  *
- * Schedule.  These two calls run a staged kernel whose workgroups wait only
- * on work of lower-numbered workgroups.  With the environment variable
- * MHC_SCHEDULE=persistent (read on every call) and 32 <= C/128 <= 64, a
- * persistent kernel runs instead: one 512-thread workgroup per compute unit,
- * every one of which must be resident at once, so nothing else may occupy
- * the device while it runs (else its waits expire and set the error word).
- * Results of the two schedules are equal to within the stated tolerances
- * (x_out and the MXFP8 codes bitwise).
+ * Schedule.  When 32 <= C/128 <= 64 and T spans enough 32-token tiles
+ * (two per stream workgroup), these two calls run a persistent kernel: one
+ * 512-thread workgroup per compute unit, every one of which must be
+ * resident at once; work that occupies compute units meanwhile delays it,
+ * and if that outlasts its bounded waits they expire and set the error word.
+ * Otherwise, or with the environment variable MHC_SCHEDULE=staged (read on
+ * every call), a staged kernel runs whose workgroups wait only on work of
+ * lower-numbered workgroups.  Results of the two schedules are equal to
+ * within the stated tolerances (x_out and the MXFP8 codes bitwise).
  * ------------------------------------------------------------------------- */
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags);
+/* Which kernel mhc_coeffs and mhc_post_pre_fused run for T tokens and
+ * channel count C on the current device under the current MHC_SCHEDULE:
+ * writes MHC_SCHEDULE_STAGED or MHC_SCHEDULE_PERSISTENT to *schedule.
+ * Returns MHC_ERR_NULL or MHC_ERR_SHAPE (nothing written) on bad arguments.
+ * Queries the device's compute-unit count (no launch, no allocation). */
+enum { MHC_SCHEDULE_STAGED = 0, MHC_SCHEDULE_PERSISTENT = 1 };
+int mhc_schedule(int64_t T, int64_t C, int* schedule);
 int mhc_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

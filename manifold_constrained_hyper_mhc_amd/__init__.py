@@ -10,8 +10,8 @@ missing library is an error, never a fallback.
 """
 from .params import Params
 from .binding import (MhcError, coeffs, coeffs_prepacked, lib, pack_phi, post,
-                      post_pre_fused, post_pre_fused_prepacked, pre, workspace, workspace_error)
+                      post_pre_fused, post_pre_fused_prepacked, pre, schedule, workspace, workspace_error)
 
 __all__ = ["Params", "MhcError", "lib", "coeffs", "coeffs_prepacked", "pre", "post",
            "post_pre_fused", "post_pre_fused_prepacked", "pack_phi", "workspace",
-           "workspace_error"]
+           "schedule", "workspace_error"]

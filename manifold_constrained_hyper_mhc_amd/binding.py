@@ -58,6 +58,7 @@ _SIG = {
     "mhc_workspace_bytes": ([_I64, _I64, ctypes.c_uint], ctypes.c_size_t),
     "mhc_workspace_init": ([_P, ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_phi_packed_bytes": ([_I64], ctypes.c_size_t),
+    "mhc_schedule": ([_I64, _I64, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "mhc_pack_phi": ([_P, _I64, _P, _P], ctypes.c_int),
     "mhc_coeffs": ([_P, _I64, _I64, _P, _P, ctypes.POINTER(MhcParams), _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_coeffs_prepacked": ([_P, _I64, _I64, _P, _P, ctypes.POINTER(MhcParams), _P, _P, ctypes.c_size_t, _P],
@@ -142,6 +143,15 @@ def workspace(T: int, C: int, device=None, *, fresh: bool = False) -> torch.Tens
         if not fresh:
             _WS[key] = ws
     return ws
+
+
+def schedule(T: int, C: int) -> str:
+    """"persistent" or "staged": the kernel mhc_coeffs and mhc_post_pre_fused
+    run for this shape on the current device (MHC_SCHEDULE=staged forces the
+    staged one)."""
+    out = ctypes.c_int(-1)
+    _check(lib().mhc_schedule(T, C, ctypes.byref(out)), "mhc_schedule")
+    return "persistent" if out.value == 1 else "staged"
 
 
 def workspace_error(ws: torch.Tensor) -> int:

@@ -92,14 +92,13 @@ bool plan_fits(const mhc::Plan& p) {
 }
 
 // Persistent kernel: one 512-thread workgroup per CU, S*L stream workgroups
-// plus 32 reduce workgroups, all resident.  Eligible when a tile's 32 tokens
-// map onto distinct splits for the level-1 reduce (32 <= S <= 64) and each
-// stream workgroup gets at least two tiles.  It runs only when the
-// environment variable MHC_SCHEDULE is "persistent" (read on every call);
-// otherwise, and for shapes it does not take, the staged kernel runs.
-bool persistent_requested() {
+// plus 32 reduce workgroups, all resident.  It runs when 32 <= S <= 64 and
+// each stream workgroup gets at least two tiles, unless the environment
+// variable MHC_SCHEDULE is "staged" (read on every call); otherwise the
+// staged kernel runs.
+bool persistent_allowed() {
   const char* v = getenv("MHC_SCHEDULE");
-  return v != nullptr && strcmp(v, "persistent") == 0;
+  return v == nullptr || strcmp(v, "staged") != 0;
 }
 
 int device_cus() {
@@ -116,12 +115,8 @@ int device_cus() {
 
 void choose_kernel(mhc::Plan& p) {
   p.lanes = 0;
-  if (!persistent_requested()) return;
+  if (!persistent_allowed()) return;
   if (p.m != 32 || p.s < 32 || p.s > 64) return;
-  // level-1 reduce: a split's share of a tile's 32*34 partial words, summed
-  // by runs of at most three splits per thread
-  const int ch = (32 * mhc::kPartVals + p.s - 1) / p.s, rt = 512 / ch;
-  if ((p.s + rt - 1) / rt > 3) return;
   const int cus = device_cus();
   const int lanes = (cus - 32) / p.s;
   if (lanes < 1 || p.tiles < 2 * (int64_t)lanes || p.s * lanes + 32 > mhc::kPersistMaxBlocks) return;
@@ -326,6 +321,16 @@ int mhc_last_hip_error(void) { return g_last_hip_error; }
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags) {
   if (check_shape(T, C) != MHC_OK || (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X))) return 0;
   return mhc::make_plan(T, C).total;
+}
+
+int mhc_schedule(int64_t T, int64_t C, int* schedule) {
+  if (schedule == nullptr) return MHC_ERR_NULL;
+  const int rc = check_shape(T, C);
+  if (rc != MHC_OK) return rc;
+  mhc::Plan p = mhc::make_plan(T, C);
+  choose_kernel(p);
+  *schedule = p.lanes > 0 ? MHC_SCHEDULE_PERSISTENT : MHC_SCHEDULE_STAGED;
+  return MHC_OK;
 }
 
 int mhc_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {

@@ -792,7 +792,11 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-constexpr int kBufNT = 2;  // buffer store cache policy: non-temporal
+// The persistent kernel's loads and stores of y, h and x_out use the default
+// cache policy: a wave covers 64 bytes of each of 16 rows, half of a
+// 128-byte line whose other half a neighbouring wave reads or writes.  With
+// the non-temporal policy the halves leave the L2 separately (measured: 29%
+// more bytes written to memory, and a slower pass).
 
 template <int MODE>
 __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs a) {
@@ -810,7 +814,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
   __shared__ float gam[FUSED ? kCC : 1];
-  float* finw = reinterpret_cast<float*>(&xslot[0][0][0]);  // reduce workgroups: [TM][NV]
+  float* finw = reinterpret_cast<float*>(&xslot[0][0][0]);  // reduce workgroups: [2][8 tokens][NV]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, C = a.C, L = a.lanes;
@@ -820,17 +824,23 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 
   if ((int)blockIdx.x >= nstream) {
     // ------------------------- reduce workgroup -------------------------
-    // Reduce workgroup j owns the tiles t = j, j + R, ... (R reduce
-    // workgroups).  Thread v sums partial words v, v + 512, ... of the tile
-    // ([TM][NV] words per split) over the S splits in split order,
-    // reloading words whose tag is stale; then each wave finalises four
-    // tokens, one per 16-lane row.
+    // Work unit u = 8 tokens: tile u / 4, tokens 8 (u % 4) .. + 7 (one half
+    // of a row block, whose partial words arrive together).  Reduce
+    // workgroup j owns the units j, j + R, ... (R reduce workgroups).
+    // Waves 2-7 gather: thread v < 8 NV sums word v of the unit (a
+    // contiguous run in every split's [TM][NV] partial) over the S splits in
+    // split order, in one pass, reloading words whose tag is stale.  Waves
+    // 0-1 finalise the previous unit meanwhile, four tokens per wave (one per
+    // 16-lane row); the sums are double-buffered in LDS.
     const int j = (int)blockIdx.x - nstream;
     const int nred = (int)gridDim.x - nstream;
+    const int nunits = tiles * (TM / 8);
     const int64_t pstride = (int64_t)TM * NV;  // one split's partial tile
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int v = tid - 128;  // gather thread's word
+    const bool act = wv >= 2 && v < 8 * NV && (v % NV) < NVU;
     uint64_t wa[16], wb[16], wc[16], wd[16];
     const uint64_t* pb = a.partials;
-    bool act = false;
     float sum = 0.0f;
     auto load_chunk = [&](uint64_t* w, int sc) __attribute__((always_inline)) {
 #pragma unroll
@@ -846,7 +856,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       if (stale()) {
         uint32_t it = 0;
         do {
-          __builtin_amdgcn_s_sleep(2);
+          __builtin_amdgcn_s_sleep(1);
           // bounded: a wait that expires sets the error word, and every
           // other wait of the launch gives up as soon as it sees it
           if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
@@ -862,41 +872,44 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       for (int k = 0; k < 16; ++k) sum += sc + k < S ? tagged_value(w[k]) : 0.0f;
     };
     static_assert(kPersistMaxS == 64, "four chunks of 16 splits");
-    float* fin = finw;  // [TM][NV] sums of the current tile
-    for (int t = j; t < tiles; t += nred) {
-      for (int v = tid; v < TM * NV; v += kPersistThreads) {
-        act = (v % NV) < NVU;
-        pb = a.partials + (int64_t)t * S * pstride + v;
-        sum = 0.0f;
-        load_chunk(wa, 0);
-        load_chunk(wb, 16);
-        load_chunk(wc, 32);
-        load_chunk(wd, 48);
-        add_chunk(wa, 0);
-        add_chunk(wb, 16);
-        add_chunk(wc, 32);
-        add_chunk(wd, 48);
-        fin[v] = act ? sum : 0.0f;
-      }
-      __syncthreads();  // the tile's sums
-      {
-        // wave w finalises tokens 4w .. 4w + 3, token 4w + r on lanes
-        // 16r .. 16r + 15
-        const int m = 4 * wave + (lane >> 4), k = lane & 15;
-        const int64_t tok = (int64_t)t * TM + m;
+    auto gather = [&](int u, float* fin) __attribute__((always_inline)) {
+      pb = a.partials + (int64_t)(u >> 2) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
+      sum = 0.0f;
+      load_chunk(wa, 0);
+      load_chunk(wb, 16);
+      load_chunk(wc, 32);
+      load_chunk(wd, 48);
+      add_chunk(wa, 0);
+      add_chunk(wb, 16);
+      add_chunk(wc, 32);
+      add_chunk(wd, 48);
+      if (v >= 0 && v < 8 * NV) fin[v] = act ? sum : 0.0f;
+    };
+    if (j < nunits && wv >= 2) gather(j, finw);
+    __syncthreads();
+    int k = 0;
+    for (int u = j; u < nunits; u += nred, ++k) {
+      float* fin = finw + (k & 1) * (8 * NV);  // this unit's sums
+      if (wv < 2) {
+        // token 4 wave + r of the unit on lanes 16r .. 16r + 15
+        const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
+        const int64_t tok = (int64_t)(u >> 2) * TM + (u & 3) * 8 + ml;
         float res, pp, q[4];
-        finalize_rows<FUSED>(fin + m * NV, a.bias, C, a.sc, lane, res, pp, q);
+        finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp, q);
         if (tok < a.T) {
-          a.coeffs_out[tok * kCoeffs + 8 + k] = res;
-          if (k < 8) a.coeffs_out[tok * kCoeffs + k] = pp;
+          a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
+          if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
         }
         if constexpr (FUSED) {
           // every row of the tile is published ([tiles][TM][4] words): the
           // stream workgroups poll whole row blocks, padding rows included
-          if (k < 4) tagged_store(a.publish + tok * 4 + k, k == 0 ? q[0] : k == 1 ? q[1] : k == 2 ? q[2] : q[3], tag);
+          if (kk < 4)
+            tagged_store(a.publish + tok * 4 + kk, kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], tag);
         }
+      } else if (u + nred < nunits) {
+        gather(u + nred, finw + ((k + 1) & 1) * (8 * NV));
       }
-      __syncthreads();  // this tile's sums are read
+      __syncthreads();  // the next unit's sums are in; this unit's are read
     }
   } else {
     // ------------------------- stream workgroup -------------------------
@@ -965,7 +978,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       const int t = r + L * (i < niter ? i : 0);
       const int64_t tok = (int64_t)t * TM + m;
       const int64_t tc = tok < a.T ? tok : 0;
-      ny = ld16_stream(a.y + tc * (int64_t)C + cl);
+      ny = *reinterpret_cast<const u32x4_t*>(a.y + tc * (int64_t)C + cl);
       const int64_t ct = (int64_t)t * TM + rb * 16 + gt / 5;
       const bool cv = gt < 16 * 5 && ct < a.T;
       ncf = reinterpret_cast<const float4*>(a.coeffs_in + (cv ? ct : 0) * kCoeffs)[1 + (cv ? gt % 5 : 0)];
@@ -989,7 +1002,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 
     // Memory-operation order of one row block (vmcnt counts them in issue
     // order; the x slot copies are invisible to the compiler's counting):
-    //   P(i): partial stores of tile t_{i-1} (3), loads of tile t_{i+1}
+    //   P(i): partial stores of tile t_{i-1} (up to 3), loads of tile t_{i+1}
     //         (FUSED: y, coefficients, q), h and x_out buffer stores
     //         (unconditional: rows past T are dropped by the bounds check)
     //   M(i): x slot copies of tile t_{i+2} (4, invisible), MFMAs, fold,
@@ -1011,12 +1024,15 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         uint64_t* part = a.partials + ((int64_t)(t - L) * S + split) * (TM * NV) + rb * 16 * NV;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-          const int idx = min(gt + k * 256, 16 * NV - 1);
+          const int idx = gt + k * 256;
           const int tm = idx / NV, vv = idx % NV;
-          const float sum = vv < NVU ? ((red[rb * 4][tm][vv] + red[rb * 4 + 1][tm][vv]) + red[rb * 4 + 2][tm][vv]) +
-                                           red[rb * 4 + 3][tm][vv]
-                                     : 0.0f;
-          tagged_store(part + idx, sum, tag);
+          // (words past the row block, and in the coefficients-only mode the
+          // unused Gram slots, are not stored: nothing reads them)
+          if (idx < 16 * NV && vv < NVU) {
+            const float sum =
+                ((red[rb * 4][tm][vv] + red[rb * 4 + 1][tm][vv]) + red[rb * 4 + 2][tm][vv]) + red[rb * 4 + 3][tm][vv];
+            tagged_store(part + idx, sum, tag);
+          }
         }
       }
       const u32x4_t cy = ny;
@@ -1051,7 +1067,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         const u32x4_t hb = pack8(hv);
         if (!MX || a.h != nullptr)
           __builtin_amdgcn_raw_buffer_store_b128(hb, buffer_rsrc(a.h + tokC0 * C, nC * (uint32_t)(2 * C)),
-                                                 (n16 * C + cl) * 2, 0, kBufNT);
+                                                 (n16 * C + cl) * 2, 0, 0);
         if constexpr (MX) {
           // a 32-channel block is the 4 lanes n16, n16 + 16, n16 + 32, n16 + 48
           float hr[8];
@@ -1111,7 +1127,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x_out + tokA0 * (4 * C), nA * (uint32_t)(8 * C));
 #pragma unroll
           for (int jr = 0; jr < 4; ++jr)
-            __builtin_amdgcn_raw_buffer_store_b128(o[jr], rx, ((n16 * 4 + jr) * C + cl) * 2, 0, kBufNT);
+            __builtin_amdgcn_raw_buffer_store_b128(o[jr], rx, ((n16 * 4 + jr) * C + cl) * 2, 0, 0);
         } else {
 #pragma unroll
           for (int jr = 0; jr < 4; ++jr) o[jr] = xin[jr];

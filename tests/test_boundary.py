@@ -37,6 +37,16 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_schedule_query():
+    """mhc_schedule validates like the other calls; without a usable device
+    (or for a decode-sized T) it reports the staged kernel."""
+    L = mhc.lib()
+    out = ctypes.c_int(-7)
+    assert L.mhc_schedule(16, 1000, ctypes.byref(out)) == 2 and out.value == -7  # MHC_ERR_SHAPE
+    assert L.mhc_schedule(16, 1024, None) == 1  # MHC_ERR_NULL
+    assert L.mhc_schedule(6, 7168, ctypes.byref(out)) == 0 and out.value == 0  # one tile: staged
+
+
 def test_abi_version_and_strerror():
     L = mhc.lib()
     assert L.mhc_abi_version() == 1

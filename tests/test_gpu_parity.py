@@ -74,6 +74,16 @@ SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048)]
 PERSISTENT = [(300, 7168), (500, 4096)]
 
 
+def test_schedule_choice(monkeypatch):
+    """The prefill shape runs the persistent kernel by default, the staged
+    one when asked for, and a decode-sized T always runs the staged one."""
+    monkeypatch.delenv("MHC_SCHEDULE", raising=False)
+    assert mhc.schedule(8192, 7168) == "persistent"
+    assert mhc.schedule(6, 7168) == "staged"
+    monkeypatch.setenv("MHC_SCHEDULE", "staged")
+    assert mhc.schedule(8192, 7168) == "staged"
+
+
 @pytest.fixture(params=["staged", "persistent"])
 def schedule(request, monkeypatch):
     """Runs the test under each kernel schedule (MHC_SCHEDULE is read by the
