@@ -159,10 +159,6 @@ Plan make_plan(int64_t T, int64_t C) {
   off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(uint64_t));
   p.off_own = off;
   off = round256(off + (size_t)p.tiles * p.s * sizeof(uint64_t));
-  p.off_red = off;
-  off = round256(off + (size_t)p.tiles * p.m * kPartVals * sizeof(uint64_t));
-  p.off_sink = off;
-  off = round256(off + kSinkBytes);
   p.off_phi = off;
   off = round256(off + phi_packed_bytes(C));
   p.total = off;
@@ -184,8 +180,6 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
-  a.reduced = reinterpret_cast<uint64_t*>(base + plan.off_red);
-  a.sink = reinterpret_cast<uint32_t*>(base + plan.off_sink);
   a.T = T;
   a.tiles = (uint32_t)plan.tiles;
   a.C = (int)C;

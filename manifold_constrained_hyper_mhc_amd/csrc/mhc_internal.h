@@ -29,7 +29,7 @@ struct Plan {
   int lanes = 0;   // persistent kernel: stream workgroups per split (0: staged kernel)
   int64_t tiles = 0;
   // workspace layout (byte offsets)
-  size_t off_pub = 0, off_part = 0, off_own = 0, off_red = 0, off_sink = 0, off_phi = 0, total = 0;
+  size_t off_pub = 0, off_part = 0, off_own = 0, off_phi = 0, total = 0;
 };
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
@@ -42,11 +42,8 @@ constexpr size_t kWsDep = 256;
 constexpr int64_t kMaxTiles = (int64_t)(1 << 20) / 32;
 constexpr size_t kWsHeaderBytes = kWsDep + (size_t)kMaxTiles * 4;
 constexpr int kPackBlocks = 5;          // 80 packed columns = 5 MFMA 16-column blocks
-// Persistent kernel: at most this many workgroups; each owns 64 bytes of a
-// sink region that takes stores whose only purpose is their place in the
-// memory-operation order.
+// Persistent kernel: at most this many workgroups (one per compute unit).
 constexpr int kPersistMaxBlocks = 512;
-constexpr size_t kSinkBytes = (size_t)kPersistMaxBlocks * 64;
 constexpr size_t kPackBytesPerRow = 160;  // 80 bf16 per flattened row k
 
 Plan make_plan(int64_t T, int64_t C);
@@ -83,8 +80,6 @@ struct SplitArgs {
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
   uint64_t* publish;   // [tiles][M][4] tagged words
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
-  uint64_t* reduced;   // [tiles][M][34] tagged split sums of each token (persistent kernel)
-  uint32_t* sink;      // [kPersistMaxBlocks][16] words nobody reads (persistent kernel)
   uint32_t* err;
   int64_t T;
   uint32_t tiles;
