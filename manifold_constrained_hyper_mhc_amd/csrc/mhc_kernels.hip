@@ -779,8 +779,9 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // wave.  Written as inline assembly so that the compiler neither counts nor
 // waits for it: callers wait with an explicit vmcnt, and the compiler's own
 // waits for other loads only get more conservative from the uncounted ops.
+// Non-temporal: every x line is read once, whole, by one wave.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(src), "s"(base)
                : "memory", "m0");
