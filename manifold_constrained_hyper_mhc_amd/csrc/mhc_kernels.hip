@@ -815,7 +815,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
   __shared__ float gam[FUSED ? kCC : 1];
-  float* finw = reinterpret_cast<float*>(&xslot[0][0][0]);  // reduce workgroups: [2][8 tokens][NV]
+  float* finw = reinterpret_cast<float*>(&xslot[0][0][0]);  // reduce workgroups: [2][8][NV] or [TM][NV] sums
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, C = a.C, L = a.lanes;
@@ -832,14 +832,15 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     // contiguous run in every split's [TM][NV] partial) over the S splits in
     // split order, in one pass, reloading words whose tag is stale.  Waves
     // 0-1 finalise the previous unit meanwhile, four tokens per wave (one per
-    // 16-lane row); the sums are double-buffered in LDS.
+    // 16-lane row); the sums are double-buffered in LDS.  (The
+    // coefficients-only mode takes whole tiles per round instead.)
     const int j = (int)blockIdx.x - nstream;
     const int nred = (int)gridDim.x - nstream;
     const int nunits = tiles * (TM / 8);
     const int64_t pstride = (int64_t)TM * NV;  // one split's partial tile
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int v = tid - 128;  // gather thread's word
-    const bool act = wv >= 2 && v < 8 * NV && (v % NV) < NVU;
+    bool act = wv >= 2 && v < 8 * NV && (v % NV) < NVU;
     uint64_t wa[16], wb[16], wc[16], wd[16];
     const uint64_t* pb = a.partials;
     float sum = 0.0f;
@@ -873,44 +874,76 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       for (int k = 0; k < 16; ++k) sum += sc + k < S ? tagged_value(w[k]) : 0.0f;
     };
     static_assert(kPersistMaxS == 64, "four chunks of 16 splits");
-    auto gather = [&](int u, float* fin) __attribute__((always_inline)) {
-      pb = a.partials + (int64_t)(u >> 2) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
-      sum = 0.0f;
-      load_chunk(wa, 0);
-      load_chunk(wb, 16);
-      load_chunk(wc, 32);
-      load_chunk(wd, 48);
-      add_chunk(wa, 0);
-      add_chunk(wb, 16);
-      add_chunk(wc, 32);
-      add_chunk(wd, 48);
-      if (v >= 0 && v < 8 * NV) fin[v] = act ? sum : 0.0f;
-    };
-    if (j < nunits && wv >= 2) gather(j, finw);
-    __syncthreads();
-    int k = 0;
-    for (int u = j; u < nunits; u += nred, ++k) {
-      float* fin = finw + (k & 1) * (8 * NV);  // this unit's sums
-      if (wv < 2) {
-        // token 4 wave + r of the unit on lanes 16r .. 16r + 15
+    if constexpr (!FUSED) {
+      // Coefficients only: nothing waits on the result but the end of the
+      // launch, so whole tiles per round (all threads gather, then every
+      // wave finalises four tokens) give more tokens per round.
+      for (int t = j; t < tiles; t += nred) {
+        for (int w = tid; w < TM * NV; w += kPersistThreads) {
+          act = (w % NV) < NVU;
+          pb = a.partials + (int64_t)t * S * pstride + w;
+          sum = 0.0f;
+          load_chunk(wa, 0);
+          load_chunk(wb, 16);
+          load_chunk(wc, 32);
+          load_chunk(wd, 48);
+          add_chunk(wa, 0);
+          add_chunk(wb, 16);
+          add_chunk(wc, 32);
+          add_chunk(wd, 48);
+          finw[w] = act ? sum : 0.0f;
+        }
+        __syncthreads();  // the tile's sums
         const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
-        const int64_t tok = (int64_t)(u >> 2) * TM + (u & 3) * 8 + ml;
+        const int64_t tok = (int64_t)t * TM + ml;
         float res, pp, q[4];
-        finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp, q);
+        finalize_rows<false>(finw + ml * NV, a.bias, C, a.sc, lane, res, pp, q);
         if (tok < a.T) {
           a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
           if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
         }
-        if constexpr (FUSED) {
-          // every row of the tile is published ([tiles][TM][4] words): the
-          // stream workgroups poll whole row blocks, padding rows included
-          if (kk < 4)
-            tagged_store(a.publish + tok * 4 + kk, kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], tag);
-        }
-      } else if (u + nred < nunits) {
-        gather(u + nred, finw + ((k + 1) & 1) * (8 * NV));
+        __syncthreads();  // this tile's sums are read
       }
-      __syncthreads();  // the next unit's sums are in; this unit's are read
+    } else {
+      auto gather = [&](int u, float* fin) __attribute__((always_inline)) {
+        pb = a.partials + (int64_t)(u >> 2) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
+        sum = 0.0f;
+        load_chunk(wa, 0);
+        load_chunk(wb, 16);
+        load_chunk(wc, 32);
+        load_chunk(wd, 48);
+        add_chunk(wa, 0);
+        add_chunk(wb, 16);
+        add_chunk(wc, 32);
+        add_chunk(wd, 48);
+        if (v >= 0 && v < 8 * NV) fin[v] = act ? sum : 0.0f;
+      };
+      if (j < nunits && wv >= 2) gather(j, finw);
+      __syncthreads();
+      int k = 0;
+      for (int u = j; u < nunits; u += nred, ++k) {
+        float* fin = finw + (k & 1) * (8 * NV);  // this unit's sums
+        if (wv < 2) {
+          // token 4 wave + r of the unit on lanes 16r .. 16r + 15
+          const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
+          const int64_t tok = (int64_t)(u >> 2) * TM + (u & 3) * 8 + ml;
+          float res, pp, q[4];
+          finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp, q);
+          if (tok < a.T) {
+            a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
+            if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
+          }
+          if constexpr (FUSED) {
+            // every row of the tile is published ([tiles][TM][4] words): the
+            // stream workgroups poll whole row blocks, padding rows included
+            if (kk < 4)
+              tagged_store(a.publish + tok * 4 + kk, kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], tag);
+          }
+        } else if (u + nred < nunits) {
+          gather(u + nred, finw + ((k + 1) & 1) * (8 * NV));
+        }
+        __syncthreads();  // the next unit's sums are in; this unit's are read
+      }
     }
   } else {
     // ------------------------- stream workgroup -------------------------
