@@ -127,7 +127,7 @@ __device__ __forceinline__ float gram_quadratic(const float* G, const float* p) 
 
 // ---------------------------------------------------------------------------
 // MXFP8: UE8M0 exponent of a block from the bits of its bf16 amax, and the
-// OCP e4m3fn code of a value with |v| <= 448, round-to-nearest-even.
+// OCP e4m3fn codes of the scaled values, round-to-nearest-even.
 // amax = (1 + f/128) 2^E and 448 = 1.75 * 2^8, so the smallest e with
 // amax <= 448 * 2^e is E - 8 when f <= 96 and E - 7 otherwise.
 // ---------------------------------------------------------------------------
@@ -141,17 +141,14 @@ __device__ __forceinline__ int mx_scale_exponent(float amax_bf16) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a < 0x3C800000u) {  // |v| < 2^-6: subnormal step 2^-9 (8 rounds up to the smallest normal)
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {  // keep 3 mantissa bits with round-to-nearest-even, rebias 127 -> 7
-    code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  }
-  return code | sign;
+// Four OCP e4m3fn codes of values with |v| <= 448, packed first value in the
+// low byte, by the gfx950 converter (round to nearest even, subnormals kept):
+// each pair is one v_cvt_pk_fp8_f32.  The codes are tested bit for bit
+// against the oracle's encoder through the MXFP8 outputs.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
 // ---------------------------------------------------------------------------

@@ -664,12 +664,8 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
           amax = __builtin_fmaxf(amax, MHC_DPP(amax, kDppQuadSwap2));
           const int ex = mx_scale_exponent(amax);
           const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
-          uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w0 |= e4m3_code(hr[e] * scale) << (8 * e);
-            w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
-          }
+          const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
+          const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
           if (valid) {
             *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + cl) = u32x2_t{w0, w1};
             if ((c8 & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
@@ -1113,12 +1109,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
           const int ex = mx_scale_exponent(amax);
           const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
-          uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w0 |= e4m3_code(hr[e] * scale) << (8 * e);
-            w1 |= e4m3_code(hr[4 + e] * scale) << (8 * e);
-          }
+          const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
+          const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
           __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, buffer_rsrc(a.h_fp8 + tokC0 * C, nC * (uint32_t)C),
                                                 n16 * C + cl, 0, 0);
           // the block's four lanes store the same scale byte
