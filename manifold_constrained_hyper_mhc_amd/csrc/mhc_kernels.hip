@@ -1052,17 +1052,20 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // the four 32-channel steps added in order
       if constexpr (doPrev) {
         uint64_t* part = a.partials + ((int64_t)(t - L) * S + split) * (TM * NV) + rb * 16 * NV;
+        // all twelve LDS reads first, then the stores (words past the row
+        // block, and in the coefficients-only mode the unused Gram slots,
+        // are not stored: nothing reads them)
+        float sum[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const int idr = min(gt + k * 256, 16 * NV - 1);
+          const int tm = idr / NV, vv = idr % NV;
+          sum[k] = ((red[rb * 4][tm][vv] + red[rb * 4 + 1][tm][vv]) + red[rb * 4 + 2][tm][vv]) + red[rb * 4 + 3][tm][vv];
+        }
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           const int idx = gt + k * 256;
-          const int tm = idx / NV, vv = idx % NV;
-          // (words past the row block, and in the coefficients-only mode the
-          // unused Gram slots, are not stored: nothing reads them)
-          if (idx < 16 * NV && vv < NVU) {
-            const float sum =
-                ((red[rb * 4][tm][vv] + red[rb * 4 + 1][tm][vv]) + red[rb * 4 + 2][tm][vv]) + red[rb * 4 + 3][tm][vv];
-            tagged_store(part + idx, sum, tag);
-          }
+          if (idx < 16 * NV && idx % NV < NVU) tagged_store(part + idx, sum[k], tag);
         }
       }
       const u32x4_t cy = ny;
