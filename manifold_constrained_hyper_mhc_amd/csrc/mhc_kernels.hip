@@ -724,7 +724,8 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 //     the other runs M, so each SIMD has one wave on its vector ALU and one
 //     on its matrix core between the two barriers of an iteration.
 //   * 32 "reduce" workgroups gather the S partial rows of 8 tokens at a
-//     time, finalise their coefficients (one wave per token) and publish
+//     time (a whole tile in the coefficients-only mode), finalise their
+//     coefficients (four tokens per wave, one per 16-lane row) and publish
 //     q_i = pre'_i * r_h.
 // Stream workgroups wait for q words published by reduce workgroups, which
 // wait for partials of stream workgroups, so the launch needs all S*L + 32
@@ -760,12 +761,12 @@ __device__ __forceinline__ bool error_seen(uint32_t* err) {
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// LDS byte address of a __shared__ object.
 // Workgroup barrier for the persistent loop: waits for this wave's LDS
 // operations, then s_barrier.  The text argument only keeps two otherwise
 // identical barriers apart in the compiled code.
 #define MHC_GROUP_BARRIER(where) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier ; " where ::: "memory")
 
+// LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
