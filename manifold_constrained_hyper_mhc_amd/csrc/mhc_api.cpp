@@ -88,7 +88,7 @@ size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 bool plan_fits(const mhc::Plan& p) {
   const int64_t ntok = (p.m + p.s - 1) / p.s;
   if (ntok > 8 || ntok * mhc::kPartVals > 256) return false;
-  return mhc::plan_run_len(p) <= mhc::kRunMax && p.m == 32 && p.tiles <= mhc::kMaxTiles;
+  return mhc::plan_run_len(p) <= mhc::kRunMax && (p.m == 32 || p.m == 16) && p.tiles <= mhc::kMaxTiles;
 }
 
 // Persistent kernel: one 512-thread workgroup per CU, S*L stream workgroups
@@ -138,7 +138,7 @@ namespace mhc {
 // Tile shape: 32 tokens x 128 channels (of every route) per workgroup.
 Plan make_plan(int64_t T, int64_t C) {
   Plan p;
-  p.m = 32;
+  p.m = T <= 16 ? 16 : 32;  // a decode-sized call takes one 16-token tile
   p.cc = 128;
   p.s = (int)(C / p.cc);
   p.tiles = (T + p.m - 1) / p.m;

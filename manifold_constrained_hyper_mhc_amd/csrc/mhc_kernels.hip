@@ -1529,8 +1529,14 @@ template <int MODE>
 static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
   const int64_t stages = p.tiles + (MODE == kModeCoeffs ? p.d1 : p.d2);
   const dim3 grid((unsigned)(stages * p.s)), block(256);
-  if (p.m != 32 || p.cc != kCC) return hipErrorInvalidConfiguration;
-  if (plan_run_len(p) <= 8) {
+  if ((p.m != 32 && p.m != 16) || p.cc != kCC) return hipErrorInvalidConfiguration;
+  if (p.m == 16) {
+    if (plan_run_len(p) <= 8) {
+      k_split<MODE, 16, 8><<<grid, block, 0, s>>>(a);
+    } else {
+      k_split<MODE, 16, kRunMax><<<grid, block, 0, s>>>(a);
+    }
+  } else if (plan_run_len(p) <= 8) {
     k_split<MODE, 32, 8><<<grid, block, 0, s>>>(a);
   } else {
     k_split<MODE, 32, kRunMax><<<grid, block, 0, s>>>(a);
