@@ -180,10 +180,12 @@ constexpr int kDppRowRor8 = 0x128;   // row_ror:8
 // the 4x4 matrix are sums over lane ^ {1, 2}, column sums over the 16-lane
 // row rotated by 4, 8, 12.  Each normalisation multiplies by the reciprocal
 // of (sum + eps).  Returns in every lane the value of coefficient
-// slot(lane); q gets pre_i * r_h.
-template <bool FUSED>
+// slot(lane).  In the fused modes publish(q), q_i = pre_i * r_h, runs
+// before the Sinkhorn iterations: the pre step needs only q, so it does not
+// wait for them.
+template <bool FUSED, class Publish>
 __device__ __forceinline__ float finalize_wave(const float* sums, const float* bias, int C, const Scalars& sc,
-                                               int lane, float* q) {
+                                               int lane, Publish&& publish) {
   const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
   const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
   const int li = lane < 16 ? 8 + lane : (lane < 24 ? lane - 16 : 0);
@@ -191,6 +193,16 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
   const float sg = 1.0f / (1.0f + expf(-l));
   const float pp = (lane >= 20 && lane < 24) ? sc.hc_post_scale * sg : sg;
   float v = expf(l);
+  if constexpr (FUSED) {
+    const float p[4] = {__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 16)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 17)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 18)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 19))};
+    const float gq = gram_quadratic(sums + 24, p);
+    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
+    const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
+    publish(q);
+  }
   const float eps = sc.sinkhorn_eps;
   for (int it = 0; it < sc.sinkhorn_iters; ++it) {
     float rs = v + MHC_DPP(v, kDppQuadSwap1);
@@ -200,18 +212,6 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
     cs = cs + MHC_DPP(cs, kDppRowRor4);
     v = v * __builtin_amdgcn_rcpf(cs + eps);
   }
-  if constexpr (FUSED) {
-    const float p[4] = {__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 16)),
-                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 17)),
-                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 18)),
-                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 19))};
-    const float gq = gram_quadratic(sums + 24, p);
-    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
-    q[0] = p[0] * rh;
-    q[1] = p[1] * rh;
-    q[2] = p[2] * rh;
-    q[3] = p[3] * rh;
-  }
   return lane < 16 ? v : pp;
 }
 
@@ -220,15 +220,24 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
 // of the row's token and, for k < 8, its pre (k < 4) or post (4 <= k < 8)
 // weight.  The Sinkhorn row and column sums are the same row-local DPP
 // moves, so the four rows run side by side.  sums: this lane's token.
-template <bool FUSED>
+// publish(q) of the fused modes runs before the Sinkhorn iterations.
+template <bool FUSED, class Publish>
 __device__ __forceinline__ void finalize_rows(const float* sums, const float* bias, int C, const Scalars& sc,
-                                              int lane, float& res, float& pp, float* q) {
+                                              int lane, float& res, float& pp, Publish&& publish) {
   const int k = lane & 15, kp = lane & 7;
   const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
   const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
   const float lp = r * sums[kp] + bias[kp];
   const float sg = 1.0f / (1.0f + expf(-lp));
   pp = kp >= 4 ? sc.hc_post_scale * sg : sg;
+  if constexpr (FUSED) {
+    const int row0 = lane & 48;
+    const float p[4] = {__shfl(pp, row0), __shfl(pp, row0 + 1), __shfl(pp, row0 + 2), __shfl(pp, row0 + 3)};
+    const float gq = gram_quadratic(sums + 24, p);
+    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
+    const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
+    publish(q);
+  }
   const float l = r * sums[8 + k] + bias[8 + k];
   float v = expf(l);
   const float eps = sc.sinkhorn_eps;
@@ -241,16 +250,6 @@ __device__ __forceinline__ void finalize_rows(const float* sums, const float* bi
     v = v * __builtin_amdgcn_rcpf(cs + eps);
   }
   res = v;
-  if constexpr (FUSED) {
-    const int row0 = lane & 48;
-    const float p[4] = {__shfl(pp, row0), __shfl(pp, row0 + 1), __shfl(pp, row0 + 2), __shfl(pp, row0 + 3)};
-    const float gq = gram_quadratic(sums + 24, p);
-    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
-    q[0] = p[0] * rh;
-    q[1] = p[1] * rh;
-    q[2] = p[2] * rh;
-    q[3] = p[3] * rh;
-  }
 }
 
 constexpr int kCC = 128;  // channels per workgroup
@@ -602,13 +601,13 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
       const int kq = k0 + wave;
       if (kq < ntok) {
         const int m = split + kq * S;
-        float q[4];
-        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, C, a.sc, lane, q);
+        uint64_t* const qdst = a.publish + ((int64_t)tR * TM + m) * 4 + (lane & 3);
+        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, C, a.sc, lane,
+                                              [=](const float* q) __attribute__((always_inline)) {
+                                                if (lane < 4) tagged_store(qdst, q[lane & 3], tag);
+                                              });
         const int64_t t = tok0 + m;
         if (t < a.T && lane < 24) a.coeffs_out[t * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
-        if constexpr (FUSED) {
-          if (lane < 4) tagged_store(a.publish + ((int64_t)tR * TM + m) * 4 + lane, q[lane], tag);
-        }
       }
     }
   }
@@ -893,8 +892,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         __syncthreads();  // the tile's sums
         const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
         const int64_t tok = (int64_t)t * TM + ml;
-        float res, pp, q[4];
-        finalize_rows<false>(finw + ml * NV, a.bias, C, a.sc, lane, res, pp, q);
+        float res, pp;
+        finalize_rows<false>(finw + ml * NV, a.bias, C, a.sc, lane, res, pp, [](const float*) {});
         if (tok < a.T) {
           a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
           if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
@@ -924,17 +923,18 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           // token 4 wave + r of the unit on lanes 16r .. 16r + 15
           const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
           const int64_t tok = (int64_t)(u >> 2) * TM + (u & 3) * 8 + ml;
-          float res, pp, q[4];
-          finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp, q);
+          float res, pp;
+          // every row of the tile is published ([tiles][TM][4] words): the
+          // stream workgroups poll whole row blocks, padding rows included
+          finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp,
+                               [&](const float* q) __attribute__((always_inline)) {
+                                 if (kk < 4)
+                                   tagged_store(a.publish + tok * 4 + kk,
+                                                kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], tag);
+                               });
           if (tok < a.T) {
             a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
             if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
-          }
-          if constexpr (FUSED) {
-            // every row of the tile is published ([tiles][TM][4] words): the
-            // stream workgroups poll whole row blocks, padding rows included
-            if (kk < 4)
-              tagged_store(a.publish + tok * 4 + kk, kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], tag);
           }
         } else if (u + nred < nunits) {
           gather(u + nred, finw + ((k + 1) & 1) * (8 * NV));
