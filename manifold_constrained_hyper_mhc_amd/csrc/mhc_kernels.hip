@@ -84,13 +84,15 @@ __global__ __launch_bounds__(256) void k_pack_phi(const float* __restrict__ phi,
 //   R  tile k - D1: workgroup s reduces tokens m with m % S == s: it gathers
 //      their S partials, sums them in split order (deterministic),
 //      finalises the coefficients on one wave per token (Sinkhorn on 16
-//      lanes) and, in the fused modes, publishes q_i, where r_h is the
-//      RMSNorm scale of g = sum_i pre'_i x'_i from the Gram matrix:
+//      lanes) and, in the fused modes, publishes q_i = pre'_i * r_h first
+//      (before the Sinkhorn iterations, which q does not need), where r_h
+//      is the RMSNorm scale of g = sum_i pre'_i x'_i from the Gram matrix:
 //      sum_c g^2 = pre'^T G pre'.
-//   C  (fused modes) tile k - D2: the pre step.  It loads x and y of its
-//      128 channels again (the loads of A left them in the caches) and
-//      recomputes x' with the post chain, bit for bit what A stored, waits
-//      for the tile's published q_i = pre'_i * r_h and writes
+//   C  (fused modes) tile k - D2: the pre step.  It reads x' of its 128
+//      channels back from x_out when phase A of the same split ran on the
+//      same XCD (their shared L2 holds the stores), and otherwise loads x
+//      and y again and recomputes x' with the post chain, bit for bit what
+//      A stored; it waits for the tile's published q_i and writes
 //      h = (sum_i q_i x'_i) * gamma as bf16 and/or MXFP8 (a 32-channel
 //      block is 4 neighbouring lanes).
 //
@@ -114,14 +116,14 @@ __global__ __launch_bounds__(256) void k_pack_phi(const float* __restrict__ phi,
 // that with the round-robin dispatch of workgroups over the 8 XCDs each XCD
 // reads only 1/8 of the packed projection (which then stays in its L2).
 //
-// Communication between workgroups uses agent-coherent 64-bit words that
-// carry a value and a tag: (float bits) | (tag << 32).  The tag of a launch
-// is the workspace's launch epoch + 1, read by every workgroup when it
-// starts; a reader polls the words it needs until their tags match, so no
-// counter sits on the critical path and no cache write-back or invalidation
-// is needed (agent-scope accesses bypass the per-XCD caches, and an aligned
-// 64-bit access is single-copy atomic, so a value is never seen with a
-// wrong tag).  Stale words of earlier launches carry older tags whatever the
+// Communication between workgroups uses 64-bit words that carry a value and
+// a tag: (float bits) | (tag << 32).  The tag of a launch is the
+// workspace's launch epoch + 1, read by every workgroup when it starts; a
+// reader polls the words it needs until their tags match, so no counter
+// sits on the critical path and no cache write-back or invalidation is
+// needed (the words are written and read with system scope, which bypasses
+// the per-XCD caches, and an aligned 64-bit access is single-copy atomic,
+// so a value is never seen with a wrong tag).  Stale words of earlier launches carry older tags whatever the
 // shapes of those launches were.  Off the critical path, the last of a
 // tile's final consumers counts the tile as done, and the one completing the
 // last tile advances the epoch and clears the counter, so the workspace
