@@ -126,7 +126,8 @@ int mhc_last_hip_error(void);
  * Otherwise, or with the environment variable MHC_SCHEDULE=staged (read on
  * every call), a staged kernel runs whose workgroups wait only on work of
  * lower-numbered workgroups.  Results of the two schedules are equal to
- * within the stated tolerances (x_out and the MXFP8 codes bitwise).
+ * within the stated tolerances; x_out is bitwise equal, and either
+ * schedule's MXFP8 codes are the exact encoding of its own bf16 h.
  * ------------------------------------------------------------------------- */
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags);
 /* Which kernel mhc_coeffs and mhc_post_pre_fused run for T tokens and
