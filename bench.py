@@ -157,6 +157,50 @@ def cpu_baseline(inp_host: dict, coeffs_host, params, budget_s: float = 10.0, ch
                       f"fp64 numpy oracle fused post->pre"}
 
 
+def time_unfused(mhc, inp, coeffs_in, packed, params, outs, stream, args, fused_bytes, fused_ms):
+    """The same step without fusion, on the same inputs: mhc_post writes x',
+    mhc_coeffs_prepacked reads it back for the next layer's coefficients and
+    mhc_pre reads it again for h.  HIP events around each launch; returns the
+    per-kernel averages and the chain's algorithmic bytes (36C + 192 per
+    token instead of the fused 20C + 176)."""
+    import torch
+
+    x, y = inp["x"], inp["y"]
+    T, C = x.shape[0], x.shape[2]
+    xp = torch.empty_like(x)
+    cf = torch.empty_like(outs["coeffs_next"])
+    h = torch.empty((T, C), dtype=torch.bfloat16, device=x.device)
+    ws = mhc.workspace(T, C, x.device)
+
+    def chain(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mhc.post(x, y, coeffs_in, out=xp)
+        if ev is not None:
+            ev[1].record(stream)
+        mhc.coeffs_prepacked(xp, packed, inp["bias_next"], params, ws=ws, out=cf)
+        if ev is not None:
+            ev[2].record(stream)
+        mhc.pre(xp, cf, inp["gamma_next"], params, out=h)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        chain()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        chain(evs[k])
+    torch.cuda.synchronize()
+    avg = lambda i, j: sum(e[i].elapsed_time(e[j]) for e in evs) / len(evs) * 1e3  # noqa: E731
+    chain_us = avg(0, 3)
+    chain_bytes = T * (36 * C + 192) + 388 * C + 96
+    return {"chain_us": chain_us, "post_us": avg(0, 1), "coeffs_us": avg(1, 2), "pre_us": avg(2, 3),
+            "chain_algorithmic_bytes": chain_bytes, "chain_gbs": chain_bytes / (chain_us * 1e-6) / 1e9,
+            "fused_over_chain_time": fused_ms * 1e3 / chain_us,
+            "note": "same inputs; x' written by post and read back by coeffs and pre"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +208,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "mxfp8", "long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="also time the unfused chain post -> coeffs -> pre on the same inputs "
+                         "(default for the long workload)")
     ap.add_argument("--copy-probe", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar="FILE", help="summarise rocprofv3 counter output and exit")
     args = ap.parse_args()
@@ -252,6 +299,13 @@ def main() -> int:
           f" {achieved:.0f} GB/s algorithmic = {achieved / HBM_PEAK_GBS:.3f} of peak; wall {wall:.3f} s",
           file=sys.stderr, flush=True)
 
+    unfused = None
+    if args.unfused or args.workload == "long":
+        unfused = time_unfused(mhc, inp, coeffs_in, packed, params, outs, stream, args, nbytes, kern_avg_ms)
+        print(f"[bench] unfused chain post -> coeffs -> pre: {unfused['chain_us']:.1f} us "
+              f"(post {unfused['post_us']:.1f}, coeffs {unfused['coeffs_us']:.1f}, pre {unfused['pre_us']:.1f}); "
+              f"fused pass {kern_avg_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         n_s = min(T, 1024)
@@ -284,6 +338,8 @@ def main() -> int:
                      "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
     }
+    if unfused is not None:
+        line["unfused_chain"] = unfused
     print(json.dumps(line), flush=True)
     return 0
 
