@@ -744,6 +744,8 @@ constexpr int kPersistTM = 32;
 constexpr int kPersistDepth = 6;  // iterations between the post and the pre step of a tile
 constexpr uint32_t kPersistSpinLimit = 1u << 18;
 constexpr int kPersistMaxS = 64;  // splits per row the reduce threads can gather
+constexpr int kCoeffsAhead = 3;   // coefficients-only pass: tiles of x held in registers ahead
+constexpr int kCoeffsWords = 25;  // coefficients-only partial words per token: 24 projections, sum of squares
 // LDS projection fragments of one (route, 32-channel step): blocks 0-3 whole
 // (64 lanes each) and the 32 lanes of block 4 whose column is < 8 (the rest
 // of block 4 is zero), in 16-byte units.
@@ -802,14 +804,21 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   constexpr bool FUSED = MODE != kModeCoeffs;
   constexpr bool MX = MODE == kModeFusedMx;
   constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
-  constexpr int NVU = FUSED ? NV : 25;
   // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
   // [2][row block][token][route][16 chunks] x 16 B (chunk c of token t at
   // position c ^ (t % 16), so that the 16 tokens a wave reads at once hit
   // distinct banks); wave partials; post coefficients; q words; gamma.
+  // The partial words are [tiles][S][TM][NV] tagged words, or
+  // [tiles][S][TM][kCoeffsWords] in the coefficients-only mode: every
+  // store instruction writes whole lines (a system-scope store that covers
+  // part of a line measured several times slower per byte).
   __shared__ __attribute__((aligned(16))) u32x4_t phi_lds[16 * kPhiFrag + 1];
-  __shared__ __attribute__((aligned(16))) u32x4_t xslot[2][2][kHalfChunks];
-  __shared__ float red[8][16][NV];  // [wave][token of its row block][projection, Gram]
+  // (the coefficients-only mode has one stage per row block instead of the
+  // slot pairs: [1][row block][row][16 chunks], chunk c of token t at c ^ t)
+  __shared__ __attribute__((aligned(16))) u32x4_t xslot[FUSED ? 2 : 1][2][kHalfChunks];
+  // [wave][token of its row block][projection, Gram] | coefficients only:
+  // [buffer][wave][token, word]
+  __shared__ float red[FUSED ? 8 : 2][FUSED ? 16 : 8][FUSED ? NV : 16 * kCoeffsWords];
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
   __shared__ float gam[FUSED ? kCC : 1];
@@ -831,14 +840,15 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     // split order, in one pass, reloading words whose tag is stale.  Waves
     // 0-1 finalise the previous unit meanwhile, four tokens per wave (one per
     // 16-lane row); the sums are double-buffered in LDS.  (The
-    // coefficients-only mode takes whole tiles per round instead.)
+    // coefficients-only mode takes whole tiles per round instead, its sums
+    // as [TM][NV] in LDS.)
     const int j = (int)blockIdx.x - nstream;
     const int nred = (int)gridDim.x - nstream;
     const int nunits = tiles * (TM / 8);
-    const int64_t pstride = (int64_t)TM * NV;  // one split's partial tile
+    const int64_t pstride = (int64_t)TM * (FUSED ? NV : kCoeffsWords);  // one split's partial tile
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int v = tid - 128;  // gather thread's word
-    bool act = wv >= 2 && v < 8 * NV && (v % NV) < NVU;
+    bool act = wv >= 2 && v < 8 * NV;
     uint64_t wa[16], wb[16], wc[16], wd[16];
     const uint64_t* pb = a.partials;
     float sum = 0.0f;
@@ -877,8 +887,9 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // launch, so whole tiles per round (all threads gather, then every
       // wave finalises four tokens) give more tokens per round.
       for (int t = j; t < tiles; t += nred) {
-        for (int w = tid; w < TM * NV; w += kPersistThreads) {
-          act = (w % NV) < NVU;
+        for (int w = tid; w < TM * kCoeffsWords; w += kPersistThreads) {
+          const int wo = (w / kCoeffsWords) * NV + w % kCoeffsWords;  // (token, word) in the [TM][NV] sums
+          act = true;
           pb = a.partials + (int64_t)t * S * pstride + w;
           sum = 0.0f;
           load_chunk(wa, 0);
@@ -889,7 +900,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           add_chunk(wb, 16);
           add_chunk(wc, 32);
           add_chunk(wd, 48);
-          finw[w] = act ? sum : 0.0f;
+          finw[wo] = sum;
         }
         __syncthreads();  // the tile's sums
         const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
@@ -985,6 +996,146 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     // block 4 fragment of this lane: its own column if < 8, else the zero fragment
     const int b4off = n16 < 8 ? 4 * kWave + g * 8 + n16 : -1;
 
+    if constexpr (!FUSED) {
+      // Coefficients only: no post and no x' ring, so x is loaded into
+      // registers kCoeffsAhead tiles ahead, with loads the compiler counts
+      // and waits for.  A wave instruction loads 4 rows x 256 bytes (whole
+      // 128-byte lines; loading the MFMA operand layout directly reads 16
+      // rows x 64 bytes per instruction, half lines, at two thirds of the
+      // rate), and the tile goes through an LDS stage into the operand
+      // layout.  Step i: tile t_i to the stage and the loads of t_{i+A};
+      // barrier; the partial words of t_{i-1} (the four waves of the row
+      // block added from LDS buffer (i - 1) & 1) and the projection of t_i
+      // into buffer i & 1; barrier.  The loop is unrolled by A so that every
+      // register buffer has a fixed index.
+      constexpr int A = kCoeffsAhead, NW = kCoeffsWords;
+      u32x4_t xq[A][4];
+      u32x4_t* const stage = &xslot[0][rb][0];
+      // chunk q = gt + 256 k of the row block's tile: row q / 16 (token
+      // row / 4, route row % 4), 16-byte chunk q % 16 of the split's 256 bytes
+      // (issued unconditionally, so that the compiler's wait counts never
+      // merge paths with and without the loads: past the last tile every
+      // lane reads the first 16 bytes of x, whose value is not used)
+      auto load_x = [&](u32x4_t* dst, int i) __attribute__((always_inline)) {
+        const bool ok = i < niter;
+        const int64_t tok0 = (int64_t)(r + L * i) * TM + rb * 16;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int q = gt + 256 * k, row = q >> 4;
+          const int64_t tok = tok0 + (row >> 2);
+          const int64_t off = (tok < a.T ? tok : 0) * (int64_t)(4 * C) + (int64_t)(row & 3) * C + c0 + 8 * (q & 15);
+          dst[k] = ld16_stream(a.x + (ok ? off : 0));
+        }
+      };
+      auto stage_write = [&](const u32x4_t* src) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int q = gt + 256 * k, row = q >> 4;
+          stage[row * 16 + ((q & 15) ^ (row >> 2))] = src[k];
+        }
+      };
+      // partial words of tile t_i: 16 tokens x NW words of this row block
+      // ([tiles][S][TM][NW] in this mode: dense, whole lines per store)
+      auto fold = [&](int i) __attribute__((always_inline)) {
+        uint64_t* part = a.partials + ((int64_t)(r + L * i) * S + split) * (TM * NW) + rb * 16 * NW;
+        const float* rr = &red[i & 1][rb * 4][0];
+        float sum[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int idx = min(gt + 256 * k, 16 * NW - 1);
+          sum[k] = ((rr[idx] + rr[16 * NW + idx]) + rr[2 * 16 * NW + idx]) + rr[3 * 16 * NW + idx];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int idx = gt + 256 * k;
+          if (idx < 16 * NW) tagged_store(part + idx, sum[k], tag);
+        }
+      };
+      // projection and sum of squares of tile t_i from the stage (rows past
+      // T read token 0 and are zeroed) -> LDS buffer i & 1
+      auto project = [&](int i) __attribute__((always_inline)) {
+        const bool live = (int64_t)(r + L * i) * TM + m < a.T;
+        u32x4_t xa[4];
+#pragma unroll
+        for (int jr = 0; jr < 4; ++jr) {
+          const u32x4_t v = stage[(n16 * 4 + jr) * 16 + ((4 * ks + g) ^ n16)];
+          xa[jr] = live ? v : u32x4_t{0, 0, 0, 0};
+        }
+        f32x4_t acc0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+#pragma unroll
+        for (int jr = 0; jr < 4; ++jr) {
+          const u32x4_t* bp = phi_lds + (jr * 4 + ks) * kPhiFrag;
+          u32x4_t bf[kPackBlocks];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) bf[b] = bp[b * kWave + lane];
+          bf[4] = b4off >= 0 ? bp[b4off] : phi_lds[16 * kPhiFrag];
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[jr]);
+#pragma unroll
+          for (int b = 0; b < kPackBlocks; ++b) {
+            if (b < 3) {
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc0, 0, 0, 0);
+            } else {
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bf[b]), acc1, 0, 0, 0);
+            }
+          }
+        }
+        // sum of squares: the diagonal of x_j x_j^T, token n in lane
+        // n + 16 (n / 4), element n % 4
+        f32x4_t gm[4];
+#pragma unroll
+        for (int jr = 0; jr < 4; ++jr)
+          gm[jr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[jr]),
+                                                          __builtin_bit_cast(bf16x8_t, xa[jr]),
+                                                          f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        float gd[4];
+#pragma unroll
+        for (int jr = 0; jr < 4; ++jr) {
+          float vv = gm[jr][0];
+          vv = (n16 & 3) == 1 ? gm[jr][1] : vv;
+          vv = (n16 & 3) == 2 ? gm[jr][2] : vv;
+          gd[jr] = (n16 & 3) == 3 ? gm[jr][3] : vv;
+        }
+        float* rw = &red[i & 1][wave][0];  // [16 tokens][NW]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v1 = acc1[e];
+          const float mid = __shfl_xor(v1, 8);
+          rw[(4 * g + e) * NW + n16] = acc0[e];
+          if (n16 < 8) rw[(4 * g + e) * NW + 16 + n16] = v1 + mid;
+        }
+        if ((n16 >> 2) == g) rw[n16 * NW + 24] = ((gd[0] + gd[1]) + gd[2]) + gd[3];
+      };
+      // step i >= 1 (step 0 has no partial words to store)
+      auto step = [&](int i, u32x4_t* xb) __attribute__((always_inline)) {
+        stage_write(xb);
+        load_x(xb, i + A);
+        MHC_GROUP_BARRIER("coefficients: stage written");
+        fold(i - 1);
+        project(i);
+        MHC_GROUP_BARRIER("coefficients: stage read");
+      };
+      if (niter > 0) {
+        __syncthreads();  // the projection slice is in LDS
+#pragma unroll
+        for (int k = 0; k < A; ++k) load_x(xq[k], k);
+        stage_write(xq[0]);
+        load_x(xq[0], A);
+        MHC_GROUP_BARRIER("coefficients: first stage written");
+        project(0);
+        MHC_GROUP_BARRIER("coefficients: first stage read");
+        // tile t_i is in xq[i % A]
+        int i = 1;
+        for (; i + A <= niter; i += A) {
+#pragma unroll
+          for (int k = 0; k < A; ++k) step(i + k, xq[(k + 1) % A]);
+        }
+#pragma unroll
+        for (int k = 0; k < A; ++k)
+          if (i + k < niter) step(i + k, xq[(k + 1) % A]);
+        fold(niter - 1);
+      }
+    } else {
+
     // x slice of this row block of tile t_i -> slot i%2: wave-instruction k
     // covers the four routes of token ks + 4k of the row block (1 KB of LDS,
     // 4 x 256 contiguous bytes of x).
@@ -1056,8 +1207,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       if constexpr (doPrev) {
         uint64_t* part = a.partials + ((int64_t)(t - L) * S + split) * (TM * NV) + rb * 16 * NV;
         // all twelve LDS reads first, then the stores (words past the row
-        // block, and in the coefficients-only mode the unused Gram slots,
-        // are not stored: nothing reads them)
+        // block are not stored)
         float sum[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -1068,7 +1218,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           const int idx = gt + k * 256;
-          if (idx < 16 * NV && idx % NV < NVU) tagged_store(part + idx, sum[k], tag);
+          if (idx < 16 * NV) tagged_store(part + idx, sum[k], tag);
         }
       }
       const u32x4_t cy = ny;
@@ -1375,6 +1525,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
   }
 
