@@ -2,6 +2,7 @@
 """Benchmark of the mHC fused post->pre pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py --workload decode --graph   # the step replayed from HIP graphs
     python bench.py --copy-probe           # copy kernel of known size (counter calibration)
     python bench.py --pmc-summary FILE...  # per-kernel means of rocprofv3 counter output
 
@@ -244,6 +245,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "mxfp8", "long"])
     ap.add_argument("--settle-ms", type=float, default=50.0,
                     help="untimed steps for this long before the warm-up steps (clock ramp)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the repack and the fused call in HIP graphs and time their replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="also time the unfused chain post -> coeffs -> pre on the same inputs "
@@ -278,7 +281,7 @@ def main() -> int:
     params = Params()
     sched = mhc.schedule(T, C)
     print(f"[bench] workload={w.name} T={T} C={C} mxfp8={mx} steps={args.steps} warmup={args.warmup} "
-          f"schedule={sched}", file=sys.stderr, flush=True)
+          f"schedule={sched} graph={args.graph}", file=sys.stderr, flush=True)
     inp = make_inputs(T, C, seed=0, rows=w.rows, device=dev)
     # incoming coefficients of this layer: computed by the library itself
     coeffs_in = mhc.coeffs(inp["x"], inp["phi"], inp["bias"], params)
@@ -292,18 +295,32 @@ def main() -> int:
     if mx:
         outs["h_fp8"] = torch.empty((T, C), dtype=torch.uint8, device=dev)
         outs["h_scale"] = torch.empty((T, C // 32), dtype=torch.uint8, device=dev)
-    L = mhc.lib()
     stream = torch.cuda.current_stream(dev)
 
+    # the two calls of a step, checked and marshalled once (mhc.Prepared)
+    pack = mhc.prepare_pack_phi(inp["phi_next"], packed)
+    fused = mhc.prepare_post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, packed, inp["bias_next"],
+                                                 inp["gamma_next"], params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
+    pack()
+    fused()
+    torch.cuda.synchronize()
+    if args.graph:
+        # each call captured once in a HIP graph (the library allocates and
+        # synchronises nothing on its call path), then replayed
+        graphs = (torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph())
+        with torch.cuda.graph(graphs[0]):
+            mhc.prepare_pack_phi(inp["phi_next"], packed)()
+        with torch.cuda.graph(graphs[1]):
+            mhc.post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, packed, inp["bias_next"], inp["gamma_next"],
+                                         params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
+        torch.cuda.synchronize()
+        pack, fused = graphs[0].replay, graphs[1].replay
+
     def step(ev=None):
-        rc = L.mhc_pack_phi(mhc.binding._ptr(inp["phi_next"]), C, mhc.binding._ptr(packed),
-                            mhc.binding._stream(dev))
-        if rc:
-            raise mhc.MhcError(rc, "mhc_pack_phi")
+        pack()
         if ev is not None:
             ev[0].record(stream)
-        mhc.post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, packed, inp["bias_next"], inp["gamma_next"],
-                                     params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
+        fused()
         if ev is not None:
             ev[1].record(stream)
 
@@ -384,7 +401,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name}: fused post->pre (projection repack + fused pass per step)",
                    "tokens": T, "hidden": C, "routes": 4, "mxfp8": mx, "bf16_h": with_h, "rows": rows,
-                   "schedule": sched,
+                   "schedule": sched, "hip_graph": bool(args.graph),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(args.workload, sched),

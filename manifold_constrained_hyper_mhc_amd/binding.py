@@ -234,16 +234,22 @@ def _flags(mxfp8: bool, recompute_x: bool) -> int:
 
 
 def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
+    # outputs the caller did not pass are allocated here (only those)
     o = dict(outs or {})
-    o.setdefault("x_out", torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev))
-    o.setdefault("coeffs_next", torch.empty((T, 24), dtype=torch.float32, device=dev))
+
+    def need(key, shape, dtype):
+        if o.get(key) is None:
+            o[key] = torch.empty(shape, dtype=dtype, device=dev)
+
+    need("x_out", (T, 4, C), torch.bfloat16)
+    need("coeffs_next", (T, 24), torch.float32)
     if want_h:
-        o.setdefault("h", torch.empty((T, C), dtype=torch.bfloat16, device=dev))
+        need("h", (T, C), torch.bfloat16)
     else:
         o["h"] = None
     if mxfp8:
-        o.setdefault("h_fp8", torch.empty((T, C), dtype=torch.uint8, device=dev))
-        o.setdefault("h_scale", torch.empty((T, C // 32), dtype=torch.uint8, device=dev))
+        need("h_fp8", (T, C), torch.uint8)
+        need("h_scale", (T, C // 32), torch.uint8)
     else:
         o["h_fp8"] = o["h_scale"] = None
     _need(o["x_out"], "x_out", torch.bfloat16, (T, 4, C), dev)
@@ -278,9 +284,35 @@ def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Para
     return o
 
 
-def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(), *,
-                             mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
-                            recompute_x: bool = False) -> dict:
+class Prepared:
+    """One library call whose arguments were checked and marshalled once:
+    calling it enqueues the same work again, on the stream that was current
+    when it was prepared (for a serving loop that would otherwise pay the
+    per-call checks).  The tensors it was prepared with must stay alive and
+    keep their storage; ``outputs`` holds the output tensors."""
+
+    def __init__(self, fn, args, what, keep, outputs=None):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+        self.outputs = outputs
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            raise MhcError(status, self._what)
+        return self.outputs
+
+
+def prepare_pack_phi(phi: torch.Tensor, out: torch.Tensor) -> Prepared:
+    L = lib()
+    C = phi.shape[0] // 4
+    _need(phi, "phi", torch.float32, (4 * C, 24))
+    _need(out, "phi_packed", torch.uint8, (int(L.mhc_phi_packed_bytes(C)),), phi.device)
+    return Prepared(L.mhc_pack_phi, (_ptr(phi), C, _ptr(out), _stream(phi.device)), "mhc_pack_phi", (phi, out), out)
+
+
+def prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next,
+                                     params: Params = Params(), *, mxfp8: bool = False, want_h: bool = True,
+                                     ws=None, outs=None, recompute_x: bool = False) -> Prepared:
     L = lib()
     T, C = _dims(x)
     dev = x.device
@@ -293,9 +325,16 @@ def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_n
     o = _fused_outputs(T, C, dev, mxfp8, want_h, outs)
     ws = workspace(T, C, dev) if ws is None else ws
     p = MhcParams.of(params)
-    _check(L.mhc_post_pre_fused_prepacked(_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next_packed), _ptr(bias_next),
-                                          _ptr(gamma_next), T, C, ctypes.byref(p), _flags(mxfp8, recompute_x),
-                                          _ptr(o["x_out"]), _ptr(o["coeffs_next"]), _ptr(o["h"]), _ptr(o["h_fp8"]),
-                                          _ptr(o["h_scale"]), _ptr(ws), ws.numel(), _stream(dev)),
-           "mhc_post_pre_fused_prepacked")
-    return o
+    args = (_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next_packed), _ptr(bias_next), _ptr(gamma_next), T, C,
+            ctypes.byref(p), _flags(mxfp8, recompute_x), _ptr(o["x_out"]), _ptr(o["coeffs_next"]), _ptr(o["h"]),
+            _ptr(o["h_fp8"]), _ptr(o["h_scale"]), _ptr(ws), ws.numel(), _stream(dev))
+    keep = (x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, ws, p, o)
+    return Prepared(L.mhc_post_pre_fused_prepacked, args, "mhc_post_pre_fused_prepacked", keep, o)
+
+
+def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(), *,
+                             mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
+                             recompute_x: bool = False) -> dict:
+    return prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params,
+                                            mxfp8=mxfp8, want_h=want_h, ws=ws, outs=outs,
+                                            recompute_x=recompute_x)()

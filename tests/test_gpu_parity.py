@@ -440,3 +440,24 @@ def test_fused_matches_gpu_composition_on_every_token(schedule):
     rms = h2.pow(2).mean(dim=1, keepdim=True).sqrt()
     herr = ((hf - h2).abs() / torch.maximum(h2.abs(), rms)).max().item()
     assert herr <= 1e-2, herr
+
+
+def test_prepared_call_is_bitwise_identical():
+    # a call checked and marshalled once (mhc.Prepared) launches the same work
+    # as the regular call, every time it is called
+    inp = small_inputs(45, 3072, seed=9)
+    d = to_dev(inp)
+    pk = torch.empty_like(mhc.pack_phi(d["phi_next"]))
+    prep_pack = mhc.prepare_pack_phi(d["phi_next"], pk)
+    prep = mhc.prepare_post_pre_fused_prepacked(d["x"], d["y"], d["coeffs"], pk, d["bias_next"], d["gamma_next"],
+                                                mxfp8=True)
+    ref = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
+    for _ in range(3):
+        for v in prep.outputs.values():
+            if v is not None:
+                v.zero_()
+        prep_pack()
+        out = prep()
+        torch.cuda.synchronize()
+        for k in ("x_out", "coeffs_next", "h", "h_fp8", "h_scale"):
+            assert torch.equal(out[k], ref[k]), k
