@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float v1 = acc[r][1][e];
-        const float mid = __shfl_xor(v1, 8);
+        const float mid = MHC_DPP(v1, kDppRowRor8);  // lane ^ 8 (rotation by 8 of a 16-lane row)
         const int row = r * 16 + 4 * g + e;
         red[(wave * TM + row) * NV + n16] = acc[r][0][e];
         if (n16 < 8) red[(wave * TM + row) * NV + 16 + n16] = v1 + mid;
@@ -1099,7 +1099,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v1 = acc1[e];
-          const float mid = __shfl_xor(v1, 8);
+          const float mid = MHC_DPP(v1, kDppRowRor8);  // lane ^ 8 (rotation by 8 of a 16-lane row)
           rw[(4 * g + e) * NW + n16] = acc0[e];
           if (n16 < 8) rw[(4 * g + e) * NW + 16 + n16] = v1 + mid;
         }
@@ -1380,7 +1380,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float v1 = acc1[e];
-        const float mid = __shfl_xor(v1, 8);
+        const float mid = MHC_DPP(v1, kDppRowRor8);  // lane ^ 8 (rotation by 8 of a 16-lane row)
         red[wave][4 * g + e][n16] = acc0[e];
         if (n16 < 8) red[wave][4 * g + e][16 + n16] = v1 + mid;
       }
