@@ -724,6 +724,10 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 //     The two row blocks run half an iteration apart: while one runs P,
 //     the other runs M, so each SIMD has one wave on its vector ALU and one
 //     on its matrix core between the two barriers of an iteration.
+//     The coefficients-only mode has neither post nor x' ring: its stream
+//     workgroups keep x in registers three tiles ahead (whole-line loads,
+//     turned into the operand layout through an LDS stage) and run both
+//     row blocks in step.
 //   * 32 "reduce" workgroups gather the S partial rows of 8 tokens at a
 //     time (a whole tile in the coefficients-only mode), finalise their
 //     coefficients (four tokens per wave, one per 16-lane row) and publish
