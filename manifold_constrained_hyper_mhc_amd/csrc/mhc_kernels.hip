@@ -360,6 +360,9 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   constexpr bool MX = MODE == kModeFusedMx;
   constexpr int W = 4, NV = kPartVals, NP = TM / 16, RB = TM / 16, NQ = TM / 4;
   constexpr int NVU = FUSED ? NV : 25;
+  // partial words per token in the workspace: [tiles][S][TM][PW], dense, so
+  // that every store instruction writes whole lines
+  constexpr int PW = NVU;
   // LDS: x' (TM*4 rows x 256 B), later reused for the wave partials and the
   // reduce-scatter run sums
   constexpr int XS_BYTES = TM * 4 * 256;
@@ -425,8 +428,8 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   const bool active = doR && pidx < npair && v < NVU;
   const int sp0 = rr * L, n = active ? (S - sp0 < L ? (S - sp0 > 0 ? S - sp0 : 0) : L) : 0;
   const uint64_t* gbase =
-      a.partials + ((int64_t)(doR ? tR : 0) * S * TM + (int64_t)sp0 * TM + split + kk * S) * NV + v;
-  const int64_t gstride = (int64_t)TM * NV;
+      a.partials + ((int64_t)(doR ? tR : 0) * S * TM + (int64_t)sp0 * TM + split + kk * S) * PW + v;
+  const int64_t gstride = (int64_t)TM * PW;
   uint64_t w[RUN];
 #pragma unroll
   for (int q = 0; q < RUN; ++q) w[q] = q < n ? tagged_load(gbase + q * gstride) : 0;
@@ -532,10 +535,10 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
     }
     __syncthreads();
 
-    uint64_t* part = a.partials + ((int64_t)tA * S + split) * (TM * NV);
+    uint64_t* part = a.partials + ((int64_t)tA * S + split) * (TM * PW);
     for (int idx = tid; idx < TM * NV; idx += 256) {
       const int vv = idx % NV;
-      if (vv >= NVU) continue;
+      if (vv >= PW) continue;
       float sum = ((red[idx] + red[TM * NV + idx]) + red[2 * TM * NV + idx]) + red[3 * TM * NV + idx];
       if constexpr (!FUSED) {
         if (vv == 24) {  // coeffs: only the trace of the Gram matrix
@@ -547,7 +550,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
                    red[ww * TM * NV + b + 27];
         }
       }
-      tagged_store(part + idx, sum, tag);
+      tagged_store(part + (idx / NV) * PW + vv, sum, tag);
     }
     __syncthreads();  // LDS free for R
     if (FUSED && tid == 0) tagged_store(a.owner + (int64_t)tA * S + split, __uint_as_float(xcd_id()), tag);
