@@ -74,7 +74,7 @@ struct SplitArgs {
   uint16_t* h;
   uint8_t* h_fp8;
   uint8_t* h_scale;
-  uint64_t* partials;  // [tiles][S][M][34] tagged words ([tiles][S][M][25]: persistent coefficients-only pass)
+  uint64_t* partials;  // [tiles][S][M][34] tagged words ([tiles][S][M][25]: coefficients-only passes)
   uint32_t* epoch;     // launch epoch (fixed offset)
   uint32_t* tiles_done;  // tiles completed in this launch (fixed offset)
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
