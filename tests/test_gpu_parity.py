@@ -461,3 +461,25 @@ def test_prepared_call_is_bitwise_identical():
         torch.cuda.synchronize()
         for k in ("x_out", "coeffs_next", "h", "h_fp8", "h_scale"):
             assert torch.equal(out[k], ref[k]), k
+
+
+def test_workspace_reuse_across_modes(schedule):
+    # one workspace for fused and coefficients-only calls in turn: the two
+    # modes lay their partial words out differently ([TM][34] and [TM][25]),
+    # so every call meets words of the other layout from an earlier launch;
+    # the launch tags must keep them out of every sum
+    T, C = 300, 7168
+    inp = small_inputs(T, C, seed=13)
+    d = to_dev(inp)
+    ws = mhc.workspace(T, C, DEV, fresh=True)
+    f1 = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], ws=ws)
+    c1 = mhc.coeffs(d["x"], d["phi"], d["bias"], ws=ws)
+    f2 = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], ws=ws)
+    c2 = mhc.coeffs(d["x"], d["phi"], d["bias"], ws=ws)
+    torch.cuda.synchronize()
+    for k in ("x_out", "coeffs_next", "h"):
+        assert torch.equal(f1[k], f2[k]), k
+    assert torch.equal(c1, c2)
+    ref = O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw())
+    assert_coeffs_close(f64(c2), ref)
+    assert mhc.workspace_error(ws) == 0
