@@ -110,8 +110,10 @@ int mhc_last_hip_error(void);
  * across several workgroups and need a caller-owned device workspace of
  * mhc_workspace_bytes(T, C, flags) bytes (256-byte aligned).  Before its
  * first use a workspace must be cleared with mhc_workspace_init (a kernel on
- * `stream`, no memset node); every call leaves it cleared again, so it can
- * be reused by any later call with any T and C whose size it covers.  One
+ * `stream`, no memset node).  Every call leaves it ready for the next one:
+ * its counters are reset, and the words it wrote carry that call's launch
+ * tag, which no later call accepts.  So it can be reused by any later call
+ * with any T and C whose size it covers.  One
  * workspace must not be used by two calls that may run concurrently.
  * Its first 4 bytes are an error word (uint32): the kernels' waits on other
  * workgroups are bounded, and one that expires sets it nonzero, after which
