@@ -4,9 +4,9 @@
 // [P3] "What changed" item 3 — see include/mhc.h for the page titles):
 //   post      x'_j = sum_i res_ji x_i + post_j y                     (k_post)
 //   coeffs    RMS-scaled 24-wide projection of the flattened row,
-//             sigmoid pre/post, Sinkhorn res                          (k_split, coeffs mode)
+//             sigmoid pre/post, Sinkhorn res                          (k_persist / k_split, coeffs mode)
 //   pre       h = RMSNorm(sum_i pre_i x_i) * gamma                    (k_pre)
-//   fused     post -> coeffs' -> pre' with x' kept on chip            (k_split, fused modes)
+//   fused     post -> coeffs' -> pre' with x' kept on chip            (k_persist / k_split, fused modes)
 #include "mhc_device.h"
 
 namespace mhc {
@@ -29,39 +29,47 @@ namespace mhc {
 // ===========================================================================
 __device__ __forceinline__ float bf16_round_f(float v) { return bf16_lo(pack_bf16x2(v, 0.0f)); }
 
+// One thread per (32-row k-step, fragment lane): it reads its 8 rows of the
+// two columns it serves (n16 for blocks 0-2, 16 + n16 % 8 for blocks 3-4)
+// once and writes its lane of all five blocks.
 __global__ __launch_bounds__(256) void k_pack_phi(const float* __restrict__ phi, int C,
                                                   u32x4_t* __restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)(4 * C / 32) * kPackBlocks * kWave;
+  const int64_t total = (int64_t)(4 * C / 32) * kWave;
   if (idx >= total) return;
   const int lane = (int)(idx & 63);
-  const int64_t qb = idx >> 6;
-  const int blk = (int)(qb % kPackBlocks);
-  const int64_t q = qb / kPackBlocks;
+  const int64_t q = idx >> 6;
   const int n16 = lane & 15, g = lane >> 4;
-  int col, term;
-  if (blk < 3) {
-    col = n16;
-    term = blk;
-  } else if (blk == 3) {
-    col = 16 + (n16 & 7);
-    term = n16 < 8 ? 0 : 1;
-  } else {
-    col = n16 < 8 ? 16 + n16 : -1;
-    term = 2;
-  }
-  float v[8];
   const int64_t k0 = q * 32 + g * 8;
+  float t[5][8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float p = col >= 0 ? phi[(k0 + e) * kCoeffs + col] : 0.0f;
-    const float hi = bf16_round_f(p);
-    const float r1 = p - hi;
-    const float mid = bf16_round_f(r1);
-    const float lo = bf16_round_f(r1 - mid);
-    v[e] = term == 0 ? hi : (term == 1 ? mid : lo);
+    const float* row = phi + (k0 + e) * kCoeffs;
+    float hi, mid, lo;
+    // blocks 0-2: hi, mid, lo of logit n16
+    {
+      const float p = row[n16];
+      hi = bf16_round_f(p);
+      const float r1 = p - hi;
+      mid = bf16_round_f(r1);
+      lo = bf16_round_f(r1 - mid);
+      t[0][e] = hi;
+      t[1][e] = mid;
+      t[2][e] = lo;
+    }
+    // blocks 3-4: [hi | mid] and [lo | 0] of logit 16 + n16 % 8
+    {
+      const float p = row[16 + (n16 & 7)];
+      hi = bf16_round_f(p);
+      const float r1 = p - hi;
+      mid = bf16_round_f(r1);
+      lo = bf16_round_f(r1 - mid);
+      t[3][e] = n16 < 8 ? hi : mid;
+      t[4][e] = n16 < 8 ? lo : 0.0f;
+    }
   }
-  out[idx] = pack8(v);
+#pragma unroll
+  for (int b = 0; b < kPackBlocks; ++b) out[(q * kPackBlocks + b) * kWave + lane] = pack8(t[b]);
 }
 
 // ===========================================================================
@@ -1679,7 +1687,7 @@ __global__ void k_fill_zero(uint32_t* p, int64_t n) {
 // Launchers
 // ===========================================================================
 hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s) {
-  const int64_t total = (int64_t)(4 * C / 32) * kPackBlocks * kWave;
+  const int64_t total = (int64_t)(4 * C / 32) * kWave;
   const int64_t blocks = (total + 255) / 256;
   k_pack_phi<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(phi, C, reinterpret_cast<u32x4_t*>(out));
   return hipGetLastError();

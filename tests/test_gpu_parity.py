@@ -483,3 +483,33 @@ def test_workspace_reuse_across_modes(schedule):
     ref = O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw())
     assert_coeffs_close(f64(c2), ref)
     assert mhc.workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("C", [1024, 7168])
+def test_pack_phi_layout(C):
+    # the packed projection, bit for bit, against its layout written out in
+    # numpy: [4C/32 k-steps][5 blocks][64 lanes][8 bf16]; lane l holds rows
+    # 32q + 8(l // 16) + e of one column; blocks 0-2 = hi, mid, lo of logits
+    # 0..15, block 3 = [hi | mid] and block 4 = [lo | 0] of logits 16..23
+    inp = make_inputs(4, C, seed=17, device="cpu")
+    phi = inp["phi"]
+    hi = phi.to(torch.bfloat16)
+    r1 = phi - hi.float()
+    mid = r1.to(torch.bfloat16)
+    lo = (r1 - mid.float()).to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().astype(np.int64) & 0xFFFF  # noqa: E731
+    H, M, Lo = bits(hi), bits(mid), bits(lo)
+    K = 4 * C
+    exp = np.zeros((K // 32, 5, 64, 8), dtype=np.int64)
+    lane = np.arange(64)
+    n16, g = lane % 16, lane // 16
+    for e in range(8):
+        rows = (np.arange(K // 32)[:, None] * 32 + 8 * g[None, :] + e)  # [k-step, lane]
+        exp[:, 0, :, e] = H[rows, n16[None, :]]
+        exp[:, 1, :, e] = M[rows, n16[None, :]]
+        exp[:, 2, :, e] = Lo[rows, n16[None, :]]
+        c2 = 16 + (n16 % 8)
+        exp[:, 3, :, e] = np.where(n16[None, :] < 8, H[rows, c2[None, :]], M[rows, c2[None, :]])
+        exp[:, 4, :, e] = np.where(n16[None, :] < 8, Lo[rows, c2[None, :]], 0)
+    got = mhc.pack_phi(phi.to(DEV)).cpu().view(torch.int16).numpy().astype(np.int64) & 0xFFFF
+    assert np.array_equal(got.reshape(exp.shape), exp)
