@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
     python bench.py --workload decode --graph   # the step replayed from HIP graphs
+    python bench.py --workload decode --cold-phi 64   # 64 prepacked projections in turn
     python bench.py --copy-probe           # copy kernel of known size (counter calibration)
     python bench.py --pmc-summary FILE...  # per-kernel means of rocprofv3 counter output
 
@@ -129,8 +130,21 @@ def algorithmic_bytes(T: int, C: int, mxfp8: bool, with_h: bool = True) -> int:
     return T * per_tok + 384 * C + 4 * C + 96
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp_host: dict, coeffs_host, params, budget_s: float = 10.0, chunk: int = 128) -> dict:
-    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the workload: with
+    every thread its numpy pools start with, then again limited to one thread
+    (a third of the budget)."""
     import numpy as np
     import threadpoolctl
 
@@ -141,24 +155,31 @@ def cpu_baseline(inp_host: dict, coeffs_host, params, budget_s: float = 10.0, ch
     cf = f64(coeffs_host)
     phi, b, g = f64(inp_host["phi_next"]), f64(inp_host["bias_next"]), f64(inp_host["gamma_next"])
     n = x.shape[0]
-    done = 0
-    t0 = time.perf_counter()
-    k = 0
-    while time.perf_counter() - t0 < budget_s:
-        s = (k * chunk) % n
-        rows = slice(s, min(s + chunk, n))
-        O.post_pre_fused(x[rows], y[rows], cf[rows], phi, b, g, hc_norm_eps=params.hc_norm_eps,
-                         rmsnorm_eps=params.rmsnorm_eps, hc_post_scale=params.hc_post_scale,
-                         sinkhorn_eps=params.sinkhorn_eps, sinkhorn_iters=params.sinkhorn_iters)
-        done += rows.stop - rows.start
-        k += 1
-    dt = time.perf_counter() - t0
+
+    def run(budget):
+        done = 0
+        t0 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t0 < budget:
+            s = (k * chunk) % n
+            rows = slice(s, min(s + chunk, n))
+            O.post_pre_fused(x[rows], y[rows], cf[rows], phi, b, g, hc_norm_eps=params.hc_norm_eps,
+                             rmsnorm_eps=params.rmsnorm_eps, hc_post_scale=params.hc_post_scale,
+                             sinkhorn_eps=params.sinkhorn_eps, sinkhorn_iters=params.sinkhorn_iters)
+            done += rows.stop - rows.start
+            k += 1
+        return done, time.perf_counter() - t0
+
+    done, dt = run(budget_s)
     threads = 1
     for pool in threadpoolctl.threadpool_info():
         threads = max(threads, int(pool.get("num_threads", 1)))
+    with threadpoolctl.threadpool_limits(limits=1):
+        done1, dt1 = run(budget_s / 3)
     return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} tokens of the same workload in chunks of {chunk} ({dt:.1f} s), "
-                      f"fp64 numpy oracle fused post->pre"}
+            "value_1_thread": done1 / dt1, "cpu_model": cpu_model(),
+            "sample": f"{done} tokens of the same workload in chunks of {chunk} ({dt:.1f} s; "
+                      f"one thread: {done1} tokens, {dt1:.1f} s), fp64 numpy oracle fused post->pre"}
 
 
 def time_unfused(mhc, inp, coeffs_in, packed, params, outs, stream, args, fused_bytes, fused_ms):
@@ -245,6 +266,9 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "mxfp8", "long"])
     ap.add_argument("--settle-ms", type=float, default=50.0,
                     help="untimed steps for this long before the warm-up steps (clock ramp)")
+    ap.add_argument("--cold-phi", type=int, default=0, metavar="N",
+                    help="rotate N prepacked next-layer projections (no repack in the step), so that the "
+                         "projection is read cold")
     ap.add_argument("--graph", action="store_true",
                     help="capture the repack and the fused call in HIP graphs and time their replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -258,6 +282,9 @@ def main() -> int:
         return pmc_summary(args.pmc_summary)
     if args.copy_probe:
         return copy_probe()
+    if args.cold_phi and args.graph:
+        print(json.dumps({"error": "--cold-phi and --graph do not combine"}))
+        return 2
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path is not built "
                                    "(every token is independent: see DESIGN.md for how it would shard)",
@@ -315,6 +342,30 @@ def main() -> int:
                                          params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
         torch.cuda.synchronize()
         pack, fused = graphs[0].replay, graphs[1].replay
+
+    if args.cold_phi:
+        # next-layer projections that do not stay in the caches: cold_phi
+        # prepacked sets (4.6 MB each at C = 7168), one per step in turn, and
+        # no repack in the step
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        cold = []
+        for _ in range(args.cold_phi):
+            ph = torch.randn((4 * C, 24), generator=gen, device=dev) * 0.02
+            pk = mhc.pack_phi(ph)
+            cold.append(mhc.prepare_post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, pk, inp["bias_next"],
+                                                             inp["gamma_next"], params, mxfp8=mx, want_h=with_h,
+                                                             ws=ws, outs=outs))
+            del ph
+        torch.cuda.synchronize()
+        turn = [0]
+
+        def pack():
+            pass
+
+        def fused():
+            cold[turn[0] % len(cold)]()
+            turn[0] += 1
 
     def step(ev=None):
         pack()
@@ -399,7 +450,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: fused post->pre (projection repack + fused pass per step)",
+        "config": {"workload": f"{w.name}: fused post->pre (" + (
+                       f"fused pass per step, one of {args.cold_phi} prepacked projections in turn)" if args.cold_phi
+                       else "projection repack + fused pass per step)"),
                    "tokens": T, "hidden": C, "routes": 4, "mxfp8": mx, "bf16_h": with_h, "rows": rows,
                    "schedule": sched, "hip_graph": bool(args.graph),
                    "parallelism": "single GPU"},
