@@ -258,6 +258,41 @@ def copy_reference(inp, outs, stream, args, fused_gbs):
             "fused_gbs_over_copy_gbs": fused_gbs / gbs}
 
 
+def time_pre_broadcast(mhc, inp, packed, params, stream, args):
+    """The first-layer pre (mhc_pre_broadcast_prepacked) on x0 = route 0 of x,
+    [T, C]: coefficients and pre of x0 standing for all 4 routes.  HIP events
+    around each call; algorithmic bytes 6C + 112 per token (x0 read by both
+    kernels, coefficients written and read back, h written) + the
+    projection, bias and gamma once."""
+    import torch
+
+    x0 = inp["x"][:, 0, :].contiguous()
+    T, C = x0.shape
+    cf = torch.empty((T, 24), dtype=torch.float32, device=x0.device)
+    h = torch.empty((T, C), dtype=torch.bfloat16, device=x0.device)
+    ws = mhc.workspace(T, C, x0.device)
+
+    def run():
+        mhc.pre_broadcast(x0, None, inp["bias_next"], inp["gamma_next"], params, ws=ws, coeffs_out=cf, h_out=h,
+                          phi_packed=packed)
+
+    for _ in range(max(3, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+    nbytes = T * (6 * C + 112) + 388 * C + 96
+    return {"us": us, "algorithmic_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+            "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "mhc_pre_broadcast_prepacked on a [T, C] first-layer input (coefficients + pre)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +304,8 @@ def main() -> int:
     ap.add_argument("--cold-phi", type=int, default=0, metavar="N",
                     help="rotate N prepacked next-layer projections (no repack in the step), so that the "
                          "projection is read cold")
+    ap.add_argument("--pre-broadcast", action="store_true",
+                    help="also time the first-layer pre of a [T, C] input (mhc_pre_broadcast)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the repack and the fused call in HIP graphs and time their replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -422,6 +459,12 @@ def main() -> int:
               f"(post {unfused['post_us']:.1f}, coeffs {unfused['coeffs_us']:.1f}, pre {unfused['pre_us']:.1f}); "
               f"fused pass {kern_avg_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    first = None
+    if args.pre_broadcast:
+        first = time_pre_broadcast(mhc, inp, packed, params, stream, args)
+        print(f"[bench] first-layer pre (broadcast [T, C] input): {first['us']:.1f} us, {first['gbs']:.0f} GB/s "
+              f"algorithmic ({first['frac_of_peak']:.3f} of peak)", file=sys.stderr, flush=True)
+
     copy_ref = copy_reference(inp, outs, stream, args, achieved)
     print(f"[bench] plain copy of x and y: {copy_ref['us']:.1f} us, {copy_ref['gbs']:.0f} GB/s "
           f"({copy_ref['frac_of_peak']:.3f} of peak); the fused pass runs at "
@@ -463,6 +506,8 @@ def main() -> int:
         "cpu_baseline": cpu,
     }
     line["copy_reference"] = copy_ref
+    if first is not None:
+        line["pre_broadcast"] = first
     if unfused is not None:
         line["unfused_chain"] = unfused
     print(json.dumps(line), flush=True)

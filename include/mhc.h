@@ -169,6 +169,25 @@ int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t 
             const mhc_params* p, uint16_t* h, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Pre of a broadcast input ([P2] review, SM12x comment: the first layer's
+ * pre takes a (T, H) input that stands for every route, which the
+ * route-flattened GEMM path cannot take as it is).  x0 [T][C] bf16 is the
+ * stream of all 4 routes, x[t][i][c] = x0[t][c]; the call computes
+ * mhc_coeffs and then mhc_pre of that stream, reading x0 (2C bytes per
+ * token) instead of a [T][4][C] copy.  Writes coeffs [T][24] (pre, post,
+ * res of this layer) and h [T][C] bf16.  Uses the workspace (see above);
+ * the same bounds, alignment and aliasing rules as mhc_coeffs and mhc_pre.
+ * Results are bitwise those of mhc_coeffs and mhc_pre on the explicit
+ * [T][4][C] copy.
+ * ------------------------------------------------------------------------- */
+int mhc_pre_broadcast(const uint16_t* x0, int64_t T, int64_t C, const float* phi, const float* bias,
+                      const float* gamma, const mhc_params* p, float* coeffs, uint16_t* h, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int mhc_pre_broadcast_prepacked(const uint16_t* x0, int64_t T, int64_t C, const void* phi_packed, const float* bias,
+                                const float* gamma, const mhc_params* p, float* coeffs, uint16_t* h,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Post ([P2] "Purpose"/review: the mHC post kernel).
  *   x_out[t][j][c] = bf16_rne(sum_i res[t][j][i] * x[t][i][c] + post[t][j] * y[t][c])
  * post and res are read from coeffs[t][4..23].  The value that is rounded is

@@ -64,6 +64,10 @@ _SIG = {
     "mhc_coeffs_prepacked": ([_P, _I64, _I64, _P, _P, ctypes.POINTER(MhcParams), _P, _P, ctypes.c_size_t, _P],
                              ctypes.c_int),
     "mhc_pre": ([_P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams), _P, _P], ctypes.c_int),
+    "mhc_pre_broadcast": ([_P, _I64, _I64, _P, _P, _P, ctypes.POINTER(MhcParams), _P, _P, _P, ctypes.c_size_t, _P],
+                          ctypes.c_int),
+    "mhc_pre_broadcast_prepacked": ([_P, _I64, _I64, _P, _P, _P, ctypes.POINTER(MhcParams), _P, _P, _P,
+                                     ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_post": ([_P, _P, _P, _I64, _I64, _P, _P], ctypes.c_int),
     "mhc_post_pre_fused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams), ctypes.c_uint,
                             _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -199,6 +203,39 @@ def coeffs_prepacked(x, phi_packed, bias, params: Params = Params(), *, ws=None,
     _check(L.mhc_coeffs_prepacked(_ptr(x), T, C, _ptr(phi_packed), _ptr(bias), ctypes.byref(p), _ptr(out),
                                   _ptr(ws), ws.numel(), _stream(dev)), "mhc_coeffs_prepacked")
     return out
+
+
+def pre_broadcast(x0, phi, bias, gamma, params: Params = Params(), *, ws=None, coeffs_out=None,
+                  h_out=None, phi_packed=None):
+    """Coefficients and pre of the [T, C] stream x0 broadcast to the 4 routes
+    (mhc_pre_broadcast, or mhc_pre_broadcast_prepacked when phi_packed is
+    given and phi is None).  Returns (coeffs [T, 24], h [T, C])."""
+    L = lib()
+    if not isinstance(x0, torch.Tensor) or x0.dim() != 2:
+        raise ValueError("x0 must have shape [T, C]")
+    T, C = int(x0.shape[0]), int(x0.shape[1])
+    dev = x0.device
+    _need(x0, "x0", torch.bfloat16, (T, C))
+    if phi is not None:
+        _need(phi, "phi", torch.float32, (4 * C, 24), dev)
+    else:
+        _need(phi_packed, "phi_packed", torch.uint8, (int(L.mhc_phi_packed_bytes(C)),), dev)
+    _need(bias, "bias", torch.float32, (24,), dev)
+    _need(gamma, "gamma", torch.float32, (C,), dev)
+    cf = torch.empty((T, 24), dtype=torch.float32, device=dev) if coeffs_out is None else coeffs_out
+    h = torch.empty((T, C), dtype=torch.bfloat16, device=dev) if h_out is None else h_out
+    _need(cf, "coeffs", torch.float32, (T, 24), dev)
+    _need(h, "h", torch.bfloat16, (T, C), dev)
+    ws = workspace(T, C, dev) if ws is None else ws
+    p = MhcParams.of(params)
+    if phi is not None:
+        _check(L.mhc_pre_broadcast(_ptr(x0), T, C, _ptr(phi), _ptr(bias), _ptr(gamma), ctypes.byref(p), _ptr(cf),
+                                   _ptr(h), _ptr(ws), ws.numel(), _stream(dev)), "mhc_pre_broadcast")
+    else:
+        _check(L.mhc_pre_broadcast_prepacked(_ptr(x0), T, C, _ptr(phi_packed), _ptr(bias), _ptr(gamma),
+                                             ctypes.byref(p), _ptr(cf), _ptr(h), _ptr(ws), ws.numel(),
+                                             _stream(dev)), "mhc_pre_broadcast_prepacked")
+    return cf, h
 
 
 def pre(x, coeffs_t, gamma, params: Params = Params(), *, out=None) -> torch.Tensor:

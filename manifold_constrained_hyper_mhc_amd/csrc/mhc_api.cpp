@@ -181,6 +181,8 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
   a.T = T;
+  a.xts = 4 * C;
+  a.xrs = C;
   a.tiles = (uint32_t)plan.tiles;
   a.C = (int)C;
   a.S = plan.s;
@@ -191,14 +193,16 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   return a;
 }
 
+// bcast: x is a [T][C] stream that stands for all 4 routes (read with route
+// stride 0).
 int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const void* phi_packed,
                 const float* bias, const mhc_params* p, float* coeffs, void* ws, size_t ws_bytes,
-                void* stream) {
+                void* stream, bool bcast = false) {
   int rc = check_shape(T, C);
   if (rc) return rc;
   if ((rc = check_params(p, true))) return rc;
   if (T == 0) return MHC_OK;
-  const size_t xb = (size_t)T * 4 * C * 2, cb = (size_t)T * 24 * 4;
+  const size_t xb = (size_t)T * (bcast ? 1 : 4) * C * 2, cb = (size_t)T * 24 * 4;
   const Span phi_span = phi ? Span{phi, (size_t)4 * C * 24 * 4} : Span{phi_packed, mhc::phi_packed_bytes(C)};
   const Span in[] = {{x, xb}, phi_span, {bias, 96}};
   const Span out[] = {{coeffs, cb}};
@@ -221,10 +225,32 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
     packed = dst;
   }
   a.x = x;
+  if (bcast) {
+    a.xts = C;
+    a.xrs = 0;
+  }
   a.phi_packed = static_cast<const uint32_t*>(packed);
   a.bias = bias;
   a.coeffs_out = coeffs;
   return hip_status(mhc::launch_split(run, mhc::kModeCoeffs, a, s));
+}
+
+// Coefficients, then pre, of a [T][C] stream broadcast to the 4 routes.
+int pre_broadcast_impl(const uint16_t* x0, int64_t T, int64_t C, const float* phi, const void* phi_packed,
+                       const float* bias, const float* gamma, const mhc_params* p, float* coeffs, uint16_t* h,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(T, C);
+  if (rc) return rc;
+  if ((rc = check_params(p, true))) return rc;
+  if (T == 0) return MHC_OK;
+  const Span phi_span = phi ? Span{phi, (size_t)4 * C * 24 * 4} : Span{phi_packed, mhc::phi_packed_bytes(C)};
+  const Span in[] = {{x0, (size_t)T * C * 2}, phi_span, {bias, 96}, {gamma, (size_t)C * 4}};
+  const Span out[] = {{coeffs, (size_t)T * 24 * 4}, {h, (size_t)T * C * 2}};
+  if ((rc = check_tensors(in, 4, out, 2))) return rc;
+  if (ws != nullptr && overlaps(Span{ws, mhc::make_plan(T, C).total}, out[1])) return MHC_ERR_ALIAS;
+  if ((rc = coeffs_impl(x0, T, C, phi, phi_packed, bias, p, coeffs, ws, ws_bytes, stream, true))) return rc;
+  return hip_status(
+      mhc::launch_pre(x0, C, 0, coeffs, gamma, T, (int)C, p->rmsnorm_eps, h, static_cast<hipStream_t>(stream)));
 }
 
 int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const float* phi,
@@ -359,6 +385,19 @@ int mhc_coeffs_prepacked(const uint16_t* x, int64_t T, int64_t C, const void* ph
   return coeffs_impl(x, T, C, nullptr, phi_packed, bias, p, coeffs, workspace, workspace_bytes, stream);
 }
 
+int mhc_pre_broadcast(const uint16_t* x0, int64_t T, int64_t C, const float* phi, const float* bias,
+                      const float* gamma, const mhc_params* p, float* coeffs, uint16_t* h, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return pre_broadcast_impl(x0, T, C, phi, nullptr, bias, gamma, p, coeffs, h, workspace, workspace_bytes, stream);
+}
+
+int mhc_pre_broadcast_prepacked(const uint16_t* x0, int64_t T, int64_t C, const void* phi_packed, const float* bias,
+                                const float* gamma, const mhc_params* p, float* coeffs, uint16_t* h,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return pre_broadcast_impl(x0, T, C, nullptr, phi_packed, bias, gamma, p, coeffs, h, workspace, workspace_bytes,
+                            stream);
+}
+
 int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t T, int64_t C,
             const mhc_params* p, uint16_t* h, void* stream) {
   int rc = check_shape(T, C);
@@ -368,7 +407,8 @@ int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t 
   const Span in[] = {{x, (size_t)T * 4 * C * 2}, {coeffs, (size_t)T * 24 * 4}, {gamma, (size_t)C * 4}};
   const Span out[] = {{h, (size_t)T * C * 2}};
   if ((rc = check_tensors(in, 3, out, 1))) return rc;
-  return hip_status(mhc::launch_pre(x, coeffs, gamma, T, (int)C, p->rmsnorm_eps, h, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      mhc::launch_pre(x, 4 * C, C, coeffs, gamma, T, (int)C, p->rmsnorm_eps, h, static_cast<hipStream_t>(stream)));
 }
 
 int mhc_post(const uint16_t* x, const uint16_t* y, const float* coeffs, int64_t T, int64_t C,

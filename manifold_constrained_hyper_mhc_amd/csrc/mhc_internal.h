@@ -82,6 +82,8 @@ struct SplitArgs {
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
   uint32_t* err;
   int64_t T;
+  int64_t xts, xrs;    // element strides of x between tokens and between routes: 4C and C, or C and 0
+                       // for a [T][C] stream broadcast to the 4 routes (coefficients mode only)
   uint32_t tiles;
   int C;
   int S;
@@ -97,8 +99,8 @@ hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s);
 hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStream_t s);
 hipError_t launch_post(const uint16_t* x, const uint16_t* y, const float* cf, int64_t T, int C,
                        uint16_t* x_out, hipStream_t s);
-hipError_t launch_pre(const uint16_t* x, const float* cf, const float* gamma, int64_t T, int C,
-                      float rmsnorm_eps, uint16_t* h, hipStream_t s);
+hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
+                      int C, float rmsnorm_eps, uint16_t* h, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace mhc

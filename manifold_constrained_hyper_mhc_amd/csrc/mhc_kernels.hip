@@ -291,9 +291,9 @@ __device__ __forceinline__ void load_stream(const SplitArgs& a, int64_t tok0, in
   for (int p = 0; p < NP; ++p) {
     const int64_t t = tok0 + p * 16 + tr;
     const bool valid = t < a.T;
-    const uint16_t* xp = a.x + (valid ? t : 0) * (int64_t)(4 * C) + cl;
+    const uint16_t* xp = a.x + (valid ? t : 0) * a.xts + cl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R.x[p][i] = valid ? ld16<LAST_USE>(xp + (int64_t)i * C) : u32x4_t{0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i) R.x[p][i] = valid ? ld16<LAST_USE>(xp + (int64_t)i * a.xrs) : u32x4_t{0, 0, 0, 0};
     if constexpr (WITH_Y) R.y[p] = valid ? ld16<LAST_USE>(a.y + t * (int64_t)C + cl) : u32x4_t{0, 0, 0, 0};
   }
 }
@@ -1038,7 +1038,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         for (int k = 0; k < 4; ++k) {
           const int q = gt + 256 * k, row = q >> 4;
           const int64_t tok = tok0 + (row >> 2);
-          const int64_t off = (tok < a.T ? tok : 0) * (int64_t)(4 * C) + (int64_t)(row & 3) * C + c0 + 8 * (q & 15);
+          const int64_t off = (tok < a.T ? tok : 0) * a.xts + (int64_t)(row & 3) * a.xrs + c0 + 8 * (q & 15);
           dst[k] = ld16_stream(a.x + (ok ? off : 0));
         }
       };
@@ -1602,10 +1602,10 @@ __device__ __forceinline__ float block128_sum(float v, float* sh) {
   return sh[0] + sh[1];
 }
 
-__device__ __forceinline__ void pre_group(const uint16_t* xr, int C, int c, const float* p, float* gv) {
+__device__ __forceinline__ void pre_group(const uint16_t* xr, int64_t xrs, int c, const float* p, float* gv) {
   float xv[4][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) unpack8(ld16_stream(xr + (int64_t)i * C + c), xv[i]);
+  for (int i = 0; i < 4; ++i) unpack8(ld16_stream(xr + (int64_t)i * xrs + c), xv[i]);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float v = p[0] * xv[0][e];
@@ -1627,20 +1627,20 @@ __device__ __forceinline__ void pre_store(uint16_t* hr, const float* gamma, int 
 }
 
 template <int G>
-__global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, const float* __restrict__ cf,
-                                             const float* __restrict__ gamma, int C, float eps,
-                                             uint16_t* __restrict__ h) {
+__global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, int64_t xts, int64_t xrs,
+                                             const float* __restrict__ cf, const float* __restrict__ gamma, int C,
+                                             float eps, uint16_t* __restrict__ h) {
   __shared__ float sh[2];
   const int64_t t = blockIdx.x;
   const int k = threadIdx.x;
   const float4 pq = *reinterpret_cast<const float4*>(cf + t * kCoeffs);
   const float p[4] = {pq.x, pq.y, pq.z, pq.w};
-  const uint16_t* xr = x + t * (int64_t)(4 * C);
+  const uint16_t* xr = x + t * xts;
   float gv[G][8];
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    pre_group(xr, C, (j * 128 + k) * 8, p, gv[j]);
+    pre_group(xr, xrs, (j * 128 + k) * 8, p, gv[j]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(gv[j][e], gv[j][e], ss);
   }
@@ -1651,20 +1651,20 @@ __global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, con
   for (int j = 0; j < G; ++j) pre_store(hr, gamma, (j * 128 + k) * 8, gv[j], rh);
 }
 
-__global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x, const float* __restrict__ cf,
-                                                  const float* __restrict__ gamma, int C, float eps,
-                                                  uint16_t* __restrict__ h) {
+__global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x, int64_t xts, int64_t xrs,
+                                                  const float* __restrict__ cf, const float* __restrict__ gamma,
+                                                  int C, float eps, uint16_t* __restrict__ h) {
   __shared__ float sh[2];
   const int64_t t = blockIdx.x;
   const int k = threadIdx.x;
   const float4 pq = *reinterpret_cast<const float4*>(cf + t * kCoeffs);
   const float p[4] = {pq.x, pq.y, pq.z, pq.w};
-  const uint16_t* xr = x + t * (int64_t)(4 * C);
+  const uint16_t* xr = x + t * xts;
   const int G = C >> 10;
   float ss = 0.0f;
   for (int j = 0; j < G; ++j) {
     float gv[8];
-    pre_group(xr, C, (j * 128 + k) * 8, p, gv);
+    pre_group(xr, xrs, (j * 128 + k) * 8, p, gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(gv[e], gv[e], ss);
   }
@@ -1673,7 +1673,7 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
   uint16_t* hr = h + t * (int64_t)C;
   for (int j = 0; j < G; ++j) {
     float gv[8];
-    pre_group(xr, C, (j * 128 + k) * 8, p, gv);
+    pre_group(xr, xrs, (j * 128 + k) * 8, p, gv);
     pre_store(hr, gamma, (j * 128 + k) * 8, gv, rh);
   }
 }
@@ -1744,19 +1744,19 @@ hipError_t launch_post(const uint16_t* x, const uint16_t* y, const float* cf, in
   return hipGetLastError();
 }
 
-hipError_t launch_pre(const uint16_t* x, const float* cf, const float* gamma, int64_t T, int C,
-                      float eps, uint16_t* h, hipStream_t s) {
+hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
+                      int C, float eps, uint16_t* h, hipStream_t s) {
   const dim3 grid((unsigned)T), block(128);
   switch (C >> 10) {
-    case 1: k_pre<1><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    case 2: k_pre<2><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    case 3: k_pre<3><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    case 4: k_pre<4><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    case 5: k_pre<5><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    case 6: k_pre<6><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    case 7: k_pre<7><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    case 8: k_pre<8><<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
-    default: k_pre_wide<<<grid, block, 0, s>>>(x, cf, gamma, C, eps, h); break;
+    case 1: k_pre<1><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 2: k_pre<2><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 3: k_pre<3><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 4: k_pre<4><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 5: k_pre<5><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 6: k_pre<6><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 7: k_pre<7><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 8: k_pre<8><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    default: k_pre_wide<<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
   }
   return hipGetLastError();
 }

@@ -362,6 +362,22 @@ def post_pre_fused(x, y, coeffs_in, phi_next, bias_next, gamma_next, *,
     return out
 
 
+def pre_broadcast(x0, phi, bias, gamma, *, hc_norm_eps, rmsnorm_eps, hc_post_scale, sinkhorn_eps,
+                  sinkhorn_iters=20):
+    """Coefficients and pre of a first-layer input: x0 [T, C] (bf16 values)
+    stands for every route ([P2] review, SM12x comment: the broadcast pre
+    takes a (T, H) input), i.e. the stream x[t, i, c] = x0[t, c].  Returns
+    (coeffs [T, 24], h [T, C] bf16 values): Coeffs and Pre of that stream.
+    """
+    x0 = np.asarray(x0, dtype=np.float64)
+    T, C = x0.shape
+    x = np.broadcast_to(x0[:, None, :], (T, N_ROUTES, C))
+    cf = coeffs(x, phi, bias, hc_norm_eps=hc_norm_eps, hc_post_scale=hc_post_scale,
+                sinkhorn_eps=sinkhorn_eps, sinkhorn_iters=sinkhorn_iters)
+    h = pre(x, cf[:, 0:4], gamma, rmsnorm_eps=rmsnorm_eps)
+    return cf, h
+
+
 def rms(a, axis=-1):
     """Root mean square along an axis (used by the comparison metric)."""
     a = np.asarray(a, dtype=np.float64)
@@ -373,5 +389,5 @@ __all__ = [
     "bf16_round", "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_round", "fma_f32",
     "post_exact",
     "e4m3_encode", "e4m3_decode", "sinkhorn", "coeffs", "pre", "post",
-    "split_coeffs", "mxfp8_scale_exponent", "mxfp8", "post_pre_fused", "rms",
+    "split_coeffs", "mxfp8_scale_exponent", "mxfp8", "post_pre_fused", "pre_broadcast", "rms",
 ]

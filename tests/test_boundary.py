@@ -118,6 +118,26 @@ def test_pre_validation():
     assert L.mhc_pre(None, None, None, 0, 1024, ctypes.byref(P), None, None) == OK
 
 
+@no_gpu
+def test_pre_broadcast_validation():
+    L = mhc.lib()
+    ws_bytes = L.mhc_workspace_bytes(4, 1024, 0)
+
+    def call(x0=None, T=4, C=1024, p=P, cf=None, h=None, ws=None, wsb=ws_bytes):
+        return L.mhc_pre_broadcast(x0 or fake(0), T, C, fake(1), fake(2), fake(3),
+                                   ctypes.byref(p) if p is not None else None, cf or fake(4), h or fake(5),
+                                   ws or fake(6), wsb, None)
+    assert call(p=None) == NULL
+    assert call(C=3000) == SHAPE
+    assert call(x0=fake(0, 8)) == ALIGN
+    assert call(h=fake(0, 4096)) == ALIAS          # h inside x0 ([4][1024] bf16 = 8 KB)
+    assert call(cf=fake(5, 16)) == ALIAS           # coeffs overlapping h
+    assert call(wsb=16) == WORKSPACE
+    bad = MhcParams(1e-6, 1e-6, 2.0, 1e-6, -1)
+    assert call(p=bad) == PARAM
+    assert L.mhc_pre_broadcast(None, 0, 1024, None, None, None, ctypes.byref(P), None, None, None, 0, None) == OK
+
+
 def fused_call(L, T=16, C=1024, flags=0, p=P, ws=None, ws_bytes=None, h=True, fp8=None, sc=None,
                x_out=None, cf_next=None, phi=None, gamma=None):
     if ws_bytes is None:

@@ -513,3 +513,26 @@ def test_pack_phi_layout(C):
         exp[:, 4, :, e] = np.where(n16[None, :] < 8, Lo[rows, c2[None, :]], 0)
     got = mhc.pack_phi(phi.to(DEV)).cpu().view(torch.int16).numpy().astype(np.int64) & 0xFFFF
     assert np.array_equal(got.reshape(exp.shape), exp)
+
+
+@pytest.mark.parametrize("T,C", [(37, 3072), (300, 7168)])
+def test_pre_broadcast(T, C, schedule):
+    # first-layer pre of a [T, C] input standing for all 4 routes: parity with
+    # the oracle, and bitwise the same as coeffs + pre of the explicit
+    # [T, 4, C] copy
+    inp = make_inputs(T, C, seed=29, rows="outliers", device="cpu")
+    x0 = inp["x"][:, 0, :].contiguous()
+    d = to_dev({"x0": x0, "phi": inp["phi"], "bias": inp["bias"], "gamma": inp["gamma"]})
+    cf, h = mhc.pre_broadcast(d["x0"], d["phi"], d["bias"], d["gamma"])
+    xr = d["x0"][:, None, :].expand(T, 4, C).contiguous()
+    cf2 = mhc.coeffs(xr, d["phi"], d["bias"])
+    h2 = mhc.pre(xr, cf2, d["gamma"])
+    pk = mhc.pack_phi(d["phi"])
+    cf3, h3 = mhc.pre_broadcast(d["x0"], None, d["bias"], d["gamma"], phi_packed=pk)
+    torch.cuda.synchronize()
+    assert torch.equal(cf, cf2) and torch.equal(h, h2)
+    assert torch.equal(cf, cf3) and torch.equal(h, h3)
+    rc, rh = O.pre_broadcast(f64(x0), f64(inp["phi"]), f64(inp["bias"]), f64(inp["gamma"]),
+                             rmsnorm_eps=P.rmsnorm_eps, **kw())
+    assert_coeffs_close(f64(cf), rc)
+    assert_bf16_close(f64(h), rh, what="h")

@@ -564,3 +564,32 @@ def test_fused_mxfp8_consistent_with_h():
     assert np.all(np.abs(dec - blk) <= np.ldexp(1.0, e)[:, :, None] * 16.0 + 0.0)
     ref = torch.from_numpy((blk * np.ldexp(1.0, -e)[:, :, None]).astype(np.float32)).to(torch.float8_e4m3fn)
     assert np.array_equal(ref.view(torch.uint8).numpy().reshape(T, C), out["h_fp8"])
+
+
+# ----------------------------------------------------------------------------
+# broadcast (first-layer) pre
+# ----------------------------------------------------------------------------
+def test_pre_broadcast_closed_forms():
+    # A stream whose 4 routes are one row x0: the projection is x0 against the
+    # route-summed phi (a [C, 24] matrix), the sum of squares is 4 * sum x0^2,
+    # and since the pre weights are positive, h = x0 / sqrt(mean x0^2 +
+    # eps / (sum pre)^2) * gamma (the norm does not see the common factor).
+    rng = np.random.default_rng(23)
+    T, C = 5, 1024
+    x0 = _bf16_values((T, C), rng)
+    phi = rng.standard_normal((4 * C, 24)) * 0.02
+    bias = rng.standard_normal(24) * 0.1
+    gamma = 1.0 + rng.standard_normal(C) * 0.05
+    cf, h = O.pre_broadcast(x0, phi, bias, gamma, rmsnorm_eps=EPS, **_kw())
+    phi_c = phi.reshape(4, C, 24).sum(axis=0)
+    r = 1.0 / np.sqrt(4.0 * np.sum(x0 * x0, axis=1) / (4 * C) + EPS)
+    logit = r[:, None] * (x0 @ phi_c) + bias[None, :]
+    np.testing.assert_allclose(cf[:, 0:4], 1.0 / (1.0 + np.exp(-logit[:, 0:4])), rtol=1e-12)
+    np.testing.assert_allclose(cf[:, 4:8], S / (1.0 + np.exp(-logit[:, 4:8])), rtol=1e-12)
+    ps = cf[:, 0:4].sum(axis=1)
+    hh = x0 / np.sqrt(np.mean(x0 * x0, axis=1) + EPS / ps ** 2)[:, None] * gamma[None, :]
+    ref = torch.from_numpy(hh).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(h, ref)
+    # res: the Sinkhorn of the broadcast logits (columns sum to 1)
+    res = cf[:, 8:].reshape(T, 4, 4)
+    np.testing.assert_allclose(res.sum(axis=1), 1.0, atol=1e-5)
