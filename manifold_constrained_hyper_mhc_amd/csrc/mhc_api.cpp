@@ -232,7 +232,7 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
   a.phi_packed = static_cast<const uint32_t*>(packed);
   a.bias = bias;
   a.coeffs_out = coeffs;
-  return hip_status(mhc::launch_split(run, mhc::kModeCoeffs, a, s));
+  return hip_status(mhc::launch_split(run, bcast ? mhc::kModeCoeffsBcast : mhc::kModeCoeffs, a, s));
 }
 
 // Coefficients, then pre, of a [T][C] stream broadcast to the 4 routes.

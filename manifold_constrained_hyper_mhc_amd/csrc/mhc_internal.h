@@ -93,7 +93,10 @@ struct SplitArgs {
   Scalars sc;
 };
 
-enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2 };
+// kModeCoeffsBcast: coefficients of a [T][C] stream that stands for all 4
+// routes (route stride 0); the persistent schedule loads each chunk once and
+// stages it for the 4 routes, the staged one reads it once per route.
+enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2, kModeCoeffsBcast = 3 };
 
 hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s);
 hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStream_t s);

@@ -816,7 +816,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 
 template <int MODE>
 __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs a) {
-  constexpr bool FUSED = MODE != kModeCoeffs;
+  constexpr bool FUSED = MODE == kModeFused || MODE == kModeFusedMx;
+  constexpr bool BCAST = MODE == kModeCoeffsBcast;
   constexpr bool MX = MODE == kModeFusedMx;
   constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
   // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
@@ -1031,9 +1032,17 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // (issued unconditionally, so that the compiler's wait counts never
       // merge paths with and without the loads: past the last tile every
       // lane reads the first 16 bytes of x, whose value is not used)
+      // (a broadcast stream: one chunk per thread, token gt / 16, chunk
+      // gt % 16, staged for all 4 routes)
       auto load_x = [&](u32x4_t* dst, int i) __attribute__((always_inline)) {
         const bool ok = i < niter;
         const int64_t tok0 = (int64_t)(r + L * i) * TM + rb * 16;
+        if constexpr (BCAST) {
+          const int64_t tok = tok0 + (gt >> 4);
+          const int64_t off = (tok < a.T ? tok : 0) * a.xts + c0 + 8 * (gt & 15);
+          dst[0] = ld16_stream(a.x + (ok ? off : 0));
+          return;
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int q = gt + 256 * k, row = q >> 4;
@@ -1043,6 +1052,12 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
       };
       auto stage_write = [&](const u32x4_t* src) __attribute__((always_inline)) {
+        if constexpr (BCAST) {
+          const int tt = gt >> 4;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) stage[(tt * 4 + k) * 16 + ((gt & 15) ^ tt)] = src[0];
+          return;
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int q = gt + 256 * k, row = q >> 4;
@@ -1602,10 +1617,20 @@ __device__ __forceinline__ float block128_sum(float v, float* sh) {
   return sh[0] + sh[1];
 }
 
+// B: a broadcast stream (route stride 0): the 4 routes are one load
+template <bool B>
 __device__ __forceinline__ void pre_group(const uint16_t* xr, int64_t xrs, int c, const float* p, float* gv) {
   float xv[4][8];
+  if constexpr (B) {
+    unpack8(ld16_stream(xr + c), xv[0]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) unpack8(ld16_stream(xr + (int64_t)i * xrs + c), xv[i]);
+    for (int i = 1; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[i][e] = xv[0][e];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack8(ld16_stream(xr + (int64_t)i * xrs + c), xv[i]);
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float v = p[0] * xv[0][e];
@@ -1626,7 +1651,7 @@ __device__ __forceinline__ void pre_store(uint16_t* hr, const float* gamma, int 
   st16_stream(hr + c, pack8(hv));
 }
 
-template <int G>
+template <int G, bool B>
 __global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, int64_t xts, int64_t xrs,
                                              const float* __restrict__ cf, const float* __restrict__ gamma, int C,
                                              float eps, uint16_t* __restrict__ h) {
@@ -1640,7 +1665,7 @@ __global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, int
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    pre_group(xr, xrs, (j * 128 + k) * 8, p, gv[j]);
+    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, gv[j]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(gv[j][e], gv[j][e], ss);
   }
@@ -1651,6 +1676,7 @@ __global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, int
   for (int j = 0; j < G; ++j) pre_store(hr, gamma, (j * 128 + k) * 8, gv[j], rh);
 }
 
+template <bool B>
 __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x, int64_t xts, int64_t xrs,
                                                   const float* __restrict__ cf, const float* __restrict__ gamma,
                                                   int C, float eps, uint16_t* __restrict__ h) {
@@ -1664,7 +1690,7 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
   float ss = 0.0f;
   for (int j = 0; j < G; ++j) {
     float gv[8];
-    pre_group(xr, xrs, (j * 128 + k) * 8, p, gv);
+    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(gv[e], gv[e], ss);
   }
@@ -1673,7 +1699,7 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
   uint16_t* hr = h + t * (int64_t)C;
   for (int j = 0; j < G; ++j) {
     float gv[8];
-    pre_group(xr, xrs, (j * 128 + k) * 8, p, gv);
+    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, gv);
     pre_store(hr, gamma, (j * 128 + k) * 8, gv, rh);
   }
 }
@@ -1725,11 +1751,13 @@ hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStrea
       case kModeCoeffs: return launch_persist_mode<kModeCoeffs>(plan, a, s);
       case kModeFused: return launch_persist_mode<kModeFused>(plan, a, s);
       case kModeFusedMx: return launch_persist_mode<kModeFusedMx>(plan, a, s);
+      case kModeCoeffsBcast: return launch_persist_mode<kModeCoeffsBcast>(plan, a, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (mode) {
-    case kModeCoeffs: return launch_split_mode<kModeCoeffs>(plan, a, s);
+    case kModeCoeffs:
+    case kModeCoeffsBcast: return launch_split_mode<kModeCoeffs>(plan, a, s);
     case kModeFused: return launch_split_mode<kModeFused>(plan, a, s);
     case kModeFusedMx: return launch_split_mode<kModeFusedMx>(plan, a, s);
     default: return hipErrorInvalidValue;
@@ -1744,19 +1772,29 @@ hipError_t launch_post(const uint16_t* x, const uint16_t* y, const float* cf, in
   return hipGetLastError();
 }
 
-hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
-                      int C, float eps, uint16_t* h, hipStream_t s) {
+template <bool B>
+static void launch_pre_b(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma,
+                         int64_t T, int C, float eps, uint16_t* h, hipStream_t s) {
   const dim3 grid((unsigned)T), block(128);
   switch (C >> 10) {
-    case 1: k_pre<1><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    case 2: k_pre<2><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    case 3: k_pre<3><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    case 4: k_pre<4><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    case 5: k_pre<5><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    case 6: k_pre<6><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    case 7: k_pre<7><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    case 8: k_pre<8><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
-    default: k_pre_wide<<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 1: k_pre<1, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 2: k_pre<2, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 3: k_pre<3, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 4: k_pre<4, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 5: k_pre<5, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 6: k_pre<6, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 7: k_pre<7, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    case 8: k_pre<8, B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+    default: k_pre_wide<B><<<grid, block, 0, s>>>(x, xts, xrs, cf, gamma, C, eps, h); break;
+  }
+}
+
+hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
+                      int C, float eps, uint16_t* h, hipStream_t s) {
+  if (xrs == 0) {
+    launch_pre_b<true>(x, xts, xrs, cf, gamma, T, C, eps, h, s);
+  } else {
+    launch_pre_b<false>(x, xts, xrs, cf, gamma, T, C, eps, h, s);
   }
   return hipGetLastError();
 }
