@@ -293,6 +293,38 @@ def time_pre_broadcast(mhc, inp, packed, params, stream, args):
             "note": "mhc_pre_broadcast_prepacked on a [T, C] first-layer input (coefficients + pre)"}
 
 
+def time_post_int8(mhc, inp, coeffs_in, stream, args):
+    """Post of an int8 sublayer output with per-token scales (mhc_post_int8)
+    on the workload's x and incoming coefficients.  HIP events around each
+    call; algorithmic bytes 17C + 84 per token (x read, x' written, int8
+    codes, the scale, post and res coefficients)."""
+    import torch
+    from manifold_constrained_hyper_mhc_amd.synthetic import make_int8_y
+
+    T, _, C = inp["x"].shape
+    yq = make_int8_y(T, C, seed=3, device=inp["x"].device)
+    out = torch.empty_like(inp["x"])
+
+    def run():
+        mhc.post_int8(inp["x"], yq["y_q"], yq["y_scale"], coeffs_in, out=out)
+
+    for _ in range(max(3, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+    nbytes = T * (17 * C + 84)
+    return {"us": us, "algorithmic_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+            "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "mhc_post_int8: int8 sublayer output with per-token scales"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +336,8 @@ def main() -> int:
     ap.add_argument("--cold-phi", type=int, default=0, metavar="N",
                     help="rotate N prepacked next-layer projections (no repack in the step), so that the "
                          "projection is read cold")
+    ap.add_argument("--post-int8", action="store_true",
+                    help="also time the post of an int8 sublayer output with per-token scales (mhc_post_int8)")
     ap.add_argument("--pre-broadcast", action="store_true",
                     help="also time the first-layer pre of a [T, C] input (mhc_pre_broadcast)")
     ap.add_argument("--graph", action="store_true",
@@ -465,6 +499,12 @@ def main() -> int:
         print(f"[bench] first-layer pre (broadcast [T, C] input): {first['us']:.1f} us, {first['gbs']:.0f} GB/s "
               f"algorithmic ({first['frac_of_peak']:.3f} of peak)", file=sys.stderr, flush=True)
 
+    pq = None
+    if args.post_int8:
+        pq = time_post_int8(mhc, inp, coeffs_in, stream, args)
+        print(f"[bench] post of int8 y: {pq['us']:.1f} us, {pq['gbs']:.0f} GB/s algorithmic "
+              f"({pq['frac_of_peak']:.3f} of peak)", file=sys.stderr, flush=True)
+
     copy_ref = copy_reference(inp, outs, stream, args, achieved)
     print(f"[bench] plain copy of x and y: {copy_ref['us']:.1f} us, {copy_ref['gbs']:.0f} GB/s "
           f"({copy_ref['frac_of_peak']:.3f} of peak); the fused pass runs at "
@@ -508,6 +548,8 @@ def main() -> int:
     line["copy_reference"] = copy_ref
     if first is not None:
         line["pre_broadcast"] = first
+    if pq is not None:
+        line["post_int8"] = pq
     if unfused is not None:
         line["unfused_chain"] = unfused
     print(json.dumps(line), flush=True)

@@ -198,6 +198,22 @@ int mhc_post(const uint16_t* x, const uint16_t* y, const float* coeffs, int64_t 
              uint16_t* x_out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Post of an int8 sublayer output ([P1] "What this fixes": the tensor-
+ * parallel all-reduce of the sublayer output runs in int8 and hands the
+ * post kernel the int8 values with one scale per token).
+ *   y[t][c] = binary32(y_q[t][c] * y_scale[t])
+ * then exactly mhc_post's chain with this y in place of the bf16 y:
+ *   x_out[t][j][c] = bf16_rne(a),  a = post_j * y;  a = fma(res[j][i], x_i, a), i = 0..3.
+ * y_q [T][C] int8 (two's complement, any value in [-128, 127]), y_scale
+ * [T] fp32, both device memory owned by the caller and read only.  Same
+ * shape, alignment (16 bytes for every pointer) and aliasing rules as
+ * mhc_post; returns MHC_ERR_NULL / MHC_ERR_ALIGN / MHC_ERR_ALIAS /
+ * MHC_ERR_SHAPE before any HIP call, MHC_ERR_HIP if the launch fails.
+ * ------------------------------------------------------------------------- */
+int mhc_post_int8(const uint16_t* x, const int8_t* y_q, const float* y_scale, const float* coeffs, int64_t T,
+                  int64_t C, uint16_t* x_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Fused post -> next pre ([P2] "Purpose"/review: the fused post->pre kernel
  * and Mega-mHC; [P1]: the shared sum of squares; [P3] item 3: the MXFP8
  * epilogue).  In one pass over the stream:

@@ -69,6 +69,7 @@ _SIG = {
     "mhc_pre_broadcast_prepacked": ([_P, _I64, _I64, _P, _P, _P, ctypes.POINTER(MhcParams), _P, _P, _P,
                                      ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_post": ([_P, _P, _P, _I64, _I64, _P, _P], ctypes.c_int),
+    "mhc_post_int8": ([_P, _P, _P, _P, _I64, _I64, _P, _P], ctypes.c_int),
     "mhc_post_pre_fused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams), ctypes.c_uint,
                             _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_post_pre_fused_prepacked": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams),
@@ -263,6 +264,23 @@ def post(x, y, coeffs_t, *, out=None) -> torch.Tensor:
     out = torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev) if out is None else out
     _need(out, "x_out", torch.bfloat16, (T, 4, C), dev)
     _check(L.mhc_post(_ptr(x), _ptr(y), _ptr(coeffs_t), T, C, _ptr(out), _stream(dev)), "mhc_post")
+    return out
+
+
+def post_int8(x, y_q, y_scale, coeffs_t, *, out=None) -> torch.Tensor:
+    """Post of an int8 sublayer output y_q [T, C] with per-token fp32 scales
+    y_scale [T] (mhc_post_int8)."""
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(y_q, "y_q", torch.int8, (T, C), dev)
+    _need(y_scale, "y_scale", torch.float32, (T,), dev)
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24), dev)
+    out = torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "x_out", torch.bfloat16, (T, 4, C), dev)
+    _check(L.mhc_post_int8(_ptr(x), _ptr(y_q), _ptr(y_scale), _ptr(coeffs_t), T, C, _ptr(out), _stream(dev)),
+           "mhc_post_int8")
     return out
 
 

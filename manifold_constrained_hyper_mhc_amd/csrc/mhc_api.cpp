@@ -423,6 +423,19 @@ int mhc_post(const uint16_t* x, const uint16_t* y, const float* coeffs, int64_t 
   return hip_status(mhc::launch_post(x, y, coeffs, T, (int)C, x_out, static_cast<hipStream_t>(stream)));
 }
 
+int mhc_post_int8(const uint16_t* x, const int8_t* y_q, const float* y_scale, const float* coeffs, int64_t T,
+                  int64_t C, uint16_t* x_out, void* stream) {
+  int rc = check_shape(T, C);
+  if (rc) return rc;
+  if (T == 0) return MHC_OK;
+  const size_t xb = (size_t)T * 4 * C * 2;
+  const Span in[] = {{x, xb}, {y_q, (size_t)T * C}, {y_scale, (size_t)T * 4}, {coeffs, (size_t)T * 24 * 4}};
+  const Span out[] = {{x_out, xb}};
+  if ((rc = check_tensors(in, 4, out, 1))) return rc;
+  return hip_status(
+      mhc::launch_post_int8(x, y_q, y_scale, coeffs, T, (int)C, x_out, static_cast<hipStream_t>(stream)));
+}
+
 int mhc_post_pre_fused(const uint16_t* x, const uint16_t* y, const float* coeffs,
                        const float* phi_next, const float* bias_next, const float* gamma_next,
                        int64_t T, int64_t C, const mhc_params* p, unsigned flags, uint16_t* x_out,

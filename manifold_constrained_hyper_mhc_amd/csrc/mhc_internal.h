@@ -102,6 +102,8 @@ hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s);
 hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStream_t s);
 hipError_t launch_post(const uint16_t* x, const uint16_t* y, const float* cf, int64_t T, int C,
                        uint16_t* x_out, hipStream_t s);
+hipError_t launch_post_int8(const uint16_t* x, const int8_t* y_q, const float* y_scale, const float* cf, int64_t T,
+                            int C, uint16_t* x_out, hipStream_t s);
 hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
                       int C, float rmsnorm_eps, uint16_t* h, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

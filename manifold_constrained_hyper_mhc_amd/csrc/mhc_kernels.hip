@@ -2,7 +2,8 @@
 //
 // The path ([P1] "What this fixes"; [P2] review "Correctness findings";
 // [P3] "What changed" item 3 — see include/mhc.h for the page titles):
-//   post      x'_j = sum_i res_ji x_i + post_j y                     (k_post)
+//   post      x'_j = sum_i res_ji x_i + post_j y                     (k_post; int8 y with
+//             per-token scales: k_post<true>)
 //   coeffs    RMS-scaled 24-wide projection of the flattened row,
 //             sigmoid pre/post, Sinkhorn res                          (k_persist / k_split, coeffs mode)
 //   pre       h = RMSNorm(sum_i pre_i x_i) * gamma                    (k_pre)
@@ -1574,9 +1575,13 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 // Post (standalone): one thread per (token, 8 channels); consecutive threads
 // read consecutive 16-byte chunks of each route.
 // ===========================================================================
-__global__ __launch_bounds__(256) void k_post(const uint16_t* __restrict__ x, const uint16_t* __restrict__ y,
-                                              const float* __restrict__ cf, int64_t T, int C,
-                                              uint16_t* __restrict__ x_out) {
+// YQ: y arrives as int8 codes [T][C] with one binary32 scale per token; its
+// value is the binary32 product code * scale, which enters the chain in
+// place of the bf16 y.
+template <bool YQ>
+__global__ __launch_bounds__(256) void k_post(const uint16_t* __restrict__ x, const void* __restrict__ y,
+                                              const float* __restrict__ y_scale, const float* __restrict__ cf,
+                                              int64_t T, int C, uint16_t* __restrict__ x_out) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int G = C >> 3;
   const int64_t t = u / G;
@@ -1592,7 +1597,15 @@ __global__ __launch_bounds__(256) void k_post(const uint16_t* __restrict__ x, co
   float xv[4][8], yy[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) unpack8(ld16_stream(xr + (int64_t)i * C), xv[i]);
-  unpack8(ld16_stream(y + t * (int64_t)C + c), yy);
+  if constexpr (YQ) {
+    const uint64_t v = __builtin_nontemporal_load(
+        reinterpret_cast<const uint64_t*>(static_cast<const int8_t*>(y) + t * (int64_t)C + c));
+    const float sc = y_scale[t];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yy[e] = (float)(int8_t)(uint8_t)(v >> (8 * e)) * sc;
+  } else {
+    unpack8(ld16_stream(static_cast<const uint16_t*>(y) + t * (int64_t)C + c), yy);
+  }
   uint16_t* xo = x_out + t * (int64_t)(4 * C) + c;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -1768,7 +1781,15 @@ hipError_t launch_post(const uint16_t* x, const uint16_t* y, const float* cf, in
                        uint16_t* x_out, hipStream_t s) {
   const int64_t units = T * (C / 8);
   const int64_t blocks = (units + 255) / 256;
-  k_post<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(x, y, cf, T, C, x_out);
+  k_post<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(x, y, nullptr, cf, T, C, x_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_int8(const uint16_t* x, const int8_t* y_q, const float* y_scale, const float* cf, int64_t T,
+                            int C, uint16_t* x_out, hipStream_t s) {
+  const int64_t units = T * (C / 8);
+  const int64_t blocks = (units + 255) / 256;
+  k_post<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(x, y_q, y_scale, cf, T, C, x_out);
   return hipGetLastError();
 }
 

@@ -303,6 +303,28 @@ def post(x, y, post_w, res) -> np.ndarray:
     return bf16_round(out)
 
 
+def post_int8(x, y_q, y_scale, post_w, res) -> np.ndarray:
+    """Post of a sublayer output that arrives as int8 codes with one binary32
+    scale per token ([P1] "What this fixes": the int8 all-reduce hands the
+    post kernel int8 values and per-token scales, and the post consumes them
+    directly).  Reading R22: the dequantised value is the binary32 product
+    y[t, c] = f32(y_q[t, c] * y_scale[t]), which then enters ``post``'s
+    binary32 chain in place of the bf16 y.
+    x [T, 4, C] bf16 values, y_q [T, C] integers in [-128, 127], y_scale [T]
+    binary32 values; returns bf16 values [T, 4, C].
+    """
+    q = np.asarray(y_q)
+    if not np.issubdtype(q.dtype, np.integer) or (q.size and (q.min() < -128 or q.max() > 127)):
+        raise ValueError("y_q must hold int8 values")
+    sc = np.asarray(y_scale, dtype=np.float64)
+    if not np.array_equal(f32_round(sc), sc):
+        raise ValueError("y_scale must hold binary32 values")
+    # an int8 times a binary32 value is exact in binary64 (8 + 24 bits), so
+    # one rounding to binary32 gives the IEEE binary32 product
+    y = f32_round(q.astype(np.float64) * sc[:, None])
+    return post(x, y, post_w, res)
+
+
 def split_coeffs(cf):
     """Views of a packed [T, 24] coefficient array: pre [T,4], post [T,4], res [T,4,4]."""
     cf = np.asarray(cf, dtype=np.float64)
@@ -387,7 +409,7 @@ def rms(a, axis=-1):
 __all__ = [
     "N_ROUTES", "N_LOGITS", "MX_BLOCK", "E4M3_MAX",
     "bf16_round", "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_round", "fma_f32",
-    "post_exact",
+    "post_exact", "post_int8",
     "e4m3_encode", "e4m3_decode", "sinkhorn", "coeffs", "pre", "post",
     "split_coeffs", "mxfp8_scale_exponent", "mxfp8", "post_pre_fused", "pre_broadcast", "rms",
 ]

@@ -138,6 +138,23 @@ def test_pre_broadcast_validation():
     assert L.mhc_pre_broadcast(None, 0, 1024, None, None, None, ctypes.byref(P), None, None, None, 0, None) == OK
 
 
+@no_gpu
+def test_post_int8_validation():
+    L = mhc.lib()
+
+    def call(T=16, C=1024, x=None, q=None, sc=None, cf=None, out=None):
+        return L.mhc_post_int8(x or fake(0), q or fake(1), sc or fake(2), cf or fake(3), T, C, out or fake(4), None)
+    assert call(C=1000) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert L.mhc_post_int8(fake(0), None, fake(2), fake(3), 16, 1024, fake(4), None) == NULL
+    assert L.mhc_post_int8(fake(0), fake(1), None, fake(3), 16, 1024, fake(4), None) == NULL
+    assert call(sc=fake(2, 4)) == ALIGN
+    assert call(q=fake(1, 8)) == ALIGN
+    assert call(out=fake(1, 4096)) == ALIAS        # output overlapping the int8 codes
+    assert call(out=fake(2, 0)) == ALIAS           # output overlapping the scales
+    assert L.mhc_post_int8(None, None, None, None, 0, 1024, None, None) == OK
+
+
 def fused_call(L, T=16, C=1024, flags=0, p=P, ws=None, ws_bytes=None, h=True, fp8=None, sc=None,
                x_out=None, cf_next=None, phi=None, gamma=None):
     if ws_bytes is None:

@@ -20,7 +20,7 @@ import torch
 import manifold_constrained_hyper_mhc_amd as mhc
 import oracle as O
 from manifold_constrained_hyper_mhc_amd.params import Params
-from manifold_constrained_hyper_mhc_amd.synthetic import WORKLOADS, make_inputs
+from manifold_constrained_hyper_mhc_amd.synthetic import WORKLOADS, make_inputs, make_int8_y
 from tests._compare import assert_bf16_close, assert_coeffs_close, f64
 
 pytestmark = pytest.mark.gpu
@@ -107,6 +107,23 @@ def test_post_bit_exact(T, C):
     _, pw, res = O.split_coeffs(f64(inp["coeffs"]))
     ref = O.post(f64(inp["x"]), f64(inp["y"]), pw, res)
     assert np.array_equal(f64(out), ref)
+
+
+@pytest.mark.parametrize("T,C", SMALL + [(300, 7168)])
+def test_post_int8_bit_exact(T, C):
+    inp = small_inputs(T, C)
+    yq = make_int8_y(T, C, seed=T + C)
+    d = to_dev(dict(inp, **yq))
+    out = mhc.post_int8(d["x"], d["y_q"], d["y_scale"], d["coeffs"])
+    torch.cuda.synchronize()
+    _, pw, res = O.split_coeffs(f64(inp["coeffs"]))
+    ref = O.post_int8(f64(inp["x"]), yq["y_q"].numpy(), f64(yq["y_scale"]), pw, res)
+    assert np.array_equal(f64(out), ref)
+    # power-of-two scales: the same as the bf16 post of y = code * scale
+    k = torch.randint(-20, 4, (T,), generator=torch.Generator().manual_seed(5))
+    s2 = torch.ldexp(torch.ones(T), k).to(DEV)
+    y2 = (d["y_q"].float() * s2[:, None]).to(torch.bfloat16)
+    assert torch.equal(mhc.post_int8(d["x"], d["y_q"], s2, d["coeffs"]), mhc.post(d["x"], y2, d["coeffs"]))
 
 
 @pytest.mark.parametrize("T,C", SMALL)

@@ -593,3 +593,99 @@ def test_pre_broadcast_closed_forms():
     # res: the Sinkhorn of the broadcast logits (columns sum to 1)
     res = cf[:, 8:].reshape(T, 4, 4)
     np.testing.assert_allclose(res.sum(axis=1), 1.0, atol=1e-5)
+
+
+# ----------------------------------------------------------------------------
+# post of an int8 sublayer output with per-token scales
+# ----------------------------------------------------------------------------
+
+def _mul_exact_f32(q, s):
+    """Correctly rounded binary32 product q * s from exact rationals."""
+    from fractions import Fraction
+    v = Fraction(int(q)) * Fraction(float(s))
+    r = np.float32(float(v))
+    best = None
+    for cand in (np.nextafter(r, np.float32(-np.inf)), r, np.nextafter(r, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - v)
+        key = (d, int(np.array(cand).view(np.uint32)) & 1)   # ties to even mantissa
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return np.float32(best[1])
+
+
+def test_post_int8_dequantises_per_token_in_binary32():
+    # post_j = 1 on one route and res = 0 leave x'_j = bf16(y) with y the
+    # binary32 product of the code and its token's scale; brute force on a
+    # sample of elements
+    rng = np.random.default_rng(41)
+    T, C = 6, 1024
+    q = rng.integers(-128, 128, (T, C))
+    s = O.f32_round(10.0 ** rng.uniform(-4, 1, T) / 127.0)
+    x = _bf16_values((T, 4, C), rng)
+    j = 2
+    pw = np.zeros((T, 4))
+    pw[:, j] = 1.0
+    out = O.post_int8(x, q, s, pw, np.zeros((T, 4, 4)))
+    assert np.all(np.delete(out, j, axis=1) == 0)
+    for t, c in zip(rng.integers(0, T, 400), rng.integers(0, C, 400)):
+        y = _mul_exact_f32(q[t, c], s[t])
+        want = torch.tensor([float(y)], dtype=torch.float32).to(torch.bfloat16).double().item()
+        assert out[t, j, c] == want, (t, c)
+
+
+def test_post_int8_power_of_two_scales_equal_bf16_post():
+    # with a power-of-two scale per token the products are exact and bf16
+    # values, so the int8 post is the bf16 post of y = q * 2**k[t]
+    rng = np.random.default_rng(43)
+    T, C = 7, 2048
+    q = rng.integers(-128, 128, (T, C))
+    k = rng.integers(-24, 6, T)
+    y = np.ldexp(q.astype(np.float64), k[:, None])
+    assert np.array_equal(O.bf16_round(y), y)
+    x = _bf16_values((T, 4, C), rng)
+    pw = O.f32_round(rng.uniform(0.0, 2.0, (T, 4)))
+    res = O.f32_round(rng.dirichlet(np.ones(4), (T, 4)))
+    got = O.post_int8(x, q, np.ldexp(1.0, k), pw, res)
+    assert np.array_equal(got, O.post(x, y, pw, res))
+    # a scale taken per channel instead of per token would differ
+    assert not np.array_equal(got, O.post(x, q * np.ldexp(1.0, k[0]), pw, res))
+
+
+def test_post_int8_rejects_bad_inputs():
+    T, C = 2, 1024
+    x = np.zeros((T, 4, C))
+    pw, res = np.zeros((T, 4)), np.zeros((T, 4, 4))
+    with pytest.raises(ValueError):
+        O.post_int8(x, np.full((T, C), 200), np.ones(T), pw, res)
+    with pytest.raises(ValueError):
+        O.post_int8(x, np.zeros((T, C), dtype=np.int64), np.full(T, 0.1), pw, res)
+
+
+def test_post_int8_rounds_the_product_to_binary32_first():
+    # y32 = 65/64 times post = 1.25 is exactly the bf16 midpoint M = 325/256,
+    # which bf16 rounds to even (324/256).  Codes and scales whose exact
+    # product is y32 + e, with 0.4 < e / 2**-23 < 0.5, dequantise to y32 in
+    # binary32 and give x' = 324/256; a product kept exact would put
+    # post * y past M by more than half a binary32 step and round up to
+    # 326/256
+    from fractions import Fraction
+    y32, u = Fraction(65, 64), Fraction(1, 2 ** 23)
+    pairs = []
+    for q in range(3, 128, 2):
+        s0 = np.float32(float(y32 / q))
+        for d in range(-4, 5):
+            s = np.float32(s0)
+            for _ in range(abs(d)):
+                s = np.nextafter(s, np.float32(np.inf if d > 0 else -np.inf))
+            e = Fraction(q) * Fraction(float(s)) - y32
+            if Fraction(2, 5) * u < e < u / 2:
+                pairs.append((q, float(s)))
+    assert len(pairs) >= 3
+    T, C = len(pairs), 1024
+    q = np.array([[p[0]] * C for p in pairs])
+    sc = np.array([p[1] for p in pairs])
+    pw = np.zeros((T, 4))
+    pw[:, 1] = 1.25
+    zero_x, zero_r = np.zeros((T, 4, C)), np.zeros((T, 4, 4))
+    assert np.all(O.post_int8(zero_x, q, sc, pw, zero_r)[:, 1] == 324 / 256)
+    assert np.all(O.post_int8(zero_x, -q, sc, pw, zero_r)[:, 1] == -324 / 256)
