@@ -320,9 +320,34 @@ def time_post_int8(mhc, inp, coeffs_in, stream, args):
     torch.cuda.synchronize()
     us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
     nbytes = T * (17 * C + 84)
-    return {"us": us, "algorithmic_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
-            "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "note": "mhc_post_int8: int8 sublayer output with per-token scales"}
+    res = {"us": us, "algorithmic_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+           "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "note": "mhc_post_int8: int8 sublayer output with per-token scales"}
+    # the fused post -> next pre of the same int8 output (prepacked projection):
+    # 19C + 180 bytes per token (x, codes, scale, coefficients in; x', h,
+    # next coefficients out)
+    packed = mhc.pack_phi(inp["phi_next"])
+    ws = mhc.workspace(T, C, inp["x"].device)
+    outs = {"x_out": out, "coeffs_next": torch.empty((T, 24), dtype=torch.float32, device=out.device),
+            "h": torch.empty((T, C), dtype=torch.bfloat16, device=out.device)}
+
+    def run_fused():
+        mhc.post_int8_pre_fused(inp["x"], yq["y_q"], yq["y_scale"], coeffs_in, None, inp["bias_next"],
+                                inp["gamma_next"], ws=ws, outs=outs, phi_packed=packed)
+
+    for _ in range(max(3, args.warmup)):
+        run_fused()
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        run_fused()
+        b.record(stream)
+    torch.cuda.synchronize()
+    fus = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+    fbytes = T * (19 * C + 180)
+    res["fused_us"] = fus
+    res["fused_frac_of_peak"] = fbytes / (fus * 1e-6) / 1e9 / HBM_PEAK_GBS
+    return res
 
 
 def main() -> int:
@@ -503,7 +528,8 @@ def main() -> int:
     if args.post_int8:
         pq = time_post_int8(mhc, inp, coeffs_in, stream, args)
         print(f"[bench] post of int8 y: {pq['us']:.1f} us, {pq['gbs']:.0f} GB/s algorithmic "
-              f"({pq['frac_of_peak']:.3f} of peak)", file=sys.stderr, flush=True)
+              f"({pq['frac_of_peak']:.3f} of peak); fused post -> next pre of int8 y: {pq['fused_us']:.1f} us "
+              f"({pq['fused_frac_of_peak']:.3f} of peak)", file=sys.stderr, flush=True)
 
     copy_ref = copy_reference(inp, outs, stream, args, achieved)
     print(f"[bench] plain copy of x and y: {copy_ref['us']:.1f} us, {copy_ref['gbs']:.0f} GB/s "

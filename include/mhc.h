@@ -253,6 +253,27 @@ int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const flo
                                  uint8_t* h_scale, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Fused post -> next pre of an int8 sublayer output ([P1] "What this fixes":
+ * the mHC post kernel fused with the int8 all-reduce handoff, int8 values
+ * plus one scale per token).  Exactly mhc_post_pre_fused with x_out =
+ * mhc_post_int8(x, y_q, y_scale, coeffs); every other argument, output,
+ * flag, workspace and error rule is that of mhc_post_pre_fused.  y_q
+ * [T][C] int8 and y_scale [T] fp32 are device memory owned by the caller,
+ * read only, 16-byte aligned; MHC_ERR_NULL if either is NULL with T > 0.
+ * ------------------------------------------------------------------------- */
+int mhc_post_int8_pre_fused(const uint16_t* x, const int8_t* y_q, const float* y_scale, const float* coeffs,
+                            const float* phi_next, const float* bias_next, const float* gamma_next, int64_t T,
+                            int64_t C, const mhc_params* p, unsigned flags, uint16_t* x_out, float* coeffs_next,
+                            uint16_t* h, uint8_t* h_fp8, uint8_t* h_scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+int mhc_post_int8_pre_fused_prepacked(const uint16_t* x, const int8_t* y_q, const float* y_scale,
+                                      const float* coeffs, const void* phi_next_packed, const float* bias_next,
+                                      const float* gamma_next, int64_t T, int64_t C, const mhc_params* p,
+                                      unsigned flags, uint16_t* x_out, float* coeffs_next, uint16_t* h,
+                                      uint8_t* h_fp8, uint8_t* h_scale, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

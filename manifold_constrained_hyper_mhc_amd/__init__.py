@@ -10,10 +10,10 @@ missing library is an error, never a fallback.
 """
 from .params import Params
 from .binding import (MhcError, Prepared, coeffs, coeffs_prepacked, lib, pack_phi, post, post_pre_fused,
-                      post_int8, post_pre_fused_prepacked, pre, pre_broadcast, prepare_pack_phi,
+                      post_int8, post_int8_pre_fused, post_pre_fused_prepacked, pre, pre_broadcast, prepare_pack_phi,
                       prepare_post_pre_fused_prepacked, schedule, workspace, workspace_error)
 
 __all__ = ["Params", "MhcError", "lib", "coeffs", "coeffs_prepacked", "pre", "post",
            "post_pre_fused", "post_pre_fused_prepacked", "pack_phi", "workspace",
            "schedule", "workspace_error", "Prepared", "prepare_pack_phi", "prepare_post_pre_fused_prepacked",
-           "pre_broadcast", "post_int8"]
+           "pre_broadcast", "post_int8", "post_int8_pre_fused"]

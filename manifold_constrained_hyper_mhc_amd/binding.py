@@ -70,6 +70,10 @@ _SIG = {
                                      ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_post": ([_P, _P, _P, _I64, _I64, _P, _P], ctypes.c_int),
     "mhc_post_int8": ([_P, _P, _P, _P, _I64, _I64, _P, _P], ctypes.c_int),
+    "mhc_post_int8_pre_fused": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams), ctypes.c_uint,
+                                 _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "mhc_post_int8_pre_fused_prepacked": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams),
+                                           ctypes.c_uint, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_post_pre_fused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams), ctypes.c_uint,
                             _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_post_pre_fused_prepacked": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams),
@@ -336,6 +340,36 @@ def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Para
                                 T, C, ctypes.byref(p), _flags(mxfp8, recompute_x), _ptr(o["x_out"]),
                                 _ptr(o["coeffs_next"]), _ptr(o["h"]), _ptr(o["h_fp8"]), _ptr(o["h_scale"]),
                                 _ptr(ws), ws.numel(), _stream(dev)), "mhc_post_pre_fused")
+    return o
+
+
+def post_int8_pre_fused(x, y_q, y_scale, coeffs_t, phi_next, bias_next, gamma_next, params: Params = Params(), *,
+                        mxfp8: bool = False, want_h: bool = True, ws=None, outs=None, recompute_x: bool = False,
+                        phi_packed=None) -> dict:
+    """post_pre_fused of an int8 sublayer output y_q [T, C] with per-token
+    fp32 scales y_scale [T] (mhc_post_int8_pre_fused, or its _prepacked
+    form when ``phi_packed`` is given and ``phi_next`` is None)."""
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(y_q, "y_q", torch.int8, (T, C), dev)
+    _need(y_scale, "y_scale", torch.float32, (T,), dev)
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24), dev)
+    if phi_packed is not None:
+        _need(phi_packed, "phi_packed", torch.uint8, (int(L.mhc_phi_packed_bytes(C)),), dev)
+        fn, phi_arg, name = L.mhc_post_int8_pre_fused_prepacked, _ptr(phi_packed), "mhc_post_int8_pre_fused_prepacked"
+    else:
+        _need(phi_next, "phi_next", torch.float32, (4 * C, 24), dev)
+        fn, phi_arg, name = L.mhc_post_int8_pre_fused, _ptr(phi_next), "mhc_post_int8_pre_fused"
+    _need(bias_next, "bias_next", torch.float32, (24,), dev)
+    _need(gamma_next, "gamma_next", torch.float32, (C,), dev)
+    o = _fused_outputs(T, C, dev, mxfp8, want_h, outs)
+    ws = workspace(T, C, dev) if ws is None else ws
+    p = MhcParams.of(params)
+    _check(fn(_ptr(x), _ptr(y_q), _ptr(y_scale), _ptr(coeffs_t), phi_arg, _ptr(bias_next), _ptr(gamma_next), T, C,
+              ctypes.byref(p), _flags(mxfp8, recompute_x), _ptr(o["x_out"]), _ptr(o["coeffs_next"]), _ptr(o["h"]),
+              _ptr(o["h_fp8"]), _ptr(o["h_scale"]), _ptr(ws), ws.numel(), _stream(dev)), name)
     return o
 
 

@@ -253,7 +253,15 @@ int pre_broadcast_impl(const uint16_t* x0, int64_t T, int64_t C, const float* ph
       mhc::launch_pre(x0, C, 0, coeffs, gamma, T, (int)C, p->rmsnorm_eps, h, static_cast<hipStream_t>(stream)));
 }
 
-int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const float* phi,
+// The sublayer output of a fused call: bf16 [T][C], or int8 codes [T][C]
+// with one fp32 scale per token.
+struct YIn {
+  const uint16_t* bf16;
+  const int8_t* q;
+  const float* scale;
+};
+
+int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float* phi,
                const void* phi_packed, const float* bias, const float* gamma, int64_t T, int64_t C,
                const mhc_params* p, unsigned flags, uint16_t* x_out, float* coeffs_next, uint16_t* h,
                uint8_t* h_fp8, uint8_t* h_scale, void* ws, size_t ws_bytes, void* stream) {
@@ -271,7 +279,15 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
   if (!mx && h == nullptr) return MHC_ERR_NULL;
   const size_t xb = (size_t)T * 4 * C * 2, yb = (size_t)T * C * 2, cb = (size_t)T * 24 * 4;
   const Span phi_span = phi ? Span{phi, (size_t)4 * C * 24 * 4} : Span{phi_packed, mhc::phi_packed_bytes(C)};
-  const Span in[] = {{x, xb}, {y, yb}, {coeffs, cb}, phi_span, {bias, 96}, {gamma, (size_t)C * 4}};
+  const bool yq = y.bf16 == nullptr;
+  Span in[7] = {{x, xb}, {coeffs, cb}, phi_span, {bias, 96}, {gamma, (size_t)C * 4}};
+  int nin = 5;
+  if (yq) {
+    in[nin++] = {y.q, (size_t)T * C};
+    in[nin++] = {y.scale, (size_t)T * 4};
+  } else {
+    in[nin++] = {y.bf16, yb};
+  }
   Span out[5];
   int nout = 0;
   out[nout++] = {x_out, xb};
@@ -281,12 +297,12 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
     out[nout++] = {h_fp8, (size_t)T * C};
     out[nout++] = {h_scale, (size_t)T * (C / 32)};
   }
-  if ((rc = check_tensors(in, 6, out, nout))) return rc;
+  if ((rc = check_tensors(in, nin, out, nout))) return rc;
   const mhc::Plan plan = mhc::make_plan(T, C);
   if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
   const Span wsp{ws, plan.total};
-  for (const Span& s : in)
-    if (overlaps(wsp, s)) return MHC_ERR_ALIAS;
+  for (int k = 0; k < nin; ++k)
+    if (overlaps(wsp, in[k])) return MHC_ERR_ALIAS;
   for (int k = 0; k < nout; ++k)
     if (overlaps(wsp, out[k])) return MHC_ERR_ALIAS;
 
@@ -301,7 +317,9 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
     packed = dst;
   }
   a.x = x;
-  a.y = y;
+  a.y = y.bf16;
+  a.y_q = y.q;
+  a.y_scale = y.scale;
   a.coeffs_in = coeffs;
   a.phi_packed = static_cast<const uint32_t*>(packed);
   a.bias = bias;
@@ -312,7 +330,8 @@ int fused_impl(const uint16_t* x, const uint16_t* y, const float* coeffs, const 
   a.h_fp8 = h_fp8;
   a.h_scale = h_scale;
   a.recompute_x = (flags & MHC_FLAG_RECOMPUTE_X) != 0;
-  return hip_status(mhc::launch_split(run, mx ? mhc::kModeFusedMx : mhc::kModeFused, a, s));
+  const int mode = (mx ? mhc::kModeFusedMx : mhc::kModeFused) | (yq ? mhc::kModeYInt8 : 0);
+  return hip_status(mhc::launch_split(run, mode, a, s));
 }
 
 }  // namespace
@@ -441,7 +460,7 @@ int mhc_post_pre_fused(const uint16_t* x, const uint16_t* y, const float* coeffs
                        int64_t T, int64_t C, const mhc_params* p, unsigned flags, uint16_t* x_out,
                        float* coeffs_next, uint16_t* h, uint8_t* h_fp8, uint8_t* h_scale,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return fused_impl(x, y, coeffs, phi_next, nullptr, bias_next, gamma_next, T, C, p, flags, x_out,
+  return fused_impl(YIn{y, nullptr, nullptr}, x, coeffs, phi_next, nullptr, bias_next, gamma_next, T, C, p, flags, x_out,
                     coeffs_next, h, h_fp8, h_scale, workspace, workspace_bytes, stream);
 }
 
@@ -452,8 +471,29 @@ int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const flo
                                  float* coeffs_next, uint16_t* h, uint8_t* h_fp8,
                                  uint8_t* h_scale, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  return fused_impl(x, y, coeffs, nullptr, phi_next_packed, bias_next, gamma_next, T, C, p, flags,
+  return fused_impl(YIn{y, nullptr, nullptr}, x, coeffs, nullptr, phi_next_packed, bias_next, gamma_next, T, C, p, flags,
                     x_out, coeffs_next, h, h_fp8, h_scale, workspace, workspace_bytes, stream);
+}
+
+int mhc_post_int8_pre_fused(const uint16_t* x, const int8_t* y_q, const float* y_scale, const float* coeffs,
+                            const float* phi_next, const float* bias_next, const float* gamma_next, int64_t T,
+                            int64_t C, const mhc_params* p, unsigned flags, uint16_t* x_out, float* coeffs_next,
+                            uint16_t* h, uint8_t* h_fp8, uint8_t* h_scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (T > 0 && (y_q == nullptr || y_scale == nullptr)) return MHC_ERR_NULL;
+  return fused_impl(YIn{nullptr, y_q, y_scale}, x, coeffs, phi_next, nullptr, bias_next, gamma_next, T, C, p, flags,
+                    x_out, coeffs_next, h, h_fp8, h_scale, workspace, workspace_bytes, stream);
+}
+
+int mhc_post_int8_pre_fused_prepacked(const uint16_t* x, const int8_t* y_q, const float* y_scale,
+                                      const float* coeffs, const void* phi_next_packed, const float* bias_next,
+                                      const float* gamma_next, int64_t T, int64_t C, const mhc_params* p,
+                                      unsigned flags, uint16_t* x_out, float* coeffs_next, uint16_t* h,
+                                      uint8_t* h_fp8, uint8_t* h_scale, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (T > 0 && (y_q == nullptr || y_scale == nullptr)) return MHC_ERR_NULL;
+  return fused_impl(YIn{nullptr, y_q, y_scale}, x, coeffs, nullptr, phi_next_packed, bias_next, gamma_next, T, C, p,
+                    flags, x_out, coeffs_next, h, h_fp8, h_scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

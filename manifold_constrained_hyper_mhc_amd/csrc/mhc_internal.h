@@ -81,6 +81,8 @@ struct SplitArgs {
   uint64_t* publish;   // [tiles][M][4] tagged words
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
   uint32_t* err;
+  const int8_t* y_q;      // int8 y [T][C] and its per-token scales [T] (fused modes with kModeYInt8)
+  const float* y_scale;
   int64_t T;
   int64_t xts, xrs;    // element strides of x between tokens and between routes: 4C and C, or C and 0
                        // for a [T][C] stream broadcast to the 4 routes (coefficients mode only)
@@ -96,7 +98,12 @@ struct SplitArgs {
 // kModeCoeffsBcast: coefficients of a [T][C] stream that stands for all 4
 // routes (route stride 0); the persistent schedule loads each chunk once and
 // stages it for the 4 routes, the staged one reads it once per route.
-enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2, kModeCoeffsBcast = 3 };
+// kModeYInt8 is a flag on the fused modes: y arrives as int8 codes with one
+// binary32 scale per token.
+enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2, kModeCoeffsBcast = 3, kModeYInt8 = 4 };
+constexpr bool mode_fused(int m) { return (m & 3) == kModeFused || (m & 3) == kModeFusedMx; }
+constexpr bool mode_mx(int m) { return (m & 3) == kModeFusedMx; }
+constexpr bool mode_yq(int m) { return (m & kModeYInt8) != 0; }
 
 hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s);
 hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStream_t s);

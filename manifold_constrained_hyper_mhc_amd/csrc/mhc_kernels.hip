@@ -284,7 +284,33 @@ struct TileRegs {
   u32x4_t y[NP];
 };
 
-template <bool WITH_Y, int TM, bool LAST_USE>
+// y of a token's 8 channels at cl: packed bf16, or (YQ) the 8 int8 codes in
+// words 0-1 and the token's binary32 scale in word 2
+template <bool YQ, bool LAST_USE>
+__device__ __forceinline__ u32x4_t load_y8(const SplitArgs& a, int64_t t, int cl) {
+  if constexpr (YQ) {
+    const uint64_t v = *reinterpret_cast<const uint64_t*>(a.y_q + t * (int64_t)a.C + cl);
+    return u32x4_t{(uint32_t)v, (uint32_t)(v >> 32), __float_as_uint(a.y_scale[t]), 0u};
+  } else {
+    return ld16<LAST_USE>(a.y + t * (int64_t)a.C + cl);
+  }
+}
+
+// the two y values of channel pair q (0..3) of a load_y8 result
+template <bool YQ>
+__device__ __forceinline__ void y_pair(const u32x4_t& v, int q, float& lo, float& hi) {
+  if constexpr (YQ) {
+    const float sc = __uint_as_float(v[2]);
+    const uint32_t w = v[q >> 1] >> (16 * (q & 1));
+    lo = (float)(int8_t)(uint8_t)w * sc;
+    hi = (float)(int8_t)(uint8_t)(w >> 8) * sc;
+  } else {
+    lo = bf16_lo(v[q]);
+    hi = bf16_hi(v[q]);
+  }
+}
+
+template <bool WITH_Y, int TM, bool LAST_USE, bool YQ = false>
 __device__ __forceinline__ void load_stream(const SplitArgs& a, int64_t tok0, int cl, int tr, TileRegs<TM / 16>& R) {
   constexpr int NP = TM / 16;
   const int C = a.C;
@@ -295,7 +321,7 @@ __device__ __forceinline__ void load_stream(const SplitArgs& a, int64_t tok0, in
     const uint16_t* xp = a.x + (valid ? t : 0) * a.xts + cl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) R.x[p][i] = valid ? ld16<LAST_USE>(xp + (int64_t)i * a.xrs) : u32x4_t{0, 0, 0, 0};
-    if constexpr (WITH_Y) R.y[p] = valid ? ld16<LAST_USE>(a.y + t * (int64_t)C + cl) : u32x4_t{0, 0, 0, 0};
+    if constexpr (WITH_Y) R.y[p] = valid ? load_y8<YQ, LAST_USE>(a, t, cl) : u32x4_t{0, 0, 0, 0};
   }
 }
 
@@ -334,7 +360,7 @@ __device__ __forceinline__ void store_post_coeffs(float4 v, int tid, float (*cfs
 }
 
 // x' = post chain of (x, y) in place, for the lane's tokens
-template <int TM>
+template <int TM, bool YQ>
 __device__ __forceinline__ void post_tile(TileRegs<TM / 16>& R, const float (*cfs)[20], int tr) {
   constexpr int NP = TM / 16;
 #pragma unroll
@@ -350,7 +376,8 @@ __device__ __forceinline__ void post_tile(TileRegs<TM / 16>& R, const float (*cf
     for (int q = 0; q < 4; ++q) {
       const float xl[4] = {bf16_lo(R.x[p][0][q]), bf16_lo(R.x[p][1][q]), bf16_lo(R.x[p][2][q]), bf16_lo(R.x[p][3][q])};
       const float xh[4] = {bf16_hi(R.x[p][0][q]), bf16_hi(R.x[p][1][q]), bf16_hi(R.x[p][2][q]), bf16_hi(R.x[p][3][q])};
-      const float yl = bf16_lo(R.y[p][q]), yh = bf16_hi(R.y[p][q]);
+      float yl, yh;
+      y_pair<YQ>(R.y[p], q, yl, yh);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         o[j][q] = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
@@ -365,8 +392,9 @@ __device__ __forceinline__ void post_tile(TileRegs<TM / 16>& R, const float (*cf
 // runs are short; long runs (hidden sizes above 7168) need more registers.
 template <int MODE, int TM, int RUN>
 __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs a) {
-  constexpr bool FUSED = MODE != kModeCoeffs;
-  constexpr bool MX = MODE == kModeFusedMx;
+  constexpr bool FUSED = mode_fused(MODE);
+  constexpr bool MX = mode_mx(MODE);
+  constexpr bool YQ = mode_yq(MODE);
   constexpr int W = 4, NV = kPartVals, NP = TM / 16, RB = TM / 16, NQ = TM / 4;
   constexpr int NVU = FUSED ? NV : 25;
   // partial words per token in the workspace: [tiles][S][TM][PW], dense, so
@@ -415,7 +443,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // again when R runs).
   if (tid == 0) s_tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   TileRegs<NP> ra;
-  if (tA >= 0) load_stream<FUSED, TM, true>(a, (int64_t)tA * TM, cl, tr, ra);
+  if (tA >= 0) load_stream<FUSED, TM, true, YQ>(a, (int64_t)tA * TM, cl, tr, ra);
   uint64_t own = 0;
   if (tid == 0 && tC >= 0) own = tagged_load(a.owner + (int64_t)tC * S + split);
   float4 cfa = make_float4(0.0f, 0.0f, 0.0f, 0.0f), cfc = cfa;
@@ -459,7 +487,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // ---------------- A: post, statistics and projection of tile tA ----------------
   if (tA >= 0) {
     const int64_t tok0 = (int64_t)tA * TM;
-    if constexpr (FUSED) post_tile<TM>(ra, cfs_a, tr);
+    if constexpr (FUSED) post_tile<TM, YQ>(ra, cfs_a, tr);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int m = p * 16 + tr;
@@ -572,7 +600,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
     if (xdirect) {
       load_xprime<TM>(a, (int64_t)tC * TM, cl, tr, rc);
     } else {
-      load_stream<true, TM, true>(a, (int64_t)tC * TM, cl, tr, rc);
+      load_stream<true, TM, true, YQ>(a, (int64_t)tC * TM, cl, tr, rc);
     }
     const float4* gp = reinterpret_cast<const float4*>(a.gamma + cl);
     const float4 g0 = gp[0], g1 = gp[1];
@@ -644,7 +672,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         }
         (&qs[0][0])[tid] = tagged_value(qw);
       }
-      if (!xdirect) post_tile<TM>(rc, cfs_c, tr);
+      if (!xdirect) post_tile<TM, YQ>(rc, cfs_c, tr);
       __syncthreads();  // qs
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
@@ -817,9 +845,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 
 template <int MODE>
 __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs a) {
-  constexpr bool FUSED = MODE == kModeFused || MODE == kModeFusedMx;
+  constexpr bool FUSED = mode_fused(MODE);
+  constexpr bool YQ = mode_yq(MODE);
   constexpr bool BCAST = MODE == kModeCoeffsBcast;
-  constexpr bool MX = MODE == kModeFusedMx;
+  constexpr bool MX = mode_mx(MODE);
   constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
   // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
   // [2][row block][token][route][16 chunks] x 16 B (chunk c of token t at
@@ -1193,7 +1222,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       const int t = r + L * (i < niter ? i : 0);
       const int64_t tok = (int64_t)t * TM + m;
       const int64_t tc = tok < a.T ? tok : 0;
-      ny = *reinterpret_cast<const u32x4_t*>(a.y + tc * (int64_t)C + cl);
+      if constexpr (YQ) {
+        ny = load_y8<true, false>(a, tc, cl);
+      } else {
+        ny = *reinterpret_cast<const u32x4_t*>(a.y + tc * (int64_t)C + cl);
+      }
       const int64_t ct = (int64_t)t * TM + rb * 16 + gt / 5;
       const bool cv = gt < 16 * 5 && ct < a.T;
       ncf = reinterpret_cast<const float4*>(a.coeffs_in + (cv ? ct : 0) * kCoeffs)[1 + (cv ? gt % 5 : 0)];
@@ -1331,7 +1364,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           for (int q = 0; q < 4; ++q) {
             const float xl[4] = {bf16_lo(xin[0][q]), bf16_lo(xin[1][q]), bf16_lo(xin[2][q]), bf16_lo(xin[3][q])};
             const float xh[4] = {bf16_hi(xin[0][q]), bf16_hi(xin[1][q]), bf16_hi(xin[2][q]), bf16_hi(xin[3][q])};
-            const float yl = bf16_lo(cy[q]), yh = bf16_hi(cy[q]);
+            float yl, yh;
+            y_pair<YQ>(cy, q, yl, yh);
 #pragma unroll
             for (int jr = 0; jr < 4; ++jr)
               o[jr][q] = pack_bf16x2(post_chain(pw[jr], yl, &rs[4 * jr], xl[0], xl[1], xl[2], xl[3]),
@@ -1734,7 +1768,7 @@ hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s) {
 
 template <int MODE>
 static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
-  const int64_t stages = p.tiles + (MODE == kModeCoeffs ? p.d1 : p.d2);
+  const int64_t stages = p.tiles + (mode_fused(MODE) ? p.d2 : p.d1);
   const dim3 grid((unsigned)(stages * p.s)), block(256);
   if ((p.m != 32 && p.m != 16) || p.cc != kCC) return hipErrorInvalidConfiguration;
   if (p.m == 16) {
@@ -1765,6 +1799,8 @@ hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStrea
       case kModeFused: return launch_persist_mode<kModeFused>(plan, a, s);
       case kModeFusedMx: return launch_persist_mode<kModeFusedMx>(plan, a, s);
       case kModeCoeffsBcast: return launch_persist_mode<kModeCoeffsBcast>(plan, a, s);
+      case kModeFused | kModeYInt8: return launch_persist_mode<kModeFused | kModeYInt8>(plan, a, s);
+      case kModeFusedMx | kModeYInt8: return launch_persist_mode<kModeFusedMx | kModeYInt8>(plan, a, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1773,6 +1809,8 @@ hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStrea
     case kModeCoeffsBcast: return launch_split_mode<kModeCoeffs>(plan, a, s);
     case kModeFused: return launch_split_mode<kModeFused>(plan, a, s);
     case kModeFusedMx: return launch_split_mode<kModeFusedMx>(plan, a, s);
+    case kModeFused | kModeYInt8: return launch_split_mode<kModeFused | kModeYInt8>(plan, a, s);
+    case kModeFusedMx | kModeYInt8: return launch_split_mode<kModeFusedMx | kModeYInt8>(plan, a, s);
     default: return hipErrorInvalidValue;
   }
 }

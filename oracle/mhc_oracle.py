@@ -313,6 +313,12 @@ def post_int8(x, y_q, y_scale, post_w, res) -> np.ndarray:
     x [T, 4, C] bf16 values, y_q [T, C] integers in [-128, 127], y_scale [T]
     binary32 values; returns bf16 values [T, 4, C].
     """
+    return post(x, dequant_int8(y_q, y_scale), post_w, res)
+
+
+def dequant_int8(y_q, y_scale) -> np.ndarray:
+    """R22: y[t, c] = f32(y_q[t, c] * y_scale[t]) for int8 codes and binary32
+    per-token scales."""
     q = np.asarray(y_q)
     if not np.issubdtype(q.dtype, np.integer) or (q.size and (q.min() < -128 or q.max() > 127)):
         raise ValueError("y_q must hold int8 values")
@@ -321,8 +327,7 @@ def post_int8(x, y_q, y_scale, post_w, res) -> np.ndarray:
         raise ValueError("y_scale must hold binary32 values")
     # an int8 times a binary32 value is exact in binary64 (8 + 24 bits), so
     # one rounding to binary32 gives the IEEE binary32 product
-    y = f32_round(q.astype(np.float64) * sc[:, None])
-    return post(x, y, post_w, res)
+    return f32_round(q.astype(np.float64) * sc[:, None])
 
 
 def split_coeffs(cf):
@@ -384,6 +389,12 @@ def post_pre_fused(x, y, coeffs_in, phi_next, bias_next, gamma_next, *,
     return out
 
 
+def post_int8_pre_fused(x, y_q, y_scale, coeffs_in, phi_next, bias_next, gamma_next, **kw):
+    """post_pre_fused of an int8 sublayer output with per-token scales ([P1]
+    "What this fixes"): the same pass with y = dequant_int8(y_q, y_scale)."""
+    return post_pre_fused(x, dequant_int8(y_q, y_scale), coeffs_in, phi_next, bias_next, gamma_next, **kw)
+
+
 def pre_broadcast(x0, phi, bias, gamma, *, hc_norm_eps, rmsnorm_eps, hc_post_scale, sinkhorn_eps,
                   sinkhorn_iters=20):
     """Coefficients and pre of a first-layer input: x0 [T, C] (bf16 values)
@@ -409,7 +420,7 @@ def rms(a, axis=-1):
 __all__ = [
     "N_ROUTES", "N_LOGITS", "MX_BLOCK", "E4M3_MAX",
     "bf16_round", "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_round", "fma_f32",
-    "post_exact", "post_int8",
+    "post_exact", "post_int8", "dequant_int8", "post_int8_pre_fused",
     "e4m3_encode", "e4m3_decode", "sinkhorn", "coeffs", "pre", "post",
     "split_coeffs", "mxfp8_scale_exponent", "mxfp8", "post_pre_fused", "pre_broadcast", "rms",
 ]

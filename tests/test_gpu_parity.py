@@ -126,6 +126,39 @@ def test_post_int8_bit_exact(T, C):
     assert torch.equal(mhc.post_int8(d["x"], d["y_q"], s2, d["coeffs"]), mhc.post(d["x"], y2, d["coeffs"]))
 
 
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("T,C", [(6, 7168), (37, 3072)] + PERSISTENT)
+def test_post_int8_pre_fused(T, C, mx, schedule):
+    inp = small_inputs(T, C, seed=13)
+    yq = make_int8_y(T, C, seed=T + 7)
+    d = to_dev(dict(inp, **yq))
+    out = mhc.post_int8_pre_fused(d["x"], d["y_q"], d["y_scale"], d["coeffs"], d["phi_next"], d["bias_next"],
+                                  d["gamma_next"], mxfp8=mx)
+    pk = mhc.pack_phi(d["phi_next"])
+    out2 = mhc.post_int8_pre_fused(d["x"], d["y_q"], d["y_scale"], d["coeffs"], None, d["bias_next"],
+                                   d["gamma_next"], mxfp8=mx, phi_packed=pk)
+    # power-of-two scales: bitwise the bf16 fused pass of y = code * scale
+    k = torch.randint(-20, 4, (T,), generator=torch.Generator().manual_seed(T))
+    s2 = torch.ldexp(torch.ones(T), k).to(DEV)
+    y2 = (d["y_q"].float() * s2[:, None]).to(torch.bfloat16)
+    out3 = mhc.post_int8_pre_fused(d["x"], d["y_q"], s2, d["coeffs"], d["phi_next"], d["bias_next"],
+                                   d["gamma_next"], mxfp8=mx)
+    out4 = mhc.post_pre_fused(d["x"], y2, d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=mx)
+    torch.cuda.synchronize()
+    for key, v in out.items():
+        if v is not None:
+            assert torch.equal(v, out2[key]), f"prepacked {key}"
+            assert torch.equal(out3[key], out4[key]), f"power-of-two scales {key}"
+    ref = O.post_int8_pre_fused(f64(inp["x"]), yq["y_q"].numpy(), f64(yq["y_scale"]), f64(inp["coeffs"]),
+                                f64(inp["phi_next"]), f64(inp["bias_next"]), f64(inp["gamma_next"]),
+                                with_mxfp8=mx, **fkw(P))
+    assert np.array_equal(f64(out["x_out"]), ref["x_out"]), "x_out differs from the oracle"
+    assert_coeffs_close(f64(out["coeffs_next"]), ref["coeffs_next"], what="coeffs_next")
+    assert_bf16_close(f64(out["h"]), ref["h"], what="h")
+    if mx:
+        check_mxfp8(out, ref)
+
+
 @pytest.mark.parametrize("T,C", SMALL)
 def test_coeffs(T, C):
     inp = small_inputs(T, C)

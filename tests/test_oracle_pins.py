@@ -689,3 +689,23 @@ def test_post_int8_rounds_the_product_to_binary32_first():
     zero_x, zero_r = np.zeros((T, 4, C)), np.zeros((T, 4, 4))
     assert np.all(O.post_int8(zero_x, q, sc, pw, zero_r)[:, 1] == 324 / 256)
     assert np.all(O.post_int8(zero_x, -q, sc, pw, zero_r)[:, 1] == -324 / 256)
+
+
+def test_post_int8_pre_fused_is_the_fused_pass_on_the_int8_post():
+    # power-of-two scales make y = q * 2**k exact bf16 values: the int8 fused
+    # pass is then the bf16 fused pass, and its x_out is post_int8's
+    rng = np.random.default_rng(47)
+    T, C = 5, 1024
+    q = rng.integers(-128, 128, (T, C))
+    k = rng.integers(-12, 2, T)
+    x = _bf16_values((T, 4, C), rng)
+    cf = O.f32_round(O.coeffs(x, rng.standard_normal((4 * C, 24)) * 0.02, rng.standard_normal(24) * 0.1, **_kw()))
+    phi, bias = rng.standard_normal((4 * C, 24)) * 0.02, rng.standard_normal(24) * 0.1
+    gamma = 1.0 + rng.standard_normal(C) * 0.05
+    fkw = dict(hc_norm_eps=EPS, rmsnorm_eps=EPS, hc_post_scale=S, sinkhorn_eps=EPS, with_mxfp8=True)
+    got = O.post_int8_pre_fused(x, q, np.ldexp(1.0, k), cf, phi, bias, gamma, **fkw)
+    want = O.post_pre_fused(x, np.ldexp(q.astype(np.float64), k[:, None]), cf, phi, bias, gamma, **fkw)
+    for key in want:
+        assert np.array_equal(got[key], want[key]), key
+    _, pw, res = O.split_coeffs(cf)
+    assert np.array_equal(got["x_out"], O.post_int8(x, q, np.ldexp(1.0, k), pw, res))
