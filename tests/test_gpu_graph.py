@@ -16,7 +16,7 @@ import torch
 
 import manifold_constrained_hyper_mhc_amd as mhc
 from manifold_constrained_hyper_mhc_amd import binding
-from manifold_constrained_hyper_mhc_amd.synthetic import make_inputs
+from manifold_constrained_hyper_mhc_amd.synthetic import make_inputs, make_int8_y
 
 pytestmark = pytest.mark.gpu
 
@@ -78,3 +78,44 @@ def test_graph_replays_match_eager(T, C, sched, mx, monkeypatch):
         for k, v in ref.items():
             assert torch.equal(got[k], v), f"replay {rep}: {k} differs from the eager step"
     assert mhc.workspace_error(ws) == 0, "a bounded wait expired"
+
+
+def test_graph_replays_int8_fused_and_broadcast_pre():
+    # the int8-input fused pass and the broadcast first-layer pre, captured
+    # together, replay bit for bit
+    T, C = 300, 7168
+    d = make_inputs(T, C, seed=23, rows="outliers", device=DEV)
+    yq = make_int8_y(T, C, seed=4, device=DEV)
+    ws = mhc.workspace(T, C, DEV, fresh=True)
+    ws2 = mhc.workspace(T, C, DEV, fresh=True)
+    cin = mhc.coeffs(d["x"], d["phi"], d["bias"], ws=ws)
+    packed = mhc.pack_phi(d["phi_next"])
+    x0 = d["x"][:, 0, :].contiguous()
+    outs = {"x_out": torch.empty((T, 4, C), dtype=torch.bfloat16, device=DEV),
+            "coeffs_next": torch.empty((T, 24), dtype=torch.float32, device=DEV),
+            "h": torch.empty((T, C), dtype=torch.bfloat16, device=DEV)}
+    cf0 = torch.empty((T, 24), dtype=torch.float32, device=DEV)
+    h0 = torch.empty((T, C), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        mhc.post_int8_pre_fused(d["x"], yq["y_q"], yq["y_scale"], cin, None, d["bias_next"], d["gamma_next"],
+                                ws=ws, outs=outs, phi_packed=packed)
+        mhc.pre_broadcast(x0, None, d["bias_next"], d["gamma_next"], ws=ws2, coeffs_out=cf0, h_out=h0,
+                          phi_packed=packed)
+
+    step()
+    torch.cuda.synchronize()
+    got = dict(outs, cf0=cf0, h0=h0)
+    ref = {k: v.clone() for k, v in got.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in got.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(got[k], v), f"replay {rep}: {k} differs from the eager step"
+    assert mhc.workspace_error(ws) == 0 and mhc.workspace_error(ws2) == 0, "a bounded wait expired"
