@@ -383,7 +383,7 @@ def main() -> int:
         return 2
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path is not built "
-                                   "(every token is independent: see DESIGN.md for how it would shard)",
+                                   "(every token is independent, so each GPU would run this same launch on its share of the tokens)",
                           "n_gpus": args.gpus}))
         return 2
 
