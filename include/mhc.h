@@ -61,7 +61,10 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 1
+/* 1: coefficients, pre, post, fused post -> pre, packing, workspace.
+ * 2: adds mhc_pre_broadcast(_prepacked), mhc_post_int8 and
+ *    mhc_post_int8_pre_fused(_prepacked); every version-1 call is unchanged. */
+#define MHC_ABI_VERSION 2
 #define MHC_NUM_ROUTES 4
 #define MHC_NUM_COEFFS 24
 #define MHC_MAX_TOKENS (1 << 20)  /* [P2] review: the kernel's token limit 2^20 */

@@ -49,7 +49,7 @@ def test_schedule_query():
 
 def test_abi_version_and_strerror():
     L = mhc.lib()
-    assert L.mhc_abi_version() == 1
+    assert L.mhc_abi_version() == 2
     for code in range(9):
         assert L.mhc_strerror(code)
     assert L.mhc_strerror(99) == b"unknown status"
