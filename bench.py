@@ -500,9 +500,12 @@ def main() -> int:
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     kern_sorted = sorted(kern_ms)
+    # a bounded wait that expired makes the outputs of that call invalid: the
+    # run is then not a measurement of the pass
     err_word = int(ws[:4].view(torch.int32).item())
     if err_word != 0:
-        print(f"[bench] WARNING: workspace error word {err_word} (a bounded wait expired)", file=sys.stderr)
+        print(f"[bench] ERROR: workspace error word {err_word}: a bounded wait expired, the outputs are invalid",
+              file=sys.stderr, flush=True)
 
     nbytes = algorithmic_bytes(T, C, mx, with_h)
     achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
@@ -578,8 +581,11 @@ def main() -> int:
         line["post_int8"] = pq
     if unfused is not None:
         line["unfused_chain"] = unfused
+    if err_word != 0:
+        line["invalid"] = f"workspace error word {err_word}: a bounded wait expired during the timed steps"
+        line["value"] = None
     print(json.dumps(line), flush=True)
-    return 0
+    return 3 if err_word != 0 else 0
 
 
 if __name__ == "__main__":

@@ -63,8 +63,10 @@ extern "C" {
 
 /* 1: coefficients, pre, post, fused post -> pre, packing, workspace.
  * 2: adds mhc_pre_broadcast(_prepacked), mhc_post_int8 and
- *    mhc_post_int8_pre_fused(_prepacked); every version-1 call is unchanged. */
-#define MHC_ABI_VERSION 2
+ *    mhc_post_int8_pre_fused(_prepacked); every version-1 call is unchanged.
+ * 3: adds mhc_workspace_check and MHC_ERR_EXPIRED; fused calls recompute the
+ *    pre of tokens whose route combination cancels (see mhc_post_pre_fused). */
+#define MHC_ABI_VERSION 3
 #define MHC_NUM_ROUTES 4
 #define MHC_NUM_COEFFS 24
 #define MHC_MAX_TOKENS (1 << 20)  /* [P2] review: the kernel's token limit 2^20 */
@@ -90,7 +92,9 @@ typedef enum mhc_status {
   MHC_ERR_FLAGS = 5,      /* unknown flag, or outputs inconsistent with flags */
   MHC_ERR_WORKSPACE = 6,  /* workspace NULL, too small or misaligned */
   MHC_ERR_PARAM = 7,      /* a scalar is negative, not finite or out of range */
-  MHC_ERR_HIP = 8         /* a HIP runtime call failed (see mhc_last_hip_error) */
+  MHC_ERR_HIP = 8,        /* a HIP runtime call failed (see mhc_last_hip_error) */
+  MHC_ERR_EXPIRED = 9     /* mhc_workspace_check: a bounded wait of a call that used the
+                             workspace expired, so that call's outputs are invalid */
 } mhc_status;
 
 /* Flags of mhc_post_pre_fused. */
@@ -121,7 +125,10 @@ int mhc_last_hip_error(void);
  * Its first 4 bytes are an error word (uint32): the kernels' waits on other
  * workgroups are bounded, and one that expires sets it nonzero, after which
  * that call's outputs are invalid.  Calls never clear it; mhc_workspace_init
- * does.  The caller reads it after synchronising with `stream`.
+ * does.  mhc_workspace_check reads it.  A caller that cannot rule out other
+ * work occupying compute units while a persistent-schedule call runs (see
+ * Schedule below: kernels on other streams, other processes on the GPU)
+ * must check the word before it uses that call's outputs.
  *
  * Schedule.  When 32 <= C/128 <= 64 and T spans enough 32-token tiles
  * (two per stream workgroup), these two calls run a persistent kernel: one
@@ -135,6 +142,14 @@ int mhc_last_hip_error(void);
  * schedule's MXFP8 codes are the exact encoding of its own bf16 h.
  * ------------------------------------------------------------------------- */
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags);
+/* Reads the workspace's error word: enqueues a 4-byte device-to-host copy on
+ * `stream` and synchronises with it (the only synchronising call of the
+ * library; it is not for graph capture).  Returns MHC_OK when no bounded wait
+ * of any call that used the workspace since its last mhc_workspace_init has
+ * expired, MHC_ERR_EXPIRED when one has (those calls' outputs are invalid;
+ * mhc_workspace_init clears the word), MHC_ERR_WORKSPACE for a NULL or
+ * misaligned workspace, MHC_ERR_HIP if the copy or the synchronisation fails. */
+int mhc_workspace_check(const void* workspace, void* stream);
 /* Which kernel mhc_coeffs and mhc_post_pre_fused run for T tokens and
  * channel count C on the current device under the current MHC_SCHEDULE:
  * writes MHC_SCHEDULE_STAGED or MHC_SCHEDULE_PERSISTENT to *schedule.
@@ -228,6 +243,15 @@ int mhc_post_int8(const uint16_t* x, const int8_t* y_q, const float* y_scale, co
  * -127 for an all-zero block), h_scale = e + 127, h_fp8 = e4m3fn_rne(h * 2^-e).
  * h may be NULL when MHC_FLAG_MXFP8 is set; h_fp8 and h_scale are required
  * with the flag and must be NULL without it.
+ * The fused pass takes sum_c g^2 of the pre from the route Gram matrix
+ * G_ij = sum_c x'_i x'_j as pre^T G pre, which shares the pass with the
+ * coefficients ([P1] "What this fixes": the sum of squares fused into post).
+ * Where the routes of g = sum_i pre_i x'_i cancel (pre^T G pre <= B / 64,
+ * B = (sum_i |pre_i| sqrt(G_ii))^2), that difference of large fp32 terms is
+ * not accurate enough; such tokens are listed in the workspace and a second
+ * kernel, always enqueued after the pass, recomputes their h (and MXFP8
+ * blocks) from x_out directly in binary64.  An exactly cancelling
+ * combination (g = 0) gives h = 0.
  * ------------------------------------------------------------------------- */
 int mhc_post_pre_fused(const uint16_t* x, const uint16_t* y, const float* coeffs,
                        const float* phi_next, const float* bias_next, const float* gamma_next,

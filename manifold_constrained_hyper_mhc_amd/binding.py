@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libmhc.so")
 FLAG_MXFP8 = 1
 FLAG_RECOMPUTE_X = 2
 _STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_ALIGN", 4: "MHC_ERR_ALIAS",
-           5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP"}
+           5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP", 9: "MHC_ERR_EXPIRED"}
+ERR_EXPIRED = 9
 
 
 class MhcParams(ctypes.Structure):
@@ -57,6 +58,7 @@ _SIG = {
     "mhc_last_hip_error": ([], ctypes.c_int),
     "mhc_workspace_bytes": ([_I64, _I64, ctypes.c_uint], ctypes.c_size_t),
     "mhc_workspace_init": ([_P, ctypes.c_size_t, _P], ctypes.c_int),
+    "mhc_workspace_check": ([_P, _P], ctypes.c_int),
     "mhc_phi_packed_bytes": ([_I64], ctypes.c_size_t),
     "mhc_schedule": ([_I64, _I64, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "mhc_pack_phi": ([_P, _I64, _P, _P], ctypes.c_int),
@@ -161,6 +163,14 @@ def schedule(T: int, C: int) -> str:
     out = ctypes.c_int(-1)
     _check(lib().mhc_schedule(T, C, ctypes.byref(out)), "mhc_schedule")
     return "persistent" if out.value == 1 else "staged"
+
+
+def check(ws: torch.Tensor) -> None:
+    """Raise MhcError (MHC_ERR_EXPIRED) if a bounded wait of any call that used
+    the workspace ``ws`` has expired since it was cleared: those calls'
+    outputs are invalid.  Synchronises torch's current stream
+    (mhc_workspace_check), so it belongs after the calls, not between them."""
+    _check(lib().mhc_workspace_check(_ptr(ws), _stream(ws.device)), "mhc_workspace_check")
 
 
 def workspace_error(ws: torch.Tensor) -> int:

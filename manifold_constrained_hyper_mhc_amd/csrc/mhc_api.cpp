@@ -159,6 +159,8 @@ Plan make_plan(int64_t T, int64_t C) {
   off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(uint64_t));
   p.off_own = off;
   off = round256(off + (size_t)p.tiles * p.s * sizeof(uint64_t));
+  p.off_fix = off;
+  off = round256(off + (size_t)T * sizeof(uint32_t));
   p.off_phi = off;
   off = round256(off + phi_packed_bytes(C));
   p.total = off;
@@ -180,6 +182,8 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
+  a.fix_word = reinterpret_cast<uint64_t*>(base + mhc::kWsFixWord);
+  a.fix_list = reinterpret_cast<uint32_t*>(base + plan.off_fix);
   a.T = T;
   a.xts = 4 * C;
   a.xrs = C;
@@ -331,7 +335,9 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   a.h_scale = h_scale;
   a.recompute_x = (flags & MHC_FLAG_RECOMPUTE_X) != 0;
   const int mode = (mx ? mhc::kModeFusedMx : mhc::kModeFused) | (yq ? mhc::kModeYInt8 : 0);
-  return hip_status(mhc::launch_split(run, mode, a, s));
+  if ((rc = hip_status(mhc::launch_split(run, mode, a, s)))) return rc;
+  // tokens whose route combination cancels get their pre recomputed directly
+  return hip_status(mhc::launch_pre_fix(a, mx, s));
 }
 
 }  // namespace
@@ -351,6 +357,7 @@ const char* mhc_strerror(int status) {
     case MHC_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MHC_ERR_PARAM: return "a scalar parameter is out of range";
     case MHC_ERR_HIP: return "a HIP runtime call failed";
+    case MHC_ERR_EXPIRED: return "a bounded wait of a call that used this workspace expired: its outputs are invalid";
     default: return "unknown status";
   }
 }
@@ -370,6 +377,17 @@ int mhc_schedule(int64_t T, int64_t C, int* schedule) {
   choose_kernel(p);
   *schedule = p.lanes > 0 ? MHC_SCHEDULE_PERSISTENT : MHC_SCHEDULE_STAGED;
   return MHC_OK;
+}
+
+int mhc_workspace_check(const void* workspace, void* stream) {
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return MHC_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  int rc = hip_status(hipMemcpyAsync(&word, static_cast<const char*>(workspace) + mhc::kWsErr, sizeof(word),
+                                     hipMemcpyDeviceToHost, s));
+  if (rc) return rc;
+  if ((rc = hip_status(hipStreamSynchronize(s)))) return rc;
+  return word != 0u ? MHC_ERR_EXPIRED : MHC_OK;
 }
 
 int mhc_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {

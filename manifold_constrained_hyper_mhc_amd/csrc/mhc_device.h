@@ -125,6 +125,32 @@ __device__ __forceinline__ float gram_quadratic(const float* G, const float* p) 
   return diag + 2.0f * off;
 }
 
+// When the routes of the pre combination cancel, p^T G p is a small
+// difference of large fp32 terms.  Each Gram entry carries an absolute error
+// of at most n u sum_c |x_i x_j| <= n u sqrt(G_ii G_jj) (n fp32 additions on
+// its longest path, at most ~170 for C <= 16384, u = 2^-24), so the error of
+// p^T G p is bounded by about (n + 12) u B with
+//   B = (sum_i |p_i| sqrt(G_ii))^2,
+// i.e. ~1.1e-5 B.  A token with p^T G p <= B / 64 could carry a relative
+// error above 1e-3 in its sum of squares; such a token is flagged and its
+// pre is recomputed from x' directly (k_pre_fix).  Independent routes give
+// p^T G p / B >= 1/4, so only strongly cancelling combinations are flagged.
+constexpr float kCancelRatio = 1.0f / 64.0f;
+__device__ __forceinline__ float gram_bound(const float* G, const float* p) {
+  const float s = __builtin_fabsf(p[0]) * sqrtf(G[0]) + __builtin_fabsf(p[1]) * sqrtf(G[1]) +
+                  __builtin_fabsf(p[2]) * sqrtf(G[2]) + __builtin_fabsf(p[3]) * sqrtf(G[3]);
+  return s * s;
+}
+// The RMSNorm factor of the fused pre from the Gram matrix (the quadratic
+// form clamped at 0, so that rounding never takes the square root of a
+// negative number) and whether the token needs the direct recomputation.
+__device__ __forceinline__ float gram_rms_factor(const float* G, const float* p, int C, float eps, bool& cancels) {
+  const float gq = gram_quadratic(G, p);
+  const float gb = gram_bound(G, p);
+  cancels = gb > 0.0f && !(gq > kCancelRatio * gb);
+  return 1.0f / sqrtf(__builtin_fmaxf(gq, 0.0f) / (float)C + eps);
+}
+
 // ---------------------------------------------------------------------------
 // MXFP8: UE8M0 exponent of a block from the bits of its bf16 amax, and the
 // OCP e4m3fn codes of the scaled values, round-to-nearest-even.

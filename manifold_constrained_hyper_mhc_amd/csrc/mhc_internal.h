@@ -29,15 +29,16 @@ struct Plan {
   int lanes = 0;   // persistent kernel: stream workgroups per split (0: staged kernel)
   int64_t tiles = 0;
   // workspace layout (byte offsets)
-  size_t off_pub = 0, off_part = 0, off_own = 0, off_phi = 0, total = 0;
+  size_t off_pub = 0, off_part = 0, off_own = 0, off_fix = 0, off_phi = 0, total = 0;
 };
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
 
 // Workspace header at fixed offsets, whatever the shape of a call: the error
-// word, the launch epoch, the tiles-done counter, then one leave counter per
+// word, the launch epoch, the tiles-done counter, the tagged count of tokens
+// whose fused pre needs the direct recomputation, then one leave counter per
 // possible tile (2^20 tokens / 32 tokens per tile).
-constexpr size_t kWsErr = 0, kWsEpoch = 4, kWsTilesDone = 8;
+constexpr size_t kWsErr = 0, kWsEpoch = 4, kWsTilesDone = 8, kWsFixWord = 16;
 constexpr size_t kWsDep = 256;
 constexpr int64_t kMaxTiles = (int64_t)(1 << 20) / 32;
 constexpr size_t kWsHeaderBytes = kWsDep + (size_t)kMaxTiles * 4;
@@ -80,6 +81,8 @@ struct SplitArgs {
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
   uint64_t* publish;   // [tiles][M][4] tagged words
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
+  uint64_t* fix_word;  // (launch tag << 32) | number of tokens in fix_list (fixed offset)
+  uint32_t* fix_list;  // [T] tokens whose fused pre is recomputed directly (k_pre_fix)
   uint32_t* err;
   const int8_t* y_q;      // int8 y [T][C] and its per-token scales [T] (fused modes with kModeYInt8)
   const float* y_scale;
@@ -114,5 +117,8 @@ hipError_t launch_post_int8(const uint16_t* x, const int8_t* y_q, const float* y
 hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
                       int C, float rmsnorm_eps, uint16_t* h, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// The direct recomputation of the pre of the tokens a fused launch flagged
+// (always launched after it: the flagged count is read on the device).
+hipError_t launch_pre_fix(const SplitArgs& a, bool mx, hipStream_t s);
 
 }  // namespace mhc

@@ -177,6 +177,24 @@ __device__ __forceinline__ float tagged_wait(const uint64_t* p, uint32_t tag, ui
   return tagged_value(w);
 }
 
+// Appends token t to the workspace list of tokens whose fused pre is
+// recomputed directly.  The count is a tagged word: a count left by an
+// earlier launch (older tag) counts as zero, so no launch has to clear it.
+__device__ __forceinline__ void flag_for_fix(const SplitArgs& a, uint32_t tag, int64_t t) {
+  uint64_t old = __hip_atomic_load(a.fix_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t idx;
+  for (;;) {
+    const bool cur = (uint32_t)(old >> 32) == tag;
+    const uint64_t nw = cur ? old + 1u : (((uint64_t)tag << 32) | 1u);
+    if (__hip_atomic_compare_exchange_strong(a.fix_word, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      idx = cur ? (uint32_t)old : 0u;
+      break;
+    }
+  }
+  if ((int64_t)idx < a.T) a.fix_list[idx] = (uint32_t)t;
+}
+
 // DPP lane moves inside rows of 16 lanes (no LDS traffic): quad_perm swaps
 // within groups of 4 lanes, row_ror rotates the 16-lane row.
 #define MHC_DPP(v, ctrl) __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
@@ -191,9 +209,10 @@ constexpr int kDppRowRor8 = 0x128;   // row_ror:8
 // the 4x4 matrix are sums over lane ^ {1, 2}, column sums over the 16-lane
 // row rotated by 4, 8, 12.  Each normalisation multiplies by the reciprocal
 // of (sum + eps).  Returns in every lane the value of coefficient
-// slot(lane).  In the fused modes publish(q), q_i = pre_i * r_h, runs
-// before the Sinkhorn iterations: the pre step needs only q, so it does not
-// wait for them.
+// slot(lane).  In the fused modes publish(q, cancels), q_i = pre_i * r_h,
+// runs before the Sinkhorn iterations: the pre step needs only q, so it does
+// not wait for them; `cancels` says that the token's pre must be recomputed
+// directly (gram_rms_factor).
 template <bool FUSED, class Publish>
 __device__ __forceinline__ float finalize_wave(const float* sums, const float* bias, int C, const Scalars& sc,
                                                int lane, Publish&& publish) {
@@ -209,10 +228,10 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 17)),
                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 18)),
                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pp), 19))};
-    const float gq = gram_quadratic(sums + 24, p);
-    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
+    bool cancels;
+    const float rh = gram_rms_factor(sums + 24, p, C, sc.rmsnorm_eps, cancels);
     const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
-    publish(q);
+    publish(q, cancels);
   }
   const float eps = sc.sinkhorn_eps;
   for (int it = 0; it < sc.sinkhorn_iters; ++it) {
@@ -231,7 +250,7 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
 // of the row's token and, for k < 8, its pre (k < 4) or post (4 <= k < 8)
 // weight.  The Sinkhorn row and column sums are the same row-local DPP
 // moves, so the four rows run side by side.  sums: this lane's token.
-// publish(q) of the fused modes runs before the Sinkhorn iterations.
+// publish(q, cancels) of the fused modes runs before the Sinkhorn iterations.
 template <bool FUSED, class Publish>
 __device__ __forceinline__ void finalize_rows(const float* sums, const float* bias, int C, const Scalars& sc,
                                               int lane, float& res, float& pp, Publish&& publish) {
@@ -244,10 +263,10 @@ __device__ __forceinline__ void finalize_rows(const float* sums, const float* bi
   if constexpr (FUSED) {
     const int row0 = lane & 48;
     const float p[4] = {__shfl(pp, row0), __shfl(pp, row0 + 1), __shfl(pp, row0 + 2), __shfl(pp, row0 + 3)};
-    const float gq = gram_quadratic(sums + 24, p);
-    const float rh = 1.0f / sqrtf(gq / (float)C + sc.rmsnorm_eps);
+    bool cancels;
+    const float rh = gram_rms_factor(sums + 24, p, C, sc.rmsnorm_eps, cancels);
     const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
-    publish(q);
+    publish(q, cancels);
   }
   const float l = r * sums[8 + k] + bias[8 + k];
   float v = expf(l);
@@ -644,11 +663,12 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
       if (kq < ntok) {
         const int m = split + kq * S;
         uint64_t* const qdst = a.publish + ((int64_t)tR * TM + m) * 4 + (lane & 3);
-        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, C, a.sc, lane,
-                                              [=](const float* q) __attribute__((always_inline)) {
-                                                if (lane < 4) tagged_store(qdst, q[lane & 3], tag);
-                                              });
         const int64_t t = tok0 + m;
+        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, C, a.sc, lane,
+                                              [=](const float* q, bool cancels) __attribute__((always_inline)) {
+                                                if (lane < 4) tagged_store(qdst, q[lane & 3], tag);
+                                                if (cancels && lane == 0 && t < a.T) flag_for_fix(a, tag, t);
+                                              });
         if (t < a.T && lane < 24) a.coeffs_out[t * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
       }
     }
@@ -952,7 +972,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
         const int64_t tok = (int64_t)t * TM + ml;
         float res, pp;
-        finalize_rows<false>(finw + ml * NV, a.bias, C, a.sc, lane, res, pp, [](const float*) {});
+        finalize_rows<false>(finw + ml * NV, a.bias, C, a.sc, lane, res, pp, [](const float*, bool) {});
         if (tok < a.T) {
           a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
           if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
@@ -986,10 +1006,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           // every row of the tile is published ([tiles][TM][4] words): the
           // stream workgroups poll whole row blocks, padding rows included
           finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp,
-                               [&](const float* q) __attribute__((always_inline)) {
+                               [&](const float* q, bool cancels) __attribute__((always_inline)) {
                                  if (kk < 4)
                                    tagged_store(a.publish + tok * 4 + kk,
                                                 kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], tag);
+                                 if (cancels && kk == 0 && tok < a.T) flag_for_fix(a, tag, tok);
                                });
           if (tok < a.T) {
             a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
@@ -1664,9 +1685,21 @@ __device__ __forceinline__ float block128_sum(float v, float* sh) {
   return sh[0] + sh[1];
 }
 
-// B: a broadcast stream (route stride 0): the 4 routes are one load
+// g = ((p0 x0 + p1 x1) + p2 x2) + p3 x3 in binary64: the product of an fp32
+// weight and a bf16 value is exact there, so routes that cancel exactly give
+// exactly 0 and nearly cancelling ones keep their leading bits.
+__device__ __forceinline__ double combine_f64(const double* p, float x0, float x1, float x2, float x3) {
+  double g = p[0] * (double)x0;
+  g = __builtin_fma(p[1], (double)x1, g);
+  g = __builtin_fma(p[2], (double)x2, g);
+  g = __builtin_fma(p[3], (double)x3, g);
+  return g;
+}
+
+// B: a broadcast stream (route stride 0): the 4 routes are one load.
+// g is combined in binary64 and kept as its nearest fp32 value.
 template <bool B>
-__device__ __forceinline__ void pre_group(const uint16_t* xr, int64_t xrs, int c, const float* p, float* gv) {
+__device__ __forceinline__ void pre_group(const uint16_t* xr, int64_t xrs, int c, const double* p, float* gv) {
   float xv[4][8];
   if constexpr (B) {
     unpack8(ld16_stream(xr + c), xv[0]);
@@ -1679,13 +1712,7 @@ __device__ __forceinline__ void pre_group(const uint16_t* xr, int64_t xrs, int c
     for (int i = 0; i < 4; ++i) unpack8(ld16_stream(xr + (int64_t)i * xrs + c), xv[i]);
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float v = p[0] * xv[0][e];
-    v = __builtin_fmaf(p[1], xv[1][e], v);
-    v = __builtin_fmaf(p[2], xv[2][e], v);
-    v = __builtin_fmaf(p[3], xv[3][e], v);
-    gv[e] = v;
-  }
+  for (int e = 0; e < 8; ++e) gv[e] = (float)combine_f64(p, xv[0][e], xv[1][e], xv[2][e], xv[3][e]);
 }
 
 __device__ __forceinline__ void pre_store(uint16_t* hr, const float* gamma, int c, const float* gv, float rh) {
@@ -1706,7 +1733,7 @@ __global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, int
   const int64_t t = blockIdx.x;
   const int k = threadIdx.x;
   const float4 pq = *reinterpret_cast<const float4*>(cf + t * kCoeffs);
-  const float p[4] = {pq.x, pq.y, pq.z, pq.w};
+  const double p[4] = {pq.x, pq.y, pq.z, pq.w};
   const uint16_t* xr = x + t * xts;
   float gv[G][8];
   float ss = 0.0f;
@@ -1731,7 +1758,7 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
   const int64_t t = blockIdx.x;
   const int k = threadIdx.x;
   const float4 pq = *reinterpret_cast<const float4*>(cf + t * kCoeffs);
-  const float p[4] = {pq.x, pq.y, pq.z, pq.w};
+  const double p[4] = {pq.x, pq.y, pq.z, pq.w};
   const uint16_t* xr = x + t * xts;
   const int G = C >> 10;
   float ss = 0.0f;
@@ -1748,6 +1775,85 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
     float gv[8];
     pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, gv);
     pre_store(hr, gamma, (j * 128 + k) * 8, gv, rh);
+  }
+}
+
+// ===========================================================================
+// Direct pre of the tokens a fused launch flagged (gram_rms_factor): their
+// route combination cancels, so the sum of squares from the Gram matrix is
+// not accurate enough.  One workgroup per flagged token (grid-stride over
+// the list): g from x' = x_out and pre' = coeffs_next[0..3] in binary64,
+// sum_c g^2 in binary64, then h (and its MXFP8 blocks) rewritten.  The count
+// is read on the device, so the kernel is always launched after a fused pass
+// (an empty list costs one launch) and the pair can be captured in a graph.
+// ===========================================================================
+template <bool MX>
+__global__ __launch_bounds__(256) void k_pre_fix(const SplitArgs a) {
+  __shared__ double part[4];
+  __shared__ uint32_t s_n;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    // the fused launch that just ended left its own tag in the epoch
+    const uint32_t tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w = __hip_atomic_load(a.fix_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t n = (uint32_t)(w >> 32) == tag ? (uint32_t)w : 0u;
+    s_n = (int64_t)n < a.T ? n : (uint32_t)a.T;
+  }
+  __syncthreads();
+  const uint32_t n = s_n;
+  const int C = a.C, nch = C >> 3;
+  for (uint32_t k = blockIdx.x; k < n; k += gridDim.x) {
+    const int64_t t = a.fix_list[k];
+    const float4 pq = *reinterpret_cast<const float4*>(a.coeffs_out + t * kCoeffs);
+    const double p[4] = {pq.x, pq.y, pq.z, pq.w};
+    const uint16_t* xr = a.x_out + t * (int64_t)(4 * C);
+    double ss = 0.0;
+    for (int j = tid; j < nch; j += 256) {
+      float xv[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unpack8(ld16(xr + (int64_t)i * C + 8 * j), xv[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double g = combine_f64(p, xv[0][e], xv[1][e], xv[2][e], xv[3][e]);
+        ss = __builtin_fma(g, g, ss);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const double rh = 1.0 / sqrt((((part[0] + part[1]) + part[2]) + part[3]) / (double)C + (double)a.sc.rmsnorm_eps);
+    for (int j = tid; j < nch; j += 256) {
+      float xv[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unpack8(ld16(xr + (int64_t)i * C + 8 * j), xv[i]);
+      const float4* gp = reinterpret_cast<const float4*>(a.gamma + 8 * j);
+      const float4 g0 = gp[0], g1 = gp[1];
+      const float gmv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      float hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        hv[e] = (float)(combine_f64(p, xv[0][e], xv[1][e], xv[2][e], xv[3][e]) * rh * (double)gmv[e]);
+      const u32x4_t hb = pack8(hv);
+      if (a.h != nullptr) st16(a.h + t * (int64_t)C + 8 * j, hb);
+      if constexpr (MX) {
+        // a 32-channel block is the chunks 4b .. 4b+3: lanes tid ^ {1, 2}
+        float hr[8];
+        unpack8(hb, hr);
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+        const int ex = mx_scale_exponent(amax);
+        const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
+        const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
+        const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
+        *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + 8 * j) = u32x2_t{w0, w1};
+        if ((j & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (j >> 2)] = (uint8_t)(ex + 127);
+      }
+    }
+    __syncthreads();  // part[] is reused by the next token
   }
 }
 
@@ -1854,6 +1960,17 @@ hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* 
     launch_pre_b<true>(x, xts, xrs, cf, gamma, T, C, eps, h, s);
   } else {
     launch_pre_b<false>(x, xts, xrs, cf, gamma, T, C, eps, h, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pre_fix(const SplitArgs& a, bool mx, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.T < 128 ? a.T : 128);
+  if (grid == 0) return hipSuccess;
+  if (mx) {
+    k_pre_fix<true><<<dim3(grid), dim3(256), 0, s>>>(a);
+  } else {
+    k_pre_fix<false><<<dim3(grid), dim3(256), 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -91,13 +91,13 @@ def make_inputs(T: int, C: int, *, seed: int = 0, rows: str = "normal",
 
 def make_int8_y(T: int, C: int, *, seed: int = 0, device="cpu", decades: tuple = (-3.0, 1.0)) -> dict:
     """An int8 sublayer output with per-token scales, drawn from
-    ``torch.Generator(seed)``: y_q [T, C] int8 uniform in [-127, 127] and
-    y_scale [T] fp32 = 10**U(*decades) / 127 (full binary32 mantissas, so the
-    dequantised products round)."""
+    ``torch.Generator(seed)``: y_q [T, C] int8 uniform over every code,
+    [-128, 127], and y_scale [T] fp32 = 10**U(*decades) / 127 (full binary32
+    mantissas, so the dequantised products round)."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(int(seed))
-    y_q = torch.randint(-127, 128, (T, C), generator=g, device=dev, dtype=torch.int8)
+    y_q = torch.randint(-128, 128, (T, C), generator=g, device=dev, dtype=torch.int8)
     lo, hi = decades
     u = torch.rand((T,), generator=g, device=dev, dtype=torch.float64)
     y_scale = (torch.pow(10.0, lo + (hi - lo) * u) / 127.0).to(torch.float32)

@@ -49,10 +49,17 @@ def test_schedule_query():
 
 def test_abi_version_and_strerror():
     L = mhc.lib()
-    assert L.mhc_abi_version() == 2
-    for code in range(9):
-        assert L.mhc_strerror(code)
+    assert L.mhc_abi_version() == 3
+    for code in range(10):
+        assert L.mhc_strerror(code) != b"unknown status"
     assert L.mhc_strerror(99) == b"unknown status"
+
+
+def test_workspace_check_validation():
+    # argument errors come back before any HIP call
+    L = mhc.lib()
+    assert L.mhc_workspace_check(None, None) == 6          # MHC_ERR_WORKSPACE
+    assert L.mhc_workspace_check(fake(0, 16), None) == 6   # not 256-byte aligned
 
 
 def test_sizes():

@@ -7,8 +7,10 @@ comes from the HIP path.
 
 Bars (tests/_compare.py): coefficients within 1e-4 relative, elementwise;
 bf16 outputs within 1e-2 of max(|oracle|, row RMS); x_out bit-exact (its bf16
-rounding is decided by the same binary32 chain on both sides); MXFP8 codes
-and scales bit-exact on every block whose bf16 h equals the oracle's.
+rounding is decided by the same binary32 chain on both sides) and within the
+bf16 bar of the plain definition (the exact sum rounded once); MXFP8 codes
+and scales bit-exact, on every block, against the oracle's encoding of the
+GPU's own bf16 h.
 Small cases compare every element; the full-size workloads (the launch
 configuration the benchmark times) compare a sample of tokens, which the
 oracle computes one row at a time.
@@ -72,6 +74,10 @@ SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048)]
 # shapes the persistent schedule takes (32 <= C/128 <= 64, enough tiles),
 # with a ragged last tile
 PERSISTENT = [(300, 7168), (500, 4096)]
+# the other hidden sizes each schedule accepts: S = 40 and 48 splits (5 and 4
+# stream workgroups per split), S = 64 (the persistent kernel's limit; the
+# staged kernel's long reduce runs), and C = 16384 (staged only, S = 128)
+WIDE = [(400, 5120), (300, 6144), (300, 8192), (300, 16384)]
 
 
 def test_schedule_choice(monkeypatch):
@@ -93,6 +99,11 @@ def schedule(request, monkeypatch):
     torch.cuda.synchronize()
     for ws in list(mhc.binding._WS.values()):
         assert mhc.workspace_error(ws) == 0, "a bounded wait expired"
+
+
+def skip_unless_schedule(T, C, schedule):
+    if mhc.schedule(T, C) != schedule:
+        pytest.skip(f"the {schedule} schedule does not take T={T}, C={C}")
 
 
 # ---------------------------------------------------------------------------
@@ -188,6 +199,7 @@ def check_fused(inp, out, p=P, mx=False, rows=None):
                            f64(inp["bias_next"]), f64(inp["gamma_next"]), with_mxfp8=mx, **fkw(p))
     g = {k: (v[sel] if v is not None and rows is not None else v) for k, v in out.items()}
     assert np.array_equal(f64(g["x_out"]), ref["x_out"]), "x_out differs from the oracle"
+    check_x_out_exact(inp, g["x_out"], sel)
     assert_coeffs_close(f64(g["coeffs_next"]), ref["coeffs_next"], what="coeffs_next")
     if g["h"] is not None:
         assert_bf16_close(f64(g["h"]), ref["h"], what="h")
@@ -196,17 +208,24 @@ def check_fused(inp, out, p=P, mx=False, rows=None):
     return ref
 
 
+def check_x_out_exact(inp, x_out, sel=slice(None)):
+    """x_out against the plain definition of post (the exact sum, rounded
+    once to bf16) under the bf16 bar: the binary32 rounding decision of R20
+    moves an element by at most one bf16 step."""
+    _, pw, res = O.split_coeffs(f64(inp["coeffs"][sel]))
+    ex = O.post_exact(f64(inp["x"][sel]), f64(inp["y"][sel]), pw, res)
+    assert_bf16_close(f64(x_out), ex, what="x_out vs the exact post")
+
+
 def check_mxfp8(g, ref):
+    """MXFP8 codes and scales: on every block, the oracle's encoding of the
+    GPU's own bf16 h, bit for bit; and the decoded values near the oracle's h."""
     T, C = ref["h"].shape
     q = g["h_fp8"].cpu().numpy()
     sc = g["h_scale"].cpu().numpy()
-    hg = f64(g["h"]).reshape(T, C // 32, 32)
-    same = np.all(hg == ref["h"].reshape(T, C // 32, 32), axis=2) & \
-        np.all(np.signbit(hg) == np.signbit(ref["h"].reshape(T, C // 32, 32)), axis=2)
-    assert same.mean() > 0.95, f"only {same.mean():.3f} of the blocks have identical bf16 h"
-    assert np.array_equal(sc[same], ref["h_scale"][same])
-    qb, rb = q.reshape(T, C // 32, 32), ref["h_fp8"].reshape(T, C // 32, 32)
-    assert np.array_equal(qb[same], rb[same])
+    qo, so = O.mxfp8(f64(g["h"]))
+    assert np.array_equal(sc, so), "MXFP8 scales differ from the encoding of the GPU's h"
+    assert np.array_equal(q, qo), "MXFP8 codes differ from the encoding of the GPU's h"
     # every block: the codes decode to the oracle's h within half an e4m3 step
     # plus the bf16 tolerance of h
     e = sc.astype(np.int64) - 127
@@ -217,8 +236,9 @@ def check_mxfp8(g, ref):
     assert np.all(np.abs(dec - ho) <= bound)
 
 
-@pytest.mark.parametrize("T,C", PERSISTENT)
+@pytest.mark.parametrize("T,C", PERSISTENT + WIDE)
 def test_coeffs_schedules(T, C, schedule):
+    skip_unless_schedule(T, C, schedule)
     inp = small_inputs(T, C, seed=11)
     d = to_dev(inp)
     cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
@@ -228,8 +248,9 @@ def test_coeffs_schedules(T, C, schedule):
 
 
 @pytest.mark.parametrize("mx", [False, True])
-@pytest.mark.parametrize("T,C", PERSISTENT)
+@pytest.mark.parametrize("T,C", PERSISTENT + WIDE)
 def test_fused_schedules(T, C, mx, schedule):
+    skip_unless_schedule(T, C, schedule)
     inp = small_inputs(T, C, seed=12)
     d = to_dev(inp)
     out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=mx)
@@ -302,9 +323,60 @@ def test_identity_post_is_exact():
     check_fused(inp, out)
 
 
+@pytest.mark.parametrize("T,C", [(37, 3072), (300, 7168)])
+def test_power_of_two_scale_invariance(T, C, schedule):
+    # with both eps at 0, scaling the stream and the sublayer output by 2^k
+    # scales every sum by a power of two exactly: the coefficients and h are
+    # bitwise unchanged and x_out is scaled exactly
+    p = Params(hc_norm_eps=0.0, rmsnorm_eps=0.0)
+    inp = small_inputs(T, C, seed=21)
+    d = to_dev(inp)
+    outs, cfs = [], []
+    for k in (0, 3, -5):
+        s = 2.0 ** k
+        xs, ys = (d["x"].float() * s).to(torch.bfloat16), (d["y"].float() * s).to(torch.bfloat16)
+        assert torch.equal(xs.float() / s, d["x"].float())
+        outs.append(mhc.post_pre_fused(xs, ys, d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], p,
+                                       mxfp8=True))
+        cfs.append(mhc.coeffs(xs, d["phi"], d["bias"], p))
+    torch.cuda.synchronize()
+    for o, k in zip(outs[1:], (3, -5)):
+        assert torch.equal(o["coeffs_next"], outs[0]["coeffs_next"])
+        assert torch.equal(o["h"], outs[0]["h"])
+        assert torch.equal(o["h_fp8"], outs[0]["h_fp8"]) and torch.equal(o["h_scale"], outs[0]["h_scale"])
+        assert torch.equal(o["x_out"].float(), outs[0]["x_out"].float() * 2.0 ** k)
+    for c in cfs[1:]:
+        assert torch.equal(c, cfs[0])
+    check_fused(inp, outs[0], p, mx=True)
+
+
 # ---------------------------------------------------------------------------
 # library behaviour
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,C,sched", [(37, 3072, "staged"), (300, 7168, "persistent")])
+def test_expired_wait_is_reported(T, C, sched, monkeypatch):
+    # The error word is set from the host before the call, standing in for a
+    # bounded wait that expired (every kernel still runs to its end: the
+    # persistent kernel's waits give up once they see the word).  The checked
+    # path must report the call's outputs as invalid until the workspace is
+    # cleared again.
+    monkeypatch.setenv("MHC_SCHEDULE", sched)
+    assert mhc.schedule(T, C) == sched
+    inp = small_inputs(T, C, seed=2)
+    d = to_dev(inp)
+    ws = mhc.workspace(T, C, DEV, fresh=True)
+    mhc.check(ws)
+    ws[0] = 1
+    mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], ws=ws)
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.check(ws)
+    assert e.value.status == mhc.ERR_EXPIRED
+    assert mhc.lib().mhc_workspace_init(ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream) == 0
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], ws=ws)
+    mhc.check(ws)
+    check_fused(inp, out)
+
+
 def test_prepacked_is_bitwise_identical():
     inp = small_inputs(45, 3072)
     d = to_dev(inp)
@@ -409,7 +481,7 @@ def full_inputs(name, seed=0):
     return d
 
 
-def sample_rows(T, extra=(), n=24, seed=1):
+def sample_rows(T, extra=(), n=64, seed=1):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(T, size=n, replace=False).tolist()) | {0, T - 1, T - 2} | set(int(v) for v in extra)
     return np.array(sorted(rows))
@@ -425,7 +497,7 @@ def test_prefill_workload_sampled(schedule):
     d = full_inputs("prefill")
     out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"])
     torch.cuda.synchronize()
-    rows = sample_rows(8192, extra=d["outlier_rows"][:8].tolist())
+    rows = sample_rows(8192, extra=d["outlier_rows"].tolist())  # every outlier row
     inp = host_rows(d, rows)
     idx = torch.from_numpy(rows).to(DEV)
     g = {k: (v.index_select(0, idx) if v is not None else None) for k, v in out.items()}
@@ -457,7 +529,7 @@ def test_long_workload_sampled(schedule):
     h = mhc.pre(d["x"], d["coeffs"], d["gamma"])
     xo = mhc.post(d["x"], d["y"], d["coeffs"])
     torch.cuda.synchronize()
-    rows = sample_rows(T, n=16)
+    rows = sample_rows(T, n=48)
     inp = host_rows(d, rows)
     idx = torch.from_numpy(rows).to(DEV)
     assert_coeffs_close(f64(cf.index_select(0, idx)),
