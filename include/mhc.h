@@ -65,13 +65,17 @@ extern "C" {
  * 2: adds mhc_pre_broadcast(_prepacked), mhc_post_int8 and
  *    mhc_post_int8_pre_fused(_prepacked); every version-1 call is unchanged.
  * 3: adds mhc_workspace_check and MHC_ERR_EXPIRED; fused calls recompute the
- *    pre of tokens whose route combination cancels (see mhc_post_pre_fused). */
-#define MHC_ABI_VERSION 3
+ *    pre of tokens whose route combination cancels (see mhc_post_pre_fused).
+ * 4: adds mhc_post_pre_fused_prepacked_static and MHC_ERR_SCRATCH. */
+#define MHC_ABI_VERSION 4
 #define MHC_NUM_ROUTES 4
 #define MHC_NUM_COEFFS 24
 #define MHC_MAX_TOKENS (1 << 20)  /* [P2] review: the kernel's token limit 2^20 */
 #define MHC_MAX_HIDDEN 16384 /* keeps a row within 128 co-resident workgroups */
 #define MHC_MXFP8_BLOCK 32
+/* Size of the library's static scratch (one per GPU), the workspace of
+ * mhc_post_pre_fused_prepacked_static. */
+#define MHC_STATIC_SCRATCH_BYTES (64u << 20)
 
 /* Scalars of the method, passed by name ([P2] review warns against a
  * positional float tail whose order differs between two paths). */
@@ -93,8 +97,9 @@ typedef enum mhc_status {
   MHC_ERR_WORKSPACE = 6,  /* workspace NULL, too small or misaligned */
   MHC_ERR_PARAM = 7,      /* a scalar is negative, not finite or out of range */
   MHC_ERR_HIP = 8,        /* a HIP runtime call failed (see mhc_last_hip_error) */
-  MHC_ERR_EXPIRED = 9     /* mhc_workspace_check: a bounded wait of a call that used the
+  MHC_ERR_EXPIRED = 9,    /* mhc_workspace_check: a bounded wait of a call that used the
                              workspace expired, so that call's outputs are invalid */
+  MHC_ERR_SCRATCH = 10    /* the call needs more workspace than MHC_STATIC_SCRATCH_BYTES */
 } mhc_status;
 
 /* Flags of mhc_post_pre_fused. */
@@ -279,6 +284,34 @@ int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const flo
                                  float* coeffs_next, uint16_t* h, uint8_t* h_fp8,
                                  uint8_t* h_scale, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mhc_post_pre_fused_prepacked without a workspace argument, for callers that
+ * cannot allocate device memory or size a workspace per call: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * call allocates and frees nothing; its workspace is a static device array of
+ * MHC_STATIC_SCRATCH_BYTES in the library (one per GPU, zero at load, held
+ * until the process ends).  The first call on a device takes the array's
+ * address (hipGetSymbolAddress) and enqueues a clear of it on `stream` before
+ * its own kernels; later calls reuse it as it was left, which the launch tags
+ * make safe (see Workspace above).
+ *   - Arguments, outputs, flags and results are those of
+ *     mhc_post_pre_fused_prepacked (bitwise the same outputs).
+ *   - Limit: the call takes T and C with mhc_workspace_bytes(T, C, flags) <=
+ *     MHC_STATIC_SCRATCH_BYTES (T <= 4064 at C = 7168, 7328 at C = 4096) and returns
+ *     MHC_ERR_SCRATCH, before any HIP call, otherwise.
+ *   - error_word: a caller-owned device uint32 (4-byte aligned, not overlapping
+ *     any other argument), required when T > 0; a bounded wait that expires
+ *     sets it nonzero and the call's outputs are then invalid.  The library
+ *     never clears it.
+ *   - Every call on a GPU shares that GPU's array: calls that may overlap in
+ *     time on one GPU (two streams, two threads) race and must not be issued.
+ * ------------------------------------------------------------------------- */
+int mhc_post_pre_fused_prepacked_static(const uint16_t* x, const uint16_t* y, const float* coeffs,
+                                        const void* phi_next_packed, const float* bias_next, const float* gamma_next,
+                                        int64_t T, int64_t C, const mhc_params* p, unsigned flags, uint16_t* x_out,
+                                        float* coeffs_next, uint16_t* h, uint8_t* h_fp8, uint8_t* h_scale,
+                                        uint32_t* error_word, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Fused post -> next pre of an int8 sublayer output ([P1] "What this fixes":

@@ -21,8 +21,10 @@ LIB_PATH = os.path.join(_HERE, "libmhc.so")
 FLAG_MXFP8 = 1
 FLAG_RECOMPUTE_X = 2
 _STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_ALIGN", 4: "MHC_ERR_ALIAS",
-           5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP", 9: "MHC_ERR_EXPIRED"}
+           5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP", 9: "MHC_ERR_EXPIRED",
+           10: "MHC_ERR_SCRATCH"}
 ERR_EXPIRED = 9
+ERR_SCRATCH = 10
 
 
 class MhcParams(ctypes.Structure):
@@ -80,6 +82,8 @@ _SIG = {
                             _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_post_pre_fused_prepacked": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams),
                                       ctypes.c_uint, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "mhc_post_pre_fused_prepacked_static": ([_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(MhcParams),
+                                             ctypes.c_uint, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
 }
 
 
@@ -437,3 +441,28 @@ def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_n
     return prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params,
                                             mxfp8=mxfp8, want_h=want_h, ws=ws, outs=outs,
                                             recompute_x=recompute_x)()
+
+
+def post_pre_fused_prepacked_static(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(),
+                                    *, error_word, mxfp8: bool = False, want_h: bool = True, outs=None,
+                                    recompute_x: bool = False) -> dict:
+    """mhc_post_pre_fused_prepacked_static: the fused pass on the library's
+    static scratch (no workspace argument).  ``error_word`` is a one-element
+    int32 GPU tensor that a bounded wait which expires sets nonzero."""
+    L = lib()
+    T, C = _dims(x)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, 4, C))
+    _need(y, "y", torch.bfloat16, (T, C), dev)
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24), dev)
+    _need(phi_next_packed, "phi_next_packed", torch.uint8, (int(L.mhc_phi_packed_bytes(C)),), dev)
+    _need(bias_next, "bias_next", torch.float32, (24,), dev)
+    _need(gamma_next, "gamma_next", torch.float32, (C,), dev)
+    _need(error_word, "error_word", torch.int32, (1,), dev)
+    o = _fused_outputs(T, C, dev, mxfp8, want_h, outs)
+    p = MhcParams.of(params)
+    _check(L.mhc_post_pre_fused_prepacked_static(
+        _ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next_packed), _ptr(bias_next), _ptr(gamma_next), T, C,
+        ctypes.byref(p), _flags(mxfp8, recompute_x), _ptr(o["x_out"]), _ptr(o["coeffs_next"]), _ptr(o["h"]),
+        _ptr(o["h_fp8"]), _ptr(o["h_scale"]), _ptr(error_word), _stream(dev)), "mhc_post_pre_fused_prepacked_static")
+    return o

@@ -1,13 +1,22 @@
 // The libmhc C ABI: argument validation, workspace layout and launches.
 // Every check runs before the first HIP call, so a rejected call has no
 // effect on the device (and the checks can be exercised without a GPU).
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mhc.h"
 #include "mhc_internal.h"
+
+// Workspace of mhc_post_pre_fused_prepacked_static, for callers that cannot
+// allocate: one copy per GPU, held until the process ends.  Host code never
+// uses this name as an address (on the host it is only a stand-in for the
+// device symbol); it takes each device's address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MHC_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -265,10 +274,36 @@ struct YIn {
   const float* scale;
 };
 
+// The device address of the static scratch on the current device, taken
+// once per device with hipGetSymbolAddress; the first call on a device also
+// enqueues a clear of the whole array on `s` (a kernel, no memset node).
+int static_scratch(void** out, hipStream_t s) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  int rc = hip_status(hipGetDevice(&dev));
+  if (rc) return rc;
+  if (dev < 0 || dev >= 64) return MHC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if ((rc = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))))) return rc;
+    if (ptr == nullptr) return MHC_ERR_HIP;
+    if ((rc = hip_status(mhc::launch_fill_zero(ptr, MHC_STATIC_SCRATCH_BYTES, s)))) return rc;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return MHC_OK;
+}
+
+// err_word: NULL for the workspace's own error word; otherwise (the static
+// scratch variant) the caller's device word that a bounded wait which expires
+// sets, and ws is ignored: the call runs on the static scratch.
 int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float* phi,
                const void* phi_packed, const float* bias, const float* gamma, int64_t T, int64_t C,
                const mhc_params* p, unsigned flags, uint16_t* x_out, float* coeffs_next, uint16_t* h,
-               uint8_t* h_fp8, uint8_t* h_scale, void* ws, size_t ws_bytes, void* stream) {
+               uint8_t* h_fp8, uint8_t* h_scale, void* ws, size_t ws_bytes, void* stream,
+               uint32_t* err_word = nullptr) {
   int rc = check_shape(T, C);
   if (rc) return rc;
   if ((rc = check_params(p, true))) return rc;
@@ -303,17 +338,31 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   }
   if ((rc = check_tensors(in, nin, out, nout))) return rc;
   const mhc::Plan plan = mhc::make_plan(T, C);
-  if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
-  const Span wsp{ws, plan.total};
-  for (int k = 0; k < nin; ++k)
-    if (overlaps(wsp, in[k])) return MHC_ERR_ALIAS;
-  for (int k = 0; k < nout; ++k)
-    if (overlaps(wsp, out[k])) return MHC_ERR_ALIAS;
-
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (err_word != nullptr) {
+    // static scratch: every check first, then the scratch's address
+    if (!plan_fits(plan)) return MHC_ERR_SHAPE;
+    if (plan.total > (size_t)MHC_STATIC_SCRATCH_BYTES) return MHC_ERR_SCRATCH;
+    if (((uintptr_t)err_word & 3u) != 0) return MHC_ERR_ALIGN;
+    const Span ew{err_word, sizeof(uint32_t)};
+    for (int k = 0; k < nin; ++k)
+      if (overlaps(ew, in[k])) return MHC_ERR_ALIAS;
+    for (int k = 0; k < nout; ++k)
+      if (overlaps(ew, out[k])) return MHC_ERR_ALIAS;
+    if ((rc = static_scratch(&ws, s))) return rc;
+  } else {
+    if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
+    const Span wsp{ws, plan.total};
+    for (int k = 0; k < nin; ++k)
+      if (overlaps(wsp, in[k])) return MHC_ERR_ALIAS;
+    for (int k = 0; k < nout; ++k)
+      if (overlaps(wsp, out[k])) return MHC_ERR_ALIAS;
+  }
+
   mhc::Plan run = plan;
   choose_kernel(run);
   mhc::SplitArgs a = split_args(run, ws, T, C, p);
+  if (err_word != nullptr) a.err = err_word;
   const void* packed = phi_packed;
   if (phi != nullptr) {
     void* dst = static_cast<char*>(ws) + plan.off_phi;
@@ -358,6 +407,9 @@ const char* mhc_strerror(int status) {
     case MHC_ERR_PARAM: return "a scalar parameter is out of range";
     case MHC_ERR_HIP: return "a HIP runtime call failed";
     case MHC_ERR_EXPIRED: return "a bounded wait of a call that used this workspace expired: its outputs are invalid";
+    case MHC_ERR_SCRATCH:
+      return "T and C need a larger workspace than the static scratch (MHC_STATIC_SCRATCH_BYTES) holds: "
+             "use the call with a caller-owned workspace";
     default: return "unknown status";
   }
 }
@@ -491,6 +543,16 @@ int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const flo
                                  void* stream) {
   return fused_impl(YIn{y, nullptr, nullptr}, x, coeffs, nullptr, phi_next_packed, bias_next, gamma_next, T, C, p, flags,
                     x_out, coeffs_next, h, h_fp8, h_scale, workspace, workspace_bytes, stream);
+}
+
+int mhc_post_pre_fused_prepacked_static(const uint16_t* x, const uint16_t* y, const float* coeffs,
+                                        const void* phi_next_packed, const float* bias_next, const float* gamma_next,
+                                        int64_t T, int64_t C, const mhc_params* p, unsigned flags, uint16_t* x_out,
+                                        float* coeffs_next, uint16_t* h, uint8_t* h_fp8, uint8_t* h_scale,
+                                        uint32_t* error_word, void* stream) {
+  if (T > 0 && error_word == nullptr) return MHC_ERR_NULL;
+  return fused_impl(YIn{y, nullptr, nullptr}, x, coeffs, nullptr, phi_next_packed, bias_next, gamma_next, T, C, p, flags,
+                    x_out, coeffs_next, h, h_fp8, h_scale, nullptr, 0, stream, error_word);
 }
 
 int mhc_post_int8_pre_fused(const uint16_t* x, const int8_t* y_q, const float* y_scale, const float* coeffs,

@@ -49,8 +49,8 @@ def test_schedule_query():
 
 def test_abi_version_and_strerror():
     L = mhc.lib()
-    assert L.mhc_abi_version() == 3
-    for code in range(10):
+    assert L.mhc_abi_version() == 4
+    for code in range(11):
         assert L.mhc_strerror(code) != b"unknown status"
     assert L.mhc_strerror(99) == b"unknown status"
 
