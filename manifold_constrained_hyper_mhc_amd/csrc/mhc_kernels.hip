@@ -162,20 +162,11 @@ __device__ __forceinline__ uint64_t tagged_load(const uint64_t* p) {
 }
 __device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-// Wait until the word at p carries `tag`; returns its value.
-__device__ __forceinline__ float tagged_wait(const uint64_t* p, uint32_t tag, uint32_t* err) {
-  uint64_t w = tagged_load(p);
-  uint32_t it = 0;
-  while ((uint32_t)(w >> 32) != tag) {
-    __builtin_amdgcn_s_sleep(1);
-    if (++it > kSpinLimit) {
-      __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    w = tagged_load(p);
-  }
-  return tagged_value(w);
-}
+// Every exchanged word of a launch with tag L carries 2 L + (g % 2), where
+// g is the generation of its ring slot (0 where the layout is not a ring),
+// so words of different launches never share a tag (until 2^31 launches
+// have wrapped the epoch), whichever layout each launch used.
+__device__ __forceinline__ uint32_t ring_tag(uint32_t tag, uint32_t gen) { return 2u * tag + (gen & 1u); }
 
 // Appends token t to the workspace list of tokens whose fused pre is
 // recomputed directly.  The count is a tagged word: a count left by an
@@ -497,10 +488,11 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // stored, when that workgroup ran on this XCD (their shared L2 holds the
   // stores); otherwise it recomputes x' from x and y.
   if (tid == 0)
-    s_xdirect = tC >= 0 && !a.recompute_x && (uint32_t)(own >> 32) == s_tag &&
+    s_xdirect = tC >= 0 && !a.recompute_x && (uint32_t)(own >> 32) == ring_tag(s_tag, 0) &&
                 __float_as_uint(tagged_value(own)) == xcd_id();
   __syncthreads();  // s_tag, cfs, s_xdirect
   const uint32_t tag = s_tag;
+  const uint32_t wtag = ring_tag(tag, 0);  // the tag of this launch's exchanged words
   const bool xdirect = s_xdirect != 0;
 
   // ---------------- A: post, statistics and projection of tile tA ----------------
@@ -606,10 +598,10 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
                    red[ww * TM * NV + b + 27];
         }
       }
-      tagged_store(part + (idx / NV) * PW + vv, sum, tag);
+      tagged_store(part + (idx / NV) * PW + vv, sum, wtag);
     }
     __syncthreads();  // LDS free for R
-    if (FUSED && tid == 0) tagged_store(a.owner + (int64_t)tA * S + split, __uint_as_float(xcd_id()), tag);
+    if (FUSED && tid == 0) tagged_store(a.owner + (int64_t)tA * S + split, __uint_as_float(xcd_id()), wtag);
   }
 
   // the loads of C (inputs only) are in flight while R runs
@@ -635,7 +627,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
     for (;;) {
       bool stale = false;
 #pragma unroll
-      for (int q = 0; q < RUN; ++q) stale |= q < n && (uint32_t)(w[q] >> 32) != tag;
+      for (int q = 0; q < RUN; ++q) stale |= q < n && (uint32_t)(w[q] >> 32) != wtag;
       if (!stale) break;
       __builtin_amdgcn_s_sleep(1);
       if (++it > kSpinLimit) {
@@ -644,7 +636,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
       }
 #pragma unroll
       for (int q = 0; q < RUN; ++q)
-        if (q < n && (uint32_t)(w[q] >> 32) != tag) w[q] = tagged_load(gbase + q * gstride);
+        if (q < n && (uint32_t)(w[q] >> 32) != wtag) w[q] = tagged_load(gbase + q * gstride);
     }
     float sum = 0.0f;
 #pragma unroll
@@ -666,7 +658,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         const int64_t t = tok0 + m;
         const float cv = finalize_wave<FUSED>(fin[kq], a.bias, C, a.sc, lane,
                                               [=](const float* q, bool cancels) __attribute__((always_inline)) {
-                                                if (lane < 4) tagged_store(qdst, q[lane & 3], tag);
+                                                if (lane < 4) tagged_store(qdst, q[lane & 3], wtag);
                                                 if (cancels && lane == 0 && t < a.T) flag_for_fix(a, tag, t);
                                               });
         if (t < a.T && lane < 24) a.coeffs_out[t * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
@@ -682,7 +674,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         const uint64_t* qp = a.publish + tok0 * 4 + tid;
         uint64_t qw = tagged_load(qp);
         uint32_t it = 0;
-        while ((uint32_t)(qw >> 32) != tag) {
+        while ((uint32_t)(qw >> 32) != wtag) {
           __builtin_amdgcn_s_sleep(1);
           if (++it > kSpinLimit) {
             __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -816,6 +808,19 @@ constexpr int kCoeffsWords = 25;  // coefficients-only partial words per token: 
 constexpr int kPhiFrag = 4 * kWave + kWave / 2;
 // 16-byte chunks of one row block's x slice: 16 tokens x 4 routes x 16
 constexpr int kHalfChunks = 16 * 4 * 16;
+// The fused passes keep their partial and q words in a ring of R = kRingK * L
+// tiles (L stream workgroups per split): tile t uses slot t % R.  Stream
+// workgroup lane r's tiles t = r + L i take slot r + L (i % kRingK), and the
+// units of tiles t and t + R meet the same reduce workgroup (R is a multiple
+// of 8 and a reduce workgroup owns every 32nd unit of 4 per tile).  A word of
+// tile t carries the tag 2 * launch_tag + (t / R) % 2, so the word an older
+// tile of the same slot left behind never passes as fresh.  Reuse is safe
+// because of the q-word chain: a stream workgroup stores tile t_{i-1}'s
+// partial words in phase P(i) only after it has seen the q words of tile
+// t_{i-D-1}, which the reduce publishes after gathering every split's words
+// of that tile; kRingK >= D + 1 then keeps a slot's old tile gathered before
+// it is overwritten, and likewise its q words read before new ones land.
+constexpr int kRingK = 8;
 
 // Whether a bounded wait of the launch has expired (read from memory; the
 // polls look at it every 16th round only, so that a poll round costs one
@@ -918,6 +923,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     uint64_t wa[16], wb[16], wc[16], wd[16];
     const uint64_t* pb = a.partials;
     float sum = 0.0f;
+    uint32_t want = ring_tag(tag, 0);  // the tag the words of the unit being gathered carry
     auto load_chunk = [&](uint64_t* w, int sc) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) w[k] = act && sc + k < S ? tagged_load(pb + (sc + k) * pstride) : 0;
@@ -926,7 +932,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       auto stale = [&]() __attribute__((always_inline)) {
         bool st = false;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) st |= act && sc + k < S && (uint32_t)(w[k] >> 32) != tag;
+        for (int k = 0; k < 16; ++k) st |= act && sc + k < S && (uint32_t)(w[k] >> 32) != want;
         return st;
       };
       if (stale()) {
@@ -941,7 +947,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           }
 #pragma unroll
           for (int k = 0; k < 16; ++k)
-            if (act && sc + k < S && (uint32_t)(w[k] >> 32) != tag) w[k] = tagged_load(pb + (sc + k) * pstride);
+            if (act && sc + k < S && (uint32_t)(w[k] >> 32) != want) w[k] = tagged_load(pb + (sc + k) * pstride);
         } while (stale());
       }
 #pragma unroll
@@ -980,8 +986,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         __syncthreads();  // this tile's sums are read
       }
     } else {
+      const int R = kRingK * L;
       auto gather = [&](int u, float* fin) __attribute__((always_inline)) {
-        pb = a.partials + (int64_t)(u >> 2) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
+        const int tu = u >> 2;
+        want = ring_tag(tag, (uint32_t)(tu / R));
+        pb = a.partials + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
         sum = 0.0f;
         load_chunk(wa, 0);
         load_chunk(wb, 16);
@@ -1001,15 +1010,18 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         if (wv < 2) {
           // token 4 wave + r of the unit on lanes 16r .. 16r + 15
           const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
-          const int64_t tok = (int64_t)(u >> 2) * TM + (u & 3) * 8 + ml;
+          const int tu = u >> 2;
+          const int64_t tok = (int64_t)tu * TM + (u & 3) * 8 + ml;
+          const int64_t ptok = (int64_t)(tu % R) * TM + (u & 3) * 8 + ml;  // ring slot of the q words
+          const uint32_t qtag = ring_tag(tag, (uint32_t)(tu / R));
           float res, pp;
-          // every row of the tile is published ([tiles][TM][4] words): the
+          // every row of the tile is published ([R][TM][4] words): the
           // stream workgroups poll whole row blocks, padding rows included
           finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp,
                                [&](const float* q, bool cancels) __attribute__((always_inline)) {
                                  if (kk < 4)
-                                   tagged_store(a.publish + tok * 4 + kk,
-                                                kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], tag);
+                                   tagged_store(a.publish + ptok * 4 + kk,
+                                                kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], qtag);
                                  if (cancels && kk == 0 && tok < a.T) flag_for_fix(a, tag, tok);
                                });
           if (tok < a.T) {
@@ -1129,7 +1141,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int idx = gt + 256 * k;
-          if (idx < 16 * NW) tagged_store(part + idx, sum[k], tag);
+          if (idx < 16 * NW) tagged_store(part + idx, sum[k], ring_tag(tag, 0));
         }
       };
       // projection and sum of squares of tile t_i from the stage (rows past
@@ -1256,8 +1268,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     // iteration i
     auto issue_q = [&](int i) __attribute__((always_inline)) {
       const int ic = i - D;
-      const int t = ic >= 0 && ic < niter ? r + L * ic : 0;
-      nq = tagged_load(a.publish + ((int64_t)t * TM + rb * 16) * 4 + (gt & 63));
+      const int slot = ic >= 0 && ic < niter ? r + L * (ic % kRingK) : 0;
+      nq = tagged_load(a.publish + ((int64_t)slot * TM + rb * 16) * 4 + (gt & 63));
     };
 
     u32x4_t ring[D][4];  // x' of the last D tiles (packed bf16, 4 routes)
@@ -1290,7 +1302,10 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // partial row of tile t_{i-1}: this row block's 16 tokens x NV words,
       // the four 32-channel steps added in order
       if constexpr (doPrev) {
-        uint64_t* part = a.partials + ((int64_t)(t - L) * S + split) * (TM * NV) + rb * 16 * NV;
+        // tile t_{i-1}, ring slot r + L ((i - 1) % kRingK)
+        uint64_t* part =
+            a.partials + ((int64_t)(r + L * ((i - 1) % kRingK)) * S + split) * (TM * NV) + rb * 16 * NV;
+        const uint32_t ptag = ring_tag(tag, (uint32_t)((i - 1) / kRingK));
         // all twelve LDS reads first, then the stores (words past the row
         // block are not stored)
         float sum[3];
@@ -1303,7 +1318,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           const int idx = gt + k * 256;
-          if (idx < 16 * NV) tagged_store(part + idx, sum[k], tag);
+          if (idx < 16 * NV) tagged_store(part + idx, sum[k], ptag);
         }
       }
       const u32x4_t cy = ny;
@@ -1505,8 +1520,9 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         const int ic = i - D;
         if (ic >= 0 && ic < niter && gt < 64) {
           uint64_t qw = nq;
-          if ((uint32_t)(qw >> 32) != tag) {
-            const uint64_t* qp = a.publish + ((int64_t)(r + L * ic) * TM + rb * 16) * 4 + gt;
+          const uint32_t qtag = ring_tag(tag, (uint32_t)(ic / kRingK));
+          if ((uint32_t)(qw >> 32) != qtag) {
+            const uint64_t* qp = a.publish + ((int64_t)(r + L * (ic % kRingK)) * TM + rb * 16) * 4 + gt;
             uint32_t it = 0;
             do {
               __builtin_amdgcn_s_sleep(1);
@@ -1515,7 +1531,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
                 break;
               }
               qw = tagged_load(qp);
-            } while ((uint32_t)(qw >> 32) != tag);
+            } while ((uint32_t)(qw >> 32) != qtag);
           }
           qs[rb * 16 + gt / 4][gt & 3] = tagged_value(qw);
         }
