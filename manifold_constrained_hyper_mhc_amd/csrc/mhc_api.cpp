@@ -127,7 +127,9 @@ void choose_kernel(mhc::Plan& p) {
   if (!persistent_allowed()) return;
   if (p.m != 32 || p.s < 32 || p.s > 64) return;
   const int cus = device_cus();
-  const int lanes = (cus - 32) / p.s;
+  int lanes = (cus - 32) / p.s;
+  // the workspace's rings hold kRingK tiles per stream workgroup lane
+  if (lanes * p.s > mhc::kMaxLaneSplits) lanes = mhc::kMaxLaneSplits / p.s;
   if (lanes < 1 || p.tiles < 2 * (int64_t)lanes || p.s * lanes + 32 > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;
 }
@@ -144,6 +146,20 @@ int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
 
 namespace mhc {
 
+// Stage delays of the reduce (d1) and the pre step (d2) behind a tile's
+// phase A in a staged launch of `tiles` tiles: a few stages absorb the spread
+// of workgroup progress; a short launch keeps them short so that its few
+// tiles are not delayed.
+static void set_delays(Plan& p, int64_t tiles) {
+  if (tiles >= 64) {
+    p.d1 = 12;
+    p.d2 = 16;
+  } else {
+    p.d1 = 1;
+    p.d2 = 2;
+  }
+}
+
 // Tile shape: 32 tokens x 128 channels (of every route) per workgroup.
 Plan make_plan(int64_t T, int64_t C) {
   Plan p;
@@ -151,29 +167,50 @@ Plan make_plan(int64_t T, int64_t C) {
   p.cc = 128;
   p.s = (int)(C / p.cc);
   p.tiles = (T + p.m - 1) / p.m;
-  // stage delays of the reduce (d1) and the pre step (d2) behind a tile's
-  // phase A: a few stages absorb the spread of workgroup progress; a short
-  // launch keeps them short so that its few tiles are not delayed
-  if (p.tiles >= 64) {
-    p.d1 = 12;
-    p.d2 = 16;
-  } else {
-    p.d1 = 1;
-    p.d2 = 2;
+  // staged launches: at most kStagedBudget bytes of partial words each
+  const size_t tile_words = (size_t)p.s * p.m * kPartVals * sizeof(uint64_t);
+  int64_t chunk = (int64_t)(kStagedBudget / tile_words);
+  chunk = chunk < 16 ? 16 : (chunk > 256 ? 256 : chunk);
+  p.chunk_tiles = p.tiles < chunk ? p.tiles : chunk;
+  set_delays(p, p.chunk_tiles);
+  // persistent rings (32-token tiles only): fused kRingK tiles per lane,
+  // coefficients only kCoeffsRingTiles
+  int64_t ring_f = 0, ring_c = 0;
+  if (p.m == 32) {
+    ring_f = (int64_t)kRingK * (kMaxLaneSplits / p.s);
+    ring_f = p.tiles < ring_f ? p.tiles : ring_f;
+    ring_c = p.tiles < kCoeffsRingTiles ? p.tiles : kCoeffsRingTiles;
   }
+  size_t part = (size_t)p.chunk_tiles * tile_words;
+  const size_t part_f = (size_t)ring_f * p.s * p.m * kPartVals * sizeof(uint64_t);
+  const size_t part_c = (size_t)ring_c * p.s * p.m * 25 * sizeof(uint64_t);
+  part = part > part_f ? part : part_f;
+  part = part > part_c ? part : part_c;
+  const int64_t pub_tiles = p.chunk_tiles > ring_f ? p.chunk_tiles : ring_f;
   size_t off = kWsHeaderBytes;
   p.off_pub = off;
-  off = round256(off + (size_t)p.tiles * p.m * 4 * sizeof(uint64_t));
+  off = round256(off + (size_t)pub_tiles * p.m * 4 * sizeof(uint64_t));
   p.off_part = off;
-  off = round256(off + (size_t)p.tiles * p.s * p.m * kPartVals * sizeof(uint64_t));
+  off = round256(off + part);
   p.off_own = off;
-  off = round256(off + (size_t)p.tiles * p.s * sizeof(uint64_t));
+  off = round256(off + (size_t)p.chunk_tiles * p.s * sizeof(uint64_t));
+  p.off_rel = off;
+  off = round256(off + (size_t)kCoeffsRingTiles * sizeof(uint64_t));
   p.off_fix = off;
   off = round256(off + (size_t)T * sizeof(uint32_t));
   p.off_phi = off;
   off = round256(off + phi_packed_bytes(C));
   p.total = off;
   return p;
+}
+
+Plan chunk_plan(const Plan& p, int64_t tokens) {
+  Plan c = p;
+  c.lanes = 0;
+  c.tiles = (tokens + p.m - 1) / p.m;
+  c.chunk_tiles = c.tiles;
+  set_delays(c, c.tiles);
+  return c;
 }
 
 }  // namespace mhc
@@ -191,6 +228,7 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
   a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
+  a.release = reinterpret_cast<uint64_t*>(base + plan.off_rel);
   a.fix_word = reinterpret_cast<uint64_t*>(base + mhc::kWsFixWord);
   a.fix_list = reinterpret_cast<uint32_t*>(base + plan.off_fix);
   a.T = T;
@@ -204,6 +242,43 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.lanes = plan.lanes;
   a.sc = scalars(p);
   return a;
+}
+
+// One coefficients or fused call: a single persistent launch, or staged
+// launches of at most run.chunk_tiles tiles each, over consecutive tokens,
+// every pointer offset to the chunk's first token.  Each fused launch is
+// followed by the direct recomputation of the tokens it flagged.
+int run_split(const mhc::Plan& run, int mode, const mhc::SplitArgs& a, hipStream_t s) {
+  const bool fused = mhc::mode_fused(mode), mx = mhc::mode_mx(mode);
+  int rc;
+  if (run.lanes > 0) {
+    if ((rc = hip_status(mhc::launch_split(run, mode, a, s)))) return rc;
+    return fused ? hip_status(mhc::launch_pre_fix(a, mx, s)) : MHC_OK;
+  }
+  const int64_t chunk = run.chunk_tiles * run.m;
+  for (int64_t t0 = 0; t0 < a.T; t0 += chunk) {
+    const int64_t n = a.T - t0 < chunk ? a.T - t0 : chunk;
+    const mhc::Plan pc = mhc::chunk_plan(run, n);
+    mhc::SplitArgs c = a;
+    c.T = n;
+    c.tiles = (uint32_t)pc.tiles;
+    c.d1 = pc.d1;
+    c.d2 = pc.d2;
+    const int64_t C = a.C;
+    c.x = a.x + t0 * a.xts;
+    if (a.y) c.y = a.y + t0 * C;
+    if (a.y_q) c.y_q = a.y_q + t0 * C;
+    if (a.y_scale) c.y_scale = a.y_scale + t0;
+    if (a.coeffs_in) c.coeffs_in = a.coeffs_in + t0 * mhc::kCoeffs;
+    if (a.x_out) c.x_out = a.x_out + t0 * 4 * C;
+    c.coeffs_out = a.coeffs_out + t0 * mhc::kCoeffs;
+    if (a.h) c.h = a.h + t0 * C;
+    if (a.h_fp8) c.h_fp8 = a.h_fp8 + t0 * C;
+    if (a.h_scale) c.h_scale = a.h_scale + t0 * (C / 32);
+    if ((rc = hip_status(mhc::launch_split(pc, mode, c, s)))) return rc;
+    if (fused && (rc = hip_status(mhc::launch_pre_fix(c, mx, s)))) return rc;
+  }
+  return MHC_OK;
 }
 
 // bcast: x is a [T][C] stream that stands for all 4 routes (read with route
@@ -245,7 +320,7 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
   a.phi_packed = static_cast<const uint32_t*>(packed);
   a.bias = bias;
   a.coeffs_out = coeffs;
-  return hip_status(mhc::launch_split(run, bcast ? mhc::kModeCoeffsBcast : mhc::kModeCoeffs, a, s));
+  return run_split(run, bcast ? mhc::kModeCoeffsBcast : mhc::kModeCoeffs, a, s);
 }
 
 // Coefficients, then pre, of a [T][C] stream broadcast to the 4 routes.
@@ -384,9 +459,8 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   a.h_scale = h_scale;
   a.recompute_x = (flags & MHC_FLAG_RECOMPUTE_X) != 0;
   const int mode = (mx ? mhc::kModeFusedMx : mhc::kModeFused) | (yq ? mhc::kModeYInt8 : 0);
-  if ((rc = hip_status(mhc::launch_split(run, mode, a, s)))) return rc;
-  // tokens whose route combination cancels get their pre recomputed directly
-  return hip_status(mhc::launch_pre_fix(a, mx, s));
+  // (tokens whose route combination cancels get their pre recomputed directly)
+  return run_split(run, mode, a, s);
 }
 
 }  // namespace

@@ -28,9 +28,21 @@ struct Plan {
   int s = 1;       // workgroups per row
   int lanes = 0;   // persistent kernel: stream workgroups per split (0: staged kernel)
   int64_t tiles = 0;
+  int64_t chunk_tiles = 0;  // staged kernel: tiles per launch (a longer call is a sequence of launches)
   // workspace layout (byte offsets)
-  size_t off_pub = 0, off_part = 0, off_own = 0, off_fix = 0, off_phi = 0, total = 0;
+  size_t off_pub = 0, off_part = 0, off_own = 0, off_rel = 0, off_fix = 0, off_phi = 0, total = 0;
 };
+
+// Workspace bounds.  The persistent kernel keeps its exchanged words in
+// rings (fused: kRingK * L tiles; coefficients only: kCoeffsRingTiles
+// tiles), with at most kMaxLaneSplits = L * S stream workgroups; the staged
+// kernel runs a call as launches of at most chunk_tiles tiles, whose partial
+// words take at most kStagedBudget bytes.  So a workspace holds about
+// kStagedBudget bytes + 4 per token + the packed projection, whatever T is.
+constexpr int kRingK = 8;
+constexpr int kCoeffsRingTiles = 32;
+constexpr int kMaxLaneSplits = 256;
+constexpr size_t kStagedBudget = (size_t)32 << 20;
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
 
@@ -48,6 +60,8 @@ constexpr int kPersistMaxBlocks = 512;
 constexpr size_t kPackBytesPerRow = 160;  // 80 bf16 per flattened row k
 
 Plan make_plan(int64_t T, int64_t C);
+// The staged launch of a chunk of `tokens` tokens of a call planned as p.
+Plan chunk_plan(const Plan& p, int64_t tokens);
 
 // Reduce-scatter of the split kernel: a workgroup owns ntok = ceil(m/s)
 // tokens of a tile; each of their ntok*34 partial words is summed over the
@@ -81,6 +95,7 @@ struct SplitArgs {
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
   uint64_t* publish;   // [tiles][M][4] tagged words
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
+  uint64_t* release;   // [kCoeffsRingTiles] coefficients-only ring: generation of each slot's gathered tile
   uint64_t* fix_word;  // (launch tag << 32) | number of tokens in fix_list (fixed offset)
   uint32_t* fix_list;  // [T] tokens whose fused pre is recomputed directly (k_pre_fix)
   uint32_t* err;

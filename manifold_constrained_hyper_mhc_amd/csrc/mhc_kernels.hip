@@ -820,7 +820,6 @@ constexpr int kHalfChunks = 16 * 4 * 16;
 // t_{i-D-1}, which the reduce publishes after gathering every split's words
 // of that tile; kRingK >= D + 1 then keeps a slot's old tile gathered before
 // it is overwritten, and likewise its q words read before new ones land.
-constexpr int kRingK = 8;
 
 // Whether a bounded wait of the launch has expired (read from memory; the
 // polls look at it every 16th round only, so that a poll round costs one
@@ -958,11 +957,21 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // Coefficients only: nothing waits on the result but the end of the
       // launch, so whole tiles per round (all threads gather, then every
       // wave finalises four tokens) give more tokens per round.
+      // The partial words live in a ring of kCoeffsRingTiles tiles: tile t in
+      // slot t % kCoeffsRingTiles, generation t / kCoeffsRingTiles.  The ring
+      // is a multiple of the 32 reduce workgroups, so every tile of a slot is
+      // gathered here, in order; once a tile's words are in, the slot's
+      // release word gets its generation (the full number, in the value
+      // field), and stream workgroups wait for it before refilling the slot.
+      static_assert(kCoeffsRingTiles % 32 == 0, "one reduce workgroup per ring slot");
       for (int t = j; t < tiles; t += nred) {
+        const int slot = t % kCoeffsRingTiles;
+        const uint32_t gen = (uint32_t)(t / kCoeffsRingTiles);
+        want = ring_tag(tag, gen);
         for (int w = tid; w < TM * kCoeffsWords; w += kPersistThreads) {
           const int wo = (w / kCoeffsWords) * NV + w % kCoeffsWords;  // (token, word) in the [TM][NV] sums
           act = true;
-          pb = a.partials + (int64_t)t * S * pstride + w;
+          pb = a.partials + (int64_t)slot * S * pstride + w;
           sum = 0.0f;
           load_chunk(wa, 0);
           load_chunk(wb, 16);
@@ -974,7 +983,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           add_chunk(wd, 48);
           finw[wo] = sum;
         }
-        __syncthreads();  // the tile's sums
+        __syncthreads();  // the tile's sums (every gather load has returned)
+        if (tid == 0) tagged_store(a.release + slot, __uint_as_float(gen), ring_tag(tag, 0));
         const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
         const int64_t tok = (int64_t)t * TM + ml;
         float res, pp;
@@ -1128,9 +1138,30 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
       };
       // partial words of tile t_i: 16 tokens x NW words of this row block
-      // ([tiles][S][TM][NW] in this mode: dense, whole lines per store)
-      auto fold = [&](int i) __attribute__((always_inline)) {
-        uint64_t* part = a.partials + ((int64_t)(r + L * i) * S + split) * (TM * NW) + rb * 16 * NW;
+      // (ring slots [kCoeffsRingTiles][S][TM][NW]: dense, whole lines per
+      // store).  rel: the slot's release word, loaded before this step's x
+      // loads so that waiting for it never waits for them; the slot's
+      // previous tile must have been gathered before it is refilled.
+      auto release_of = [&](int i) __attribute__((always_inline)) {
+        return tagged_load(a.release + (r + L * i) % kCoeffsRingTiles);
+      };
+      auto fold = [&](int i, uint64_t rel) __attribute__((always_inline)) {
+        const int t = r + L * i;
+        const uint32_t gen = (uint32_t)(t / kCoeffsRingTiles);
+        uint64_t* part = a.partials + ((int64_t)(t % kCoeffsRingTiles) * S + split) * (TM * NW) + rb * 16 * NW;
+        if (gen > 0) {
+          const uint32_t rtag = ring_tag(tag, 0);
+          uint32_t it = 0;
+          while ((uint32_t)(rel >> 32) != rtag || (uint32_t)rel < gen - 1u) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
+              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            rel = tagged_load(a.release + t % kCoeffsRingTiles);
+          }
+        }
+        const uint32_t ptag = ring_tag(tag, gen);
         const float* rr = &red[i & 1][rb * 4][0];
         float sum[2];
 #pragma unroll
@@ -1141,7 +1172,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int idx = gt + 256 * k;
-          if (idx < 16 * NW) tagged_store(part + idx, sum[k], ring_tag(tag, 0));
+          if (idx < 16 * NW) tagged_store(part + idx, sum[k], ptag);
         }
       };
       // projection and sum of squares of tile t_i from the stage (rows past
@@ -1200,10 +1231,12 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       };
       // step i >= 1 (step 0 has no partial words to store)
       auto step = [&](int i, u32x4_t* xb) __attribute__((always_inline)) {
+        const uint64_t rel = release_of(i - 1);
+        __builtin_amdgcn_sched_barrier(0);
         stage_write(xb);
         load_x(xb, i + A);
         MHC_GROUP_BARRIER("coefficients: stage written");
-        fold(i - 1);
+        fold(i - 1, rel);
         project(i);
         MHC_GROUP_BARRIER("coefficients: stage read");
       };
@@ -1225,7 +1258,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k < A; ++k)
           if (i + k < niter) step(i + k, xq[(k + 1) % A]);
-        fold(niter - 1);
+        fold(niter - 1, release_of(niter - 1));
       }
     } else {
 

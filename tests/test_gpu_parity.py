@@ -258,6 +258,24 @@ def test_fused_schedules(T, C, mx, schedule):
     check_fused(inp, out, mx=mx)
 
 
+# calls that wrap the persistent rings (fused: 8 tiles per stream lane, 32
+# tiles at C = 7168; coefficients only: 32 tiles) or run as several staged
+# launches (C = 16384: 28 tiles per launch), every element against the oracle
+RINGS = [(1100, 7168), (1200, 4096), (1000, 16384)]
+
+
+@pytest.mark.parametrize("T,C", RINGS)
+def test_rings_and_chunked_launches(T, C, schedule):
+    skip_unless_schedule(T, C, schedule)
+    inp = small_inputs(T, C, rows="outliers", seed=31)
+    d = to_dev(inp)
+    cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
+    torch.cuda.synchronize()
+    assert_coeffs_close(f64(cf), O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw()))
+    check_fused(inp, out, mx=True)
+
+
 @pytest.mark.parametrize("T,C", SMALL)
 def test_fused(T, C):
     inp = small_inputs(T, C)

@@ -2,8 +2,9 @@
 allocates nothing), through the C ABI, against the same pass with a
 caller-owned workspace: bitwise the same outputs, on two calls in a row, the
 second with a smaller input (the scratch keeps the first call's contents),
-and the oracle on the small case.  Also the size limit (MHC_ERR_SCRATCH
-before any HIP call) and the ABI constants.
+and the oracle on the small case.  Also that every accepted shape fits the
+scratch (the workspace is bounded), a prefill-sized call, and the ABI
+constants.
 """
 import ctypes
 
@@ -63,29 +64,35 @@ def test_static_scratch_matches_workspace_call():
     assert_bf16_close(f64(out["h"]), r["h"])
 
 
-def test_static_scratch_limit_and_constants():
+def test_static_scratch_covers_every_shape():
     L = mhc.lib()
     assert L.mhc_abi_version() == 4
     assert L.mhc_strerror(mhc.ERR_SCRATCH) != b"unknown status"
-    limit = 64 << 20
-    T, C = 4065, 7168  # the smallest T at C = 7168 whose workspace exceeds the scratch
-    assert L.mhc_workspace_bytes(T, C, 0) > limit >= L.mhc_workspace_bytes(T - 1, C, 0)
-    d = make_inputs(T, C, seed=1, device=DEV)
+    limit = 64 << 20  # MHC_STATIC_SCRATCH_BYTES
+    # the workspace is bounded: every accepted shape fits the static scratch
+    for C in range(1024, 16385, 1024):
+        assert 0 < L.mhc_workspace_bytes(1 << 20, C, 1) <= limit, C
+    # a prefill-sized call on the scratch, bitwise the workspace call
+    T, C = 8192, 4096
+    d = make_inputs(T, C, seed=1, rows="decades", device=DEV)
     cf = torch.zeros((T, 24), dtype=torch.float32, device=DEV)
+    cf[:, 0:8] = 0.5
+    cf[:, 8:24] = torch.eye(4, device=DEV).reshape(16)
     pk = mhc.pack_phi(d["phi_next"])
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    with pytest.raises(mhc.MhcError) as e:
-        mhc.post_pre_fused_prepacked_static(d["x"], d["y"], cf, pk, d["bias_next"], d["gamma_next"],
-                                            error_word=err)
-    assert e.value.status == mhc.ERR_SCRATCH
-    # a NULL error word is refused (T = 16 of the same tensors)
+    out = mhc.post_pre_fused_prepacked_static(d["x"], d["y"], cf, pk, d["bias_next"], d["gamma_next"], mxfp8=True,
+                                              error_word=err)
+    ref = mhc.post_pre_fused_prepacked(d["x"], d["y"], cf, pk, d["bias_next"], d["gamma_next"], mxfp8=True,
+                                       ws=mhc.workspace(T, C, DEV, fresh=True))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for k, v in ref.items():
+        if v is not None:
+            assert torch.equal(out[k], v), k
+    # a NULL error word is refused before any HIP call
     p = mhc.binding.MhcParams.of(P)
-    x_out = torch.empty_like(d["x"][:16])
-    cn = torch.empty((16, 24), dtype=torch.float32, device=DEV)
-    h = torch.empty((16, C), dtype=torch.bfloat16, device=DEV)
     rc = L.mhc_post_pre_fused_prepacked_static(
         d["x"].data_ptr(), d["y"].data_ptr(), cf.data_ptr(), pk.data_ptr(), d["bias_next"].data_ptr(),
-        d["gamma_next"].data_ptr(), 16, C, ctypes.byref(p), 0, x_out.data_ptr(), cn.data_ptr(), h.data_ptr(),
-        None, None, None, torch.cuda.current_stream().cuda_stream)
+        d["gamma_next"].data_ptr(), 16, C, ctypes.byref(p), 0, out["x_out"].data_ptr(),
+        out["coeffs_next"].data_ptr(), out["h"].data_ptr(), None, None, None, torch.cuda.current_stream().cuda_stream)
     assert rc == 1  # MHC_ERR_NULL
-    torch.cuda.synchronize()
