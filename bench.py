@@ -261,9 +261,10 @@ def copy_reference(inp, outs, stream, args, fused_gbs):
 def time_pre_broadcast(mhc, inp, packed, params, stream, args):
     """The first-layer pre (mhc_pre_broadcast_prepacked) on x0 = route 0 of x,
     [T, C]: coefficients and pre of x0 standing for all 4 routes.  HIP events
-    around each call; algorithmic bytes 6C + 112 per token (x0 read by both
-    kernels, coefficients written and read back, h written) + the
-    projection, bias and gamma once."""
+    around each call.  Algorithmic bytes 4C + 112 per token (x0 read once,
+    h written, the coefficients written and their pre read back) + the
+    projection, bias and gamma once; the library reads x0 twice (the
+    coefficients kernel, then the pre kernel), so its traffic is 6C + 112."""
     import torch
 
     x0 = inp["x"][:, 0, :].contiguous()
@@ -287,10 +288,13 @@ def time_pre_broadcast(mhc, inp, packed, params, stream, args):
         b.record(stream)
     torch.cuda.synchronize()
     us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
-    nbytes = T * (6 * C + 112) + 388 * C + 96
+    nbytes = T * (4 * C + 112) + 388 * C + 96
+    two_pass = T * (6 * C + 112) + 388 * C + 96
     return {"us": us, "algorithmic_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
             "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "note": "mhc_pre_broadcast_prepacked on a [T, C] first-layer input (coefficients + pre)"}
+            "two_pass_bytes": two_pass, "two_pass_frac_of_peak": two_pass / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "mhc_pre_broadcast_prepacked on a [T, C] first-layer input (coefficients + pre); "
+                    "algorithmic bytes read x0 once, the two kernels read it twice"}
 
 
 def time_post_int8(mhc, inp, coeffs_in, stream, args):

@@ -122,10 +122,13 @@ int device_cus() {
   return cache[dev];
 }
 
-void choose_kernel(mhc::Plan& p) {
+// min_s: the fewest splits per row that take the persistent kernel (the
+// coefficients of a broadcast stream, split into pseudo-routes, take it from
+// 8 on; every other call from 32 on).
+void choose_kernel(mhc::Plan& p, int min_s = 32) {
   p.lanes = 0;
   if (!persistent_allowed()) return;
-  if (p.m != 32 || p.s < 32 || p.s > 64) return;
+  if (p.m != 32 || p.s < min_s || p.s > 64) return;
   const int cus = device_cus();
   int lanes = (cus - 32) / p.s;
   // the workspace's rings hold kRingK tiles per stream workgroup lane
@@ -173,10 +176,11 @@ Plan make_plan(int64_t T, int64_t C) {
   chunk = chunk < 16 ? 16 : (chunk > 256 ? 256 : chunk);
   p.chunk_tiles = p.tiles < chunk ? p.tiles : chunk;
   set_delays(p, p.chunk_tiles);
-  // persistent rings (32-token tiles only): fused kRingK tiles per lane,
-  // coefficients only kCoeffsRingTiles
+  // persistent rings (32-token tiles, at most 64 splits: where the
+  // persistent kernel can run): fused kRingK tiles per lane, coefficients
+  // only kCoeffsRingTiles
   int64_t ring_f = 0, ring_c = 0;
-  if (p.m == 32) {
+  if (p.m == 32 && p.s <= 64) {
     ring_f = (int64_t)kRingK * (kMaxLaneSplits / p.s);
     ring_f = p.tiles < ring_f ? p.tiles : ring_f;
     ring_c = p.tiles < kCoeffsRingTiles ? p.tiles : kCoeffsRingTiles;
@@ -234,6 +238,9 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.T = T;
   a.xts = 4 * C;
   a.xrs = C;
+  a.cs = 128;
+  a.prs = (int)C;
+  a.rms_c = (int)C;
   a.tiles = (uint32_t)plan.tiles;
   a.C = (int)C;
   a.S = plan.s;
@@ -244,16 +251,16 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   return a;
 }
 
-// One coefficients or fused call: a single persistent launch, or staged
+// One coefficients or fused call: a single persistent launch (a fused one
+// followed by the recomputation of the tokens it listed), or staged
 // launches of at most run.chunk_tiles tiles each, over consecutive tokens,
-// every pointer offset to the chunk's first token.  Each fused launch is
-// followed by the direct recomputation of the tokens it flagged.
+// every pointer offset to the chunk's first token (their last workgroups
+// recompute the listed tokens themselves).
 int run_split(const mhc::Plan& run, int mode, const mhc::SplitArgs& a, hipStream_t s) {
-  const bool fused = mhc::mode_fused(mode), mx = mhc::mode_mx(mode);
   int rc;
   if (run.lanes > 0) {
     if ((rc = hip_status(mhc::launch_split(run, mode, a, s)))) return rc;
-    return fused ? hip_status(mhc::launch_pre_fix(a, mx, s)) : MHC_OK;
+    return mhc::mode_fused(mode) ? hip_status(mhc::launch_fix_flagged(a, mode, s)) : MHC_OK;
   }
   const int64_t chunk = run.chunk_tiles * run.m;
   for (int64_t t0 = 0; t0 < a.T; t0 += chunk) {
@@ -276,13 +283,28 @@ int run_split(const mhc::Plan& run, int mode, const mhc::SplitArgs& a, hipStream
     if (a.h_fp8) c.h_fp8 = a.h_fp8 + t0 * C;
     if (a.h_scale) c.h_scale = a.h_scale + t0 * (C / 32);
     if ((rc = hip_status(mhc::launch_split(pc, mode, c, s)))) return rc;
-    if (fused && (rc = hip_status(mhc::launch_pre_fix(c, mx, s)))) return rc;
   }
   return MHC_OK;
 }
 
-// bcast: x is a [T][C] stream that stands for all 4 routes (read with route
-// stride 0).
+// The coefficients of a [T][C] stream x0 standing for all 4 routes are
+// computed on pseudo-routes: a split takes 512 consecutive channels of x0 as
+// 4 routes of 128, against the projection summed over the routes (packed
+// with launch_pack_phi_sum), so each channel is read and projected once.  Its
+// plan is the plan of hidden size C / 4 (C / 512 splits).  Where that plan
+// does not fit the staged kernel's reduce (C = 1024, or C = 2048 with
+// 32-token tiles), the 4 routes are the same x0 read with route stride 0
+// against the 4-route projection.
+bool bcast_pseudo(const mhc::Plan& pb) { return plan_fits(pb); }
+
+// Workspace bytes of every layout a call of T tokens and C channels can use.
+size_t workspace_need(int64_t T, int64_t C) {
+  const size_t a = mhc::make_plan(T, C).total;
+  const mhc::Plan pb = mhc::make_plan(T, C / 4);
+  return bcast_pseudo(pb) && pb.total > a ? pb.total : a;
+}
+
+// bcast: x is a [T][C] stream that stands for all 4 routes.
 int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const void* phi_packed,
                 const float* bias, const mhc_params* p, float* coeffs, void* ws, size_t ws_bytes,
                 void* stream, bool bcast = false) {
@@ -295,7 +317,15 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
   const Span in[] = {{x, xb}, phi_span, {bias, 96}};
   const Span out[] = {{coeffs, cb}};
   if ((rc = check_tensors(in, 3, out, 1))) return rc;
-  const mhc::Plan plan = mhc::make_plan(T, C);
+  mhc::Plan plan = mhc::make_plan(T, C);
+  bool pseudo = false;
+  if (bcast) {
+    const mhc::Plan pb = mhc::make_plan(T, C / 4);
+    if (bcast_pseudo(pb)) {
+      plan = pb;
+      pseudo = true;
+    }
+  }
   if ((rc = check_workspace(ws, ws_bytes, plan))) return rc;
   const Span wsp{ws, plan.total};
   if (overlaps(wsp, out[0])) return MHC_ERR_ALIAS;
@@ -304,23 +334,32 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   mhc::Plan run = plan;
-  choose_kernel(run);
+  choose_kernel(run, pseudo ? 8 : 32);
   mhc::SplitArgs a = split_args(run, ws, T, C, p);
   const void* packed = phi_packed;
-  if (phi != nullptr) {
-    void* dst = static_cast<char*>(ws) + plan.off_phi;
+  void* dst = static_cast<char*>(ws) + plan.off_phi;
+  if (pseudo) {
+    if ((rc = hip_status(mhc::launch_pack_phi_sum(phi, phi_packed, (int)C, dst, s)))) return rc;
+    packed = dst;
+  } else if (phi != nullptr) {
     if ((rc = hip_status(mhc::launch_pack_phi(phi, (int)C, dst, s)))) return rc;
     packed = dst;
   }
   a.x = x;
-  if (bcast) {
+  if (pseudo) {
+    a.xts = C;
+    a.xrs = 128;
+    a.cs = 512;
+    a.prs = 128;
+    a.rms_c = (int)(C / 4);
+  } else if (bcast) {
     a.xts = C;
     a.xrs = 0;
   }
   a.phi_packed = static_cast<const uint32_t*>(packed);
   a.bias = bias;
   a.coeffs_out = coeffs;
-  return run_split(run, bcast ? mhc::kModeCoeffsBcast : mhc::kModeCoeffs, a, s);
+  return run_split(run, mhc::kModeCoeffs, a, s);
 }
 
 // Coefficients, then pre, of a [T][C] stream broadcast to the 4 routes.
@@ -335,7 +374,7 @@ int pre_broadcast_impl(const uint16_t* x0, int64_t T, int64_t C, const float* ph
   const Span in[] = {{x0, (size_t)T * C * 2}, phi_span, {bias, 96}, {gamma, (size_t)C * 4}};
   const Span out[] = {{coeffs, (size_t)T * 24 * 4}, {h, (size_t)T * C * 2}};
   if ((rc = check_tensors(in, 4, out, 2))) return rc;
-  if (ws != nullptr && overlaps(Span{ws, mhc::make_plan(T, C).total}, out[1])) return MHC_ERR_ALIAS;
+  if (ws != nullptr && overlaps(Span{ws, workspace_need(T, C)}, out[1])) return MHC_ERR_ALIAS;
   if ((rc = coeffs_impl(x0, T, C, phi, phi_packed, bias, p, coeffs, ws, ws_bytes, stream, true))) return rc;
   return hip_status(
       mhc::launch_pre(x0, C, 0, coeffs, gamma, T, (int)C, p->rmsnorm_eps, h, static_cast<hipStream_t>(stream)));
@@ -492,7 +531,7 @@ int mhc_last_hip_error(void) { return g_last_hip_error; }
 
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags) {
   if (check_shape(T, C) != MHC_OK || (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X))) return 0;
-  return mhc::make_plan(T, C).total;
+  return workspace_need(T, C);
 }
 
 int mhc_schedule(int64_t T, int64_t C, int* schedule) {

@@ -40,7 +40,7 @@ struct Plan {
 // words take at most kStagedBudget bytes.  So a workspace holds about
 // kStagedBudget bytes + 4 per token + the packed projection, whatever T is.
 constexpr int kRingK = 8;
-constexpr int kCoeffsRingTiles = 32;
+constexpr int kCoeffsRingTiles = 64;
 constexpr int kMaxLaneSplits = 256;
 constexpr size_t kStagedBudget = (size_t)32 << 20;
 
@@ -97,13 +97,20 @@ struct SplitArgs {
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
   uint64_t* release;   // [kCoeffsRingTiles] coefficients-only ring: generation of each slot's gathered tile
   uint64_t* fix_word;  // (launch tag << 32) | number of tokens in fix_list (fixed offset)
-  uint32_t* fix_list;  // [T] tokens whose fused pre is recomputed directly (k_pre_fix)
+  uint32_t* fix_list;  // [T] tokens whose fused pre is recomputed directly (fix_flagged)
   uint32_t* err;
   const int8_t* y_q;      // int8 y [T][C] and its per-token scales [T] (fused modes with kModeYInt8)
   const float* y_scale;
   int64_t T;
-  int64_t xts, xrs;    // element strides of x between tokens and between routes: 4C and C, or C and 0
-                       // for a [T][C] stream broadcast to the 4 routes (coefficients mode only)
+  int64_t xts, xrs;    // element strides of x between tokens and between routes: 4C and C, or (a
+                       // [T][C] stream broadcast to the routes, coefficients mode only) C and 0, or
+                       // C and 128 for its pseudo-routes (see cs)
+  int cs;              // channels per split in x's channel space: 128, or 512 for a broadcast stream
+                       // split into 4 pseudo-routes of 128 consecutive channels
+  int prs;             // rows of the packed projection between two routes: C, or 128 (pseudo-routes
+                       // over a route-summed projection of C rows)
+  int rms_c;           // the RMS scale divides the sum of squares by 4 rms_c: C, or C / 4 when the
+                       // split rows cover each channel of a broadcast stream once instead of 4 times
   uint32_t tiles;
   int C;
   int S;
@@ -113,17 +120,18 @@ struct SplitArgs {
   Scalars sc;
 };
 
-// kModeCoeffsBcast: coefficients of a [T][C] stream that stands for all 4
-// routes (route stride 0); the persistent schedule loads each chunk once and
-// stages it for the 4 routes, the staged one reads it once per route.
 // kModeYInt8 is a flag on the fused modes: y arrives as int8 codes with one
 // binary32 scale per token.
-enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2, kModeCoeffsBcast = 3, kModeYInt8 = 4 };
+enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2, kModeYInt8 = 4 };
 constexpr bool mode_fused(int m) { return (m & 3) == kModeFused || (m & 3) == kModeFusedMx; }
 constexpr bool mode_mx(int m) { return (m & 3) == kModeFusedMx; }
 constexpr bool mode_yq(int m) { return (m & kModeYInt8) != 0; }
 
 hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s);
+// Packed route-summed projection of C rows, Phi[c] = ((phi[c] + phi[C+c]) +
+// phi[2C+c]) + phi[3C+c], from fp32 phi or (phi == NULL) from the packed
+// 4-route projection `packed`.
+hipError_t launch_pack_phi_sum(const float* phi, const void* packed, int C, void* out, hipStream_t s);
 hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStream_t s);
 hipError_t launch_post(const uint16_t* x, const uint16_t* y, const float* cf, int64_t T, int C,
                        uint16_t* x_out, hipStream_t s);
@@ -132,8 +140,8 @@ hipError_t launch_post_int8(const uint16_t* x, const int8_t* y_q, const float* y
 hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
                       int C, float rmsnorm_eps, uint16_t* h, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-// The direct recomputation of the pre of the tokens a fused launch flagged
-// (always launched after it: the flagged count is read on the device).
-hipError_t launch_pre_fix(const SplitArgs& a, bool mx, hipStream_t s);
+// After a persistent fused launch: the direct pre of the tokens it listed
+// (the count is read on the device, so it is always launched).
+hipError_t launch_fix_flagged(const SplitArgs& a, int mode, hipStream_t s);
 
 }  // namespace mhc

@@ -73,6 +73,80 @@ __global__ __launch_bounds__(256) void k_pack_phi(const float* __restrict__ phi,
   for (int b = 0; b < kPackBlocks; ++b) out[(q * kPackBlocks + b) * kWave + lane] = pack8(t[b]);
 }
 
+// hi, mid and lo of one fp32 value (their sum is the value for |v| >= 2^-100)
+__device__ __forceinline__ void split3(float v, float& hi, float& mid, float& lo) {
+  hi = bf16_round_f(v);
+  const float r1 = v - hi;
+  mid = bf16_round_f(r1);
+  lo = bf16_round_f(r1 - mid);
+}
+
+// The projection of a broadcast stream summed over its routes, packed like
+// k_pack_phi packs a projection of C rows: Phi[c][m] = ((phi[c][m] +
+// phi[C + c][m]) + phi[2C + c][m]) + phi[3C + c][m] in fp32.  PACKED: the
+// route values come from the 4-route packed layout (hi + mid + lo, exact in
+// fp32), so both inputs give the same bits.  One thread per (32-row k-step,
+// fragment lane), as in k_pack_phi.
+template <bool PACKED>
+__global__ __launch_bounds__(256) void k_pack_phi_sum(const float* __restrict__ phi, const u32x4_t* __restrict__ pk,
+                                                      int C, u32x4_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)(C / 32) * kWave;
+  if (idx >= total) return;
+  const int lane = (int)(idx & 63);
+  const int64_t q = idx >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int lo16 = 16 * g + (n16 & 7);  // block 3/4 lane of logit 16 + n16 % 8 (hi/lo; mid at + 8)
+  float va[8], vb[8];  // route sums of logit n16 and of logit 16 + n16 % 8, rows 32q + 8g + e
+#pragma unroll
+  for (int e = 0; e < 8; ++e) va[e] = vb[e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float ra[8], rb[8];
+    if constexpr (PACKED) {
+      const u32x4_t* f = pk + ((int64_t)j * (C / 32) + q) * (kPackBlocks * kWave);
+      float h0[8], m0[8], l0[8], h1[8], m1[8], l1[8];
+      unpack8(f[0 * kWave + lane], h0);
+      unpack8(f[1 * kWave + lane], m0);
+      unpack8(f[2 * kWave + lane], l0);
+      unpack8(f[3 * kWave + lo16], h1);
+      unpack8(f[3 * kWave + lo16 + 8], m1);
+      unpack8(f[4 * kWave + lo16], l1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ra[e] = (h0[e] + m0[e]) + l0[e];
+        rb[e] = (h1[e] + m1[e]) + l1[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float* row = phi + ((int64_t)j * C + q * 32 + g * 8 + e) * kCoeffs;
+        ra[e] = row[n16];
+        rb[e] = row[16 + (n16 & 7)];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      va[e] = j == 0 ? ra[e] : va[e] + ra[e];
+      vb[e] = j == 0 ? rb[e] : vb[e] + rb[e];
+    }
+  }
+  float t[5][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float hi, mid, lo;
+    split3(va[e], hi, mid, lo);
+    t[0][e] = hi;
+    t[1][e] = mid;
+    t[2][e] = lo;
+    split3(vb[e], hi, mid, lo);
+    t[3][e] = n16 < 8 ? hi : mid;
+    t[4][e] = n16 < 8 ? lo : 0.0f;
+  }
+#pragma unroll
+  for (int b = 0; b < kPackBlocks; ++b) out[(q * kPackBlocks + b) * kWave + lane] = pack8(t[b]);
+}
+
 // ===========================================================================
 // Split-row kernel (a staggered pipeline over tiles).
 //
@@ -168,9 +242,19 @@ __device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_flo
 // have wrapped the epoch), whichever layout each launch used.
 __device__ __forceinline__ uint32_t ring_tag(uint32_t tag, uint32_t gen) { return 2u * tag + (gen & 1u); }
 
+__device__ __forceinline__ void store_sys32(void* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint32_t load_sys32(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Appends token t to the workspace list of tokens whose fused pre is
-// recomputed directly.  The count is a tagged word: a count left by an
-// earlier launch (older tag) counts as zero, so no launch has to clear it.
+// recomputed directly (fix_flagged).  The count is a tagged word: a count
+// left by an earlier launch (older tag) counts as zero, so no launch has to
+// clear it.  The entry is written through to memory (system scope), where
+// the launch's last workgroup reads it.
 __device__ __forceinline__ void flag_for_fix(const SplitArgs& a, uint32_t tag, int64_t t) {
   uint64_t old = __hip_atomic_load(a.fix_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t idx;
@@ -183,7 +267,7 @@ __device__ __forceinline__ void flag_for_fix(const SplitArgs& a, uint32_t tag, i
       break;
     }
   }
-  if ((int64_t)idx < a.T) a.fix_list[idx] = (uint32_t)t;
+  if ((int64_t)idx < a.T) store_sys32(a.fix_list + idx, (uint32_t)t);
 }
 
 // DPP lane moves inside rows of 16 lanes (no LDS traffic): quad_perm swaps
@@ -200,7 +284,7 @@ constexpr int kDppRowRor8 = 0x128;   // row_ror:8
 // the 4x4 matrix are sums over lane ^ {1, 2}, column sums over the 16-lane
 // row rotated by 4, 8, 12.  Each normalisation multiplies by the reciprocal
 // of (sum + eps).  Returns in every lane the value of coefficient
-// slot(lane).  In the fused modes publish(q, cancels), q_i = pre_i * r_h,
+// slot(lane).  In the fused modes publish(q, pre, cancels), q_i = pre_i * r_h,
 // runs before the Sinkhorn iterations: the pre step needs only q, so it does
 // not wait for them; `cancels` says that the token's pre must be recomputed
 // directly (gram_rms_factor).
@@ -222,7 +306,7 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
     bool cancels;
     const float rh = gram_rms_factor(sums + 24, p, C, sc.rmsnorm_eps, cancels);
     const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
-    publish(q, cancels);
+    publish(q, p, cancels);
   }
   const float eps = sc.sinkhorn_eps;
   for (int it = 0; it < sc.sinkhorn_iters; ++it) {
@@ -241,7 +325,7 @@ __device__ __forceinline__ float finalize_wave(const float* sums, const float* b
 // of the row's token and, for k < 8, its pre (k < 4) or post (4 <= k < 8)
 // weight.  The Sinkhorn row and column sums are the same row-local DPP
 // moves, so the four rows run side by side.  sums: this lane's token.
-// publish(q, cancels) of the fused modes runs before the Sinkhorn iterations.
+// publish(q, pre, cancels) of the fused modes runs before the Sinkhorn iterations.
 template <bool FUSED, class Publish>
 __device__ __forceinline__ void finalize_rows(const float* sums, const float* bias, int C, const Scalars& sc,
                                               int lane, float& res, float& pp, Publish&& publish) {
@@ -257,7 +341,7 @@ __device__ __forceinline__ void finalize_rows(const float* sums, const float* bi
     bool cancels;
     const float rh = gram_rms_factor(sums + 24, p, C, sc.rmsnorm_eps, cancels);
     const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
-    publish(q, cancels);
+    publish(q, p, cancels);
   }
   const float l = r * sums[8 + k] + bias[8 + k];
   float v = expf(l);
@@ -317,6 +401,121 @@ __device__ __forceinline__ void y_pair(const u32x4_t& v, int q, float& lo, float
   } else {
     lo = bf16_lo(v[q]);
     hi = bf16_hi(v[q]);
+  }
+}
+
+// g = ((p0 x0 + p1 x1) + p2 x2) + p3 x3 in binary64: the product of an fp32
+// weight and a bf16 value is exact there, so routes that cancel exactly give
+// exactly 0 and nearly cancelling ones keep their leading bits.
+__device__ __forceinline__ double combine_f64(const double* p, float x0, float x1, float x2, float x3) {
+  double g = p[0] * (double)x0;
+  g = __builtin_fma(p[1], (double)x1, g);
+  g = __builtin_fma(p[2], (double)x2, g);
+  g = __builtin_fma(p[3], (double)x3, g);
+  return g;
+}
+
+// x' of 8 channels of token t, all 4 routes, from the inputs: the post chain
+// of post_tile, bit for bit what x_out holds.  pw, rs: the token's post and
+// res coefficients.
+template <bool YQ>
+__device__ __forceinline__ void xprime8(const SplitArgs& a, int64_t t, int c, const float* pw, const float* rs,
+                                        float (*xp)[8]) {
+  u32x4_t xin[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xin[i] = ld16(a.x + t * a.xts + (int64_t)i * a.xrs + c);
+  const u32x4_t yv = load_y8<YQ, false>(a, t, c);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float xl[4] = {bf16_lo(xin[0][q]), bf16_lo(xin[1][q]), bf16_lo(xin[2][q]), bf16_lo(xin[3][q])};
+    const float xh[4] = {bf16_hi(xin[0][q]), bf16_hi(xin[1][q]), bf16_hi(xin[2][q]), bf16_hi(xin[3][q])};
+    float yl, yh;
+    y_pair<YQ>(yv, q, yl, yh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t o = pack_bf16x2(post_chain(pw[j], yl, &rs[4 * j], xl[0], xl[1], xl[2], xl[3]),
+                                     post_chain(pw[j], yh, &rs[4 * j], xh[0], xh[1], xh[2], xh[3]));
+      xp[j][2 * q] = bf16_lo(o);
+      xp[j][2 * q + 1] = bf16_hi(o);
+    }
+  }
+}
+
+// The direct pre of the tokens a fused launch listed because their route
+// combination cancels (gram_rms_factor): run by the staged launch's last
+// workgroup (NT threads), once every other workgroup has left, or by
+// k_fix_flagged after a persistent launch; either way the list and the
+// listed tokens' pre weights (written through to memory before the tokens'
+// q words) are complete.  Per token: x' recomputed from x, y and the post
+// coefficients (inputs only, so nothing another XCD wrote is read), g in
+// binary64, sum_c g^2 in binary64, then h and its MXFP8 blocks written; the
+// pre step left these tokens' rows unwritten (the sign of q0).  A launch
+// with no listed token only reads the count.
+template <bool YQ, bool MX, int NT>
+__device__ void fix_flagged(const SplitArgs& a, uint32_t tag, double* red, uint32_t first = 0, uint32_t stride = 1) {
+  const int tid = threadIdx.x;
+  const uint64_t w = __hip_atomic_load(a.fix_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  uint32_t n = (uint32_t)(w >> 32) == tag ? (uint32_t)w : 0u;
+  if ((int64_t)n > a.T) n = (uint32_t)a.T;
+  const int C = a.C, nch = C >> 3;
+  for (uint32_t k = first; k < n; k += stride) {
+    const int64_t t = load_sys32(a.fix_list + k);
+    double p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = (double)__uint_as_float(load_sys32(a.coeffs_out + t * kCoeffs + i));
+    float pw[4], rs[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = a.coeffs_in[t * kCoeffs + 4 + i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rs[i] = a.coeffs_in[t * kCoeffs + 8 + i];
+    double ss = 0.0;
+    for (int j = tid; j < nch; j += NT) {
+      float xp[4][8];
+      xprime8<YQ>(a, t, 8 * j, pw, rs, xp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double g = combine_f64(p, xp[0][e], xp[1][e], xp[2][e], xp[3][e]);
+        ss = __builtin_fma(g, g, ss);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    double tot = red[0];
+#pragma unroll
+    for (int wv = 1; wv < NT / 64; ++wv) tot += red[wv];
+    const double rh = 1.0 / sqrt(tot / (double)C + (double)a.sc.rmsnorm_eps);
+    for (int j = tid; j < nch; j += NT) {
+      float xp[4][8];
+      xprime8<YQ>(a, t, 8 * j, pw, rs, xp);
+      const float4* gp = reinterpret_cast<const float4*>(a.gamma + 8 * j);
+      const float4 g0 = gp[0], g1 = gp[1];
+      const float gmv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      float hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        hv[e] = (float)(combine_f64(p, xp[0][e], xp[1][e], xp[2][e], xp[3][e]) * rh * (double)gmv[e]);
+      const u32x4_t hb = pack8(hv);
+      if (a.h != nullptr) st16(a.h + t * (int64_t)C + 8 * j, hb);
+      if constexpr (MX) {
+        // a 32-channel block is the chunks 4b .. 4b+3: lanes tid ^ {1, 2}
+        float hr[8];
+        unpack8(hb, hr);
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+        const int ex = mx_scale_exponent(amax);
+        const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
+        const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
+        const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
+        *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + 8 * j) = u32x2_t{w0, w1};
+        if ((j & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (j >> 2)] = (uint8_t)(ex + 127);
+      }
+    }
+    __syncthreads();  // red[] is reused by the next token
   }
 }
 
@@ -440,7 +639,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   const int tR = (stage - a.d1 >= 0 && stage - a.d1 < tiles) ? stage - a.d1 : -1;
   const int tC = (FUSED && stage - a.d2 >= 0 && stage - a.d2 < tiles) ? stage - a.d2 : -1;
   const int C = a.C;
-  const int c0 = split * kCC;
+  const int c0 = split * a.cs;
   const int c8 = tid & 15, tr = tid >> 4;
   const int cl = c0 + c8 * 8;  // this lane's first channel in A and C
   const int n16 = lane & 15, g = lane >> 4;
@@ -517,7 +716,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
     u32x4_t bfrag[4][kPackBlocks];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t kstep = ((int64_t)j * C + c0 + wave * 32) >> 5;
+      const int64_t kstep = ((int64_t)j * a.prs + c0 + wave * 32) >> 5;
       const u32x4_t* bp = reinterpret_cast<const u32x4_t*>(a.phi_packed) + kstep * (kPackBlocks * kWave) + lane;
 #pragma unroll
       for (int b = 0; b < kPackBlocks; ++b) bfrag[j][b] = bp[b * kWave];
@@ -656,10 +855,20 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         const int m = split + kq * S;
         uint64_t* const qdst = a.publish + ((int64_t)tR * TM + m) * 4 + (lane & 3);
         const int64_t t = tok0 + m;
-        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, C, a.sc, lane,
-                                              [=](const float* q, bool cancels) __attribute__((always_inline)) {
-                                                if (lane < 4) tagged_store(qdst, q[lane & 3], wtag);
-                                                if (cancels && lane == 0 && t < a.T) flag_for_fix(a, tag, t);
+        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, a.rms_c, a.sc, lane,
+                                              [=](const float* q, const float* pw, bool cancels)
+                                                  __attribute__((always_inline)) {
+                                                // a cancelling token: listed (and its pre weights written
+                                                // through) before its q words, whose sign bit on q0 tells
+                                                // the pre step to leave its h to the recomputation
+                                                if (cancels && t < a.T) {
+                                                  if (lane < 4) store_sys32(a.coeffs_out + t * kCoeffs + lane,
+                                                                            __float_as_uint(pw[lane & 3]));
+                                                  if (lane == 0) flag_for_fix(a, tag, t);
+                                                  __builtin_amdgcn_s_waitcnt(0);
+                                                }
+                                                const float qv = q[lane & 3];
+                                                if (lane < 4) tagged_store(qdst, (lane == 0 && cancels) ? -qv : qv, wtag);
                                               });
         if (t < a.T && lane < 24) a.coeffs_out[t * kCoeffs + (lane < 16 ? 8 + lane : lane - 16)] = cv;
       }
@@ -692,6 +901,9 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         const int64_t t = tok0 + m;
         const bool valid = t < a.T;
         const float q0 = qs[m][0], q1 = qs[m][1], q2 = qs[m][2], q3 = qs[m][3];
+        // a negative q0 marks a token whose h the launch's last workgroup
+        // recomputes directly (fix_flagged): its stores are left to that
+        const bool keep = valid && !__builtin_signbit(q0);
         float xv[4][8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) unpack8(rc.x[p][i], xv[i]);
@@ -705,7 +917,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
           hv[e] = vv * gm[e];
         }
         const u32x4_t hb = pack8(hv);
-        if (a.h != nullptr && valid) st16_stream(a.h + t * (int64_t)C + cl, hb);
+        if (a.h != nullptr && keep) st16_stream(a.h + t * (int64_t)C + cl, hb);
         if constexpr (MX) {
           // a 32-channel block is the 4 lanes c8 = 4b .. 4b+3
           float hr[8];
@@ -719,7 +931,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
           const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
           const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
           const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
-          if (valid) {
+          if (keep) {
             *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + cl) = u32x2_t{w0, w1};
             if ((c8 & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
           }
@@ -732,10 +944,14 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // The last of a tile's S final consumers (C in the fused modes, R in the
   // coeffs mode) counts the tile done; the one that completes the last tile
   // advances the launch epoch.
+  // In the fused modes that workgroup then recomputes the pre of the tokens
+  // whose route combination cancels (every tile's pre steps have run, so the
+  // list is complete).
   const int tLeave = FUSED ? tC : tR;
   if (tLeave >= 0) {
     __syncthreads();
     if (tid == 0) {
+      uint32_t last = 0;
       const uint32_t old = __hip_atomic_fetch_add(a.dep + tLeave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (old == (uint32_t)S - 1u) {
         __hip_atomic_store(a.dep + tLeave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -743,8 +959,14 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         if (done == a.tiles - 1u) {
           __hip_atomic_store(a.tiles_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last = 1;
         }
       }
+      s_xdirect = last;  // (no longer needed for its first use: reused as the flag)
+    }
+    if constexpr (FUSED) {
+      __syncthreads();
+      if (s_xdirect != 0) fix_flagged<YQ, MX, 256>(a, tag, reinterpret_cast<double*>(lds));
     }
   }
 }
@@ -871,7 +1093,6 @@ template <int MODE>
 __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs a) {
   constexpr bool FUSED = mode_fused(MODE);
   constexpr bool YQ = mode_yq(MODE);
-  constexpr bool BCAST = MODE == kModeCoeffsBcast;
   constexpr bool MX = mode_mx(MODE);
   constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
   // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
@@ -964,6 +1185,84 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // release word gets its generation (the full number, in the value
       // field), and stream workgroups wait for it before refilling the slot.
       static_assert(kCoeffsRingTiles % 32 == 0, "one reduce workgroup per ring slot");
+      // finalise tile t from the sums in LDS (every wave four tokens), then
+      // the coefficients out
+      auto finalize_tile = [&](int t) __attribute__((always_inline)) {
+        const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
+        const int64_t tok = (int64_t)t * TM + ml;
+        float res, pp;
+        finalize_rows<false>(finw + ml * NV, a.bias, a.rms_c, a.sc, lane, res, pp,
+                             [](const float*, const float*, bool) {});
+        if (tok < a.T) {
+          a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
+          if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
+        }
+      };
+      if (S <= 16) {
+        // Few splits (a broadcast stream on pseudo-routes): thread v takes
+        // the words v and v + 512 of the tile's TM * 25, both in one round
+        // of loads, and the next tile's loads are issued before this tile
+        // is finalised, so the gather latency overlaps the finalisation.
+        constexpr int NWT = TM * kCoeffsWords;  // 800
+        uint64_t w0[16], w1[16];
+        const bool has1 = tid + kPersistThreads < NWT;
+        auto issue = [&](int t) __attribute__((always_inline)) {
+          const uint64_t* base = a.partials + (int64_t)(t % kCoeffsRingTiles) * S * pstride + tid;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            w0[k] = k < S ? tagged_load(base + k * pstride) : 0;
+            w1[k] = k < S && has1 ? tagged_load(base + k * pstride + kPersistThreads) : 0;
+          }
+        };
+        auto settle = [&](int t) __attribute__((always_inline)) {
+          const uint64_t* base = a.partials + (int64_t)(t % kCoeffsRingTiles) * S * pstride + tid;
+          const uint32_t wt = ring_tag(tag, (uint32_t)(t / kCoeffsRingTiles));
+          auto stale = [&]() __attribute__((always_inline)) {
+            bool st = false;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+              st |= k < S && ((uint32_t)(w0[k] >> 32) != wt || (has1 && (uint32_t)(w1[k] >> 32) != wt));
+            return st;
+          };
+          if (stale()) {
+            uint32_t it = 0;
+            do {
+              __builtin_amdgcn_s_sleep(1);
+              if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
+                __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+              }
+#pragma unroll
+              for (int k = 0; k < 16; ++k) {
+                if (k < S && (uint32_t)(w0[k] >> 32) != wt) w0[k] = tagged_load(base + k * pstride);
+                if (k < S && has1 && (uint32_t)(w1[k] >> 32) != wt) w1[k] = tagged_load(base + k * pstride + kPersistThreads);
+              }
+            } while (stale());
+          }
+          float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            s0 += k < S ? tagged_value(w0[k]) : 0.0f;
+            s1 += k < S ? tagged_value(w1[k]) : 0.0f;
+          }
+          finw[(tid / kCoeffsWords) * NV + tid % kCoeffsWords] = s0;
+          if (has1) {
+            const int v1 = tid + kPersistThreads;
+            finw[(v1 / kCoeffsWords) * NV + v1 % kCoeffsWords] = s1;
+          }
+        };
+        if (j < tiles) issue(j);
+        for (int t = j; t < tiles; t += nred) {
+          settle(t);
+          __syncthreads();  // the tile's sums (every gather load has returned)
+          if (tid == 0)
+            tagged_store(a.release + t % kCoeffsRingTiles, __uint_as_float((uint32_t)(t / kCoeffsRingTiles)),
+                         ring_tag(tag, 0));
+          if (t + nred < tiles) issue(t + nred);
+          finalize_tile(t);
+          __syncthreads();  // this tile's sums are read
+        }
+      } else
       for (int t = j; t < tiles; t += nred) {
         const int slot = t % kCoeffsRingTiles;
         const uint32_t gen = (uint32_t)(t / kCoeffsRingTiles);
@@ -985,14 +1284,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
         __syncthreads();  // the tile's sums (every gather load has returned)
         if (tid == 0) tagged_store(a.release + slot, __uint_as_float(gen), ring_tag(tag, 0));
-        const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
-        const int64_t tok = (int64_t)t * TM + ml;
-        float res, pp;
-        finalize_rows<false>(finw + ml * NV, a.bias, C, a.sc, lane, res, pp, [](const float*, bool) {});
-        if (tok < a.T) {
-          a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
-          if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
-        }
+        finalize_tile(t);
         __syncthreads();  // this tile's sums are read
       }
     } else {
@@ -1028,11 +1320,21 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           // every row of the tile is published ([R][TM][4] words): the
           // stream workgroups poll whole row blocks, padding rows included
           finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp,
-                               [&](const float* q, bool cancels) __attribute__((always_inline)) {
+                               [&](const float* q, const float* pw, bool cancels) __attribute__((always_inline)) {
+                                 // a cancelling token: listed (and its pre weights written through)
+                                 // before its q words, whose sign bit on q0 tells the pre step to
+                                 // leave its h to the recomputation
+                                 if (cancels && tok < a.T) {
+                                   if (kk < 4)
+                                     store_sys32(a.coeffs_out + tok * kCoeffs + kk,
+                                                 __float_as_uint(kk == 0 ? pw[0] : kk == 1 ? pw[1] : kk == 2 ? pw[2] : pw[3]));
+                                   if (kk == 0) flag_for_fix(a, tag, tok);
+                                   __builtin_amdgcn_s_waitcnt(0);
+                                 }
                                  if (kk < 4)
                                    tagged_store(a.publish + ptok * 4 + kk,
-                                                kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], qtag);
-                                 if (cancels && kk == 0 && tok < a.T) flag_for_fix(a, tag, tok);
+                                                kk == 0 ? (cancels ? -q[0] : q[0]) : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3],
+                                                qtag);
                                });
           if (tok < a.T) {
             a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
@@ -1047,7 +1349,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   } else {
     // ------------------------- stream workgroup -------------------------
     const int split = (int)blockIdx.x % S, r = (int)blockIdx.x / S;
-    const int c0 = split * kCC;
+    const int c0 = split * a.cs;
     const int n16 = lane & 15, g = lane >> 4;
     // (wave index made provably uniform, so that branches on the row block
     // are scalar and buffer resources stay in scalar registers)
@@ -1066,7 +1368,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       for (int idx = tid; idx < 16 * kPhiFrag; idx += kPersistThreads) {
         const int jk = idx / kPhiFrag, o = idx % kPhiFrag;
         const int jr = jk >> 2, kq = jk & 3;
-        const int64_t kstep = ((int64_t)jr * C + c0 + kq * 32) >> 5;
+        const int64_t kstep = ((int64_t)jr * a.prs + c0 + kq * 32) >> 5;
         int b, ln;
         if (o < 4 * kWave) {
           b = o >> 6;
@@ -1105,17 +1407,9 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // (issued unconditionally, so that the compiler's wait counts never
       // merge paths with and without the loads: past the last tile every
       // lane reads the first 16 bytes of x, whose value is not used)
-      // (a broadcast stream: one chunk per thread, token gt / 16, chunk
-      // gt % 16, staged for all 4 routes)
       auto load_x = [&](u32x4_t* dst, int i) __attribute__((always_inline)) {
         const bool ok = i < niter;
         const int64_t tok0 = (int64_t)(r + L * i) * TM + rb * 16;
-        if constexpr (BCAST) {
-          const int64_t tok = tok0 + (gt >> 4);
-          const int64_t off = (tok < a.T ? tok : 0) * a.xts + c0 + 8 * (gt & 15);
-          dst[0] = ld16_stream(a.x + (ok ? off : 0));
-          return;
-        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int q = gt + 256 * k, row = q >> 4;
@@ -1125,12 +1419,6 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
       };
       auto stage_write = [&](const u32x4_t* src) __attribute__((always_inline)) {
-        if constexpr (BCAST) {
-          const int tt = gt >> 4;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) stage[(tt * 4 + k) * 16 + ((gt & 15) ^ tt)] = src[0];
-          return;
-        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int q = gt + 256 * k, row = q >> 4;
@@ -1364,6 +1652,10 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         const int64_t tokC0 = (int64_t)(r + L * (i - D)) * TM + rb * 16;
         const uint32_t nC = (uint32_t)max((int64_t)0, min((int64_t)16, a.T - tokC0));
         const float q0 = qs[m][0], q1 = qs[m][1], q2 = qs[m][2], q3 = qs[m][3];
+        // a negative q0 marks a token whose h the launch's last workgroup
+        // recomputes directly (fix_flagged): its stores go past the end of
+        // the buffer range, where the hardware drops them
+        const uint32_t drop = __builtin_signbit(q0) ? 0x80000000u : 0u;
         float hv[8];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
@@ -1386,7 +1678,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         const u32x4_t hb = pack8(hv);
         if (!MX || a.h != nullptr)
           __builtin_amdgcn_raw_buffer_store_b128(hb, buffer_rsrc(a.h + tokC0 * C, nC * (uint32_t)(2 * C)),
-                                                 (n16 * C + cl) * 2, 0, 0);
+                                                 ((n16 * C + cl) * 2) | drop, 0, 0);
         if constexpr (MX) {
           // a 32-channel block is the 4 lanes n16, n16 + 16, n16 + 32, n16 + 48
           float hr[8];
@@ -1401,11 +1693,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
           const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
           __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, buffer_rsrc(a.h_fp8 + tokC0 * C, nC * (uint32_t)C),
-                                                n16 * C + cl, 0, 0);
+                                                (n16 * C + cl) | drop, 0, 0);
           // the block's four lanes store the same scale byte
           __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(ex + 127),
                                                buffer_rsrc(a.h_scale + tokC0 * (C / 32), nC * (uint32_t)(C / 32)),
-                                               n16 * (C / 32) + (cl >> 5), 0, 0);
+                                               (n16 * (C / 32) + (cl >> 5)) | drop, 0, 0);
         }
       }
       if constexpr (FUSED) {
@@ -1665,6 +1957,9 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   }
 
   // ---- leave: the last workgroup to finish advances the launch epoch ----
+  // (The listed tokens of a fused launch are recomputed by k_fix_flagged,
+  // launched after this kernel: the recomputation inlined here raised the
+  // register allocation of the whole kernel and slowed its main loop.)
   __syncthreads();
   if (tid == 0) {
     const uint32_t done = __hip_atomic_fetch_add(a.tiles_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1673,6 +1968,16 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// The direct pre of the tokens a persistent fused launch listed (see
+// fix_flagged), launched after it on the same stream; its tag is the epoch
+// the launch left.  Workgroup b takes the listed tokens b, b + grid, ...
+template <bool YQ, bool MX>
+__global__ __launch_bounds__(256) void k_fix_flagged(const SplitArgs a) {
+  __shared__ double red[4];
+  const uint32_t tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  fix_flagged<YQ, MX, 256>(a, tag, red, blockIdx.x, gridDim.x);
 }
 
 // ===========================================================================
@@ -1734,34 +2039,26 @@ __device__ __forceinline__ float block128_sum(float v, float* sh) {
   return sh[0] + sh[1];
 }
 
-// g = ((p0 x0 + p1 x1) + p2 x2) + p3 x3 in binary64: the product of an fp32
-// weight and a bf16 value is exact there, so routes that cancel exactly give
-// exactly 0 and nearly cancelling ones keep their leading bits.
-__device__ __forceinline__ double combine_f64(const double* p, float x0, float x1, float x2, float x3) {
-  double g = p[0] * (double)x0;
-  g = __builtin_fma(p[1], (double)x1, g);
-  g = __builtin_fma(p[2], (double)x2, g);
-  g = __builtin_fma(p[3], (double)x3, g);
-  return g;
-}
 
-// B: a broadcast stream (route stride 0): the 4 routes are one load.
-// g is combined in binary64 and kept as its nearest fp32 value.
+// g of 8 channels: the 4 routes combined in binary64 and kept as the nearest
+// fp32 value.  B: a broadcast stream (route stride 0), whose routes are all
+// x0: g = psum * x0 with psum = ((p0 + p1) + p2) + p3 in fp32 (no
+// cancellation is possible, every pre weight being positive).
 template <bool B>
-__device__ __forceinline__ void pre_group(const uint16_t* xr, int64_t xrs, int c, const double* p, float* gv) {
-  float xv[4][8];
+__device__ __forceinline__ void pre_group(const uint16_t* xr, int64_t xrs, int c, const double* p, float psum,
+                                          float* gv) {
   if constexpr (B) {
-    unpack8(ld16_stream(xr + c), xv[0]);
+    float x0[8];
+    unpack8(ld16_stream(xr + c), x0);
 #pragma unroll
-    for (int i = 1; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xv[i][e] = xv[0][e];
+    for (int e = 0; e < 8; ++e) gv[e] = psum * x0[e];
   } else {
+    float xv[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) unpack8(ld16_stream(xr + (int64_t)i * xrs + c), xv[i]);
-  }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) gv[e] = (float)combine_f64(p, xv[0][e], xv[1][e], xv[2][e], xv[3][e]);
+    for (int e = 0; e < 8; ++e) gv[e] = (float)combine_f64(p, xv[0][e], xv[1][e], xv[2][e], xv[3][e]);
+  }
 }
 
 __device__ __forceinline__ void pre_store(uint16_t* hr, const float* gamma, int c, const float* gv, float rh) {
@@ -1783,12 +2080,13 @@ __global__ __launch_bounds__(128) void k_pre(const uint16_t* __restrict__ x, int
   const int k = threadIdx.x;
   const float4 pq = *reinterpret_cast<const float4*>(cf + t * kCoeffs);
   const double p[4] = {pq.x, pq.y, pq.z, pq.w};
+  const float psum = ((pq.x + pq.y) + pq.z) + pq.w;
   const uint16_t* xr = x + t * xts;
   float gv[G][8];
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, gv[j]);
+    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, psum, gv[j]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(gv[j][e], gv[j][e], ss);
   }
@@ -1808,12 +2106,13 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
   const int k = threadIdx.x;
   const float4 pq = *reinterpret_cast<const float4*>(cf + t * kCoeffs);
   const double p[4] = {pq.x, pq.y, pq.z, pq.w};
+  const float psum = ((pq.x + pq.y) + pq.z) + pq.w;
   const uint16_t* xr = x + t * xts;
   const int G = C >> 10;
   float ss = 0.0f;
   for (int j = 0; j < G; ++j) {
     float gv[8];
-    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, gv);
+    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, psum, gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(gv[e], gv[e], ss);
   }
@@ -1822,87 +2121,8 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
   uint16_t* hr = h + t * (int64_t)C;
   for (int j = 0; j < G; ++j) {
     float gv[8];
-    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, gv);
+    pre_group<B>(xr, xrs, (j * 128 + k) * 8, p, psum, gv);
     pre_store(hr, gamma, (j * 128 + k) * 8, gv, rh);
-  }
-}
-
-// ===========================================================================
-// Direct pre of the tokens a fused launch flagged (gram_rms_factor): their
-// route combination cancels, so the sum of squares from the Gram matrix is
-// not accurate enough.  One workgroup per flagged token (grid-stride over
-// the list): g from x' = x_out and pre' = coeffs_next[0..3] in binary64,
-// sum_c g^2 in binary64, then h (and its MXFP8 blocks) rewritten.  The count
-// is read on the device, so the kernel is always launched after a fused pass
-// (an empty list costs one launch) and the pair can be captured in a graph.
-// ===========================================================================
-template <bool MX>
-__global__ __launch_bounds__(256) void k_pre_fix(const SplitArgs a) {
-  __shared__ double part[4];
-  __shared__ uint32_t s_n;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    // the fused launch that just ended left its own tag in the epoch
-    const uint32_t tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t w = __hip_atomic_load(a.fix_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t n = (uint32_t)(w >> 32) == tag ? (uint32_t)w : 0u;
-    s_n = (int64_t)n < a.T ? n : (uint32_t)a.T;
-  }
-  __syncthreads();
-  const uint32_t n = s_n;
-  const int C = a.C, nch = C >> 3;
-  for (uint32_t k = blockIdx.x; k < n; k += gridDim.x) {
-    const int64_t t = a.fix_list[k];
-    const float4 pq = *reinterpret_cast<const float4*>(a.coeffs_out + t * kCoeffs);
-    const double p[4] = {pq.x, pq.y, pq.z, pq.w};
-    const uint16_t* xr = a.x_out + t * (int64_t)(4 * C);
-    double ss = 0.0;
-    for (int j = tid; j < nch; j += 256) {
-      float xv[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) unpack8(ld16(xr + (int64_t)i * C + 8 * j), xv[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double g = combine_f64(p, xv[0][e], xv[1][e], xv[2][e], xv[3][e]);
-        ss = __builtin_fma(g, g, ss);
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-    if ((tid & 63) == 0) part[tid >> 6] = ss;
-    __syncthreads();
-    const double rh = 1.0 / sqrt((((part[0] + part[1]) + part[2]) + part[3]) / (double)C + (double)a.sc.rmsnorm_eps);
-    for (int j = tid; j < nch; j += 256) {
-      float xv[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) unpack8(ld16(xr + (int64_t)i * C + 8 * j), xv[i]);
-      const float4* gp = reinterpret_cast<const float4*>(a.gamma + 8 * j);
-      const float4 g0 = gp[0], g1 = gp[1];
-      const float gmv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      float hv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        hv[e] = (float)(combine_f64(p, xv[0][e], xv[1][e], xv[2][e], xv[3][e]) * rh * (double)gmv[e]);
-      const u32x4_t hb = pack8(hv);
-      if (a.h != nullptr) st16(a.h + t * (int64_t)C + 8 * j, hb);
-      if constexpr (MX) {
-        // a 32-channel block is the chunks 4b .. 4b+3: lanes tid ^ {1, 2}
-        float hr[8];
-        unpack8(hb, hr);
-        float amax = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(hr[e]));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
-        const int ex = mx_scale_exponent(amax);
-        const float scale = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex, ex <= 120
-        const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
-        const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
-        *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + 8 * j) = u32x2_t{w0, w1};
-        if ((j & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (j >> 2)] = (uint8_t)(ex + 127);
-      }
-    }
-    __syncthreads();  // part[] is reused by the next token
   }
 }
 
@@ -1918,6 +2138,19 @@ hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s) {
   const int64_t total = (int64_t)(4 * C / 32) * kWave;
   const int64_t blocks = (total + 255) / 256;
   k_pack_phi<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(phi, C, reinterpret_cast<u32x4_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_phi_sum(const float* phi, const void* packed, int C, void* out, hipStream_t s) {
+  const int64_t total = (int64_t)(C / 32) * kWave;
+  const int64_t blocks = (total + 255) / 256;
+  u32x4_t* o = reinterpret_cast<u32x4_t*>(out);
+  if (phi != nullptr) {
+    k_pack_phi_sum<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(phi, nullptr, C, o);
+  } else {
+    k_pack_phi_sum<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(nullptr, reinterpret_cast<const u32x4_t*>(packed),
+                                                                      C, o);
+  }
   return hipGetLastError();
 }
 
@@ -1953,15 +2186,13 @@ hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStrea
       case kModeCoeffs: return launch_persist_mode<kModeCoeffs>(plan, a, s);
       case kModeFused: return launch_persist_mode<kModeFused>(plan, a, s);
       case kModeFusedMx: return launch_persist_mode<kModeFusedMx>(plan, a, s);
-      case kModeCoeffsBcast: return launch_persist_mode<kModeCoeffsBcast>(plan, a, s);
       case kModeFused | kModeYInt8: return launch_persist_mode<kModeFused | kModeYInt8>(plan, a, s);
       case kModeFusedMx | kModeYInt8: return launch_persist_mode<kModeFusedMx | kModeYInt8>(plan, a, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (mode) {
-    case kModeCoeffs:
-    case kModeCoeffsBcast: return launch_split_mode<kModeCoeffs>(plan, a, s);
+    case kModeCoeffs: return launch_split_mode<kModeCoeffs>(plan, a, s);
     case kModeFused: return launch_split_mode<kModeFused>(plan, a, s);
     case kModeFusedMx: return launch_split_mode<kModeFusedMx>(plan, a, s);
     case kModeFused | kModeYInt8: return launch_split_mode<kModeFused | kModeYInt8>(plan, a, s);
@@ -2013,13 +2244,16 @@ hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* 
   return hipGetLastError();
 }
 
-hipError_t launch_pre_fix(const SplitArgs& a, bool mx, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.T < 128 ? a.T : 128);
+hipError_t launch_fix_flagged(const SplitArgs& a, int mode, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.T < 32 ? a.T : 32);
   if (grid == 0) return hipSuccess;
-  if (mx) {
-    k_pre_fix<true><<<dim3(grid), dim3(256), 0, s>>>(a);
-  } else {
-    k_pre_fix<false><<<dim3(grid), dim3(256), 0, s>>>(a);
+  const dim3 g(grid), b(256);
+  switch (mode) {
+    case kModeFused: k_fix_flagged<false, false><<<g, b, 0, s>>>(a); break;
+    case kModeFusedMx: k_fix_flagged<false, true><<<g, b, 0, s>>>(a); break;
+    case kModeFused | kModeYInt8: k_fix_flagged<true, false><<<g, b, 0, s>>>(a); break;
+    case kModeFusedMx | kModeYInt8: k_fix_flagged<true, true><<<g, b, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -74,6 +74,12 @@ def test_sizes():
     assert 0 < w1 <= w2
     assert L.mhc_workspace_bytes(0, 1024, 0) > 0
     assert L.mhc_workspace_bytes(1 << 20, 16384, 1) % 256 == 0 and L.mhc_workspace_bytes(1 << 20, 16384, 1) > 0
+    # bounded: every accepted shape fits the static scratch (64 MiB), and the
+    # size stops growing with T beyond the staged launch budget
+    for C in range(1024, 16385, 1024):
+        assert L.mhc_workspace_bytes(1 << 20, C, 1) <= 64 << 20, C
+        grow = L.mhc_workspace_bytes(1 << 20, C, 0) - L.mhc_workspace_bytes(1 << 16, C, 0)
+        assert grow <= 4 * ((1 << 20) - (1 << 16)) + 256, C  # only the 4-byte list entries
 
 
 # ---------------------------------------------------------------------------
