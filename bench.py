@@ -2,7 +2,8 @@
 """Benchmark of the mHC fused post->pre pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
-    python bench.py --workload decode --graph   # the step replayed from HIP graphs
+    python bench.py --workload decode --graph [--graph-steps 16]  # the step replayed from a HIP graph
+    python bench.py --workload decode --defer-sinkhorn  # the Sinkhorn on a side stream
     python bench.py --workload decode --cold-phi 64   # 64 prepacked projections in turn
     python bench.py --copy-probe           # copy kernel of known size (counter calibration)
     python bench.py --pmc-summary FILE...  # per-kernel means of rocprofv3 counter output
@@ -370,7 +371,12 @@ def main() -> int:
     ap.add_argument("--pre-broadcast", action="store_true",
                     help="also time the first-layer pre of a [T, C] input (mhc_pre_broadcast)")
     ap.add_argument("--graph", action="store_true",
-                    help="capture the repack and the fused call in HIP graphs and time their replays")
+                    help="capture the step (repack + fused call) in one HIP graph and time its replays")
+    ap.add_argument("--graph-steps", type=int, default=1, metavar="N",
+                    help="with --graph: capture N steps in the graph (one replay runs N steps)")
+    ap.add_argument("--defer-sinkhorn", action="store_true",
+                    help="fused call with the Sinkhorn deferred (MHC_FLAG_DEFER_SINKHORN) and mhc_sinkhorn on a "
+                         "side stream after an event; the next step's repack overlaps it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="also time the unfused chain post -> coeffs -> pre on the same inputs "
@@ -382,8 +388,11 @@ def main() -> int:
         return pmc_summary(args.pmc_summary)
     if args.copy_probe:
         return copy_probe()
-    if args.cold_phi and args.graph:
-        print(json.dumps({"error": "--cold-phi and --graph do not combine"}))
+    if args.graph and (args.cold_phi or args.defer_sinkhorn):
+        print(json.dumps({"error": "--graph combines with neither --cold-phi nor --defer-sinkhorn"}))
+        return 2
+    if args.graph and args.steps % args.graph_steps != 0:
+        print(json.dumps({"error": "--steps must be a multiple of --graph-steps"}))
         return 2
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path is not built "
@@ -427,21 +436,40 @@ def main() -> int:
     # the two calls of a step, checked and marshalled once (mhc.Prepared)
     pack = mhc.prepare_pack_phi(inp["phi_next"], packed)
     fused = mhc.prepare_post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, packed, inp["bias_next"],
-                                                 inp["gamma_next"], params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
+                                                 inp["gamma_next"], params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs,
+                                                 defer_sinkhorn=args.defer_sinkhorn)
     pack()
     fused()
     torch.cuda.synchronize()
+    sink = None
+    if args.defer_sinkhorn:
+        # the deferred Sinkhorn of each step on a side stream, after an event
+        # recorded behind the fused call; the next step's fused call (which
+        # rewrites the coefficients) waits for it, its repack does not
+        side = torch.cuda.Stream(device=dev)
+        sink = mhc.prepare_sinkhorn(outs["coeffs_next"], params, stream=side)
+        sink_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+        fused_done, sink_done = torch.cuda.Event(), torch.cuda.Event()
+        sink_done.record(side)
+    steps_per_call = 1
     if args.graph:
-        # each call captured once in a HIP graph (the library allocates and
-        # synchronises nothing on its call path), then replayed
-        graphs = (torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph())
-        with torch.cuda.graph(graphs[0]):
-            mhc.prepare_pack_phi(inp["phi_next"], packed)()
-        with torch.cuda.graph(graphs[1]):
-            mhc.post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, packed, inp["bias_next"], inp["gamma_next"],
-                                         params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
+        # graph_steps whole steps captured in one HIP graph (the library
+        # allocates and synchronises nothing on its call path), then replayed:
+        # one replay per graph_steps steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.graph_steps):
+                mhc.prepare_pack_phi(inp["phi_next"], packed)()
+                mhc.post_pre_fused_prepacked(inp["x"], inp["y"], coeffs_in, packed, inp["bias_next"],
+                                             inp["gamma_next"], params, mxfp8=mx, want_h=with_h, ws=ws, outs=outs)
         torch.cuda.synchronize()
-        pack, fused = graphs[0].replay, graphs[1].replay
+        steps_per_call = args.graph_steps
+
+        def pack():
+            pass
+
+        fused = graph.replay
 
     if args.cold_phi:
         # next-layer projections that do not stay in the caches: cold_phi
@@ -467,13 +495,24 @@ def main() -> int:
             cold[turn[0] % len(cold)]()
             turn[0] += 1
 
-    def step(ev=None):
+    def step(ev=None, k=None):
         pack()
+        if sink is not None:
+            stream.wait_event(sink_done)
         if ev is not None:
             ev[0].record(stream)
         fused()
         if ev is not None:
             ev[1].record(stream)
+        if sink is not None:
+            fused_done.record(stream)
+            side.wait_event(fused_done)
+            if k is not None:
+                sink_ev[k][0].record(side)
+            sink()
+            if k is not None:
+                sink_ev[k][1].record(side)
+            sink_done.record(side)
 
     # The GPU's clocks ramp for the first ~10-20 ms of sustained load after
     # an idle period (a fused pass measured 5% slower over its first ~30
@@ -489,20 +528,27 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    n_calls = args.steps // steps_per_call
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for k in range(args.steps):
-        step(evs[k])
+    for k in range(n_calls):
+        step(evs[k], k)
     t_end.record(stream)
+    if sink is not None:
+        stream.wait_event(sink_done)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    # (with a graph of several steps, one bracket covers steps_per_call steps)
+    kern_ms = [a.elapsed_time(b) / steps_per_call for a, b in evs]
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    sink_us = None
+    if sink is not None:
+        sink_us = sum(a.elapsed_time(b) for a, b in sink_ev) / len(sink_ev) * 1e3
     kern_sorted = sorted(kern_ms)
     # a bounded wait that expired makes the outputs of that call invalid: the
     # run is then not a measurement of the pass
@@ -571,6 +617,8 @@ def main() -> int:
                        else "projection repack + fused pass per step)"),
                    "tokens": T, "hidden": C, "routes": 4, "mxfp8": mx, "bf16_h": with_h, "rows": rows,
                    "schedule": sched, "hip_graph": bool(args.graph),
+                   "graph_steps": steps_per_call if args.graph else None,
+                   "defer_sinkhorn": bool(args.defer_sinkhorn),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(args.workload, sched),
@@ -579,6 +627,11 @@ def main() -> int:
         "cpu_baseline": cpu,
     }
     line["copy_reference"] = copy_ref
+    if sink_us is not None:
+        line["deferred_sinkhorn"] = {
+            "fused_call_us": kern_avg_ms * 1e3, "sinkhorn_us": sink_us,
+            "note": "the fused call (critical path: h complete at its end) on the main stream; mhc_sinkhorn on a "
+                    "side stream after an event, overlapping the next step's repack"}
     if first is not None:
         line["pre_broadcast"] = first
     if pq is not None:

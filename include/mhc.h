@@ -66,8 +66,9 @@ extern "C" {
  *    mhc_post_int8_pre_fused(_prepacked); every version-1 call is unchanged.
  * 3: adds mhc_workspace_check and MHC_ERR_EXPIRED; fused calls recompute the
  *    pre of tokens whose route combination cancels (see mhc_post_pre_fused).
- * 4: adds mhc_post_pre_fused_prepacked_static and MHC_ERR_SCRATCH. */
-#define MHC_ABI_VERSION 4
+ * 4: adds mhc_post_pre_fused_prepacked_static and MHC_ERR_SCRATCH.
+ * 5: adds MHC_FLAG_DEFER_SINKHORN and mhc_sinkhorn. */
+#define MHC_ABI_VERSION 5
 #define MHC_NUM_ROUTES 4
 #define MHC_NUM_COEFFS 24
 #define MHC_MAX_TOKENS (1 << 20)  /* [P2] review: the kernel's token limit 2^20 */
@@ -108,6 +109,16 @@ typedef enum mhc_status {
  * L2 holds the lines) and recomputes x' from x and y elsewhere; with this
  * flag it always recomputes.  Results are bitwise identical either way. */
 #define MHC_FLAG_RECOMPUTE_X 2u
+/* Decode-latency mode ([P3] "Measured and deliberately left out": the mHC
+ * statistics and Sinkhorn run on a side stream, off the critical path of
+ * the next projection).  The fused call writes everything as usual except
+ * coeffs_next[t][8..23], which it leaves holding exp(logits), the
+ * Sinkhorn's input; h (which needs only the pre weights) is complete when
+ * the call's work ends.  mhc_sinkhorn then finishes res in place, on any
+ * stream ordered after the call (e.g. a side stream waiting on an event
+ * recorded after it) and before anything reads res (the next post).  The
+ * two calls together write bitwise what one call without the flag writes. */
+#define MHC_FLAG_DEFER_SINKHORN 4u
 
 /* ---------------------------------------------------------------------------
  * Library information
@@ -267,6 +278,17 @@ int mhc_post_pre_fused(const uint16_t* x, const uint16_t* y, const float* coeffs
                        int64_t T, int64_t C, const mhc_params* p, unsigned flags,
                        uint16_t* x_out, float* coeffs_next, uint16_t* h, uint8_t* h_fp8,
                        uint8_t* h_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The deferred Sinkhorn of MHC_FLAG_DEFER_SINKHORN: p->sinkhorn_iters
+ * iterations (rows, then columns, each divided by sum + p->sinkhorn_eps) in
+ * place on coeffs[t][8..23] (row-major 4x4, row j = output route) for
+ * t < T; the other coefficient slots are not touched.  coeffs [T][24] fp32,
+ * device memory owned by the caller, 16-byte aligned.  Validates like the
+ * other calls (MHC_ERR_SHAPE, MHC_ERR_PARAM, MHC_ERR_NULL, MHC_ERR_ALIGN)
+ * before its one launch on `stream`; T == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+int mhc_sinkhorn(float* coeffs, int64_t T, const mhc_params* p, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Pre-packed projection.  The two calls above first repack phi (fp32) into

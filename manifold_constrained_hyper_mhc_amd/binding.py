@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmhc.so")
 
 FLAG_MXFP8 = 1
 FLAG_RECOMPUTE_X = 2
+FLAG_DEFER_SINKHORN = 4
 _STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_ALIGN", 4: "MHC_ERR_ALIAS",
            5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP", 9: "MHC_ERR_EXPIRED",
            10: "MHC_ERR_SCRATCH"}
@@ -61,6 +62,7 @@ _SIG = {
     "mhc_workspace_bytes": ([_I64, _I64, ctypes.c_uint], ctypes.c_size_t),
     "mhc_workspace_init": ([_P, ctypes.c_size_t, _P], ctypes.c_int),
     "mhc_workspace_check": ([_P, _P], ctypes.c_int),
+    "mhc_sinkhorn": ([_P, _I64, ctypes.POINTER(MhcParams), _P], ctypes.c_int),
     "mhc_phi_packed_bytes": ([_I64], ctypes.c_size_t),
     "mhc_schedule": ([_I64, _I64, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "mhc_pack_phi": ([_P, _I64, _P, _P], ctypes.c_int),
@@ -302,8 +304,22 @@ def post_int8(x, y_q, y_scale, coeffs_t, *, out=None) -> torch.Tensor:
     return out
 
 
-def _flags(mxfp8: bool, recompute_x: bool) -> int:
-    return (FLAG_MXFP8 if mxfp8 else 0) | (FLAG_RECOMPUTE_X if recompute_x else 0)
+def _flags(mxfp8: bool, recompute_x: bool, defer_sinkhorn: bool = False) -> int:
+    return ((FLAG_MXFP8 if mxfp8 else 0) | (FLAG_RECOMPUTE_X if recompute_x else 0) |
+            (FLAG_DEFER_SINKHORN if defer_sinkhorn else 0))
+
+
+def sinkhorn(coeffs_t, params: Params = Params(), *, stream=None) -> torch.Tensor:
+    """mhc_sinkhorn: finish the deferred Sinkhorn of a fused call made with
+    ``defer_sinkhorn=True``, in place on coeffs_t [T, 24] (slots 8..23), on
+    ``stream`` (a torch.cuda.Stream; default: the current one)."""
+    L = lib()
+    T = int(coeffs_t.shape[0]) if isinstance(coeffs_t, torch.Tensor) else -1
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24))
+    st = ctypes.c_void_p((stream if stream is not None else torch.cuda.current_stream(coeffs_t.device)).cuda_stream)
+    p = MhcParams.of(params)
+    _check(L.mhc_sinkhorn(_ptr(coeffs_t), T, ctypes.byref(p), st), "mhc_sinkhorn")
+    return coeffs_t
 
 
 def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
@@ -337,7 +353,7 @@ def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
 
 def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Params = Params(), *,
                    mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
-                  recompute_x: bool = False) -> dict:
+                   recompute_x: bool = False, defer_sinkhorn: bool = False) -> dict:
     L = lib()
     T, C = _dims(x)
     dev = x.device
@@ -351,7 +367,7 @@ def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Para
     ws = workspace(T, C, dev) if ws is None else ws
     p = MhcParams.of(params)
     _check(L.mhc_post_pre_fused(_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next), _ptr(bias_next), _ptr(gamma_next),
-                                T, C, ctypes.byref(p), _flags(mxfp8, recompute_x), _ptr(o["x_out"]),
+                                T, C, ctypes.byref(p), _flags(mxfp8, recompute_x, defer_sinkhorn), _ptr(o["x_out"]),
                                 _ptr(o["coeffs_next"]), _ptr(o["h"]), _ptr(o["h_fp8"]), _ptr(o["h_scale"]),
                                 _ptr(ws), ws.numel(), _stream(dev)), "mhc_post_pre_fused")
     return o
@@ -415,7 +431,8 @@ def prepare_pack_phi(phi: torch.Tensor, out: torch.Tensor) -> Prepared:
 
 def prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next,
                                      params: Params = Params(), *, mxfp8: bool = False, want_h: bool = True,
-                                     ws=None, outs=None, recompute_x: bool = False) -> Prepared:
+                                     ws=None, outs=None, recompute_x: bool = False,
+                                     defer_sinkhorn: bool = False) -> Prepared:
     L = lib()
     T, C = _dims(x)
     dev = x.device
@@ -429,18 +446,29 @@ def prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next,
     ws = workspace(T, C, dev) if ws is None else ws
     p = MhcParams.of(params)
     args = (_ptr(x), _ptr(y), _ptr(coeffs_t), _ptr(phi_next_packed), _ptr(bias_next), _ptr(gamma_next), T, C,
-            ctypes.byref(p), _flags(mxfp8, recompute_x), _ptr(o["x_out"]), _ptr(o["coeffs_next"]), _ptr(o["h"]),
-            _ptr(o["h_fp8"]), _ptr(o["h_scale"]), _ptr(ws), ws.numel(), _stream(dev))
+            ctypes.byref(p), _flags(mxfp8, recompute_x, defer_sinkhorn), _ptr(o["x_out"]), _ptr(o["coeffs_next"]),
+            _ptr(o["h"]), _ptr(o["h_fp8"]), _ptr(o["h_scale"]), _ptr(ws), ws.numel(), _stream(dev))
     keep = (x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, ws, p, o)
     return Prepared(L.mhc_post_pre_fused_prepacked, args, "mhc_post_pre_fused_prepacked", keep, o)
 
 
 def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(), *,
                              mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
-                             recompute_x: bool = False) -> dict:
+                             recompute_x: bool = False, defer_sinkhorn: bool = False) -> dict:
     return prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params,
                                             mxfp8=mxfp8, want_h=want_h, ws=ws, outs=outs,
-                                            recompute_x=recompute_x)()
+                                            recompute_x=recompute_x, defer_sinkhorn=defer_sinkhorn)()
+
+
+def prepare_sinkhorn(coeffs_t, params: Params = Params(), *, stream=None) -> Prepared:
+    """mhc_sinkhorn checked and marshalled once (see Prepared)."""
+    L = lib()
+    T = int(coeffs_t.shape[0]) if isinstance(coeffs_t, torch.Tensor) else -1
+    _need(coeffs_t, "coeffs", torch.float32, (T, 24))
+    st = ctypes.c_void_p((stream if stream is not None else torch.cuda.current_stream(coeffs_t.device)).cuda_stream)
+    p = MhcParams.of(params)
+    return Prepared(L.mhc_sinkhorn, (_ptr(coeffs_t), T, ctypes.byref(p), st), "mhc_sinkhorn", (coeffs_t, p),
+                    coeffs_t)
 
 
 def post_pre_fused_prepacked_static(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(),

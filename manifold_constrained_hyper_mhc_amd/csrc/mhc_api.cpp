@@ -421,7 +421,7 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   int rc = check_shape(T, C);
   if (rc) return rc;
   if ((rc = check_params(p, true))) return rc;
-  if (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X)) return MHC_ERR_FLAGS;
+  if (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X | MHC_FLAG_DEFER_SINKHORN)) return MHC_ERR_FLAGS;
   const bool mx = (flags & MHC_FLAG_MXFP8) != 0;
   if (mx) {
     if (T > 0 && (h_fp8 == nullptr || h_scale == nullptr)) return MHC_ERR_NULL;
@@ -497,6 +497,8 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   a.h_fp8 = h_fp8;
   a.h_scale = h_scale;
   a.recompute_x = (flags & MHC_FLAG_RECOMPUTE_X) != 0;
+  // deferred Sinkhorn: the res slots get exp(logits), mhc_sinkhorn finishes them
+  if (flags & MHC_FLAG_DEFER_SINKHORN) a.sc.sinkhorn_iters = 0;
   const int mode = (mx ? mhc::kModeFusedMx : mhc::kModeFused) | (yq ? mhc::kModeYInt8 : 0);
   // (tokens whose route combination cancels get their pre recomputed directly)
   return run_split(run, mode, a, s);
@@ -530,7 +532,8 @@ const char* mhc_strerror(int status) {
 int mhc_last_hip_error(void) { return g_last_hip_error; }
 
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags) {
-  if (check_shape(T, C) != MHC_OK || (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X))) return 0;
+  if (check_shape(T, C) != MHC_OK || (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X | MHC_FLAG_DEFER_SINKHORN)))
+    return 0;
   return workspace_need(T, C);
 }
 
@@ -542,6 +545,16 @@ int mhc_schedule(int64_t T, int64_t C, int* schedule) {
   choose_kernel(p);
   *schedule = p.lanes > 0 ? MHC_SCHEDULE_PERSISTENT : MHC_SCHEDULE_STAGED;
   return MHC_OK;
+}
+
+int mhc_sinkhorn(float* coeffs, int64_t T, const mhc_params* p, void* stream) {
+  if (T < 0 || T > MHC_MAX_TOKENS) return MHC_ERR_SHAPE;
+  int rc = check_params(p, true);
+  if (rc) return rc;
+  if (T == 0) return MHC_OK;
+  if (coeffs == nullptr) return MHC_ERR_NULL;
+  if (!aligned16(coeffs)) return MHC_ERR_ALIGN;
+  return hip_status(mhc::launch_sinkhorn(coeffs, T, p->sinkhorn_eps, p->sinkhorn_iters, static_cast<hipStream_t>(stream)));
 }
 
 int mhc_workspace_check(const void* workspace, void* stream) {

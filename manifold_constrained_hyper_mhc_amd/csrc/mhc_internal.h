@@ -140,6 +140,8 @@ hipError_t launch_post_int8(const uint16_t* x, const int8_t* y_q, const float* y
 hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* cf, const float* gamma, int64_t T,
                       int C, float rmsnorm_eps, uint16_t* h, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// `iters` Sinkhorn iterations in place on coeffs[t][8..23] (which hold exp(logits)).
+hipError_t launch_sinkhorn(float* coeffs, int64_t T, float eps, int iters, hipStream_t s);
 // After a persistent fused launch: the direct pre of the tokens it listed
 // (the count is read on the device, so it is always launched).
 hipError_t launch_fix_flagged(const SplitArgs& a, int mode, hipStream_t s);

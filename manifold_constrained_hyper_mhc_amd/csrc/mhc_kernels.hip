@@ -2126,6 +2126,30 @@ __global__ __launch_bounds__(128) void k_pre_wide(const uint16_t* __restrict__ x
   }
 }
 
+// ===========================================================================
+// Sinkhorn iterations on stored coefficients: the res entries coeffs[t][8..23]
+// hold exp(logits) (a fused call with the Sinkhorn deferred) and get `iters`
+// iterations in place, with the arithmetic of finalize_rows (one token per
+// 16-lane row, row and column sums by the same DPP moves, each normalisation
+// a multiplication by the hardware reciprocal of sum + eps), so the result is
+// bitwise the one an undeferred call writes.
+// ===========================================================================
+__global__ __launch_bounds__(256) void k_sinkhorn(float* __restrict__ cf, int64_t T, float eps, int iters) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // 16 lanes per token
+  const int k = lane & 15;
+  float v = t < T ? cf[t * kCoeffs + 8 + k] : 1.0f;
+  for (int it = 0; it < iters; ++it) {
+    float rs = v + MHC_DPP(v, kDppQuadSwap1);
+    rs = rs + MHC_DPP(rs, kDppQuadSwap2);
+    v = v * __builtin_amdgcn_rcpf(rs + eps);
+    float cs = v + MHC_DPP(v, kDppRowRor8);
+    cs = cs + MHC_DPP(cs, kDppRowRor4);
+    v = v * __builtin_amdgcn_rcpf(cs + eps);
+  }
+  if (t < T) cf[t * kCoeffs + 8 + k] = v;
+}
+
 __global__ void k_fill_zero(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -2255,6 +2279,13 @@ hipError_t launch_fix_flagged(const SplitArgs& a, int mode, hipStream_t s) {
     case kModeFusedMx | kModeYInt8: k_fix_flagged<true, true><<<g, b, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_sinkhorn(float* cf, int64_t T, float eps, int iters, hipStream_t s) {
+  const int64_t blocks = (T * 16 + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  k_sinkhorn<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(cf, T, eps, iters);
   return hipGetLastError();
 }
 
