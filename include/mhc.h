@@ -34,7 +34,9 @@
  *       bias      [24] fp32, gamma [C] fp32
  *       h_fp8     [T][C]    uint8    OCP e4m3fn codes
  *       h_scale   [T][C/32] uint8    UE8M0 exponent bytes (bias 127),
- *                                     linear (not swizzled) layout
+ *                                     linear layout (or, with
+ *                                     MHC_FLAG_MXFP8_MFMA_SCALES, the MX
+ *                                     matrix-core operand order)
  *   - T is the token count, 0 <= T <= MHC_MAX_TOKENS; T == 0 validates the
  *     scalars and returns MHC_OK without touching memory (pointers may then
  *     be NULL).  C is the hidden size, a positive multiple of 1024 and at
@@ -67,8 +69,9 @@ extern "C" {
  * 3: adds mhc_workspace_check and MHC_ERR_EXPIRED; fused calls recompute the
  *    pre of tokens whose route combination cancels (see mhc_post_pre_fused).
  * 4: adds mhc_post_pre_fused_prepacked_static and MHC_ERR_SCRATCH.
- * 5: adds MHC_FLAG_DEFER_SINKHORN and mhc_sinkhorn. */
-#define MHC_ABI_VERSION 5
+ * 5: adds MHC_FLAG_DEFER_SINKHORN and mhc_sinkhorn.
+ * 6: adds MHC_FLAG_MXFP8_MFMA_SCALES. */
+#define MHC_ABI_VERSION 6
 #define MHC_NUM_ROUTES 4
 #define MHC_NUM_COEFFS 24
 #define MHC_MAX_TOKENS (1 << 20)  /* [P2] review: the kernel's token limit 2^20 */
@@ -119,6 +122,22 @@ typedef enum mhc_status {
  * recorded after it) and before anything reads res (the next post).  The
  * two calls together write bitwise what one call without the flag writes. */
 #define MHC_FLAG_DEFER_SINKHORN 4u
+/* With MHC_FLAG_MXFP8: write the UE8M0 scale bytes in the operand order of
+ * the gfx950 MX-scaled matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4
+ * that a consumer GEMM with h as its A matrix (rows = tokens, K = channels)
+ * feeds them from, instead of the linear [T][C/32] layout ([P3]
+ * "Correctness": the quantizer's scales are compared as the consumer's
+ * swizzled scale block).  In that instruction lane l of a wave holds row
+ * l % 16 and the 32 channels of K-block l / 16 of a 128-channel K-tile, i.e.
+ * one MX block, and takes its scale from one byte (op_sel) of a 32-bit
+ * register.  The layout is [ceil(T/16)][C/512][64][4] bytes: byte
+ * ((rb * (C/512) + kg) * 64 + l) * 4 + b holds the scale of token
+ * 16 rb + l % 16 and 32-channel block 16 kg + 4 b + l / 16, so one dword
+ * per lane carries the scales of the 4 K-tiles 4 kg .. 4 kg + 3 (op_sel b).
+ * h_scale then holds ceil(T/16) * 16 * C/32 bytes; the bytes of the rows
+ * past T in the last 16-row block are written as those of all-zero blocks
+ * (0).  The codes h_fp8 are unchanged. */
+#define MHC_FLAG_MXFP8_MFMA_SCALES 8u
 
 /* ---------------------------------------------------------------------------
  * Library information

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libmhc.so")
 FLAG_MXFP8 = 1
 FLAG_RECOMPUTE_X = 2
 FLAG_DEFER_SINKHORN = 4
+FLAG_MXFP8_MFMA_SCALES = 8
 _STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_ALIGN", 4: "MHC_ERR_ALIAS",
            5: "MHC_ERR_FLAGS", 6: "MHC_ERR_WORKSPACE", 7: "MHC_ERR_PARAM", 8: "MHC_ERR_HIP", 9: "MHC_ERR_EXPIRED",
            10: "MHC_ERR_SCRATCH"}
@@ -304,9 +305,19 @@ def post_int8(x, y_q, y_scale, coeffs_t, *, out=None) -> torch.Tensor:
     return out
 
 
-def _flags(mxfp8: bool, recompute_x: bool, defer_sinkhorn: bool = False) -> int:
-    return ((FLAG_MXFP8 if mxfp8 else 0) | (FLAG_RECOMPUTE_X if recompute_x else 0) |
-            (FLAG_DEFER_SINKHORN if defer_sinkhorn else 0))
+def _flags(mxfp8, recompute_x: bool, defer_sinkhorn: bool = False) -> int:
+    """mxfp8: False, True (linear scale layout) or "mfma" (the MX matrix-core
+    operand order of the scales, MHC_FLAG_MXFP8_MFMA_SCALES)."""
+    return ((FLAG_MXFP8 if mxfp8 else 0) | (FLAG_MXFP8_MFMA_SCALES if mxfp8 == "mfma" else 0) |
+            (FLAG_RECOMPUTE_X if recompute_x else 0) | (FLAG_DEFER_SINKHORN if defer_sinkhorn else 0))
+
+
+def scale_shape(T: int, C: int, mxfp8) -> tuple:
+    """Shape of h_scale: [T, C/32] (linear), or the flat bytes of the MX
+    matrix-core operand order, ceil(T/16)*16 * C/32 (mxfp8 == "mfma")."""
+    if mxfp8 == "mfma":
+        return ((T + 15) // 16 * 16 * (C // 32),)
+    return (T, C // 32)
 
 
 def sinkhorn(coeffs_t, params: Params = Params(), *, stream=None) -> torch.Tensor:
@@ -338,7 +349,7 @@ def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
         o["h"] = None
     if mxfp8:
         need("h_fp8", (T, C), torch.uint8)
-        need("h_scale", (T, C // 32), torch.uint8)
+        need("h_scale", scale_shape(T, C, mxfp8), torch.uint8)
     else:
         o["h_fp8"] = o["h_scale"] = None
     _need(o["x_out"], "x_out", torch.bfloat16, (T, 4, C), dev)
@@ -347,12 +358,12 @@ def _fused_outputs(T, C, dev, mxfp8, want_h, outs):
         _need(o["h"], "h", torch.bfloat16, (T, C), dev)
     if mxfp8:
         _need(o["h_fp8"], "h_fp8", torch.uint8, (T, C), dev)
-        _need(o["h_scale"], "h_scale", torch.uint8, (T, C // 32), dev)
+        _need(o["h_scale"], "h_scale", torch.uint8, scale_shape(T, C, mxfp8), dev)
     return o
 
 
 def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Params = Params(), *,
-                   mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
+                   mxfp8=False, want_h: bool = True, ws=None, outs=None,
                    recompute_x: bool = False, defer_sinkhorn: bool = False) -> dict:
     L = lib()
     T, C = _dims(x)
@@ -374,7 +385,7 @@ def post_pre_fused(x, y, coeffs_t, phi_next, bias_next, gamma_next, params: Para
 
 
 def post_int8_pre_fused(x, y_q, y_scale, coeffs_t, phi_next, bias_next, gamma_next, params: Params = Params(), *,
-                        mxfp8: bool = False, want_h: bool = True, ws=None, outs=None, recompute_x: bool = False,
+                        mxfp8=False, want_h: bool = True, ws=None, outs=None, recompute_x: bool = False,
                         phi_packed=None) -> dict:
     """post_pre_fused of an int8 sublayer output y_q [T, C] with per-token
     fp32 scales y_scale [T] (mhc_post_int8_pre_fused, or its _prepacked
@@ -430,7 +441,7 @@ def prepare_pack_phi(phi: torch.Tensor, out: torch.Tensor) -> Prepared:
 
 
 def prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next,
-                                     params: Params = Params(), *, mxfp8: bool = False, want_h: bool = True,
+                                     params: Params = Params(), *, mxfp8=False, want_h: bool = True,
                                      ws=None, outs=None, recompute_x: bool = False,
                                      defer_sinkhorn: bool = False) -> Prepared:
     L = lib()
@@ -453,7 +464,7 @@ def prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next,
 
 
 def post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(), *,
-                             mxfp8: bool = False, want_h: bool = True, ws=None, outs=None,
+                             mxfp8=False, want_h: bool = True, ws=None, outs=None,
                              recompute_x: bool = False, defer_sinkhorn: bool = False) -> dict:
     return prepare_post_pre_fused_prepacked(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params,
                                             mxfp8=mxfp8, want_h=want_h, ws=ws, outs=outs,
@@ -472,7 +483,7 @@ def prepare_sinkhorn(coeffs_t, params: Params = Params(), *, stream=None) -> Pre
 
 
 def post_pre_fused_prepacked_static(x, y, coeffs_t, phi_next_packed, bias_next, gamma_next, params: Params = Params(),
-                                    *, error_word, mxfp8: bool = False, want_h: bool = True, outs=None,
+                                    *, error_word, mxfp8=False, want_h: bool = True, outs=None,
                                     recompute_x: bool = False) -> dict:
     """mhc_post_pre_fused_prepacked_static: the fused pass on the library's
     static scratch (no workspace argument).  ``error_word`` is a one-element

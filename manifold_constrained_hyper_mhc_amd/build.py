@@ -63,7 +63,25 @@ def build(verbose: bool = True) -> str:
         print("[build]", " ".join(cmd), flush=True)
     _run(cmd)
     os.replace(tmp, LIB)
+    build_test_helpers(cc, verbose)
     return LIB
+
+
+# Test-only HIP helpers (not part of libmhc): built next to their source in
+# tests/, loaded only by the GPU tests.
+TEST_HELPERS = [("mx_consumer.hip", "libmx_consumer.so")]
+
+
+def build_test_helpers(cc: str, verbose: bool = True) -> None:
+    tests = os.path.join(ROOT, "tests")
+    for src, lib in TEST_HELPERS:
+        out = os.path.join(tests, lib)
+        tmp = out + ".tmp"
+        cmd = [cc, *common_flags(), "-shared", "-x", "hip", os.path.join(tests, src), "-o", tmp]
+        if verbose:
+            print("[build]", " ".join(cmd), flush=True)
+        _run(cmd)
+        os.replace(tmp, out)
 
 
 if __name__ == "__main__":

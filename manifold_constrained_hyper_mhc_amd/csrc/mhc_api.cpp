@@ -421,8 +421,11 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   int rc = check_shape(T, C);
   if (rc) return rc;
   if ((rc = check_params(p, true))) return rc;
-  if (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X | MHC_FLAG_DEFER_SINKHORN)) return MHC_ERR_FLAGS;
+  if (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X | MHC_FLAG_DEFER_SINKHORN | MHC_FLAG_MXFP8_MFMA_SCALES))
+    return MHC_ERR_FLAGS;
   const bool mx = (flags & MHC_FLAG_MXFP8) != 0;
+  const bool mfma_scales = (flags & MHC_FLAG_MXFP8_MFMA_SCALES) != 0;
+  if (mfma_scales && !mx) return MHC_ERR_FLAGS;
   if (mx) {
     if (T > 0 && (h_fp8 == nullptr || h_scale == nullptr)) return MHC_ERR_NULL;
   } else if (h_fp8 != nullptr || h_scale != nullptr) {
@@ -447,8 +450,10 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   out[nout++] = {coeffs_next, cb};
   if (h) out[nout++] = {h, yb};
   if (mx) {
+    // the matrix-core scale order covers whole 16-row blocks
+    const int64_t scale_rows = mfma_scales ? (T + 15) / 16 * 16 : T;
     out[nout++] = {h_fp8, (size_t)T * C};
-    out[nout++] = {h_scale, (size_t)T * (C / 32)};
+    out[nout++] = {h_scale, (size_t)scale_rows * (C / 32)};
   }
   if ((rc = check_tensors(in, nin, out, nout))) return rc;
   const mhc::Plan plan = mhc::make_plan(T, C);
@@ -497,6 +502,7 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   a.h_fp8 = h_fp8;
   a.h_scale = h_scale;
   a.recompute_x = (flags & MHC_FLAG_RECOMPUTE_X) != 0;
+  a.scale_mfma = mfma_scales ? 1 : 0;
   // deferred Sinkhorn: the res slots get exp(logits), mhc_sinkhorn finishes them
   if (flags & MHC_FLAG_DEFER_SINKHORN) a.sc.sinkhorn_iters = 0;
   const int mode = (mx ? mhc::kModeFusedMx : mhc::kModeFused) | (yq ? mhc::kModeYInt8 : 0);
@@ -532,7 +538,8 @@ const char* mhc_strerror(int status) {
 int mhc_last_hip_error(void) { return g_last_hip_error; }
 
 size_t mhc_workspace_bytes(int64_t T, int64_t C, unsigned flags) {
-  if (check_shape(T, C) != MHC_OK || (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X | MHC_FLAG_DEFER_SINKHORN)))
+  if (check_shape(T, C) != MHC_OK ||
+      (flags & ~(MHC_FLAG_MXFP8 | MHC_FLAG_RECOMPUTE_X | MHC_FLAG_DEFER_SINKHORN | MHC_FLAG_MXFP8_MFMA_SCALES)))
     return 0;
   return workspace_need(T, C);
 }

@@ -167,6 +167,17 @@ __device__ __forceinline__ int mx_scale_exponent(float amax_bf16) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Byte offset of the scale of token t's 32-channel block blk in h_scale:
+// linear [T][C/32], or (mfma) the A-operand scale order of
+// v_mfma_scale_f32_16x16x128_f8f6f4, [T/16][C/512][64 lanes][4 bytes] with
+// lane 16 (blk % 4) + t % 16 and byte (blk / 4) % 4 of row block t / 16 and
+// 512-channel group blk / 16.
+__device__ __forceinline__ int64_t mx_scale_offset(int64_t t, int blk, int C, bool mfma) {
+  if (!mfma) return t * (int64_t)(C >> 5) + blk;
+  const int64_t lane = 16 * (blk & 3) + (t & 15);
+  return ((((t >> 4) * (int64_t)(C >> 9) + (blk >> 4)) * 64 + lane) << 2) + ((blk >> 2) & 3);
+}
+
 // Four OCP e4m3fn codes of values with |v| <= 448, packed first value in the
 // low byte, by the gfx950 converter (round to nearest even, subnormals kept):
 // each pair is one v_cvt_pk_fp8_f32.  The codes are tested bit for bit

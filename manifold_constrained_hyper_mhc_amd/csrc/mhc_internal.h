@@ -117,6 +117,7 @@ struct SplitArgs {
   int d1, d2;
   int lanes;           // persistent kernel: stream workgroups per split
   int recompute_x;     // the pre step never reads x_out back
+  int scale_mfma;      // MXFP8 scale bytes in the MX matrix-core operand order (mx_scale_offset)
   Scalars sc;
 };
 

@@ -512,7 +512,7 @@ __device__ void fix_flagged(const SplitArgs& a, uint32_t tag, double* red, uint3
         const uint32_t w0 = e4m3_pack4(hr[0] * scale, hr[1] * scale, hr[2] * scale, hr[3] * scale);
         const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
         *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + 8 * j) = u32x2_t{w0, w1};
-        if ((j & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (j >> 2)] = (uint8_t)(ex + 127);
+        if ((j & 3) == 0) a.h_scale[mx_scale_offset(t, j >> 2, C, a.scale_mfma != 0)] = (uint8_t)(ex + 127);
       }
     }
     __syncthreads();  // red[] is reused by the next token
@@ -933,7 +933,11 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
           const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
           if (keep) {
             *reinterpret_cast<u32x2_t*>(a.h_fp8 + t * (int64_t)C + cl) = u32x2_t{w0, w1};
-            if ((c8 & 3) == 0) a.h_scale[t * (int64_t)(C / 32) + (cl >> 5)] = (uint8_t)(ex + 127);
+            if ((c8 & 3) == 0) a.h_scale[mx_scale_offset(t, cl >> 5, C, a.scale_mfma != 0)] = (uint8_t)(ex + 127);
+          } else if (!valid && a.scale_mfma && t < ((a.T + 15) & ~(int64_t)15) && (c8 & 3) == 0) {
+            // a padding row of the last 16-row block: its h is all zero (x'
+            // rows past T load as 0), so its scale byte is 0
+            a.h_scale[mx_scale_offset(t, cl >> 5, C, true)] = (uint8_t)(ex + 127);
           }
         }
       }
@@ -1694,10 +1698,16 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           const uint32_t w1 = e4m3_pack4(hr[4] * scale, hr[5] * scale, hr[6] * scale, hr[7] * scale);
           __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w0, w1}, buffer_rsrc(a.h_fp8 + tokC0 * C, nC * (uint32_t)C),
                                                 (n16 * C + cl) | drop, 0, 0);
-          // the block's four lanes store the same scale byte
+          // the block's four lanes store the same scale byte; the
+          // matrix-core order covers whole 16-row blocks (rows past T hold
+          // h = 0, whose scale byte is 0), up to ceil(T/16)*16 rows
+          const int blk = cl >> 5;
+          const uint32_t nS = a.scale_mfma ? (tokC0 < a.T ? 16u : 0u) : nC;
+          const uint32_t soff = a.scale_mfma ? (uint32_t)mx_scale_offset(n16, blk, C, true)
+                                             : (uint32_t)(n16 * (C / 32) + blk);
           __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(ex + 127),
-                                               buffer_rsrc(a.h_scale + tokC0 * (C / 32), nC * (uint32_t)(C / 32)),
-                                               (n16 * (C / 32) + (cl >> 5)) | drop, 0, 0);
+                                               buffer_rsrc(a.h_scale + tokC0 * (C / 32), nS * (uint32_t)(C / 32)),
+                                               soff | drop, 0, 0);
         }
       }
       if constexpr (FUSED) {

@@ -369,6 +369,30 @@ def mxfp8(h_bf16):
     return q, scale
 
 
+def mxfp8_scales_mfma(scale) -> np.ndarray:
+    """UE8M0 scale bytes [T, C/32] in the operand order of the gfx950
+    MX-scaled matrix instruction that a consumer GEMM with h as its A matrix
+    reads them in (reading R23 of the pages' "swizzled UE8M0 scale block",
+    [P3] "Correctness": the layout belongs to the consumer's matrix
+    instruction; here v_mfma_scale_f32_16x16x128_f8f6f4, whose lane l holds
+    row l % 16 and the 32-channel K-block l / 16 of a 128-channel K-tile and
+    reads its scale from one byte of a 32-bit register).
+
+    Layout [ceil(T/16)][C/512][64][4]: byte ((rb * C/512 + kg) * 64 + l) * 4
+    + b is the scale of token 16 rb + l % 16 and block 16 kg + 4 b + l / 16;
+    rows past T are the bytes of all-zero blocks (0).  A pure permutation of
+    the linear bytes plus that padding.
+    """
+    s = np.asarray(scale, dtype=np.uint8)
+    T, nb = s.shape
+    assert nb % 16 == 0, "C must be a multiple of 512"
+    tp = (T + 15) // 16 * 16
+    pad = np.zeros((tp, nb), dtype=np.uint8)
+    pad[:T] = s
+    # [rb][r][kg][b][lb]  ->  [rb][kg][lb][r][b]   (lane l = 16 lb + r)
+    return pad.reshape(tp // 16, 16, nb // 16, 4, 4).transpose(0, 2, 4, 1, 3).reshape(-1).copy()
+
+
 def post_pre_fused(x, y, coeffs_in, phi_next, bias_next, gamma_next, *,
                    hc_norm_eps, rmsnorm_eps, hc_post_scale, sinkhorn_eps,
                    sinkhorn_iters=20, with_mxfp8=False):
@@ -422,5 +446,5 @@ __all__ = [
     "bf16_round", "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_round", "fma_f32",
     "post_exact", "post_int8", "dequant_int8", "post_int8_pre_fused",
     "e4m3_encode", "e4m3_decode", "sinkhorn", "coeffs", "pre", "post",
-    "split_coeffs", "mxfp8_scale_exponent", "mxfp8", "post_pre_fused", "pre_broadcast", "rms",
+    "split_coeffs", "mxfp8_scale_exponent", "mxfp8", "mxfp8_scales_mfma", "post_pre_fused", "pre_broadcast", "rms",
 ]

@@ -49,7 +49,7 @@ def test_schedule_query():
 
 def test_abi_version_and_strerror():
     L = mhc.lib()
-    assert L.mhc_abi_version() == 5
+    assert L.mhc_abi_version() == 6
     for code in range(11):
         assert L.mhc_strerror(code) != b"unknown status"
     assert L.mhc_strerror(99) == b"unknown status"
@@ -80,7 +80,7 @@ def test_sizes():
     assert L.mhc_phi_packed_bytes(1000) == 0          # not a multiple of 1024
     assert L.mhc_workspace_bytes(8192, 7168, 0) >= 4 * 7168 * 160
     assert L.mhc_workspace_bytes(8192, 7168, 2) == L.mhc_workspace_bytes(8192, 7168, 0)
-    assert L.mhc_workspace_bytes(8192, 7168, 8) == 0  # unknown flag
+    assert L.mhc_workspace_bytes(8192, 7168, 16) == 0  # unknown flag
     assert L.mhc_workspace_bytes(-1, 7168, 0) == 0
     w1, w2 = L.mhc_workspace_bytes(16, 1024, 0), L.mhc_workspace_bytes(17, 1024, 0)
     assert 0 < w1 <= w2
@@ -194,8 +194,9 @@ def fused_call(L, T=16, C=1024, flags=0, p=P, ws=None, ws_bytes=None, h=True, fp
 def test_fused_validation():
     L = mhc.lib()
     assert fused_call(L, C=1536) == SHAPE
-    assert fused_call(L, flags=8) == FLAGS
-    assert fused_call(L, flags=2 | 8) == FLAGS
+    assert fused_call(L, flags=16) == FLAGS
+    assert fused_call(L, flags=2 | 16) == FLAGS
+    assert fused_call(L, flags=8) == FLAGS                          # matrix-core scale order without MXFP8
     assert fused_call(L, flags=2, fp8=fake(9)) == FLAGS             # fp8 output without the MXFP8 flag
     assert fused_call(L, fp8=fake(9)) == FLAGS                      # fp8 output without the flag
     assert fused_call(L, flags=1, fp8=fake(9)) == NULL              # flag without the scale output
