@@ -142,45 +142,75 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(inp_host: dict, coeffs_host, params, budget_s: float = 10.0, chunk: int = 128) -> dict:
-    """The fp64 oracle, as it stands, on a bounded sample of the workload: with
-    every thread its numpy pools start with, then again limited to one thread
-    (a third of the budget)."""
-    import numpy as np
-    import threadpoolctl
+_TP_LIMIT = None
 
+
+def _oracle_worker_init():
+    # one thread per worker process: the processes are the parallelism
+    global _TP_LIMIT
+    import threadpoolctl
+    _TP_LIMIT = threadpoolctl.threadpool_limits(limits=1)
+
+
+def _oracle_run(task):
+    """Run the oracle's fused post->pre over chunks of the given rows for
+    `budget` seconds; returns (tokens done, seconds)."""
+    x, y, cf, phi, b, g, kw, budget, chunk = task
     import oracle as O
+
+    n = x.shape[0]
+    done, k = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget:
+        s = (k * chunk) % n
+        rows = slice(s, min(s + chunk, n))
+        O.post_pre_fused(x[rows], y[rows], cf[rows], phi, b, g, **kw)
+        done += rows.stop - rows.start
+        k += 1
+    return done, time.perf_counter() - t0
+
+
+def start_oracle_pool():
+    """Worker processes for the all-cores oracle leg, forked before anything
+    touches the GPU (a forked child of a process with a live GPU context is
+    not safe).  At most 16 processes: the host cores one GPU is given."""
+    import multiprocessing as mp
+
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    return mp.get_context("fork").Pool(n, initializer=_oracle_worker_init), n
+
+
+def cpu_baseline(pool, nproc: int, inp_host: dict, coeffs_host, params, budget_s: float = 10.0,
+                 chunk: int = 64) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    `nproc` processes of one thread each, every one on its own slice of the
+    sample, all for the same `budget_s` seconds (tokens/s summed), then one
+    thread alone for a third of the budget."""
+    import threadpoolctl
 
     f64 = lambda t: t.to("cpu").double().numpy()  # noqa: E731
     x, y = f64(inp_host["x"]), f64(inp_host["y"])
     cf = f64(coeffs_host)
     phi, b, g = f64(inp_host["phi_next"]), f64(inp_host["bias_next"]), f64(inp_host["gamma_next"])
     n = x.shape[0]
-
-    def run(budget):
-        done = 0
-        t0 = time.perf_counter()
-        k = 0
-        while time.perf_counter() - t0 < budget:
-            s = (k * chunk) % n
-            rows = slice(s, min(s + chunk, n))
-            O.post_pre_fused(x[rows], y[rows], cf[rows], phi, b, g, hc_norm_eps=params.hc_norm_eps,
-                             rmsnorm_eps=params.rmsnorm_eps, hc_post_scale=params.hc_post_scale,
-                             sinkhorn_eps=params.sinkhorn_eps, sinkhorn_iters=params.sinkhorn_iters)
-            done += rows.stop - rows.start
-            k += 1
-        return done, time.perf_counter() - t0
-
-    done, dt = run(budget_s)
-    threads = 1
-    for pool in threadpoolctl.threadpool_info():
-        threads = max(threads, int(pool.get("num_threads", 1)))
+    kw = dict(hc_norm_eps=params.hc_norm_eps, rmsnorm_eps=params.rmsnorm_eps, hc_post_scale=params.hc_post_scale,
+              sinkhorn_eps=params.sinkhorn_eps, sinkhorn_iters=params.sinkhorn_iters)
+    per = max(chunk, n // nproc)
+    tasks = []
+    for i in range(nproc):
+        s = (i * per) % n
+        sl = slice(s, min(s + per, n))
+        tasks.append((x[sl], y[sl], cf[sl], phi, b, g, kw, budget_s, chunk))
+    res = pool.map(_oracle_run, tasks, chunksize=1)
+    done = sum(d for d, _ in res)
+    value = sum(d / t for d, t in res)
     with threadpoolctl.threadpool_limits(limits=1):
-        done1, dt1 = run(budget_s / 3)
-    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        done1, dt1 = _oracle_run((x, y, cf, phi, b, g, kw, budget_s / 3, chunk))
+    return {"value": value, "unit": "tokens/s", "cores": nproc, "kind": "oracle",
             "value_1_thread": done1 / dt1, "cpu_model": cpu_model(),
-            "sample": f"{done} tokens of the same workload in chunks of {chunk} ({dt:.1f} s; "
-                      f"one thread: {done1} tokens, {dt1:.1f} s), fp64 numpy oracle fused post->pre"}
+            "sample": f"{nproc} processes x 1 thread, each on {per} of the first {n} tokens of the same workload "
+                      f"in chunks of {chunk} for {budget_s:.0f} s ({done} tokens in all); one thread alone: "
+                      f"{done1} tokens in {dt1:.1f} s; fp64 numpy oracle fused post->pre"}
 
 
 def time_unfused(mhc, inp, coeffs_in, packed, params, outs, stream, args, fused_bytes, fused_ms):
@@ -257,6 +287,58 @@ def copy_reference(inp, outs, stream, args, fused_gbs):
     return {"what": "torch copies x -> [T,4,C] and y -> [T,C] buffers (reads + writes 20C bytes per token)",
             "us": us, "bytes": nbytes, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
             "fused_gbs_over_copy_gbs": fused_gbs / gbs}
+
+
+def copy_ceiling(inp, stream, args, fused_gbs, lanes):
+    """Hand-written copies and reads of x and y (libmhc_bench.so): the
+    bandwidth a plain stream of the same tensors reaches, linear (16 bytes
+    per lane, 4 loads in flight) and in the persistent fused kernel's access
+    pattern (256-byte pieces of 128-row tiles, S splits x `lanes` workgroups).
+    HIP events around each pair of launches (x, then y)."""
+    import ctypes
+
+    import torch
+
+    lib_path = os.path.join(ROOT, "manifold_constrained_hyper_mhc_amd", "libmhc_bench.so")
+    L = ctypes.CDLL(lib_path)
+    L.bench_copy.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.bench_copy.restype = ctypes.c_int
+    x, y = inp["x"], inp["y"]
+    T, _, C = x.shape
+    dx, dy = torch.empty_like(x), torch.empty_like(y)
+    S = 2 * C // 256
+    sink = torch.empty(max(1024, S * lanes) * 256 * 16, dtype=torch.uint8, device=x.device)
+    st = ctypes.c_void_p(stream.cuda_stream)
+    nbytes = x.numel() * 2 + y.numel() * 2
+
+    def run(kind):
+        for src, dst, rows in ((x, dx, 4 * T), (y, dy, T)):
+            rc = L.bench_copy(kind, src.data_ptr(), dst.data_ptr(), rows, 2 * C, lanes, sink.data_ptr(), st)
+            if rc != 0:
+                raise RuntimeError(f"bench_copy kind {kind}: {rc}")
+
+    out = {}
+    names = {0: "linear_copy", 1: "linear_read", 2: "piece_copy", 3: "piece_read"}
+    for kind, name in names.items():
+        for _ in range(3):
+            run(kind)
+        torch.cuda.synchronize()
+        n = max(5, min(args.steps, 20))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            run(kind)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+        moved = nbytes * (2 if kind in (0, 2) else 1)
+        gbs = moved / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "bytes": moved, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+    out["what"] = ("hand-written copies (read + write) and reads of x [T,4,C] and y [T,C]: linear, and in the fused "
+                   f"kernel's pattern (256-byte pieces of 128-row tiles, {S} splits x {lanes} workgroups)")
+    out["fused_gbs_over_piece_copy_gbs"] = fused_gbs / out["piece_copy"]["gbs"]
+    return out
 
 
 def time_pre_broadcast(mhc, inp, packed, params, stream, args):
@@ -400,6 +482,18 @@ def main() -> int:
                           "n_gpus": args.gpus}))
         return 2
 
+    pool = nproc = None
+    if not args.no_cpu_baseline:
+        pool, nproc = start_oracle_pool()
+    try:
+        return run(args, pool, nproc)
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
+
+
+def run(args, pool, nproc) -> int:
     import torch
 
     import manifold_constrained_hyper_mhc_amd as mhc
@@ -588,14 +682,21 @@ def main() -> int:
     print(f"[bench] plain copy of x and y: {copy_ref['us']:.1f} us, {copy_ref['gbs']:.0f} GB/s "
           f"({copy_ref['frac_of_peak']:.3f} of peak); the fused pass runs at "
           f"{copy_ref['fused_gbs_over_copy_gbs']:.3f} of it", file=sys.stderr, flush=True)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    S = C // 128
+    lanes = max(1, min((cus - 32) // S, 256 // S))
+    ceiling = copy_ceiling(inp, stream, args, achieved, lanes)
+    print("[bench] hand-written ceilings of x and y: " + ", ".join(
+        f"{k} {v['gbs']:.0f} GB/s ({v['frac_of_peak']:.3f})" for k, v in ceiling.items() if isinstance(v, dict)),
+        file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
         n_s = min(T, 1024)
         host = {k: inp[k][:n_s].cpu() for k in ("x", "y")}
         host.update({k: inp[k].cpu() for k in ("phi_next", "bias_next", "gamma_next")})
-        cpu = cpu_baseline(host, coeffs_in[:n_s].cpu(), params)
-        print(f"[bench] cpu oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(pool, nproc, host, coeffs_in[:n_s].cpu(), params)
+        print(f"[bench] cpu oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} processes of one thread (one thread alone: {cpu['value_1_thread']:.1f})", file=sys.stderr, flush=True)
 
     rows = {"normal": "N(0,1)", "outliers": "N(0,1), 1% of rows x100", "decades": "N(0,1) x 10^U(-2,3) per row"}[w.rows]
     line = {
@@ -627,6 +728,7 @@ def main() -> int:
         "cpu_baseline": cpu,
     }
     line["copy_reference"] = copy_ref
+    line["copy_ceiling"] = ceiling
     if sink_us is not None:
         line["deferred_sinkhorn"] = {
             "fused_call_us": kern_avg_ms * 1e3, "sinkhorn_us": sink_us,

@@ -63,8 +63,23 @@ def build(verbose: bool = True) -> str:
         print("[build]", " ".join(cmd), flush=True)
     _run(cmd)
     os.replace(tmp, LIB)
+    build_bench_helper(cc, verbose)
     build_test_helpers(cc, verbose)
     return LIB
+
+
+# The measurement aid of bench.py (plain copies for the bandwidth ceilings),
+# a library of its own next to libmhc.so.
+BENCH_LIB = os.path.join(HERE, "libmhc_bench.so")
+
+
+def build_bench_helper(cc: str, verbose: bool = True) -> None:
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [cc, *common_flags(), "-shared", "-x", "hip", os.path.join(CSRC, "bench_copy.hip"), "-o", tmp]
+    if verbose:
+        print("[build]", " ".join(cmd), flush=True)
+    _run(cmd)
+    os.replace(tmp, BENCH_LIB)
 
 
 # Test-only HIP helpers (not part of libmhc): built next to their source in
