@@ -186,7 +186,10 @@ Plan make_plan(int64_t T, int64_t C) {
     ring_c = p.tiles < kCoeffsRingTiles ? p.tiles : kCoeffsRingTiles;
   }
   size_t part = (size_t)p.chunk_tiles * tile_words;
-  const size_t part_f = (size_t)ring_f * p.s * p.m * kPartVals * sizeof(uint64_t);
+  // persistent fused pass: binary32 values, then one release flag per
+  // (slot, split, row block)
+  const size_t flag_rel = round256((size_t)ring_f * p.s * p.m * kPartVals * sizeof(float));
+  const size_t part_f = flag_rel + (size_t)ring_f * p.s * 2 * sizeof(uint64_t);
   const size_t part_c = (size_t)ring_c * p.s * p.m * 25 * sizeof(uint64_t);
   part = part > part_f ? part : part_f;
   part = part > part_c ? part : part_c;
@@ -195,6 +198,7 @@ Plan make_plan(int64_t T, int64_t C) {
   p.off_pub = off;
   off = round256(off + (size_t)pub_tiles * p.m * 4 * sizeof(uint64_t));
   p.off_part = off;
+  p.off_flag = off + flag_rel;
   off = round256(off + part);
   p.off_own = off;
   off = round256(off + (size_t)p.chunk_tiles * p.s * sizeof(uint64_t));
@@ -231,6 +235,7 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   a.dep = reinterpret_cast<uint32_t*>(base + mhc::kWsDep);
   a.publish = reinterpret_cast<uint64_t*>(base + plan.off_pub);
   a.partials = reinterpret_cast<uint64_t*>(base + plan.off_part);
+  a.pflag = reinterpret_cast<uint64_t*>(base + plan.off_flag);
   a.owner = reinterpret_cast<uint64_t*>(base + plan.off_own);
   a.release = reinterpret_cast<uint64_t*>(base + plan.off_rel);
   a.fix_word = reinterpret_cast<uint64_t*>(base + mhc::kWsFixWord);

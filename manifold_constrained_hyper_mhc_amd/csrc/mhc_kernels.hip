@@ -1292,21 +1292,44 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         __syncthreads();  // this tile's sums are read
       }
     } else {
+      // The fused pass's partial values are plain binary32 words, released
+      // per (tile, split, row block) by a tagged flag that the stream
+      // workgroup stores once the values are complete in memory: the wave
+      // polls the S flags of a unit's row block (lane k: split k), then
+      // loads the values with system scope, after the flags.
       const int R = kRingK * L;
+      const float* pf = reinterpret_cast<const float*>(a.partials);
+      auto flags_in = [&](const uint64_t* fb) __attribute__((always_inline)) {
+        const uint64_t f = lane < S ? tagged_load(fb + 2 * lane) : 0;
+        return __builtin_amdgcn_ballot_w64(lane < S && (uint32_t)(f >> 32) != want) == 0;
+      };
       auto gather = [&](int u, float* fin) __attribute__((always_inline)) {
         const int tu = u >> 2;
         want = ring_tag(tag, (uint32_t)(tu / R));
-        pb = a.partials + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
-        sum = 0.0f;
-        load_chunk(wa, 0);
-        load_chunk(wb, 16);
-        load_chunk(wc, 32);
-        load_chunk(wd, 48);
-        add_chunk(wa, 0);
-        add_chunk(wb, 16);
-        add_chunk(wc, 32);
-        add_chunk(wd, 48);
-        if (v >= 0 && v < 8 * NV) fin[v] = act ? sum : 0.0f;
+        const uint64_t* fb = a.pflag + (int64_t)(tu % R) * S * 2 + ((u & 3) >> 1);
+        if (!flags_in(fb)) {
+          uint32_t it = 0;
+          do {
+            __builtin_amdgcn_s_sleep(1);
+            // bounded: a wait that expires sets the error word, and every
+            // other wait of the launch gives up as soon as it sees it
+            if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
+              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          } while (!flags_in(fb));
+        }
+        // the value loads stay behind the flag loads they depend on
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const float* vb = pf + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
+        float f[kPersistMaxS];
+#pragma unroll
+        for (int k = 0; k < kPersistMaxS; ++k)
+          f[k] = act && k < S ? __uint_as_float(load_sys32(vb + k * pstride)) : 0.0f;
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kPersistMaxS; ++k) acc += k < S ? f[k] : 0.0f;
+        if (v >= 0 && v < 8 * NV) fin[v] = act ? acc : 0.0f;
       };
       if (j < nunits && wv >= 2) gather(j, finw);
       __syncthreads();
@@ -1624,14 +1647,23 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       constexpr bool doC = FUSED && decltype(kC)::value;
       constexpr bool doPrev = decltype(kPrev)::value;
       const int t = r + L * i;
-      // partial row of tile t_{i-1}: this row block's 16 tokens x NV words,
+      // release of tile t_{i-2}'s partial values, stored in phase P(i-1):
+      // every wave of the row block has since waited for all its memory
+      // operations but the slot copies issued after them, and passed a
+      // barrier, so those write-through stores are complete and the flag
+      // cannot be seen before them
+      if (i >= 2 && i <= niter + 1 && gt == 0) {
+        const int ip = i - 2;
+        tagged_store(a.pflag + ((int64_t)(r + L * (ip % kRingK)) * S + split) * 2 + rb, 0.0f,
+                     ring_tag(tag, (uint32_t)(ip / kRingK)));
+      }
+      // partial row of tile t_{i-1}: this row block's 16 tokens x NV values,
       // the four 32-channel steps added in order
       if constexpr (doPrev) {
         // tile t_{i-1}, ring slot r + L ((i - 1) % kRingK)
-        uint64_t* part =
-            a.partials + ((int64_t)(r + L * ((i - 1) % kRingK)) * S + split) * (TM * NV) + rb * 16 * NV;
-        const uint32_t ptag = ring_tag(tag, (uint32_t)((i - 1) / kRingK));
-        // all twelve LDS reads first, then the stores (words past the row
+        float* part = reinterpret_cast<float*>(a.partials) +
+                      ((int64_t)(r + L * ((i - 1) % kRingK)) * S + split) * (TM * NV) + rb * 16 * NV;
+        // all twelve LDS reads first, then the stores (values past the row
         // block are not stored)
         float sum[3];
 #pragma unroll
@@ -1643,7 +1675,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
           const int idx = gt + k * 256;
-          if (idx < 16 * NV) tagged_store(part + idx, sum[k], ptag);
+          if (idx < 16 * NV) store_sys32(part + idx, __float_as_uint(sum[k]));
         }
       }
       const u32x4_t cy = ny;
