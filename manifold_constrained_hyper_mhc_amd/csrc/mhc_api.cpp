@@ -186,13 +186,14 @@ Plan make_plan(int64_t T, int64_t C) {
     ring_c = p.tiles < kCoeffsRingTiles ? p.tiles : kCoeffsRingTiles;
   }
   size_t part = (size_t)p.chunk_tiles * tile_words;
-  // persistent fused pass: binary32 values, then one release flag per
-  // (slot, split, row block)
-  const size_t flag_rel = round256((size_t)ring_f * p.s * p.m * kPartVals * sizeof(float));
-  const size_t part_f = flag_rel + (size_t)ring_f * p.s * 2 * sizeof(uint64_t);
-  const size_t part_c = (size_t)ring_c * p.s * p.m * 25 * sizeof(uint64_t);
-  part = part > part_f ? part : part_f;
-  part = part > part_c ? part : part_c;
+  // persistent passes: binary32 values in their ring, then one release flag
+  // per (slot, split, row block), after the larger of the two rings' values
+  const size_t vals_f = (size_t)ring_f * p.s * p.m * kPartVals * sizeof(float);
+  const size_t vals_c = (size_t)ring_c * p.s * p.m * kCoeffsWords * sizeof(float);
+  const size_t flag_rel = round256(vals_f > vals_c ? vals_f : vals_c);
+  const int64_t ring_max = ring_f > ring_c ? ring_f : ring_c;
+  const size_t part_r = flag_rel + (size_t)ring_max * p.s * 2 * sizeof(uint64_t);
+  part = part > part_r ? part : part_r;
   const int64_t pub_tiles = p.chunk_tiles > ring_f ? p.chunk_tiles : ring_f;
   size_t off = kWsHeaderBytes;
   p.off_pub = off;

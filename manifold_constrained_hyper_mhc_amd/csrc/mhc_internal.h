@@ -31,7 +31,7 @@ struct Plan {
   int64_t chunk_tiles = 0;  // staged kernel: tiles per launch (a longer call is a sequence of launches)
   // workspace layout (byte offsets)
   size_t off_pub = 0, off_part = 0, off_own = 0, off_rel = 0, off_fix = 0, off_phi = 0, total = 0;
-  size_t off_flag = 0;  // persistent fused pass: release flags, inside the partial region after its values
+  size_t off_flag = 0;  // persistent passes: release flags, inside the partial region after the values
 };
 
 // Workspace bounds.  The persistent kernel keeps its exchanged words in
@@ -46,6 +46,7 @@ constexpr int kMaxLaneSplits = 256;
 constexpr size_t kStagedBudget = (size_t)32 << 20;
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
+constexpr int kCoeffsWords = 25;        // per token, coefficients only: projection + sum of squares
 
 // Workspace header at fixed offsets, whatever the shape of a call: the error
 // word, the launch epoch, the tiles-done counter, the tagged count of tokens
@@ -90,9 +91,10 @@ struct SplitArgs {
   uint16_t* h;
   uint8_t* h_fp8;
   uint8_t* h_scale;
-  uint64_t* partials;  // [tiles][S][M][34] tagged words ([tiles][S][M][25]: coefficients-only passes;
-                       // persistent fused pass: [R][S][M][34] plain binary32 values, released by pflag)
-  uint64_t* pflag;     // persistent fused pass: [R][S][2 row blocks] tagged release flags
+  uint64_t* partials;  // staged kernel: [tiles][S][M][34] tagged words ([..][25]: coefficients only);
+                       // persistent kernel: [R][S][M][34] ([kCoeffsRingTiles][S][M][25]) plain
+                       // binary32 values, released by pflag
+  uint64_t* pflag;     // persistent kernel: [ring slots][S][2 row blocks] tagged release flags
   uint32_t* epoch;     // launch epoch (fixed offset)
   uint32_t* tiles_done;  // tiles completed in this launch (fixed offset)
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)

@@ -1027,7 +1027,6 @@ constexpr int kPersistDepth = 6;  // iterations between the post and the pre ste
 constexpr uint32_t kPersistSpinLimit = 1u << 18;
 constexpr int kPersistMaxS = 64;  // splits per row the reduce threads can gather
 constexpr int kCoeffsAhead = 3;   // coefficients-only pass: tiles of x held in registers ahead
-constexpr int kCoeffsWords = 25;  // coefficients-only partial words per token: 24 projections, sum of squares
 // LDS projection fragments of one (route, 32-channel step): blocks 0-3 whole
 // (64 lanes each) and the 32 lanes of block 4 whose column is < 8 (the rest
 // of block 4 is zero), in 16-byte units.
@@ -1038,14 +1037,18 @@ constexpr int kHalfChunks = 16 * 4 * 16;
 // tiles (L stream workgroups per split): tile t uses slot t % R.  Stream
 // workgroup lane r's tiles t = r + L i take slot r + L (i % kRingK), and the
 // units of tiles t and t + R meet the same reduce workgroup (R is a multiple
-// of 8 and a reduce workgroup owns every 32nd unit of 4 per tile).  A word of
-// tile t carries the tag 2 * launch_tag + (t / R) % 2, so the word an older
-// tile of the same slot left behind never passes as fresh.  Reuse is safe
-// because of the q-word chain: a stream workgroup stores tile t_{i-1}'s
-// partial words in phase P(i) only after it has seen the q words of tile
-// t_{i-D-1}, which the reduce publishes after gathering every split's words
+// of 8 and a reduce workgroup owns every 32nd unit of 4 per tile).  The
+// release flag and the q words of tile t carry the tag
+// 2 * launch_tag + (t / R) % 2, so the flag or q word an older tile of the
+// same slot left behind never passes as fresh (the partial values
+// themselves carry no tag: they are read only after their flag).  Reuse is
+// safe because of the q-word chain: a stream workgroup stores tile t_{i-1}'s
+// partial values in phase P(i) only after it has seen the q words of tile
+// t_{i-D-1}, which the reduce publishes after gathering every split's values
 // of that tile; kRingK >= D + 1 then keeps a slot's old tile gathered before
 // it is overwritten, and likewise its q words read before new ones land.
+// The flag of tile t_{i-1} follows in phase P(i+1), so the old tile's flag
+// has been read too.
 
 // Whether a bounded wait of the launch has expired (read from memory; the
 // polls look at it every 16th round only, so that a poll round costs one
@@ -1103,10 +1106,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   // [2][row block][token][route][16 chunks] x 16 B (chunk c of token t at
   // position c ^ (t % 16), so that the 16 tokens a wave reads at once hit
   // distinct banks); wave partials; post coefficients; q words; gamma.
-  // The partial words are [tiles][S][TM][NV] tagged words, or
-  // [tiles][S][TM][kCoeffsWords] in the coefficients-only mode: every
-  // store instruction writes whole lines (a system-scope store that covers
-  // part of a line measured several times slower per byte).
+  // The partial values are [ring slot][S][TM][NV] binary32 words, or
+  // [ring slot][S][TM][kCoeffsWords] in the coefficients-only mode, each
+  // (slot, split, row block) released by one tagged flag: every store
+  // instruction writes whole lines (a system-scope store that covers part
+  // of a line measured several times slower per byte).
   __shared__ __attribute__((aligned(16))) u32x4_t phi_lds[16 * kPhiFrag + 1];
   // (the coefficients-only mode has one stage per row block instead of the
   // slot pairs: [1][row block][row][16 chunks], chunk c of token t at c ^ t)
@@ -1130,9 +1134,9 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     // Work unit u = 8 tokens: tile u / 4, tokens 8 (u % 4) .. + 7 (one half
     // of a row block, whose partial words arrive together).  Reduce
     // workgroup j owns the units j, j + R, ... (R reduce workgroups).
-    // Waves 2-7 gather: thread v < 8 NV sums word v of the unit (a
+    // Waves 2-7 gather: thread v < 8 NV sums value v of the unit (a
     // contiguous run in every split's [TM][NV] partial) over the S splits in
-    // split order, in one pass, reloading words whose tag is stale.  Waves
+    // split order, in one pass, once the unit's release flags are in.  Waves
     // 0-1 finalise the previous unit meanwhile, four tokens per wave (one per
     // 16-lane row); the sums are double-buffered in LDS.  (The
     // coefficients-only mode takes whole tiles per round instead, its sums
@@ -1143,41 +1147,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     const int64_t pstride = (int64_t)TM * (FUSED ? NV : kCoeffsWords);  // one split's partial tile
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int v = tid - 128;  // gather thread's word
-    bool act = wv >= 2 && v < 8 * NV;
-    uint64_t wa[16], wb[16], wc[16], wd[16];
-    const uint64_t* pb = a.partials;
-    float sum = 0.0f;
-    uint32_t want = ring_tag(tag, 0);  // the tag the words of the unit being gathered carry
-    auto load_chunk = [&](uint64_t* w, int sc) __attribute__((always_inline)) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) w[k] = act && sc + k < S ? tagged_load(pb + (sc + k) * pstride) : 0;
-    };
-    auto add_chunk = [&](uint64_t* w, int sc) __attribute__((always_inline)) {
-      auto stale = [&]() __attribute__((always_inline)) {
-        bool st = false;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) st |= act && sc + k < S && (uint32_t)(w[k] >> 32) != want;
-        return st;
-      };
-      if (stale()) {
-        uint32_t it = 0;
-        do {
-          __builtin_amdgcn_s_sleep(1);
-          // bounded: a wait that expires sets the error word, and every
-          // other wait of the launch gives up as soon as it sees it
-          if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
-            __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-#pragma unroll
-          for (int k = 0; k < 16; ++k)
-            if (act && sc + k < S && (uint32_t)(w[k] >> 32) != want) w[k] = tagged_load(pb + (sc + k) * pstride);
-        } while (stale());
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k) sum += sc + k < S ? tagged_value(w[k]) : 0.0f;
-    };
-    static_assert(kPersistMaxS == 64, "four chunks of 16 splits");
+    const bool act = wv >= 2 && v < 8 * NV;
+    uint32_t want = ring_tag(tag, 0);  // the tag the flags of the unit being gathered carry
     if constexpr (!FUSED) {
       // Coefficients only: nothing waits on the result but the end of the
       // launch, so whole tiles per round (all threads gather, then every
@@ -1189,6 +1160,32 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // release word gets its generation (the full number, in the value
       // field), and stream workgroups wait for it before refilling the slot.
       static_assert(kCoeffsRingTiles % 32 == 0, "one reduce workgroup per ring slot");
+      // The partial values are plain binary32 words, released per (tile,
+      // split, row block) by a tagged flag: every wave polls the 2 S flags
+      // of a tile (lane k: split k, both row blocks), then loads the values
+      // with system scope, after the flags.
+      const float* pf = reinterpret_cast<const float*>(a.partials);
+      auto tile_flags_in = [&](int t) __attribute__((always_inline)) {
+        const uint32_t wt = ring_tag(tag, (uint32_t)(t / kCoeffsRingTiles));
+        const uint64_t* fb = a.pflag + (int64_t)(t % kCoeffsRingTiles) * S * 2;
+        const uint64_t f0 = lane < S ? tagged_load(fb + 2 * lane) : 0;
+        const uint64_t f1 = lane < S ? tagged_load(fb + 2 * lane + 1) : 0;
+        return __builtin_amdgcn_ballot_w64(lane < S && ((uint32_t)(f0 >> 32) != wt || (uint32_t)(f1 >> 32) != wt)) == 0;
+      };
+      auto wait_tile = [&](int t) __attribute__((always_inline)) {
+        if (!tile_flags_in(t)) {
+          uint32_t it = 0;
+          do {
+            __builtin_amdgcn_s_sleep(1);
+            if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
+              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          } while (!tile_flags_in(t));
+        }
+        // the value loads stay behind the flag loads they depend on
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      };
       // finalise tile t from the sums in LDS (every wave four tokens), then
       // the coefficients out
       auto finalize_tile = [&](int t) __attribute__((always_inline)) {
@@ -1208,46 +1205,25 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         // of loads, and the next tile's loads are issued before this tile
         // is finalised, so the gather latency overlaps the finalisation.
         constexpr int NWT = TM * kCoeffsWords;  // 800
-        uint64_t w0[16], w1[16];
+        float w0[16], w1[16];
         const bool has1 = tid + kPersistThreads < NWT;
+        // the next tile's values, loaded once its flags are in (those of the
+        // first tile are waited for here; later ones after a finalisation)
         auto issue = [&](int t) __attribute__((always_inline)) {
-          const uint64_t* base = a.partials + (int64_t)(t % kCoeffsRingTiles) * S * pstride + tid;
+          wait_tile(t);
+          const float* base = pf + (int64_t)(t % kCoeffsRingTiles) * S * pstride + tid;
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
-            w0[k] = k < S ? tagged_load(base + k * pstride) : 0;
-            w1[k] = k < S && has1 ? tagged_load(base + k * pstride + kPersistThreads) : 0;
+            w0[k] = k < S ? __uint_as_float(load_sys32(base + k * pstride)) : 0.0f;
+            w1[k] = k < S && has1 ? __uint_as_float(load_sys32(base + k * pstride + kPersistThreads)) : 0.0f;
           }
         };
-        auto settle = [&](int t) __attribute__((always_inline)) {
-          const uint64_t* base = a.partials + (int64_t)(t % kCoeffsRingTiles) * S * pstride + tid;
-          const uint32_t wt = ring_tag(tag, (uint32_t)(t / kCoeffsRingTiles));
-          auto stale = [&]() __attribute__((always_inline)) {
-            bool st = false;
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-              st |= k < S && ((uint32_t)(w0[k] >> 32) != wt || (has1 && (uint32_t)(w1[k] >> 32) != wt));
-            return st;
-          };
-          if (stale()) {
-            uint32_t it = 0;
-            do {
-              __builtin_amdgcn_s_sleep(1);
-              if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
-                __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-              }
-#pragma unroll
-              for (int k = 0; k < 16; ++k) {
-                if (k < S && (uint32_t)(w0[k] >> 32) != wt) w0[k] = tagged_load(base + k * pstride);
-                if (k < S && has1 && (uint32_t)(w1[k] >> 32) != wt) w1[k] = tagged_load(base + k * pstride + kPersistThreads);
-              }
-            } while (stale());
-          }
+        auto settle = [&](int) __attribute__((always_inline)) {
           float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
-            s0 += k < S ? tagged_value(w0[k]) : 0.0f;
-            s1 += k < S ? tagged_value(w1[k]) : 0.0f;
+            s0 += k < S ? w0[k] : 0.0f;
+            s1 += k < S ? w1[k] : 0.0f;
           }
           finw[(tid / kCoeffsWords) * NV + tid % kCoeffsWords] = s0;
           if (has1) {
@@ -1270,21 +1246,17 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       for (int t = j; t < tiles; t += nred) {
         const int slot = t % kCoeffsRingTiles;
         const uint32_t gen = (uint32_t)(t / kCoeffsRingTiles);
-        want = ring_tag(tag, gen);
+        wait_tile(t);
         for (int w = tid; w < TM * kCoeffsWords; w += kPersistThreads) {
           const int wo = (w / kCoeffsWords) * NV + w % kCoeffsWords;  // (token, word) in the [TM][NV] sums
-          act = true;
-          pb = a.partials + (int64_t)slot * S * pstride + w;
-          sum = 0.0f;
-          load_chunk(wa, 0);
-          load_chunk(wb, 16);
-          load_chunk(wc, 32);
-          load_chunk(wd, 48);
-          add_chunk(wa, 0);
-          add_chunk(wb, 16);
-          add_chunk(wc, 32);
-          add_chunk(wd, 48);
-          finw[wo] = sum;
+          const float* vb = pf + (int64_t)slot * S * pstride + w;
+          float f[kPersistMaxS];
+#pragma unroll
+          for (int k = 0; k < kPersistMaxS; ++k) f[k] = k < S ? __uint_as_float(load_sys32(vb + k * pstride)) : 0.0f;
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < kPersistMaxS; ++k) acc += k < S ? f[k] : 0.0f;
+          finw[wo] = acc;
         }
         __syncthreads();  // the tile's sums (every gather load has returned)
         if (tid == 0) tagged_store(a.release + slot, __uint_as_float(gen), ring_tag(tag, 0));
@@ -1463,7 +1435,15 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       auto fold = [&](int i, uint64_t rel) __attribute__((always_inline)) {
         const int t = r + L * i;
         const uint32_t gen = (uint32_t)(t / kCoeffsRingTiles);
-        uint64_t* part = a.partials + ((int64_t)(t % kCoeffsRingTiles) * S + split) * (TM * NW) + rb * 16 * NW;
+        float* part = reinterpret_cast<float*>(a.partials) + ((int64_t)(t % kCoeffsRingTiles) * S + split) * (TM * NW) +
+                      rb * 16 * NW;
+        // all of this wave's memory operations but the step's four x loads
+        // (issued last) are complete: the partial values the step before
+        // stored among them, which the flag stored after the next barrier
+        // releases
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        __builtin_amdgcn_sched_barrier(0);
         if (gen > 0) {
           const uint32_t rtag = ring_tag(tag, 0);
           uint32_t it = 0;
@@ -1476,7 +1456,6 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
             rel = tagged_load(a.release + t % kCoeffsRingTiles);
           }
         }
-        const uint32_t ptag = ring_tag(tag, gen);
         const float* rr = &red[i & 1][rb * 4][0];
         float sum[2];
 #pragma unroll
@@ -1487,8 +1466,15 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int idx = gt + 256 * k;
-          if (idx < 16 * NW) tagged_store(part + idx, sum[k], ptag);
+          if (idx < 16 * NW) store_sys32(part + idx, __float_as_uint(sum[k]));
         }
+      };
+      // release flag of this row block's partial values of tile t_i
+      auto flag = [&](int i) __attribute__((always_inline)) {
+        const int t = r + L * i;
+        if (gt == 0)
+          tagged_store(a.pflag + ((int64_t)(t % kCoeffsRingTiles) * S + split) * 2 + rb, 0.0f,
+                       ring_tag(tag, (uint32_t)(t / kCoeffsRingTiles)));
       };
       // projection and sum of squares of tile t_i from the stage (rows past
       // T read token 0 and are zeroed) -> LDS buffer i & 1
@@ -1545,7 +1531,10 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         if ((n16 >> 2) == g) rw[n16 * NW + 24] = ((gd[0] + gd[1]) + gd[2]) + gd[3];
       };
       // step i >= 1 (step 0 has no partial words to store)
+      // (the values of tile t_{i-3} were stored in step i - 2, complete at
+      // the wait of step i - 1's fold, before its last barrier)
       auto step = [&](int i, u32x4_t* xb) __attribute__((always_inline)) {
+        if (i >= 3) flag(i - 3);
         const uint64_t rel = release_of(i - 1);
         __builtin_amdgcn_sched_barrier(0);
         stage_write(xb);
@@ -1574,6 +1563,12 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         for (int k = 0; k < A; ++k)
           if (i + k < niter) step(i + k, xq[(k + 1) % A]);
         fold(niter - 1, release_of(niter - 1));
+        // the last three tiles' values are complete in every wave: their flags
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        for (int k = niter >= 3 ? niter - 3 : 0; k < niter; ++k) flag(k);
       }
     } else {
 
