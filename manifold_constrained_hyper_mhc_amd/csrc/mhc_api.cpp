@@ -130,11 +130,16 @@ void choose_kernel(mhc::Plan& p, int min_s = 32) {
   if (!persistent_allowed()) return;
   if (p.m != 32 || p.s < min_s || p.s > 64) return;
   const int cus = device_cus();
-  int lanes = (cus - 32) / p.s;
+  // coefficients at <= 16 splits (a broadcast stream on pseudo-routes):
+  // each stream workgroup's tiles are few and short, and the reduce's
+  // per-tile latency sets the pace, so 64 reduce workgroups
+  const int reds = p.s <= 16 ? 64 : 32;
+  int lanes = (cus - reds) / p.s;
   // the workspace's rings hold kRingK tiles per stream workgroup lane
   if (lanes * p.s > mhc::kMaxLaneSplits) lanes = mhc::kMaxLaneSplits / p.s;
-  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes || p.s * lanes + 32 > mhc::kPersistMaxBlocks) return;
+  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes || p.s * lanes + reds > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;
+  p.reds = reds;
 }
 
 int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {

@@ -1159,7 +1159,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // gathered here, in order; once a tile's words are in, the slot's
       // release word gets its generation (the full number, in the value
       // field), and stream workgroups wait for it before refilling the slot.
-      static_assert(kCoeffsRingTiles % 32 == 0, "one reduce workgroup per ring slot");
+      static_assert(kCoeffsRingTiles % 32 == 0 && kCoeffsRingTiles % 64 == 0, "one reduce workgroup per ring slot");
       // The partial values are plain binary32 words, released per (tile,
       // split, row block) by a tagged flag: every wave polls the 2 S flags
       // of a tile (lane k: split k, both row blocks), then loads the values
@@ -2236,7 +2236,8 @@ static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream
 
 template <int MODE>
 static hipError_t launch_persist_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(p.s * p.lanes + kPersistTM)), block(kPersistThreads);
+  if (p.reds != 32 && !(p.reds == 64 && MODE == kModeCoeffs && p.s <= 16)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(p.s * p.lanes + p.reds)), block(kPersistThreads);
   k_persist<MODE><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
