@@ -335,8 +335,37 @@ def copy_ceiling(inp, stream, args, fused_gbs, lanes):
         moved = nbytes * (2 if kind in (0, 2) else 1)
         gbs = moved / (us * 1e-6) / 1e9
         out[name] = {"us": us, "bytes": moved, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+    # the same copy with wider pieces (the fused kernel's projection slice in
+    # LDS fixes its piece at 256 bytes): the stream workgroup count, and all CUs
+    L.bench_copy_pieces.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p]
+    L.bench_copy_pieces.restype = ctypes.c_int
+    sweep = {}
+    for wg in (S * lanes, torch.cuda.get_device_properties(x.device).multi_processor_count):
+        for pb in (256, 512, 1024, 2048):
+            def runw():
+                for src, dst, rows in ((x, dx, 4 * T), (y, dy, T)):
+                    rc = L.bench_copy_pieces(src.data_ptr(), dst.data_ptr(), rows, 2 * C, pb, wg, st)
+                    if rc != 0:
+                        raise RuntimeError(f"bench_copy_pieces {pb}: {rc}")
+            for _ in range(2):
+                runw()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 5
+            a.record(stream)
+            for _ in range(n):
+                runw()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / n * 1e3
+            wgs = (2 * C // pb) * max(1, wg // (2 * C // pb))
+            sweep[f"{pb}B_{wgs}wg"] = round(2 * nbytes / (us * 1e-6) / 1e9, 1)
+    out["piece_width_sweep_gbs"] = sweep
     out["what"] = ("hand-written copies (read + write) and reads of x [T,4,C] and y [T,C]: linear, and in the fused "
-                   f"kernel's pattern (256-byte pieces of 128-row tiles, {S} splits x {lanes} workgroups)")
+                   f"kernel's pattern (256-byte pieces of 128-row tiles, {S} splits x {lanes} workgroups); "
+                   "piece_width_sweep_gbs: the piece copy with wider pieces, at the stream workgroup count and at one "
+                   "workgroup per CU")
     out["fused_gbs_over_piece_copy_gbs"] = fused_gbs / out["piece_copy"]["gbs"]
     return out
 
@@ -687,8 +716,10 @@ def run(args, pool, nproc) -> int:
     lanes = max(1, min((cus - 32) // S, 256 // S))
     ceiling = copy_ceiling(inp, stream, args, achieved, lanes)
     print("[bench] hand-written ceilings of x and y: " + ", ".join(
-        f"{k} {v['gbs']:.0f} GB/s ({v['frac_of_peak']:.3f})" for k, v in ceiling.items() if isinstance(v, dict)),
-        file=sys.stderr, flush=True)
+        f"{k} {v['gbs']:.0f} GB/s ({v['frac_of_peak']:.3f})" for k, v in ceiling.items()
+        if isinstance(v, dict) and "gbs" in v), file=sys.stderr, flush=True)
+    print("[bench] piece copy by piece width: " + ", ".join(
+        f"{k} {v:.0f} GB/s" for k, v in ceiling["piece_width_sweep_gbs"].items()), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
