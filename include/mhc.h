@@ -287,10 +287,11 @@ int mhc_post_int8(const uint16_t* x, const int8_t* y_q, const float* y_scale, co
  * coefficients ([P1] "What this fixes": the sum of squares fused into post).
  * Where the routes of g = sum_i pre_i x'_i cancel (pre^T G pre <= B / 64,
  * B = (sum_i |pre_i| sqrt(G_ii))^2), that difference of large fp32 terms is
- * not accurate enough; such tokens are listed in the workspace and a second
- * kernel, always enqueued after the pass, recomputes their h (and MXFP8
- * blocks) from x_out directly in binary64.  An exactly cancelling
- * combination (g = 0) gives h = 0.
+ * not accurate enough; such tokens are listed in the workspace and their h
+ * (and MXFP8 blocks) is recomputed after the pass, in binary64, from x'
+ * recomputed from x, y and coeffs (the inputs): by the staged kernel's last
+ * workgroup, or by a second kernel always enqueued after a persistent
+ * launch.  An exactly cancelling combination (g = 0) gives h = 0.
  * ------------------------------------------------------------------------- */
 int mhc_post_pre_fused(const uint16_t* x, const uint16_t* y, const float* coeffs,
                        const float* phi_next, const float* bias_next, const float* gamma_next,
@@ -345,7 +346,7 @@ int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const flo
  *   - Limit: the call takes T and C with mhc_workspace_bytes(T, C, flags) <=
  *     MHC_STATIC_SCRATCH_BYTES and returns MHC_ERR_SCRATCH, before any HIP
  *     call, otherwise.  The workspace is bounded (see Workspace above), and
- *     every T and C the library accepts fits (at most ~47 MB).
+ *     every T and C the library accepts fits (at most ~46 MiB).
  *   - error_word: a caller-owned device uint32 (4-byte aligned, not overlapping
  *     any other argument), required when T > 0; a bounded wait that expires
  *     sets it nonzero and the call's outputs are then invalid.  The library
