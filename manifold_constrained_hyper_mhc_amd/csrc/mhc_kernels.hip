@@ -1084,6 +1084,15 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
                : "memory", "m0");
 }
 
+// The same copy with the default cache policy, for data that other
+// workgroups of the XCD read too (the projection slice).
+__device__ __forceinline__ void lds_dma16_shared(const void* src, uint32_t base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+
 // Buffer resource over [base, base + bytes): the hardware drops stores at
 // offsets past the end, so a store to a row past T needs no branch (raw
 // buffer, gfx9 resource word 3).
@@ -1361,10 +1370,17 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     const int xpos = (4 * ks + g) ^ n16;  // LDS position of this lane's chunk in a row
     const int niter = r < tiles ? (tiles - r + L - 1) / L : 0;
 
-    // projection slice -> LDS (and one zero fragment for block 4's unused lanes)
+    // projection slice -> LDS: asynchronous global -> LDS copies, all of a
+    // wave's in flight at once (lane l of copy k fills fragment
+    // k * 512 + 64 wave + l), waited for together with the first tiles'
+    // loads below; and one zero fragment for block 4's unused lanes
     {
+      static_assert(16 * kPhiFrag % kPersistThreads == 0, "whole waves of fragments");
       const u32x4_t* pk = reinterpret_cast<const u32x4_t*>(a.phi_packed);
-      for (int idx = tid; idx < 16 * kPhiFrag; idx += kPersistThreads) {
+#pragma unroll
+      for (int k = 0; k < 16 * kPhiFrag / kPersistThreads; ++k) {
+        const int base = k * kPersistThreads + wv * kWave;
+        const int idx = base + lane;
         const int jk = idx / kPhiFrag, o = idx % kPhiFrag;
         const int jr = jk >> 2, kq = jk & 3;
         const int64_t kstep = ((int64_t)jr * a.prs + c0 + kq * 32) >> 5;
@@ -1376,13 +1392,14 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           b = 4;
           ln = ((o - 4 * kWave) >> 3) * 16 + ((o - 4 * kWave) & 7);
         }
-        phi_lds[idx] = pk[(kstep * kPackBlocks + b) * kWave + ln];
+        lds_dma16_shared(pk + (kstep * kPackBlocks + b) * kWave + ln,
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_address(&phi_lds[base])));
       }
       if (tid == 0) phi_lds[16 * kPhiFrag] = u32x4_t{0, 0, 0, 0};
     }
-    if constexpr (FUSED) {
-      if (tid < kCC) gam[tid] = a.gamma[c0 + tid];
-    }
+    // gamma slice: loaded now, stored to LDS after the prologue's wait
+    // (a compiler wait for it here would also wait for the copies above)
+    const float gam_v = FUSED && tid < kCC ? a.gamma[c0 + tid] : 0.0f;
     // block 4 fragment of this lane: its own column if < 8, else the zero fragment
     const int b4off = n16 < 8 ? 4 * kWave + g * 8 + n16 : -1;
 
@@ -1545,9 +1562,13 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         MHC_GROUP_BARRIER("coefficients: stage read");
       };
       if (niter > 0) {
-        __syncthreads();  // the projection slice is in LDS
 #pragma unroll
         for (int k = 0; k < A; ++k) load_x(xq[k], k);
+        // the projection copies (issued before these 4 A loads) have landed
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * A));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();  // the projection slice is in LDS
         stage_write(xq[0]);
         load_x(xq[0], A);
         MHC_GROUP_BARRIER("coefficients: first stage written");
@@ -1916,9 +1937,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         issue_q(0);
       }
       issue_x(1);
+      // everything so far has landed: the projection copies, the slots, y
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_sched_barrier(0);
+      if (FUSED && tid < kCC) gam[tid] = gam_v;
       if (rb == 0) prepP(0, No{});
       __syncthreads();
       // step i: [row block 0: P(i)       | row block 1: M(i-1), prep P(i)]   barrier
@@ -1991,6 +2014,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       __builtin_amdgcn_sched_barrier(0);
     }
     }
+    // (a workgroup without tiles: its projection copies land before its LDS
+    // is released)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- leave: the last workgroup to finish advances the launch epoch ----
