@@ -183,12 +183,13 @@ Plan make_plan(int64_t T, int64_t C) {
   set_delays(p, p.chunk_tiles);
   // persistent rings (32-token tiles, at most 64 splits: where the
   // persistent kernel can run): fused kRingK tiles per lane, coefficients
-  // only kCoeffsRingTiles
+  // only coeffs_ring_tiles(s)
   int64_t ring_f = 0, ring_c = 0;
   if (p.m == 32 && p.s <= 64) {
     ring_f = (int64_t)kRingK * (kMaxLaneSplits / p.s);
     ring_f = p.tiles < ring_f ? p.tiles : ring_f;
-    ring_c = p.tiles < kCoeffsRingTiles ? p.tiles : kCoeffsRingTiles;
+    const int64_t cr = coeffs_ring_tiles(p.s);
+    ring_c = p.tiles < cr ? p.tiles : cr;
   }
   size_t part = (size_t)p.chunk_tiles * tile_words;
   // persistent passes: binary32 values in their ring, then one release flag
@@ -209,7 +210,7 @@ Plan make_plan(int64_t T, int64_t C) {
   p.off_own = off;
   off = round256(off + (size_t)p.chunk_tiles * p.s * sizeof(uint64_t));
   p.off_rel = off;
-  off = round256(off + (size_t)kCoeffsRingTiles * sizeof(uint64_t));
+  off = round256(off + (size_t)kCoeffsRingTilesWide * sizeof(uint64_t));
   p.off_fix = off;
   off = round256(off + (size_t)T * sizeof(uint32_t));
   p.off_phi = off;

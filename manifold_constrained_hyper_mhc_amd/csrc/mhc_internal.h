@@ -36,13 +36,18 @@ struct Plan {
 };
 
 // Workspace bounds.  The persistent kernel keeps its exchanged words in
-// rings (fused: kRingK * L tiles; coefficients only: kCoeffsRingTiles
+// rings (fused: kRingK * L tiles; coefficients only: coeffs_ring_tiles(S)
 // tiles), with at most kMaxLaneSplits = L * S stream workgroups; the staged
 // kernel runs a call as launches of at most chunk_tiles tiles, whose partial
 // words take at most kStagedBudget bytes.  So a workspace holds about
 // kStagedBudget bytes + 4 per token + the packed projection, whatever T is.
 constexpr int kRingK = 8;
+// Coefficients-only ring: 64 tiles, or 512 at <= 16 splits (many stream
+// lanes, whose release flags trail their values by A + 2 steps: the ring
+// keeps at least 16 steps of every lane in flight).
 constexpr int kCoeffsRingTiles = 64;
+constexpr int kCoeffsRingTilesWide = 512;
+inline int coeffs_ring_tiles(int s) { return s <= 16 ? kCoeffsRingTilesWide : kCoeffsRingTiles; }
 constexpr int kMaxLaneSplits = 256;
 constexpr size_t kStagedBudget = (size_t)32 << 20;
 
@@ -93,7 +98,7 @@ struct SplitArgs {
   uint8_t* h_fp8;
   uint8_t* h_scale;
   uint64_t* partials;  // staged kernel: [tiles][S][M][34] tagged words ([..][25]: coefficients only);
-                       // persistent kernel: [R][S][M][34] ([kCoeffsRingTiles][S][M][25]) plain
+                       // persistent kernel: [R][S][M][34] ([cring][S][M][25]) plain
                        // binary32 values, released by pflag
   uint64_t* pflag;     // persistent kernel: [ring slots][S][2 row blocks] tagged release flags
   uint32_t* epoch;     // launch epoch (fixed offset)
@@ -101,7 +106,7 @@ struct SplitArgs {
   uint32_t* dep;       // [kMaxTiles] workgroups of a tile that have left (fixed offset)
   uint64_t* publish;   // [tiles][M][4] tagged words
   uint64_t* owner;     // [tiles][S] tagged XCD id of the workgroup that ran phase A
-  uint64_t* release;   // [kCoeffsRingTiles] coefficients-only ring: generation of each slot's gathered tile
+  uint64_t* release;   // [cring] coefficients-only ring: generation of each slot's gathered tile
   uint64_t* fix_word;  // (launch tag << 32) | number of tokens in fix_list (fixed offset)
   uint32_t* fix_list;  // [T] tokens whose fused pre is recomputed directly (fix_flagged)
   uint32_t* err;

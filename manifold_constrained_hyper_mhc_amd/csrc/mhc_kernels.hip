@@ -1021,6 +1021,10 @@ template <bool B>
 struct BoolC {
   static constexpr bool value = B;
 };
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 constexpr int kPersistThreads = 512;
 constexpr int kPersistTM = 32;
 constexpr int kPersistDepth = 6;  // iterations between the post and the pre step of a tile
@@ -1162,27 +1166,29 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // Coefficients only: nothing waits on the result but the end of the
       // launch, so whole tiles per round (all threads gather, then every
       // wave finalises four tokens) give more tokens per round.
-      // The partial words live in a ring of kCoeffsRingTiles tiles: tile t in
-      // slot t % kCoeffsRingTiles, generation t / kCoeffsRingTiles.  The ring
-      // is a multiple of the 32 reduce workgroups, so every tile of a slot is
-      // gathered here, in order; once a tile's words are in, the slot's
-      // release word gets its generation (the full number, in the value
-      // field), and stream workgroups wait for it before refilling the slot.
-      static_assert(kCoeffsRingTiles % 32 == 0 && kCoeffsRingTiles % 64 == 0, "one reduce workgroup per ring slot");
+      // The partial values live in a ring of cring tiles (coeffs_ring_tiles:
+      // kCoeffsRingTilesWide at <= 16 splits, else kCoeffsRingTiles): tile t
+      // in slot t % cring, generation t / cring.  The ring is a multiple of
+      // the reduce workgroup count, so every tile of a slot is gathered here,
+      // in order; once a tile's values are in, the slot's release word gets
+      // its generation (the full number, in the value field), and stream
+      // workgroups wait for it before refilling the slot.
+      static_assert(kCoeffsRingTiles % 32 == 0 && kCoeffsRingTilesWide % 64 == 0, "one reduce workgroup per slot");
       // The partial values are plain binary32 words, released per (tile,
       // split, row block) by a tagged flag: every wave polls the 2 S flags
       // of a tile (lane k: split k, both row blocks), then loads the values
       // with system scope, after the flags.
       const float* pf = reinterpret_cast<const float*>(a.partials);
-      auto tile_flags_in = [&](int t) __attribute__((always_inline)) {
-        const uint32_t wt = ring_tag(tag, (uint32_t)(t / kCoeffsRingTiles));
-        const uint64_t* fb = a.pflag + (int64_t)(t % kCoeffsRingTiles) * S * 2;
+      auto tile_flags_in = [&](int t, auto kRing) __attribute__((always_inline)) {
+        constexpr int cring = decltype(kRing)::value;
+        const uint32_t wt = ring_tag(tag, (uint32_t)(t / cring));
+        const uint64_t* fb = a.pflag + (int64_t)(t % cring) * S * 2;
         const uint64_t f0 = lane < S ? tagged_load(fb + 2 * lane) : 0;
         const uint64_t f1 = lane < S ? tagged_load(fb + 2 * lane + 1) : 0;
         return __builtin_amdgcn_ballot_w64(lane < S && ((uint32_t)(f0 >> 32) != wt || (uint32_t)(f1 >> 32) != wt)) == 0;
       };
-      auto wait_tile = [&](int t) __attribute__((always_inline)) {
-        if (!tile_flags_in(t)) {
+      auto wait_tile = [&](int t, auto kRing) __attribute__((always_inline)) {
+        if (!tile_flags_in(t, kRing)) {
           uint32_t it = 0;
           do {
             __builtin_amdgcn_s_sleep(1);
@@ -1190,7 +1196,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
               __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               break;
             }
-          } while (!tile_flags_in(t));
+          } while (!tile_flags_in(t, kRing));
         }
         // the value loads stay behind the flag loads they depend on
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1209,6 +1215,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
       };
       if (S <= 16) {
+        constexpr int cring = kCoeffsRingTilesWide;
+        using Ring = IntC<kCoeffsRingTilesWide>;
         // Few splits (a broadcast stream on pseudo-routes): thread v takes
         // the words v and v + 512 of the tile's TM * 25, both in one round
         // of loads, and the next tile's loads are issued before this tile
@@ -1219,8 +1227,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         // the next tile's values, loaded once its flags are in (those of the
         // first tile are waited for here; later ones after a finalisation)
         auto issue = [&](int t) __attribute__((always_inline)) {
-          wait_tile(t);
-          const float* base = pf + (int64_t)(t % kCoeffsRingTiles) * S * pstride + tid;
+          wait_tile(t, Ring{});
+          const float* base = pf + (int64_t)(t % cring) * S * pstride + tid;
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             w0[k] = k < S ? __uint_as_float(load_sys32(base + k * pstride)) : 0.0f;
@@ -1245,7 +1253,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           settle(t);
           __syncthreads();  // the tile's sums (every gather load has returned)
           if (tid == 0)
-            tagged_store(a.release + t % kCoeffsRingTiles, __uint_as_float((uint32_t)(t / kCoeffsRingTiles)),
+            tagged_store(a.release + t % cring, __uint_as_float((uint32_t)(t / cring)),
                          ring_tag(tag, 0));
           if (t + nred < tiles) issue(t + nred);
           finalize_tile(t);
@@ -1253,9 +1261,10 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
       } else
       for (int t = j; t < tiles; t += nred) {
-        const int slot = t % kCoeffsRingTiles;
-        const uint32_t gen = (uint32_t)(t / kCoeffsRingTiles);
-        wait_tile(t);
+        constexpr int cring = kCoeffsRingTiles;
+        const int slot = t % cring;
+        const uint32_t gen = (uint32_t)(t / cring);
+        wait_tile(t, IntC<kCoeffsRingTiles>{});
         for (int w = tid; w < TM * kCoeffsWords; w += kPersistThreads) {
           const int wo = (w / kCoeffsWords) * NV + w % kCoeffsWords;  // (token, word) in the [TM][NV] sums
           const float* vb = pf + (int64_t)slot * S * pstride + w;
@@ -1441,27 +1450,41 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           stage[row * 16 + ((q & 15) ^ (row >> 2))] = src[k];
         }
       };
-      // partial words of tile t_i: 16 tokens x NW words of this row block
-      // (ring slots [kCoeffsRingTiles][S][TM][NW]: dense, whole lines per
-      // store).  rel: the slot's release word, loaded before this step's x
-      // loads so that waiting for it never waits for them; the slot's
-      // previous tile must have been gathered before it is refilled.
+      // partial values of tile t_i: 16 tokens x NW words of this row block
+      // (ring slots [cring][S][TM][NW]: dense, whole lines per store).  A
+      // slot that held an earlier tile (generation > 0) is refilled only
+      // once its release word says that tile was gathered.  Two schedules
+      // (one loop copy each, so that the compiler's wait counting follows
+      // one of them):
+      //   early flags (the 64-tile ring, >= 32 splits): the release word is
+      //     loaded at the start of the step, before its x loads, and every
+      //     fold first waits for all of the wave's memory operations but
+      //     those x loads (the partial values stored in the step before
+      //     among them), whose flag the next step stores at its start;
+      //   late flags (the 512-tile ring of a broadcast stream's <= 16
+      //     splits, where a call seldom reuses a slot): nothing waits in the
+      //     fold unless the slot is reused (the release word is loaded
+      //     there); the flag of tile t_{i-A-2} is stored after the first
+      //     barrier of step i (see step).
+      // (the ring: kCoeffsRingTilesWide tiles in the late schedule, which runs
+      // at <= 16 splits, kCoeffsRingTiles in the early one; coeffs_ring_tiles)
       auto release_of = [&](int i) __attribute__((always_inline)) {
         return tagged_load(a.release + (r + L * i) % kCoeffsRingTiles);
       };
-      auto fold = [&](int i, uint64_t rel) __attribute__((always_inline)) {
+      auto fold = [&](int i, uint64_t rel, auto kLate) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(kLate)::value;
+        constexpr int cring = LATE ? kCoeffsRingTilesWide : kCoeffsRingTiles;
         const int t = r + L * i;
-        const uint32_t gen = (uint32_t)(t / kCoeffsRingTiles);
-        float* part = reinterpret_cast<float*>(a.partials) + ((int64_t)(t % kCoeffsRingTiles) * S + split) * (TM * NW) +
+        const uint32_t gen = (uint32_t)(t / cring);
+        float* part = reinterpret_cast<float*>(a.partials) + ((int64_t)(t % cring) * S + split) * (TM * NW) +
                       rb * 16 * NW;
-        // all of this wave's memory operations but the step's four x loads
-        // (issued last) are complete: the partial values the step before
-        // stored among them, which the flag stored after the next barrier
-        // releases
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!LATE) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (gen > 0) {
+          if constexpr (LATE) rel = tagged_load(a.release + t % cring);
           const uint32_t rtag = ring_tag(tag, 0);
           uint32_t it = 0;
           while ((uint32_t)(rel >> 32) != rtag || (uint32_t)rel < gen - 1u) {
@@ -1470,7 +1493,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
               __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               break;
             }
-            rel = tagged_load(a.release + t % kCoeffsRingTiles);
+            rel = tagged_load(a.release + t % cring);
           }
         }
         const float* rr = &red[i & 1][rb * 4][0];
@@ -1487,11 +1510,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
       };
       // release flag of this row block's partial values of tile t_i
-      auto flag = [&](int i) __attribute__((always_inline)) {
+      auto flag = [&](int i, auto kLate) __attribute__((always_inline)) {
+        constexpr int cring = decltype(kLate)::value ? kCoeffsRingTilesWide : kCoeffsRingTiles;
         const int t = r + L * i;
         if (gt == 0)
-          tagged_store(a.pflag + ((int64_t)(t % kCoeffsRingTiles) * S + split) * 2 + rb, 0.0f,
-                       ring_tag(tag, (uint32_t)(t / kCoeffsRingTiles)));
+          tagged_store(a.pflag + ((int64_t)(t % cring) * S + split) * 2 + rb, 0.0f, ring_tag(tag, (uint32_t)(t / cring)));
       };
       // projection and sum of squares of tile t_i from the stage (rows past
       // T read token 0 and are zeroed) -> LDS buffer i & 1
@@ -1547,19 +1570,69 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
         if ((n16 >> 2) == g) rw[n16 * NW + 24] = ((gd[0] + gd[1]) + gd[2]) + gd[3];
       };
-      // step i >= 1 (step 0 has no partial words to store)
-      // (the values of tile t_{i-3} were stored in step i - 2, complete at
-      // the wait of step i - 1's fold, before its last barrier)
-      auto step = [&](int i, u32x4_t* xb) __attribute__((always_inline)) {
-        if (i >= 3) flag(i - 3);
+      // step i >= 1 (step 0 has no partial values to store)
+      //   early flags: the flag of tile t_{i-3} (its values were stored in
+      //     step i - 2 and complete at the wait of step i - 1's fold, before
+      //     its last barrier); the release word of tile t_{i-1}'s slot; the
+      //     x loads of tile t_{i+A}; barrier; the fold of t_{i-1}.
+      //   late flags: the x loads of tile t_{i+A}; barrier; the flag of tile
+      //     t_{i-A-2} (its values were issued in step i - A - 1, before the
+      //     x loads of tile t_i, which every wave waited for in stage_write
+      //     before that barrier, so they are complete in memory); the fold
+      //     of t_{i-1}.
+      auto step_early = [&](int i, u32x4_t* xb) __attribute__((always_inline)) {
+        if (i >= 3) flag(i - 3, BoolC<false>{});
         const uint64_t rel = release_of(i - 1);
         __builtin_amdgcn_sched_barrier(0);
         stage_write(xb);
         load_x(xb, i + A);
-        MHC_GROUP_BARRIER("coefficients: stage written");
-        fold(i - 1, rel);
+        MHC_GROUP_BARRIER("coefficients, early flags: stage written");
+        fold(i - 1, rel, BoolC<false>{});
         project(i);
-        MHC_GROUP_BARRIER("coefficients: stage read");
+        MHC_GROUP_BARRIER("coefficients, early flags: stage read");
+      };
+      auto step_late = [&](int i, u32x4_t* xb) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        stage_write(xb);
+        load_x(xb, i + A);
+        MHC_GROUP_BARRIER("coefficients, late flags: stage written");
+        if (i >= A + 2) flag(i - A - 2, BoolC<true>{});
+        fold(i - 1, 0, BoolC<true>{});
+        project(i);
+        MHC_GROUP_BARRIER("coefficients, late flags: stage read");
+      };
+      auto run = [&](auto kLate) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(kLate)::value;
+        // tile t_i is in xq[i % A]
+        int i = 1;
+        for (; i + A <= niter; i += A) {
+#pragma unroll
+          for (int k = 0; k < A; ++k) {
+            if constexpr (LATE) {
+              step_late(i + k, xq[(k + 1) % A]);
+            } else {
+              step_early(i + k, xq[(k + 1) % A]);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < A; ++k) {
+          if (i + k < niter) {
+            if constexpr (LATE) {
+              step_late(i + k, xq[(k + 1) % A]);
+            } else {
+              step_early(i + k, xq[(k + 1) % A]);
+            }
+          }
+        }
+        fold(niter - 1, LATE ? (uint64_t)0 : release_of(niter - 1), kLate);
+        // the last tiles' values are complete in every wave: their flags
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        constexpr int kTail = LATE ? A + 2 : 3;
+        for (int k = niter >= kTail ? niter - kTail : 0; k < niter; ++k) flag(k, kLate);
       };
       if (niter > 0) {
 #pragma unroll
@@ -1574,22 +1647,11 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         MHC_GROUP_BARRIER("coefficients: first stage written");
         project(0);
         MHC_GROUP_BARRIER("coefficients: first stage read");
-        // tile t_i is in xq[i % A]
-        int i = 1;
-        for (; i + A <= niter; i += A) {
-#pragma unroll
-          for (int k = 0; k < A; ++k) step(i + k, xq[(k + 1) % A]);
+        if (S <= 16) {
+          run(BoolC<true>{});
+        } else {
+          run(BoolC<false>{});
         }
-#pragma unroll
-        for (int k = 0; k < A; ++k)
-          if (i + k < niter) step(i + k, xq[(k + 1) % A]);
-        fold(niter - 1, release_of(niter - 1));
-        // the last three tiles' values are complete in every wave: their flags
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        for (int k = niter >= 3 ? niter - 3 : 0; k < niter; ++k) flag(k);
       }
     } else {
 

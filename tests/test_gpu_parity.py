@@ -684,6 +684,31 @@ def test_pre_broadcast(T, C, schedule):
     assert_bf16_close(f64(h2), rh, what="h of the replicated stream")
 
 
+def test_pre_broadcast_wide_ring_wraps():
+    # T = 20000 at C = 7168: the coefficients run on 14 pseudo-route splits
+    # (persistent kernel, 13 stream lanes per split), whose ring holds 512
+    # tiles; 625 tiles wrap it.  Sampled rows against the oracle (every token
+    # is independent, so the oracle runs on those rows alone), and a second
+    # call bitwise equal to the first.
+    T, C = 20000, 7168
+    d = make_inputs(T, C, seed=31, rows="outliers", device=DEV)
+    x0 = d["x"][:, 0, :].contiguous()
+    ws = mhc.workspace(T, C, DEV, fresh=True)
+    cf, h = mhc.pre_broadcast(x0, d["phi"], d["bias"], d["gamma"], ws=ws)
+    torch.cuda.synchronize()
+    cf1, h1 = cf.clone(), h.clone()
+    cf, h = mhc.pre_broadcast(x0, d["phi"], d["bias"], d["gamma"], ws=ws)
+    torch.cuda.synchronize()
+    mhc.check(ws)
+    assert torch.equal(cf, cf1) and torch.equal(h, h1)
+    rows = sample_rows(T, extra=(16383, 16384, 16385))
+    idx = torch.from_numpy(rows).to(DEV)
+    rc, rh = O.pre_broadcast(f64(x0.index_select(0, idx)), f64(d["phi"]), f64(d["bias"]), f64(d["gamma"]),
+                             rmsnorm_eps=P.rmsnorm_eps, **kw())
+    assert_coeffs_close(f64(cf.index_select(0, idx)), rc)
+    assert_bf16_close(f64(h.index_select(0, idx)), rh, what="h")
+
+
 def skip_unless_schedule_bcast(T, C, schedule):
     # the broadcast call's coefficients take the persistent kernel on
     # pseudo-routes (C / 512 >= 8 splits) with two tiles per stream workgroup:
