@@ -655,7 +655,8 @@ def test_pack_phi_layout(C):
     assert np.array_equal(got.reshape(exp.shape), exp)
 
 
-@pytest.mark.parametrize("T,C", [(37, 3072), (300, 7168), (2048, 7168), (2300, 4096), (16, 2048), (37, 1024)])
+@pytest.mark.parametrize("T,C", [(37, 3072), (300, 7168), (2048, 7168), (2300, 4096), (16, 2048), (37, 1024),
+                                 (2048, 8192), (2048, 6144), (4096, 5120)])
 def test_pre_broadcast(T, C, schedule):
     # First-layer pre of a [T, C] input standing for all 4 routes, against the
     # oracle's plain definition (coefficients and pre of the replicated
@@ -711,8 +712,8 @@ def test_pre_broadcast_wide_ring_wraps():
 
 def skip_unless_schedule_bcast(T, C, schedule):
     # the broadcast call's coefficients take the persistent kernel on
-    # pseudo-routes (C / 512 >= 8 splits) with two tiles per stream workgroup:
-    # from 32 tiles at C = 7168 (16 per split), 56 at C = 4096 (28 per split);
-    # T = 2300 at C = 4096 also wraps the 64-tile ring
-    if schedule == "persistent" and (T, C) not in ((2048, 7168), (2300, 4096)):
+    # pseudo-routes (C / 512 >= 8 splits, 192 / (C / 512) stream lanes per
+    # split) with two tiles per stream workgroup: at T = 2048 or more for
+    # these hidden sizes (16, 12, 10, 8 and 14 splits)
+    if schedule == "persistent" and T < 2048:
         pytest.skip(f"the broadcast call runs the staged schedule at T={T}, C={C}")
