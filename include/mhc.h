@@ -152,9 +152,10 @@ int mhc_last_hip_error(void);
  * across several workgroups and need a caller-owned device workspace of
  * mhc_workspace_bytes(T, C, flags) bytes (256-byte aligned).  Its size is
  * bounded whatever T is: the partial sums live in rings reused as the tiles
- * pass, or a long call runs as several launches, so it holds at most ~32 MiB
- * of partial sums, 4 bytes per token (the list of tokens whose pre is
- * recomputed) and the packed projection (640 C bytes).  Before its
+ * pass, or a long call runs as several launches, so it holds at most
+ * ~128 MiB of partial sums, 4 bytes per token (the list of tokens whose pre
+ * is recomputed) and the packed projection (640 C bytes): at most ~143 MiB
+ * (T = 2^20, C = 16384), ~130 MiB at T = 8192, C = 7168.  Before its
  * first use a workspace must be cleared with mhc_workspace_init (a kernel on
  * `stream`, no memset node).  Every call leaves it ready for the next one:
  * its counters are reset, and the words it wrote carry that call's launch
@@ -343,10 +344,11 @@ int mhc_post_pre_fused_prepacked(const uint16_t* x, const uint16_t* y, const flo
  * make safe (see Workspace above).
  *   - Arguments, outputs, flags and results are those of
  *     mhc_post_pre_fused_prepacked (bitwise the same outputs).
- *   - Limit: the call takes T and C with mhc_workspace_bytes(T, C, flags) <=
- *     MHC_STATIC_SCRATCH_BYTES and returns MHC_ERR_SCRATCH, before any HIP
- *     call, otherwise.  The workspace is bounded (see Workspace above), and
- *     every T and C the library accepts fits (at most ~46 MiB).
+ *   - Limit: the call plans its work for the array: a long staged call
+ *     runs as launches of at most 32 MiB of partial sums (more launches than
+ *     with a workspace of mhc_workspace_bytes), so that every T and C the
+ *     library accepts fits (at most ~46 MiB); a shape that would not fit
+ *     returns MHC_ERR_SCRATCH before any HIP call.
  *   - error_word: a caller-owned device uint32 (4-byte aligned, not overlapping
  *     any other argument), required when T > 0; a bounded wait that expires
  *     sets it nonzero and the call's outputs are then invalid.  The library

@@ -169,15 +169,15 @@ static void set_delays(Plan& p, int64_t tiles) {
 }
 
 // Tile shape: 32 tokens x 128 channels (of every route) per workgroup.
-Plan make_plan(int64_t T, int64_t C) {
+Plan make_plan(int64_t T, int64_t C, size_t staged_budget) {
   Plan p;
   p.m = T <= 16 ? 16 : 32;  // a decode-sized call takes one 16-token tile
   p.cc = 128;
   p.s = (int)(C / p.cc);
   p.tiles = (T + p.m - 1) / p.m;
-  // staged launches: at most kStagedBudget bytes of partial words each
+  // staged launches: at most staged_budget bytes of partial words each
   const size_t tile_words = (size_t)p.s * p.m * kPartVals * sizeof(uint64_t);
-  int64_t chunk = (int64_t)(kStagedBudget / tile_words);
+  int64_t chunk = (int64_t)(staged_budget / tile_words);
   chunk = chunk < 16 ? 16 : (chunk > 256 ? 256 : chunk);
   p.chunk_tiles = p.tiles < chunk ? p.tiles : chunk;
   set_delays(p, p.chunk_tiles);
@@ -468,7 +468,9 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
     out[nout++] = {h_scale, (size_t)scale_rows * (C / 32)};
   }
   if ((rc = check_tensors(in, nin, out, nout))) return rc;
-  const mhc::Plan plan = mhc::make_plan(T, C);
+  // (the static scratch: staged launches of at most kStagedBudgetStatic
+  // bytes of partial words, so that every accepted shape fits)
+  const mhc::Plan plan = mhc::make_plan(T, C, err_word != nullptr ? mhc::kStagedBudgetStatic : mhc::kStagedBudget);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (err_word != nullptr) {
     // static scratch: every check first, then the scratch's address

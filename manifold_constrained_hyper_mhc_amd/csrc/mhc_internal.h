@@ -39,8 +39,11 @@ struct Plan {
 // rings (fused: kRingK * L tiles; coefficients only: coeffs_ring_tiles(S)
 // tiles), with at most kMaxLaneSplits = L * S stream workgroups; the staged
 // kernel runs a call as launches of at most chunk_tiles tiles, whose partial
-// words take at most kStagedBudget bytes.  So a workspace holds about
-// kStagedBudget bytes + 4 per token + the packed projection, whatever T is.
+// words take at most kStagedBudget bytes (kStagedBudgetStatic on the static
+// scratch).  So a workspace holds about that budget + 4 bytes per token +
+// the packed projection, whatever T is.  (Each staged launch pays its
+// pipeline's fill and drain: the larger budget keeps a prefill-sized call in
+// one launch up to C = 7168 and in three at C = 16384.)
 constexpr int kRingK = 8;
 // Coefficients-only ring: 64 tiles, or 512 at <= 16 splits (many stream
 // lanes, whose release flags trail their values by A + 2 steps: the ring
@@ -49,7 +52,8 @@ constexpr int kCoeffsRingTiles = 64;
 constexpr int kCoeffsRingTilesWide = 512;
 inline int coeffs_ring_tiles(int s) { return s <= 16 ? kCoeffsRingTilesWide : kCoeffsRingTiles; }
 constexpr int kMaxLaneSplits = 256;
-constexpr size_t kStagedBudget = (size_t)32 << 20;
+constexpr size_t kStagedBudget = (size_t)128 << 20;
+constexpr size_t kStagedBudgetStatic = (size_t)32 << 20;
 
 constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram matrix
 constexpr int kCoeffsWords = 25;        // per token, coefficients only: projection + sum of squares
@@ -67,7 +71,7 @@ constexpr int kPackBlocks = 5;          // 80 packed columns = 5 MFMA 16-column 
 constexpr int kPersistMaxBlocks = 512;
 constexpr size_t kPackBytesPerRow = 160;  // 80 bf16 per flattened row k
 
-Plan make_plan(int64_t T, int64_t C);
+Plan make_plan(int64_t T, int64_t C, size_t staged_budget = kStagedBudget);
 // The staged launch of a chunk of `tokens` tokens of a call planned as p.
 Plan chunk_plan(const Plan& p, int64_t tokens);
 

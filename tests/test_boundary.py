@@ -86,12 +86,14 @@ def test_sizes():
     assert 0 < w1 <= w2
     assert L.mhc_workspace_bytes(0, 1024, 0) > 0
     assert L.mhc_workspace_bytes(1 << 20, 16384, 1) % 256 == 0 and L.mhc_workspace_bytes(1 << 20, 16384, 1) > 0
-    # bounded: every accepted shape fits the static scratch (64 MiB), and the
-    # size stops growing with T beyond the staged launch budget
+    # bounded: at most ~143 MiB for any accepted shape, and the size stops
+    # growing with T beyond the staged launch budget
     for C in range(1024, 16385, 1024):
-        assert L.mhc_workspace_bytes(1 << 20, C, 1) <= 64 << 20, C
+        assert L.mhc_workspace_bytes(1 << 20, C, 1) <= 144 << 20, C
         grow = L.mhc_workspace_bytes(1 << 20, C, 0) - L.mhc_workspace_bytes(1 << 16, C, 0)
         assert grow <= 4 * ((1 << 20) - (1 << 16)) + 256, C  # only the 4-byte list entries
+
+
 
 
 # ---------------------------------------------------------------------------
@@ -258,3 +260,24 @@ def test_binding_rejects_bad_tensors_before_the_library():
     xb = torch.zeros((2, 4, 1024), dtype=torch.bfloat16)
     with pytest.raises(ValueError):      # CPU tensors are refused
         mhc.post(xb, torch.zeros((2, 1024), dtype=torch.bfloat16), torch.zeros((2, 24)))
+
+
+@no_gpu
+def test_static_scratch_plan_fits_every_shape():
+    # The static entry point plans its staged launches for its 64 MiB array.
+    # Every accepted shape gets past its scratch check (MHC_ERR_SCRATCH = 10)
+    # to the next one, the error word's alignment (MHC_ERR_ALIGN = 3): a
+    # misaligned error word ends the call there, before any HIP call, so the
+    # tensors can be far-apart addresses that are never touched.
+    L = mhc.lib()
+    p = MhcParams(1e-6, 1e-6, 2.0, 1e-6, 20)
+
+    def far(k, off=0):  # 1 TiB apart: the largest x (2^20 x 4 x 16384 bf16) is 128 GiB
+        return ctypes.c_void_p(0x100000000000 + (k << 40) + off)
+
+    for C in range(1024, 16385, 1024):
+        for T in (1 << 20, 100000, 8192, 6):
+            rc = L.mhc_post_pre_fused_prepacked_static(
+                far(0), far(1), far(2), far(3), far(4), far(5), T, C, ctypes.byref(p), 1,
+                far(6), far(7), far(8), far(9), far(10), far(11, 1), None)
+            assert rc == ALIGN, (T, C, rc)

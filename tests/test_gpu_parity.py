@@ -276,6 +276,27 @@ def test_rings_and_chunked_launches(T, C, schedule):
     check_fused(inp, out, mx=True)
 
 
+def test_chunked_staged_launches():
+    # C = 16384 (128 splits) always takes the staged kernel, whose launches
+    # hold at most 128 MiB of partial words: 115 tiles here, so T = 4000
+    # (125 tiles) runs as two launches, the second offset by 3680 tokens.
+    # Sampled rows on both sides of the seam, against the oracle.
+    T, C = 4000, 16384
+    assert mhc.schedule(T, C) == "staged"
+    d = make_inputs(T, C, seed=33, rows="outliers", device=DEV)
+    d["coeffs"] = oracle_coeffs_in(d["x"][:256], d["phi"], d["bias"]).to(DEV)
+    d["coeffs"] = d["coeffs"].repeat((T + 255) // 256, 1)[:T].contiguous()
+    cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
+    out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(T, extra=(3678, 3679, 3680, 3681, 3999))
+    idx = torch.from_numpy(rows).to(DEV)
+    inp = host_rows(d, rows)
+    assert_coeffs_close(f64(cf.index_select(0, idx)), O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw()))
+    g = {k: (v.index_select(0, idx) if v is not None else None) for k, v in out.items()}
+    check_fused(inp, g, mx=True)
+
+
 @pytest.mark.parametrize("T,C", SMALL)
 def test_fused(T, C):
     inp = small_inputs(T, C)

@@ -68,10 +68,8 @@ def test_static_scratch_covers_every_shape():
     L = mhc.lib()
     assert L.mhc_abi_version() >= 4
     assert L.mhc_strerror(mhc.ERR_SCRATCH) != b"unknown status"
-    limit = 64 << 20  # MHC_STATIC_SCRATCH_BYTES
-    # the workspace is bounded: every accepted shape fits the static scratch
-    for C in range(1024, 16385, 1024):
-        assert 0 < L.mhc_workspace_bytes(1 << 20, C, 1) <= limit, C
+    # (that every accepted shape's plan fits the static scratch is checked
+    # without a GPU in test_boundary.py)
     # a prefill-sized call on the scratch, bitwise the workspace call
     T, C = 8192, 4096
     d = make_inputs(T, C, seed=1, rows="decades", device=DEV)
