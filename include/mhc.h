@@ -170,7 +170,7 @@ int mhc_last_hip_error(void);
  * Schedule below: kernels on other streams, other processes on the GPU)
  * must check the word before it uses that call's outputs.
  *
- * Schedule.  When 32 <= C/128 <= 64 and T spans enough 32-token tiles
+ * Schedule.  When 16 <= C/128 <= 64 and T spans enough 32-token tiles
  * (two per stream workgroup), these two calls run a persistent kernel: one
  * 512-thread workgroup per compute unit, every one of which must be
  * resident at once; work that occupies compute units meanwhile delays it,

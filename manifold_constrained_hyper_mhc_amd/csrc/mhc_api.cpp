@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "mhc.h"
@@ -101,8 +102,9 @@ bool plan_fits(const mhc::Plan& p) {
 }
 
 // Persistent kernel: one 512-thread workgroup per CU, S*L stream workgroups
-// plus 32 reduce workgroups, all resident.  It runs when 32 <= S <= 64 and
-// each stream workgroup gets at least two tiles, unless the environment
+// plus 32 or 64 reduce workgroups, all resident.  It runs when 16 <= S <= 64
+// (8 <= S for the coefficients of a broadcast stream) and each stream
+// workgroup gets at least two tiles, unless the environment
 // variable MHC_SCHEDULE is "staged" (read on every call); otherwise the
 // staged kernel runs.
 bool persistent_allowed() {
@@ -122,22 +124,34 @@ int device_cus() {
   return cache[dev];
 }
 
-// min_s: the fewest splits per row that take the persistent kernel (the
-// coefficients of a broadcast stream, split into pseudo-routes, take it from
-// 8 on; every other call from 32 on).
-void choose_kernel(mhc::Plan& p, int min_s = 32) {
+// Which call a persistent launch serves: the fused pass, the coefficients
+// of a 4-route stream, or those of a broadcast stream on pseudo-routes.
+enum class Use { kFused, kCoeffs, kCoeffsPseudo };
+
+// The persistent kernel takes 16 to 64 splits per row (8 to 64 for the
+// coefficients of a broadcast stream on pseudo-routes); the fused pass and
+// the coefficients of a 4-route stream take it for the same shapes.  Its
+// reduce workgroups: 32, or 64 at <= 16 splits for the fused pass and the
+// broadcast coefficients.  At so few splits the stream workgroups' tiles
+// are short, and the reduce workgroups, which take one unit at a time and
+// wait for its flags and then its values, set the pace at 32; the
+// coefficients of a 4-route stream run faster with the two extra stream
+// lanes that 32 leave.
+void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   p.lanes = 0;
   if (!persistent_allowed()) return;
-  if (p.m != 32 || p.s < min_s || p.s > 64) return;
+  const bool pseudo = use == Use::kCoeffsPseudo;
+  if (p.m != 32 || p.s < (pseudo ? 8 : 16) || p.s > 64) return;
   const int cus = device_cus();
-  // coefficients at <= 16 splits (a broadcast stream on pseudo-routes):
-  // each stream workgroup's tiles are few and short, and the reduce's
-  // per-tile latency sets the pace, so 64 reduce workgroups
-  const int reds = p.s <= 16 ? 64 : 32;
-  int lanes = (cus - reds) / p.s;
+  const int reds = p.s <= 16 && use != Use::kCoeffs ? 64 : 32;
+  // the lane count that decides the schedule: with 32 reduce workgroups
+  // outside a broadcast stream, so that both calls take the same one
+  int lanes = (cus - (pseudo ? reds : 32)) / p.s;
   // the workspace's rings hold kRingK tiles per stream workgroup lane
   if (lanes * p.s > mhc::kMaxLaneSplits) lanes = mhc::kMaxLaneSplits / p.s;
-  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes || p.s * lanes + reds > mhc::kPersistMaxBlocks) return;
+  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes) return;
+  lanes = std::min(lanes, (cus - reds) / p.s);
+  if (lanes < 1 || p.s * lanes + reds > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;
   p.reds = reds;
 }
@@ -346,7 +360,7 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   mhc::Plan run = plan;
-  choose_kernel(run, pseudo ? 8 : 32);
+  choose_kernel(run, pseudo ? Use::kCoeffsPseudo : Use::kCoeffs);
   mhc::SplitArgs a = split_args(run, ws, T, C, p);
   const void* packed = phi_packed;
   void* dst = static_cast<char*>(ws) + plan.off_phi;

@@ -522,7 +522,6 @@ __device__ void fix_flagged(const SplitArgs& a, uint32_t tag, double* red, uint3
 template <bool WITH_Y, int TM, bool LAST_USE, bool YQ = false>
 __device__ __forceinline__ void load_stream(const SplitArgs& a, int64_t tok0, int cl, int tr, TileRegs<TM / 16>& R) {
   constexpr int NP = TM / 16;
-  const int C = a.C;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int64_t t = tok0 + p * 16 + tr;
@@ -1456,13 +1455,14 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // once its release word says that tile was gathered.  Two schedules
       // (one loop copy each, so that the compiler's wait counting follows
       // one of them):
-      //   early flags (the 64-tile ring, >= 32 splits): the release word is
+      //   early flags (the 64-tile ring, >= 17 splits): the release word is
       //     loaded at the start of the step, before its x loads, and every
       //     fold first waits for all of the wave's memory operations but
       //     those x loads (the partial values stored in the step before
       //     among them), whose flag the next step stores at its start;
-      //   late flags (the 512-tile ring of a broadcast stream's <= 16
-      //     splits, where a call seldom reuses a slot): nothing waits in the
+      //   late flags (the 512-tile ring at <= 16 splits: a broadcast
+      //     stream's pseudo-routes, or C = 2048; a call seldom reuses a
+      //     slot there): nothing waits in the
       //     fold unless the slot is reused (the release word is loaded
       //     there); the flag of tile t_{i-A-2} is stored after the first
       //     barrier of step i (see step).
@@ -2326,7 +2326,7 @@ static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream
 
 template <int MODE>
 static hipError_t launch_persist_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
-  if (p.reds != 32 && !(p.reds == 64 && MODE == kModeCoeffs && p.s <= 16)) return hipErrorInvalidConfiguration;
+  if (p.reds != 32 && !(p.reds == 64 && p.s <= 16)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(p.s * p.lanes + p.reds)), block(kPersistThreads);
   k_persist<MODE><<<grid, block, 0, s>>>(a);
   return hipGetLastError();

@@ -71,9 +71,9 @@ def to_dev(inp):
 
 SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048)]
 
-# shapes the persistent schedule takes (32 <= C/128 <= 64, enough tiles),
-# with a ragged last tile
-PERSISTENT = [(300, 7168), (500, 4096)]
+# shapes the persistent schedule takes (16 <= C/128 <= 64, enough tiles),
+# with a ragged last tile: 56, 32, 24 and 16 splits
+PERSISTENT = [(300, 7168), (500, 4096), (1000, 3072), (1000, 2048)]
 # the other hidden sizes each schedule accepts: S = 40 and 48 splits (5 and 4
 # stream workgroups per split), S = 64 (the persistent kernel's limit; the
 # staged kernel's long reduce runs), and C = 16384 (staged only, S = 128)
@@ -290,6 +290,39 @@ def test_chunked_staged_launches():
     out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
     torch.cuda.synchronize()
     rows = sample_rows(T, extra=(3678, 3679, 3680, 3681, 3999))
+    idx = torch.from_numpy(rows).to(DEV)
+    inp = host_rows(d, rows)
+    assert_coeffs_close(f64(cf.index_select(0, idx)), O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw()))
+    g = {k: (v.index_select(0, idx) if v is not None else None) for k, v in out.items()}
+    check_fused(inp, g, mx=True)
+
+
+def test_sixteen_splits_rings_wrap():
+    # C = 2048 (16 splits) takes the persistent kernel: the fused pass with
+    # 12 stream lanes per split and 64 reduce workgroups (a ring of 96
+    # tiles), the coefficients with 14 lanes and 32 reduce workgroups (the
+    # late-release schedule at <= 16 splits: a ring of 512 tiles);
+    # T = 17000 (532 tiles) wraps both.  Sampled rows on both sides of the coefficients ring's
+    # seam against the oracle, and a second call bitwise equal to the first.
+    T, C = 17000, 2048
+    assert mhc.schedule(T, C) == "persistent"
+    d = make_inputs(T, C, seed=34, rows="outliers", device=DEV)
+    d["coeffs"] = oracle_coeffs_in(d["x"][:256], d["phi"], d["bias"]).to(DEV)
+    d["coeffs"] = d["coeffs"].repeat((T + 255) // 256, 1)[:T].contiguous()
+    ws = mhc.workspace(T, C, DEV, fresh=True)
+    outs = []
+    for _ in range(2):
+        cf = mhc.coeffs(d["x"], d["phi"], d["bias"], ws=ws)
+        out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"],
+                                 mxfp8=True, ws=ws)
+        torch.cuda.synchronize()
+        outs.append((cf.clone(), {k: (v.clone() if v is not None else None) for k, v in out.items()}))
+    mhc.check(ws)
+    (cf, out), (cf2, out2) = outs
+    assert torch.equal(cf, cf2)
+    for k, v in out.items():
+        assert v is None or torch.equal(v, out2[k]), f"output {k} of the second call differs"
+    rows = sample_rows(T, extra=(3071, 3072, 3073, 16383, 16384, 16385))
     idx = torch.from_numpy(rows).to(DEV)
     inp = host_rows(d, rows)
     assert_coeffs_close(f64(cf.index_select(0, idx)), O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw()))
