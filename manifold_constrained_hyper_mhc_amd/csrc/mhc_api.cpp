@@ -278,7 +278,8 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
 }
 
 // One coefficients or fused call: a single persistent launch (a fused one
-// followed by the recomputation of the tokens it listed), or staged
+// without the MXFP8 epilogue followed by the recomputation of the tokens it
+// listed; with it, the kernel's last workgroup recomputes them), or staged
 // launches of at most run.chunk_tiles tiles each, over consecutive tokens,
 // every pointer offset to the chunk's first token (their last workgroups
 // recompute the listed tokens themselves).

@@ -442,11 +442,12 @@ __device__ __forceinline__ void xprime8(const SplitArgs& a, int64_t t, int c, co
 }
 
 // The direct pre of the tokens a fused launch listed because their route
-// combination cancels (gram_rms_factor): run by the staged launch's last
-// workgroup (NT threads), once every other workgroup has left, or by
-// k_fix_flagged after a persistent launch; either way the list and the
-// listed tokens' pre weights (written through to memory before the tokens'
-// q words) are complete.  Per token: x' recomputed from x, y and the post
+// combination cancels (gram_rms_factor): run by the last workgroup of the
+// launch (NT threads: 256 in a staged launch, 512 in a persistent one with
+// the MXFP8 epilogue), once every other workgroup has left, or by
+// k_fix_flagged after any other persistent launch; either way the list and
+// the listed tokens' pre weights (written through to memory before the
+// tokens' q words) are complete.  Per token: x' recomputed from x, y and the post
 // coefficients (inputs only, so nothing another XCD wrote is read), g in
 // binary64, sum_c g^2 in binary64, then h and its MXFP8 blocks written; the
 // pre step left these tokens' rows unwritten (the sign of q0).  A launch
@@ -1133,6 +1134,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
   __shared__ float gam[FUSED ? kCC : 1];
+  __shared__ uint32_t s_last;  // this workgroup left last
   float* finw = reinterpret_cast<float*>(&xslot[0][0][0]);  // reduce workgroups: [2][8][NV] or [TM][NV] sums
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2084,22 +2086,43 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   }
 
   // ---- leave: the last workgroup to finish advances the launch epoch ----
-  // (The listed tokens of a fused launch are recomputed by k_fix_flagged,
-  // launched after this kernel: the recomputation inlined here raised the
-  // register allocation of the whole kernel and slowed its main loop.)
+  // The listed tokens of a fused launch are recomputed after every reduce
+  // workgroup has left (the list is then complete): in the MXFP8 modes by
+  // this workgroup, here; in the others by k_fix_flagged, launched after
+  // this kernel, which measured faster for them (the tail here changes the
+  // main loop's register allocation: MXFP8 prefill 161 -> 158 us, bf16
+  // prefill 268 -> 273 us).
   __syncthreads();
   if (tid == 0) {
+    uint32_t last = 0;
     const uint32_t done = __hip_atomic_fetch_add(a.tiles_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == gridDim.x - 1u) {
       __hip_atomic_store(a.tiles_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = 1;
+    }
+    s_last = last;
+  }
+  if constexpr (FUSED && MX) {
+    __syncthreads();
+    if (s_last != 0) {
+      // The arguments are read here through the kernel-argument segment's
+      // address (the kernel's one argument sits at its start), made opaque,
+      // so that the compiler cannot hoist these loads to the kernel's entry:
+      // hoisted, their scalar registers stay live through the main loop and
+      // raise its spills.  (Taking the address of the argument itself
+      // copies it to scratch memory, which slowed the whole kernel 1.66x.)
+      const SplitArgs* ap = (const SplitArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(ap));
+      fix_flagged<YQ, MX, kPersistThreads>(*ap, tag, reinterpret_cast<double*>(&red[0][0][0]));
     }
   }
 }
 
-// The direct pre of the tokens a persistent fused launch listed (see
-// fix_flagged), launched after it on the same stream; its tag is the epoch
-// the launch left.  Workgroup b takes the listed tokens b, b + grid, ...
+// The direct pre of the tokens a persistent fused launch without the MXFP8
+// epilogue listed (see fix_flagged), launched after it on the same stream;
+// its tag is the epoch the launch left.  Workgroup b takes the listed
+// tokens b, b + grid, ...
 template <bool YQ, bool MX>
 __global__ __launch_bounds__(256) void k_fix_flagged(const SplitArgs a) {
   __shared__ double red[4];
@@ -2402,9 +2425,9 @@ hipError_t launch_fix_flagged(const SplitArgs& a, int mode, hipStream_t s) {
   const dim3 g(grid), b(256);
   switch (mode) {
     case kModeFused: k_fix_flagged<false, false><<<g, b, 0, s>>>(a); break;
-    case kModeFusedMx: k_fix_flagged<false, true><<<g, b, 0, s>>>(a); break;
     case kModeFused | kModeYInt8: k_fix_flagged<true, false><<<g, b, 0, s>>>(a); break;
-    case kModeFusedMx | kModeYInt8: k_fix_flagged<true, true><<<g, b, 0, s>>>(a); break;
+    case kModeFusedMx:
+    case kModeFusedMx | kModeYInt8: return hipSuccess;  // the kernel's last workgroup did it
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
