@@ -72,12 +72,15 @@ def to_dev(inp):
 SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048)]
 
 # shapes the persistent schedule takes (16 <= C/128 <= 64, enough tiles),
-# with a ragged last tile: 56, 32, 24 and 16 splits
-PERSISTENT = [(300, 7168), (500, 4096), (1000, 3072), (1000, 2048)]
+# with a ragged last tile: 56, 32, 24 and 16 splits, and the fewest tiles
+# it takes at 56 and 16 splits (two per stream workgroup: 8 tiles with 4
+# stream lanes, 28 with 14)
+PERSISTENT = [(300, 7168), (500, 4096), (1000, 3072), (1000, 2048), (225, 7168), (865, 2048)]
 # the other hidden sizes each schedule accepts: S = 40 and 48 splits (5 and 4
 # stream workgroups per split), S = 64 (the persistent kernel's limit; the
-# staged kernel's long reduce runs), and C = 16384 (staged only, S = 128)
-WIDE = [(400, 5120), (300, 6144), (300, 8192), (300, 16384)]
+# staged kernel's long reduce runs), and C = 9216, 12288 and 16384 (staged
+# only, S = 72, 96 and 128)
+WIDE = [(400, 5120), (300, 6144), (300, 8192), (200, 9216), (200, 12288), (300, 16384)]
 
 
 def test_schedule_choice(monkeypatch):
@@ -88,6 +91,23 @@ def test_schedule_choice(monkeypatch):
     assert mhc.schedule(6, 7168) == "staged"
     monkeypatch.setenv("MHC_SCHEDULE", "staged")
     assert mhc.schedule(8192, 7168) == "staged"
+
+
+def test_schedule_thresholds(monkeypatch):
+    """The persistent kernel needs two tiles per stream workgroup: on a
+    256-CU MI355X, 4 stream lanes at C = 7168 (8 tiles: T > 224) and 14 at
+    C = 2048 (28 tiles: T > 864); fewer than 16 splits (C = 1024) and more
+    than 64 (C = 9216) run the staged kernel."""
+    monkeypatch.delenv("MHC_SCHEDULE", raising=False)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the thresholds below are those of a 256-CU device")
+    assert mhc.schedule(225, 7168) == "persistent"
+    assert mhc.schedule(224, 7168) == "staged"
+    assert mhc.schedule(865, 2048) == "persistent"
+    assert mhc.schedule(864, 2048) == "staged"
+    assert mhc.schedule(65536, 1024) == "staged"
+    assert mhc.schedule(65536, 9216) == "staged"
+    assert mhc.schedule(65536, 8192) == "persistent"
 
 
 @pytest.fixture(params=["staged", "persistent"])
