@@ -59,10 +59,11 @@ constexpr int kPartVals = 24 + kGram;   // per token: projection + route Gram ma
 constexpr int kCoeffsWords = 25;        // per token, coefficients only: projection + sum of squares
 
 // Workspace header at fixed offsets, whatever the shape of a call: the error
-// word, the launch epoch, the tiles-done counter, the tagged count of tokens
-// whose fused pre needs the direct recomputation, then one leave counter per
-// possible tile (2^20 tokens / 32 tokens per tile).
-constexpr size_t kWsErr = 0, kWsEpoch = 4, kWsTilesDone = 8, kWsFixWord = 16;
+// word, the tiles-done counter, the ticket counter of a one-tile launch and
+// the launch epoch (the low and high halves of one 64-bit word), the tagged
+// count of tokens whose fused pre needs the direct recomputation, then one
+// leave counter per possible tile (2^20 tokens / 32 tokens per tile).
+constexpr size_t kWsErr = 0, kWsTilesDone = 4, kWsTicket = 8, kWsEpoch = 12, kWsFixWord = 16;
 constexpr size_t kWsDep = 256;
 constexpr int64_t kMaxTiles = (int64_t)(1 << 20) / 32;
 constexpr size_t kWsHeaderBytes = kWsDep + (size_t)kMaxTiles * 4;

@@ -287,14 +287,16 @@ constexpr int kDppRowRor8 = 0x128;   // row_ror:8
 // slot(lane).  In the fused modes publish(q, pre, cancels), q_i = pre_i * r_h,
 // runs before the Sinkhorn iterations: the pre step needs only q, so it does
 // not wait for them; `cancels` says that the token's pre must be recomputed
-// directly (gram_rms_factor).
+// directly (gram_rms_factor).  bias_lane: bias[wave_bias_index(lane)],
+// loaded by the caller ahead of time.
+__device__ __forceinline__ int wave_bias_index(int lane) { return lane < 16 ? 8 + lane : (lane < 24 ? lane - 16 : 0); }
 template <bool FUSED, class Publish>
-__device__ __forceinline__ float finalize_wave(const float* sums, const float* bias, int C, const Scalars& sc,
+__device__ __forceinline__ float finalize_wave(const float* sums, float bias_lane, int C, const Scalars& sc,
                                                int lane, Publish&& publish) {
   const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
   const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
-  const int li = lane < 16 ? 8 + lane : (lane < 24 ? lane - 16 : 0);
-  const float l = r * sums[li] + bias[li];
+  const int li = wave_bias_index(lane);
+  const float l = r * sums[li] + bias_lane;
   const float sg = 1.0f / (1.0f + expf(-l));
   const float pp = (lane >= 20 && lane < 24) ? sc.hc_post_scale * sg : sg;
   float v = expf(l);
@@ -598,14 +600,23 @@ __device__ __forceinline__ void post_tile(TileRegs<TM / 16>& R, const float (*cf
 }
 
 // Four workgroups per CU (<= 128 VGPRs, 4 x 39.5 KB of LDS) when the reduce
-// runs are short; long runs (hidden sizes above 7168) need more registers.
+// runs are short; long runs (hidden sizes above 7168) need more registers,
+// and so does a 16-token tile (a launch of a few hundred workgroups at most,
+// whose projection fragments are in registers with its stream).
 template <int MODE, int TM, int RUN>
-__global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs a) {
+__global__ __launch_bounds__(256, RUN <= 8 && TM == 32 ? 4 : 2) void k_split(const SplitArgs a) {
   constexpr bool FUSED = mode_fused(MODE);
   constexpr bool MX = mode_mx(MODE);
   constexpr bool YQ = mode_yq(MODE);
   constexpr int W = 4, NV = kPartVals, NP = TM / 16, RB = TM / 16, NQ = TM / 4;
   constexpr int NVU = FUSED ? NV : 25;
+  // 16-token tiles: a call of at most 16 tokens, one tile, latency-bound.
+  // Its workgroups take their jobs in the order they start (see below); its
+  // pre step recomputes x' (the workgroup that stored it runs at the same
+  // time, so the read-back path would seldom apply), phase A then neither
+  // waits for its x' stores nor announces them, and its projection
+  // fragments are loaded with its stream.
+  constexpr bool ONE = TM == 16;
   // partial words per token in the workspace: [tiles][S][TM][PW], dense, so
   // that every store instruction writes whole lines
   constexpr int PW = NVU;
@@ -619,25 +630,54 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   __shared__ float cfs_c[FUSED ? TM : 1][20];
   __shared__ float fin[kMaxTileTokensPerGroup][NV];
   __shared__ float qs[FUSED ? TM : 1][4];
-  __shared__ uint32_t s_tag, s_xdirect;
+  __shared__ uint32_t s_tag, s_xdirect, s_job;
   u32x4_t* xs = reinterpret_cast<u32x4_t*>(lds);
   float* red = reinterpret_cast<float*>(lds);   // [W][TM][NV]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S;
-  int stage, split;
-  if ((S & 7) == 0) {
-    const int per = S >> 3, b = (int)blockIdx.x, j = b >> 3;
-    stage = j / per;
-    split = (b & 7) * per + j % per;
-  } else {
-    stage = (int)(blockIdx.x / S);
-    split = (int)(blockIdx.x % S);
-  }
   const int tiles = (int)a.tiles;
-  const int tA = stage < tiles ? stage : -1;
-  const int tR = (stage - a.d1 >= 0 && stage - a.d1 < tiles) ? stage - a.d1 : -1;
-  const int tC = (FUSED && stage - a.d2 >= 0 && stage - a.d2 < tiles) ? stage - a.d2 : -1;
+  int split, tA, tR, tC;
+  if constexpr (ONE) {
+    // A launch's workgroups start on the XCDs one after another (about half
+    // a microsecond apart), so a job bound to blockIdx may wait for the last
+    // XCD.  Here each workgroup takes a ticket in the order it starts, with
+    // the launch epoch in the same 64-bit word (ticket in the low half, epoch
+    // in the high half): tickets [0, S) run phase A of split t, the next
+    // min(S, TM) the reduce of the tokens split t - S owns, the last S (fused
+    // modes) the pre step of split t - S - min(S, TM).  A job waits only for
+    // jobs of lower tickets, which have started.  The last ticket advances
+    // the epoch and clears the ticket: every workgroup has read the epoch.
+    static_assert(kWsEpoch == kWsTicket + 4 && kWsTicket % 8 == 0, "ticket and epoch share a 64-bit word");
+    if (tid == 0) {
+      uint64_t* lw = reinterpret_cast<uint64_t*>(a.epoch - 1);
+      const uint64_t old = __hip_atomic_fetch_add(lw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t next = (uint32_t)(old >> 32) + 1u;
+      s_tag = next;
+      s_job = (uint32_t)old;
+      if ((uint32_t)old == gridDim.x - 1u)
+        __hip_atomic_store(lw, (uint64_t)next << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // s_job, s_tag
+    const int job = (int)s_job, nR = S < TM ? S : TM;
+    tA = job < S ? 0 : -1;
+    tR = job >= S && job < S + nR ? 0 : -1;
+    tC = FUSED && job >= S + nR ? 0 : -1;
+    split = tA >= 0 ? job : (tR >= 0 ? job - S : job - S - nR);
+  } else {
+    int stage;
+    if ((S & 7) == 0) {
+      const int per = S >> 3, b = (int)blockIdx.x, j = b >> 3;
+      stage = j / per;
+      split = (b & 7) * per + j % per;
+    } else {
+      stage = (int)(blockIdx.x / S);
+      split = (int)(blockIdx.x % S);
+    }
+    tA = stage < tiles ? stage : -1;
+    tR = (stage - a.d1 >= 0 && stage - a.d1 < tiles) ? stage - a.d1 : -1;
+    tC = (FUSED && stage - a.d2 >= 0 && stage - a.d2 < tiles) ? stage - a.d2 : -1;
+  }
   const int C = a.C;
   const int c0 = split * a.cs;
   const int c8 = tid & 15, tr = tid >> 4;
@@ -650,11 +690,11 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // and R's gather of the partials of tile tR (written by workgroups of stage
   // tR, D1 stages earlier, normally complete by now; stale words are polled
   // again when R runs).
-  if (tid == 0) s_tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  if (!ONE && tid == 0) s_tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   TileRegs<NP> ra;
   if (tA >= 0) load_stream<FUSED, TM, true, YQ>(a, (int64_t)tA * TM, cl, tr, ra);
   uint64_t own = 0;
-  if (tid == 0 && tC >= 0) own = tagged_load(a.owner + (int64_t)tC * S + split);
+  if (!ONE && tid == 0 && tC >= 0) own = tagged_load(a.owner + (int64_t)tC * S + split);
   float4 cfa = make_float4(0.0f, 0.0f, 0.0f, 0.0f), cfc = cfa;
   if constexpr (FUSED) {
     if (tA >= 0) cfa = fetch_post_coeffs<TM>(a, (int64_t)tA * TM, tid);
@@ -679,6 +719,8 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   uint64_t w[RUN];
 #pragma unroll
   for (int q = 0; q < RUN; ++q) w[q] = q < n ? tagged_load(gbase + q * gstride) : 0;
+  // this lane's bias entry for the finalisation (loaded now, off its path)
+  const float bias_lane = doR ? a.bias[wave_bias_index(lane)] : 0.0f;
   if constexpr (FUSED) {
     store_post_coeffs<TM>(cfa, tid, cfs_a);
     store_post_coeffs<TM>(cfc, tid, cfs_c);
@@ -687,7 +729,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // stored, when that workgroup ran on this XCD (their shared L2 holds the
   // stores); otherwise it recomputes x' from x and y.
   if (tid == 0)
-    s_xdirect = tC >= 0 && !a.recompute_x && (uint32_t)(own >> 32) == ring_tag(s_tag, 0) &&
+    s_xdirect = !ONE && tC >= 0 && !a.recompute_x && (uint32_t)(own >> 32) == ring_tag(s_tag, 0) &&
                 __float_as_uint(tagged_value(own)) == xcd_id();
   __syncthreads();  // s_tag, cfs, s_xdirect
   const uint32_t tag = s_tag;
@@ -697,6 +739,18 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // ---------------- A: post, statistics and projection of tile tA ----------------
   if (tA >= 0) {
     const int64_t tok0 = (int64_t)tA * TM;
+    // projection fragments of the wave's 32-channel step, all four routes
+    u32x4_t bfrag[4][kPackBlocks];
+    auto load_bfrag = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t kstep = ((int64_t)j * a.prs + c0 + wave * 32) >> 5;
+        const u32x4_t* bp = reinterpret_cast<const u32x4_t*>(a.phi_packed) + kstep * (kPackBlocks * kWave) + lane;
+#pragma unroll
+        for (int b = 0; b < kPackBlocks; ++b) bfrag[j][b] = bp[b * kWave];
+      }
+    };
+    if constexpr (ONE) load_bfrag();
     if constexpr (FUSED) post_tile<TM, YQ>(ra, cfs_a, tr);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -711,16 +765,9 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
 #pragma unroll
       for (int j = 0; j < 4; ++j) xs[xs_offset(m, j, c8)] = ra.x[p][j];
     }
-    // projection fragments of the wave's 32-channel step, all four routes,
-    // in flight together while the workgroup meets at the barrier
-    u32x4_t bfrag[4][kPackBlocks];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t kstep = ((int64_t)j * a.prs + c0 + wave * 32) >> 5;
-      const u32x4_t* bp = reinterpret_cast<const u32x4_t*>(a.phi_packed) + kstep * (kPackBlocks * kWave) + lane;
-#pragma unroll
-      for (int b = 0; b < kPackBlocks; ++b) bfrag[j][b] = bp[b * kWave];
-    }
+    // (otherwise the fragments are loaded now, in flight together while
+    // the workgroup meets at the barrier)
+    if constexpr (!ONE) load_bfrag();
     __syncthreads();  // x' staged
 
     f32x4_t acc[RB][2];
@@ -775,7 +822,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
           if (e <= jr) red[(wave * TM + row) * NV + 24 + gram_slot(e, jr)] = gv[qg][e];
       }
     }
-    if constexpr (FUSED) {
+    if constexpr (FUSED && !ONE) {
       // every wave's x' stores have reached the L2 before the owner word
       // (stored after this barrier) announces them
       __builtin_amdgcn_s_waitcnt(0);
@@ -800,7 +847,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
       tagged_store(part + (idx / NV) * PW + vv, sum, wtag);
     }
     __syncthreads();  // LDS free for R
-    if (FUSED && tid == 0) tagged_store(a.owner + (int64_t)tA * S + split, __uint_as_float(xcd_id()), wtag);
+    if (FUSED && !ONE && tid == 0) tagged_store(a.owner + (int64_t)tA * S + split, __uint_as_float(xcd_id()), wtag);
   }
 
   // the loads of C (inputs only) are in flight while R runs
@@ -855,7 +902,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         const int m = split + kq * S;
         uint64_t* const qdst = a.publish + ((int64_t)tR * TM + m) * 4 + (lane & 3);
         const int64_t t = tok0 + m;
-        const float cv = finalize_wave<FUSED>(fin[kq], a.bias, a.rms_c, a.sc, lane,
+        const float cv = finalize_wave<FUSED>(fin[kq], bias_lane, a.rms_c, a.sc, lane,
                                               [=](const float* q, const float* pw, bool cancels)
                                                   __attribute__((always_inline)) {
                                                 // a cancelling token: listed (and its pre weights written
@@ -879,6 +926,8 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   if constexpr (FUSED) {
     if (tC >= 0) {
       const int64_t tok0 = (int64_t)tC * TM;
+      // (one tile: x' first, so that only the pre itself follows the q words)
+      if (ONE && !xdirect) post_tile<TM, YQ>(rc, cfs_c, tr);
       if (tid < TM * 4) {
         const uint64_t* qp = a.publish + tok0 * 4 + tid;
         uint64_t qw = tagged_load(qp);
@@ -893,7 +942,7 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
         }
         (&qs[0][0])[tid] = tagged_value(qw);
       }
-      if (!xdirect) post_tile<TM, YQ>(rc, cfs_c, tr);
+      if (!ONE && !xdirect) post_tile<TM, YQ>(rc, cfs_c, tr);
       __syncthreads();  // qs
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
@@ -951,6 +1000,18 @@ __global__ __launch_bounds__(256, RUN <= 8 ? 4 : 2) void k_split(const SplitArgs
   // In the fused modes that workgroup then recomputes the pre of the tokens
   // whose route combination cancels (every tile's pre steps have run, so the
   // list is complete).
+  // (One tile: the epoch advanced with the last ticket, and the pre step of
+  // split 0 recomputes the listed tokens as soon as its own rows are out:
+  // it has seen every token's q words, which follow their listing.)
+  if constexpr (ONE) {
+    if constexpr (FUSED) {
+      if (tC >= 0 && split == 0) {
+        __syncthreads();  // qs, LDS free
+        fix_flagged<YQ, MX, 256>(a, tag, reinterpret_cast<double*>(lds));
+      }
+    }
+    return;
+  }
   const int tLeave = FUSED ? tC : tR;
   if (tLeave >= 0) {
     __syncthreads();
@@ -2331,8 +2392,11 @@ hipError_t launch_pack_phi_sum(const float* phi, const void* packed, int C, void
 template <int MODE>
 static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
   const int64_t stages = p.tiles + (mode_fused(MODE) ? p.d2 : p.d1);
-  const dim3 grid((unsigned)(stages * p.s)), block(256);
-  if ((p.m != 32 && p.m != 16) || p.cc != kCC) return hipErrorInvalidConfiguration;
+  // one 16-token tile: S phase-A jobs, min(S, 16) reduce jobs, S pre jobs
+  const int64_t nR = p.s < 16 ? p.s : 16;
+  const int64_t blocks = p.m == 16 ? p.s + nR + (mode_fused(MODE) ? p.s : 0) : stages * p.s;
+  const dim3 grid((unsigned)blocks), block(256);
+  if ((p.m != 32 && p.m != 16) || p.cc != kCC || (p.m == 16 && p.tiles != 1)) return hipErrorInvalidConfiguration;
   if (p.m == 16) {
     if (plan_run_len(p) <= 8) {
       k_split<MODE, 16, 8><<<grid, block, 0, s>>>(a);

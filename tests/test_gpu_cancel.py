@@ -37,16 +37,17 @@ def _gpu_ready():
 def fix_count(ws):
     """Tokens the last fused call listed for the direct recomputation: the
     workspace's tagged count word (offset 16) when its tag is the launch epoch
-    (offset 4)."""
+    (offset 12)."""
     head = ws[:24].cpu().numpy()
-    epoch = int(head[4:8].view(np.uint32)[0])
+    epoch = int(head[12:16].view(np.uint32)[0])
     word = int(head[16:24].view(np.uint64)[0])
     return (word & 0xFFFFFFFF) if (word >> 32) == epoch else 0
 
 
 @pytest.mark.parametrize("mx", [False, True])
 @pytest.mark.parametrize("T,C,sched", [(37, 3072, "staged"), (300, 7168, "persistent"), (300, 7168, "staged"),
-                                       (500, 4096, "persistent"), (1000, 2048, "persistent")])
+                                       (500, 4096, "persistent"), (1000, 2048, "persistent"),
+                                       (12, 7168, "staged"), (16, 1024, "staged")])
 def test_fused_on_cancelling_routes(T, C, sched, mx, monkeypatch):
     monkeypatch.setenv("MHC_SCHEDULE", sched)
     assert mhc.schedule(T, C) == sched
