@@ -11,6 +11,7 @@ a call of another shape (which leaves other tags and ring contents behind),
 and compares every output with the first call's, bit for bit; the workspace
 error word must stay clear.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -103,3 +104,41 @@ def test_broadcast_pre_repeated_bitwise():
         else:
             _assert_same(first, {"coeffs": cf, "h": h}, "broadcast pre", rep)
     mhc.check(ws)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_decode_repeated_bitwise(mx):
+    # one-tile launches take their jobs by ticket, with the launch epoch in
+    # the ticket's word; the last ticket advances the epoch and clears the
+    # count.  Many calls in a row on one workspace, alternating with a
+    # 32-token-tile call (staged) and a persistent one (which advance the
+    # same epoch by other paths), and with coefficients-only one-tile calls
+    # (fewer jobs per launch): every decode output bitwise equal to the
+    # first call's, the error word clear.
+    w = WORKLOADS["decode"]
+    d = make_inputs(w.T, w.C, seed=11, device=DEV)
+    cf = _coeffs_in(w.T, w.C, seed=12)
+    mid = make_inputs(40, w.C, seed=13, device=DEV)
+    cf_mid = _coeffs_in(40, w.C, seed=14)
+    big = make_inputs(300, w.C, seed=15, device=DEV)
+    cf_big = _coeffs_in(300, w.C, seed=16)
+    ws = mhc.workspace(300, w.C, DEV, fresh=True)
+    first = None
+    for rep in range(REPS * 2):
+        out = mhc.post_pre_fused(d["x"], d["y"], cf, d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=mx, ws=ws)
+        cfo = mhc.coeffs(d["x"], d["phi"], d["bias"], ws=ws)
+        if rep % 3 == 1:
+            mhc.post_pre_fused(mid["x"], mid["y"], cf_mid, mid["phi_next"], mid["bias_next"], mid["gamma_next"], ws=ws)
+        if rep % 5 == 2:
+            mhc.post_pre_fused(big["x"], big["y"], cf_big, big["phi_next"], big["bias_next"], big["gamma_next"], ws=ws)
+        torch.cuda.synchronize()
+        out = {k: (v.clone() if v is not None else None) for k, v in out.items()}
+        out["coeffs"] = cfo.clone()
+        if first is None:
+            first = out
+        else:
+            _assert_same(first, out, "decode", rep)
+    mhc.check(ws)
+    # the ticket count is back to zero after every one-tile launch
+    head = ws[:16].cpu().numpy()
+    assert int(head[8:12].view(np.uint32)[0]) == 0
