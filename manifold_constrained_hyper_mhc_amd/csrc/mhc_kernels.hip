@@ -601,22 +601,24 @@ __device__ __forceinline__ void post_tile(TileRegs<TM / 16>& R, const float (*cf
 
 // Four workgroups per CU (<= 128 VGPRs, 4 x 39.5 KB of LDS) when the reduce
 // runs are short; long runs (hidden sizes above 7168) need more registers,
-// and so does a 16-token tile (a launch of a few hundred workgroups at most,
-// whose projection fragments are in registers with its stream).
-template <int MODE, int TM, int RUN>
-__global__ __launch_bounds__(256, RUN <= 8 && TM == 32 ? 4 : 2) void k_split(const SplitArgs a) {
+// and so does a launch by tickets (a short, latency-bound call, whose
+// projection fragments are in registers with its stream).
+// TK: a launch of one tile (at most 32 tokens, latency-bound), whose
+// workgroups take their jobs by ticket, in the order they start (see
+// below); its pre step recomputes x' (the workgroup that stored it runs at
+// the same time, so the read-back path would seldom apply), phase A then
+// neither waits for its x' stores nor announces them, and its projection
+// fragments are loaded with its stream.  (Launches of 2 to 4 tiles by
+// tickets, every phase A first, measured slower than the staged pipeline:
+// 17.7 vs 17.0 us at 64 tokens, 25.6 vs 19.5 us at 128.)
+template <int MODE, int TM, int RUN, bool TK>
+__global__ __launch_bounds__(256, RUN <= 8 && !TK ? 4 : 2) void k_split(const SplitArgs a) {
   constexpr bool FUSED = mode_fused(MODE);
   constexpr bool MX = mode_mx(MODE);
   constexpr bool YQ = mode_yq(MODE);
   constexpr int W = 4, NV = kPartVals, NP = TM / 16, RB = TM / 16, NQ = TM / 4;
   constexpr int NVU = FUSED ? NV : 25;
-  // 16-token tiles: a call of at most 16 tokens, one tile, latency-bound.
-  // Its workgroups take their jobs in the order they start (see below); its
-  // pre step recomputes x' (the workgroup that stored it runs at the same
-  // time, so the read-back path would seldom apply), phase A then neither
-  // waits for its x' stores nor announces them, and its projection
-  // fragments are loaded with its stream.
-  constexpr bool ONE = TM == 16;
+  constexpr bool ONE = TK;
   // partial words per token in the workspace: [tiles][S][TM][PW], dense, so
   // that every store instruction writes whole lines
   constexpr int PW = NVU;
@@ -1000,9 +1002,9 @@ __global__ __launch_bounds__(256, RUN <= 8 && TM == 32 ? 4 : 2) void k_split(con
   // In the fused modes that workgroup then recomputes the pre of the tokens
   // whose route combination cancels (every tile's pre steps have run, so the
   // list is complete).
-  // (One tile: the epoch advanced with the last ticket, and the pre step of
-  // split 0 recomputes the listed tokens as soon as its own rows are out:
-  // it has seen every token's q words, which follow their listing.)
+  // (By tickets: the epoch advanced with the last ticket, and the pre step
+  // of split 0 recomputes the listed tokens as soon as its own rows are
+  // out, having seen every token's q words, which follow their listing.)
   if constexpr (ONE) {
     if constexpr (FUSED) {
       if (tC >= 0 && split == 0) {
@@ -2392,21 +2394,22 @@ hipError_t launch_pack_phi_sum(const float* phi, const void* packed, int C, void
 template <int MODE>
 static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
   const int64_t stages = p.tiles + (mode_fused(MODE) ? p.d2 : p.d1);
-  // one 16-token tile: S phase-A jobs, min(S, 16) reduce jobs, S pre jobs
-  const int64_t nR = p.s < 16 ? p.s : 16;
-  const int64_t blocks = p.m == 16 ? p.s + nR + (mode_fused(MODE) ? p.s : 0) : stages * p.s;
+  // by tickets (one tile): S phase-A jobs, min(S, m) reduce jobs, S pre jobs
+  const bool tk = p.tiles == 1;
+  const int64_t nR = p.s < p.m ? p.s : p.m;
+  const int64_t blocks = tk ? p.s + nR + (mode_fused(MODE) ? p.s : 0) : stages * p.s;
   const dim3 grid((unsigned)blocks), block(256);
-  if ((p.m != 32 && p.m != 16) || p.cc != kCC || (p.m == 16 && p.tiles != 1)) return hipErrorInvalidConfiguration;
+  if ((p.m != 32 && p.m != 16) || p.cc != kCC || (p.m == 16 && !tk)) return hipErrorInvalidConfiguration;
+  const bool short_runs = plan_run_len(p) <= 8;
   if (p.m == 16) {
-    if (plan_run_len(p) <= 8) {
-      k_split<MODE, 16, 8><<<grid, block, 0, s>>>(a);
-    } else {
-      k_split<MODE, 16, kRunMax><<<grid, block, 0, s>>>(a);
-    }
-  } else if (plan_run_len(p) <= 8) {
-    k_split<MODE, 32, 8><<<grid, block, 0, s>>>(a);
+    if (short_runs) k_split<MODE, 16, 8, true><<<grid, block, 0, s>>>(a);
+    else k_split<MODE, 16, kRunMax, true><<<grid, block, 0, s>>>(a);
+  } else if (tk) {
+    if (short_runs) k_split<MODE, 32, 8, true><<<grid, block, 0, s>>>(a);
+    else k_split<MODE, 32, kRunMax, true><<<grid, block, 0, s>>>(a);
   } else {
-    k_split<MODE, 32, kRunMax><<<grid, block, 0, s>>>(a);
+    if (short_runs) k_split<MODE, 32, 8, false><<<grid, block, 0, s>>>(a);
+    else k_split<MODE, 32, kRunMax, false><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -47,7 +47,7 @@ def fix_count(ws):
 @pytest.mark.parametrize("mx", [False, True])
 @pytest.mark.parametrize("T,C,sched", [(37, 3072, "staged"), (300, 7168, "persistent"), (300, 7168, "staged"),
                                        (500, 4096, "persistent"), (1000, 2048, "persistent"),
-                                       (12, 7168, "staged"), (16, 1024, "staged")])
+                                       (12, 7168, "staged"), (16, 1024, "staged"), (30, 4096, "staged")])
 def test_fused_on_cancelling_routes(T, C, sched, mx, monkeypatch):
     monkeypatch.setenv("MHC_SCHEDULE", sched)
     assert mhc.schedule(T, C) == sched

@@ -69,7 +69,7 @@ def to_dev(inp):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
 
-SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048)]
+SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048), (25, 7168)]
 
 # shapes the persistent schedule takes (16 <= C/128 <= 64, enough tiles),
 # with a ragged last tile: 56, 32, 24 and 16 splits, and the fewest tiles
@@ -296,12 +296,14 @@ def test_rings_and_chunked_launches(T, C, schedule):
     check_fused(inp, out, mx=True)
 
 
-def test_chunked_staged_launches():
+@pytest.mark.parametrize("T,seam", [(4000, 3680), (3685, 3680)])
+def test_chunked_staged_launches(T, seam):
     # C = 16384 (128 splits) always takes the staged kernel, whose launches
     # hold at most 128 MiB of partial words: 115 tiles here, so T = 4000
-    # (125 tiles) runs as two launches, the second offset by 3680 tokens.
+    # (125 tiles) runs as two launches, the second offset by 3680 tokens,
+    # and T = 3685 ends with a launch of one 5-token tile (taken by tickets).
     # Sampled rows on both sides of the seam, against the oracle.
-    T, C = 4000, 16384
+    C = 16384
     assert mhc.schedule(T, C) == "staged"
     d = make_inputs(T, C, seed=33, rows="outliers", device=DEV)
     d["coeffs"] = oracle_coeffs_in(d["x"][:256], d["phi"], d["bias"]).to(DEV)
@@ -309,7 +311,7 @@ def test_chunked_staged_launches():
     cf = mhc.coeffs(d["x"], d["phi"], d["bias"])
     out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=True)
     torch.cuda.synchronize()
-    rows = sample_rows(T, extra=(3678, 3679, 3680, 3681, 3999))
+    rows = sample_rows(T, extra=(seam - 2, seam - 1, seam, seam + 1, T - 1))
     idx = torch.from_numpy(rows).to(DEV)
     inp = host_rows(d, rows)
     assert_coeffs_close(f64(cf.index_select(0, idx)), O.coeffs(f64(inp["x"]), f64(inp["phi"]), f64(inp["bias"]), **kw()))
