@@ -171,13 +171,14 @@ int mhc_last_hip_error(void);
  * must check the word before it uses that call's outputs.
  *
  * Schedule.  When 16 <= C/128 <= 64 and T spans enough 32-token tiles
- * (two per stream workgroup), these two calls run a persistent kernel: one
+ * (four per stream workgroup), these two calls run a persistent kernel: one
  * 512-thread workgroup per compute unit, every one of which must be
  * resident at once; work that occupies compute units meanwhile delays it,
  * and if that outlasts its bounded waits they expire and set the error word.
  * Otherwise, or with the environment variable MHC_SCHEDULE=staged (read on
  * every call), a staged kernel runs whose workgroups wait only on work of
- * lower-numbered workgroups.  Results of the two schedules are equal to
+ * workgroups that started before them (lower-numbered ones, or in a launch
+ * of one tile, lower tickets taken in the order of starting).  Results of the two schedules are equal to
  * within the stated tolerances; x_out is bitwise equal, and either
  * schedule's MXFP8 codes are the exact encoding of its own bf16 h.
  * ------------------------------------------------------------------------- */

@@ -104,7 +104,7 @@ bool plan_fits(const mhc::Plan& p) {
 // Persistent kernel: one 512-thread workgroup per CU, S*L stream workgroups
 // plus 32 or 64 reduce workgroups, all resident.  It runs when 16 <= S <= 64
 // (8 <= S for the coefficients of a broadcast stream) and each stream
-// workgroup gets at least two tiles, unless the environment
+// workgroup gets at least four tiles (two: broadcast coefficients), unless the environment
 // variable MHC_SCHEDULE is "staged" (read on every call); otherwise the
 // staged kernel runs.
 bool persistent_allowed() {
@@ -149,7 +149,13 @@ void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   int lanes = (cus - (pseudo ? reds : 32)) / p.s;
   // the workspace's rings hold kRingK tiles per stream workgroup lane
   if (lanes * p.s > mhc::kMaxLaneSplits) lanes = mhc::kMaxLaneSplits / p.s;
-  if (lanes < 1 || p.tiles < 2 * (int64_t)lanes) return;
+  // Enough tiles for the persistent kernel's fixed cost: four per stream
+  // workgroup (two for the broadcast coefficients).  Below that the staged
+  // kernel measured faster: at C = 7168 (4 lanes) up to 12 tiles (T = 384:
+  // 33.0 vs 35.0 us fused), at C = 4096 (7 lanes) up to 24 (T = 768: 33.2 vs
+  // 37.8 us), at C = 2048 (14 lanes) up to 64 (T = 2048: 39.4 vs 41.0 us);
+  // above, the persistent one (T = 512 at C = 7168: 38.0 vs 39.8 us).
+  if (lanes < 1 || p.tiles < (pseudo ? 2 : 4) * (int64_t)lanes) return;
   lanes = std::min(lanes, (cus - reds) / p.s);
   if (lanes < 1 || p.s * lanes + reds > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;

@@ -45,8 +45,8 @@ def fix_count(ws):
 
 
 @pytest.mark.parametrize("mx", [False, True])
-@pytest.mark.parametrize("T,C,sched", [(37, 3072, "staged"), (300, 7168, "persistent"), (300, 7168, "staged"),
-                                       (500, 4096, "persistent"), (1000, 2048, "persistent"),
+@pytest.mark.parametrize("T,C,sched", [(37, 3072, "staged"), (520, 7168, "persistent"), (300, 7168, "staged"),
+                                       (900, 4096, "persistent"), (1800, 2048, "persistent"),
                                        (12, 7168, "staged"), (16, 1024, "staged"), (30, 4096, "staged")])
 def test_fused_on_cancelling_routes(T, C, sched, mx, monkeypatch):
     monkeypatch.setenv("MHC_SCHEDULE", sched)
@@ -96,7 +96,7 @@ def test_no_recomputation_on_the_benchmark_distributions():
     # independent N(0,1) routes with 1% outlier rows: nothing is listed, so the
     # recomputation kernel only reads the count
     from manifold_constrained_hyper_mhc_amd.synthetic import make_inputs
-    T, C = 300, 7168
+    T, C = 520, 7168
     inp = make_inputs(T, C, seed=2, rows="outliers", device=DEV)
     cf = torch.zeros((T, 24), dtype=torch.float32, device=DEV)
     cf[:, 0:8] = 0.5

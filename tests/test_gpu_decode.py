@@ -32,7 +32,7 @@ def _gpu_ready():
 
 @pytest.mark.parametrize("mx", [False, True])
 @pytest.mark.parametrize("T,C,sched", [(6, 7168, "staged"), (16, 4096, "staged"), (64, 7168, "staged"),
-                                       (300, 7168, "persistent")])
+                                       (520, 7168, "persistent")])
 def test_deferred_sinkhorn_on_a_side_stream(T, C, sched, mx, monkeypatch):
     monkeypatch.setenv("MHC_SCHEDULE", sched)
     assert mhc.schedule(T, C) == sched

@@ -24,7 +24,7 @@ DEV = "cuda:0"
 
 # (T, C, schedule, MXFP8): a decode step (one 16-token tile), prefill-shaped
 # launches of both schedules with ragged last tiles, and the MXFP8 epilogue
-CASES = [(6, 7168, "staged", False), (300, 7168, "persistent", False), (500, 4096, "persistent", True),
+CASES = [(6, 7168, "staged", False), (520, 7168, "persistent", False), (900, 4096, "persistent", True),
          (300, 7168, "staged", True)]
 
 
@@ -83,7 +83,7 @@ def test_graph_replays_match_eager(T, C, sched, mx, monkeypatch):
 def test_graph_replays_int8_fused_and_broadcast_pre():
     # the int8-input fused pass and the broadcast first-layer pre, captured
     # together, replay bit for bit
-    T, C = 300, 7168
+    T, C = 520, 7168
     d = make_inputs(T, C, seed=23, rows="outliers", device=DEV)
     yq = make_int8_y(T, C, seed=4, device=DEV)
     ws = mhc.workspace(T, C, DEV, fresh=True)

@@ -40,8 +40,8 @@ def coeffs_in(T):
     return cf
 
 
-@pytest.mark.parametrize("T,C,sched", [(6, 7168, "staged"), (37, 3072, "staged"), (300, 7168, "persistent"),
-                                       (300, 7168, "staged"), (500, 4096, "persistent"), (45, 16384, "staged")])
+@pytest.mark.parametrize("T,C,sched", [(6, 7168, "staged"), (37, 3072, "staged"), (520, 7168, "persistent"),
+                                       (300, 7168, "staged"), (900, 4096, "persistent"), (45, 16384, "staged")])
 def test_mfma_scale_bytes(T, C, sched, monkeypatch):
     monkeypatch.setenv("MHC_SCHEDULE", sched)
     assert mhc.schedule(T, C) == sched

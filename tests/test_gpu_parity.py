@@ -73,14 +73,14 @@ SMALL = [(16, 1024), (37, 3072), (1, 1024), (6, 7168), (70, 2048), (25, 7168)]
 
 # shapes the persistent schedule takes (16 <= C/128 <= 64, enough tiles),
 # with a ragged last tile: 56, 32, 24 and 16 splits, and the fewest tiles
-# it takes at 56 and 16 splits (two per stream workgroup: 8 tiles with 4
-# stream lanes, 28 with 14)
-PERSISTENT = [(300, 7168), (500, 4096), (1000, 3072), (1000, 2048), (225, 7168), (865, 2048)]
+# it takes at 56 and 16 splits (four per stream workgroup: 16 tiles with 4
+# stream lanes, 56 with 14)
+PERSISTENT = [(520, 7168), (900, 4096), (1200, 3072), (1800, 2048), (481, 7168), (1761, 2048)]
 # the other hidden sizes each schedule accepts: S = 40 and 48 splits (5 and 4
 # stream workgroups per split), S = 64 (the persistent kernel's limit; the
 # staged kernel's long reduce runs), and C = 9216, 12288 and 16384 (staged
 # only, S = 72, 96 and 128)
-WIDE = [(400, 5120), (300, 6144), (300, 8192), (200, 9216), (200, 12288), (300, 16384)]
+WIDE = [(650, 5120), (500, 6144), (400, 8192), (200, 9216), (200, 12288), (300, 16384)]
 
 
 def test_schedule_choice(monkeypatch):
@@ -94,17 +94,17 @@ def test_schedule_choice(monkeypatch):
 
 
 def test_schedule_thresholds(monkeypatch):
-    """The persistent kernel needs two tiles per stream workgroup: on a
-    256-CU MI355X, 4 stream lanes at C = 7168 (8 tiles: T > 224) and 14 at
-    C = 2048 (28 tiles: T > 864); fewer than 16 splits (C = 1024) and more
+    """The persistent kernel takes four tiles per stream workgroup: on a
+    256-CU MI355X, 4 stream lanes at C = 7168 (16 tiles: T > 480) and 14 at
+    C = 2048 (56 tiles: T > 1760); fewer than 16 splits (C = 1024) and more
     than 64 (C = 9216) run the staged kernel."""
     monkeypatch.delenv("MHC_SCHEDULE", raising=False)
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the thresholds below are those of a 256-CU device")
-    assert mhc.schedule(225, 7168) == "persistent"
-    assert mhc.schedule(224, 7168) == "staged"
-    assert mhc.schedule(865, 2048) == "persistent"
-    assert mhc.schedule(864, 2048) == "staged"
+    assert mhc.schedule(481, 7168) == "persistent"
+    assert mhc.schedule(480, 7168) == "staged"
+    assert mhc.schedule(1761, 2048) == "persistent"
+    assert mhc.schedule(1760, 2048) == "staged"
     assert mhc.schedule(65536, 1024) == "staged"
     assert mhc.schedule(65536, 9216) == "staged"
     assert mhc.schedule(65536, 8192) == "persistent"
@@ -417,7 +417,7 @@ def test_identity_post_is_exact():
     check_fused(inp, out)
 
 
-@pytest.mark.parametrize("T,C", [(37, 3072), (300, 7168)])
+@pytest.mark.parametrize("T,C", [(37, 3072), (520, 7168)])
 def test_power_of_two_scale_invariance(T, C, schedule):
     # with both eps at 0, scaling the stream and the sublayer output by 2^k
     # scales every sum by a power of two exactly: the coefficients and h are
@@ -447,7 +447,7 @@ def test_power_of_two_scale_invariance(T, C, schedule):
 # ---------------------------------------------------------------------------
 # library behaviour
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("T,C,sched", [(37, 3072, "staged"), (300, 7168, "persistent")])
+@pytest.mark.parametrize("T,C,sched", [(37, 3072, "staged"), (520, 7168, "persistent")])
 def test_expired_wait_is_reported(T, C, sched, monkeypatch):
     # The error word is set from the host before the call, standing in for a
     # bounded wait that expired (every kernel still runs to its end: the
@@ -502,9 +502,9 @@ def test_recompute_flag_is_bitwise_identical(mx):
 
 
 def test_deterministic_and_workspace_reuse():
-    ws = mhc.workspace(300, 7168, DEV, fresh=True)
+    ws = mhc.workspace(520, 7168, DEV, fresh=True)
     runs = []
-    for T, C in [(40, 2048), (300, 7168), (7, 1024), (40, 2048)]:
+    for T, C in [(40, 2048), (520, 7168), (7, 1024), (40, 2048)]:
         inp = small_inputs(T, C, seed=T)
         d = to_dev(inp)
         out = mhc.post_pre_fused(d["x"], d["y"], d["coeffs"], d["phi_next"], d["bias_next"], d["gamma_next"], ws=ws)
@@ -684,7 +684,7 @@ def test_workspace_reuse_across_modes(schedule):
     # modes lay their partial words out differently ([TM][34] and [TM][25]),
     # so every call meets words of the other layout from an earlier launch;
     # the launch tags must keep them out of every sum
-    T, C = 300, 7168
+    T, C = 520, 7168
     inp = small_inputs(T, C, seed=13)
     d = to_dev(inp)
     ws = mhc.workspace(T, C, DEV, fresh=True)

@@ -120,9 +120,9 @@ def test_decode_repeated_bitwise(mx):
     cf = _coeffs_in(w.T, w.C, seed=12)
     mid = make_inputs(40, w.C, seed=13, device=DEV)
     cf_mid = _coeffs_in(40, w.C, seed=14)
-    big = make_inputs(300, w.C, seed=15, device=DEV)
-    cf_big = _coeffs_in(300, w.C, seed=16)
-    ws = mhc.workspace(300, w.C, DEV, fresh=True)
+    big = make_inputs(520, w.C, seed=15, device=DEV)
+    cf_big = _coeffs_in(520, w.C, seed=16)
+    ws = mhc.workspace(520, w.C, DEV, fresh=True)
     first = None
     for rep in range(REPS * 2):
         out = mhc.post_pre_fused(d["x"], d["y"], cf, d["phi_next"], d["bias_next"], d["gamma_next"], mxfp8=mx, ws=ws)

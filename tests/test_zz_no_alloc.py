@@ -43,7 +43,7 @@ def inputs(T, C, seed):
 def test_static_scratch_matches_workspace_call():
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     # the second call is smaller: it meets the first call's words in the scratch
-    for T, C, mx in [(300, 7168, True), (37, 3072, False)]:
+    for T, C, mx in [(520, 7168, True), (37, 3072, False)]:
         inp = inputs(T, C, seed=T)
         d = {k: v.to(DEV) for k, v in inp.items()}
         pk = mhc.pack_phi(d["phi_next"])
