@@ -328,13 +328,22 @@ __device__ __forceinline__ float finalize_wave(const float* sums, float bias_lan
 // weight.  The Sinkhorn row and column sums are the same row-local DPP
 // moves, so the four rows run side by side.  sums: this lane's token.
 // publish(q, pre, cancels) of the fused modes runs before the Sinkhorn iterations.
-template <bool FUSED, class Publish>
-__device__ __forceinline__ void finalize_rows(const float* sums, const float* bias, int C, const Scalars& sc,
+// bias: the bias vector, or this lane's two entries of it loaded beforehand
+// (LaneBias), so that the finalisation waits for no memory load.
+struct LaneBias {
+  float p, r;  // bias[lane % 8], bias[8 + lane % 16]
+};
+__device__ __forceinline__ float bias_pw(const float* b, int kp) { return b[kp]; }
+__device__ __forceinline__ float bias_pw(const LaneBias& b, int) { return b.p; }
+__device__ __forceinline__ float bias_res(const float* b, int k) { return b[8 + k]; }
+__device__ __forceinline__ float bias_res(const LaneBias& b, int) { return b.r; }
+template <bool FUSED, class Bias, class Publish>
+__device__ __forceinline__ void finalize_rows(const float* sums, const Bias& bias, int C, const Scalars& sc,
                                               int lane, float& res, float& pp, Publish&& publish) {
   const int k = lane & 15, kp = lane & 7;
   const float ss = FUSED ? ((sums[24] + sums[25]) + sums[26]) + sums[27] : sums[24];
   const float r = 1.0f / sqrtf(ss / (float)(kRoutes * C) + sc.hc_norm_eps);
-  const float lp = r * sums[kp] + bias[kp];
+  const float lp = r * sums[kp] + bias_pw(bias, kp);
   const float sg = 1.0f / (1.0f + expf(-lp));
   pp = kp >= 4 ? sc.hc_post_scale * sg : sg;
   if constexpr (FUSED) {
@@ -345,7 +354,7 @@ __device__ __forceinline__ void finalize_rows(const float* sums, const float* bi
     const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
     publish(q, p, cancels);
   }
-  const float l = r * sums[8 + k] + bias[8 + k];
+  const float l = r * sums[8 + k] + bias_res(bias, k);
   float v = expf(l);
   const float eps = sc.sinkhorn_eps;
   for (int it = 0; it < sc.sinkhorn_iters; ++it) {
@@ -1386,6 +1395,9 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         if (v >= 0 && v < 8 * NV) fin[v] = act ? acc : 0.0f;
       };
       if (j < nunits && wv >= 2) gather(j, finw);
+      // the finalising waves' bias entries, loaded once (so that no round's
+      // finalisation waits for a memory load)
+      const LaneBias lb = wv < 2 ? LaneBias{a.bias[lane & 7], a.bias[8 + (lane & 15)]} : LaneBias{0.0f, 0.0f};
       __syncthreads();
       int k = 0;
       for (int u = j; u < nunits; u += nred, ++k) {
@@ -1400,7 +1412,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           float res, pp;
           // every row of the tile is published ([R][TM][4] words): the
           // stream workgroups poll whole row blocks, padding rows included
-          finalize_rows<FUSED>(fin + ml * NV, a.bias, C, a.sc, lane, res, pp,
+          finalize_rows<FUSED>(fin + ml * NV, lb, C, a.sc, lane, res, pp,
                                [&](const float* q, const float* pw, bool cancels) __attribute__((always_inline)) {
                                  // a cancelling token: listed (and its pre weights written through)
                                  // before its q words, whose sign bit on q0 tells the pre step to
