@@ -546,14 +546,10 @@ def run(args, pool, nproc) -> int:
     coeffs_in = mhc.coeffs(inp["x"], inp["phi"], inp["bias"], params)
     ws = mhc.workspace(T, C, dev)
     packed = torch.empty(int(mhc.lib().mhc_phi_packed_bytes(C)), dtype=torch.uint8, device=dev)
-    outs = {"x_out": torch.empty((T, 4, C), dtype=torch.bfloat16, device=dev),
-            "coeffs_next": torch.empty((T, 24), dtype=torch.float32, device=dev)}
+    # the outputs as the library allocates them (x_out and h placed off the
+    # alignment of x and y modulo 1 KiB: binding.PLACE_OFFSET)
     with_h = not mx
-    if with_h:
-        outs["h"] = torch.empty((T, C), dtype=torch.bfloat16, device=dev)
-    if mx:
-        outs["h_fp8"] = torch.empty((T, C), dtype=torch.uint8, device=dev)
-        outs["h_scale"] = torch.empty((T, C // 32), dtype=torch.uint8, device=dev)
+    outs = mhc.fused_outputs(inp["x"], inp["y"], mxfp8=mx, want_h=with_h)
     stream = torch.cuda.current_stream(dev)
 
     # the two calls of a step, checked and marshalled once (mhc.Prepared)

@@ -281,3 +281,17 @@ def test_static_scratch_plan_fits_every_shape():
                 far(0), far(1), far(2), far(3), far(4), far(5), T, C, ctypes.byref(p), 1,
                 far(6), far(7), far(8), far(9), far(10), far(11, 1), None)
             assert rc == ALIGN, (T, C, rc)
+
+
+def test_output_placement():
+    # the outputs the binding allocates start PLACE_OFFSET bytes past their
+    # reference modulo 1 KiB, whatever the reference's own alignment
+    from manifold_constrained_hyper_mhc_amd import binding
+    assert binding.PLACE_OFFSET % 256 == 0 and 0 < binding.PLACE_OFFSET < 1024
+    big = torch.empty(64 * 4 * 1024 + 2048, dtype=torch.bfloat16)
+    for skip in (0, 128, 256, 384):
+        ref = big[skip: skip + 64 * 4 * 1024].view(64, 4, 1024)
+        for shape, dtype in (((64, 4, 1024), torch.bfloat16), ((64, 1024), torch.bfloat16)):
+            t = binding._placed_empty(shape, dtype, torch.device("cpu"), ref)
+            assert tuple(t.shape) == shape and t.is_contiguous()
+            assert (t.data_ptr() - ref.data_ptr()) % 1024 == binding.PLACE_OFFSET
