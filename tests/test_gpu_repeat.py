@@ -142,3 +142,19 @@ def test_decode_repeated_bitwise(mx):
     # the ticket count is back to zero after every one-tile launch
     head = ws[:16].cpu().numpy()
     assert int(head[8:12].view(np.uint32)[0]) == 0
+
+
+def test_output_placement_does_not_change_results():
+    # the binding places x_out and h off the alignment of x and y (a matter of
+    # speed only): outputs in plain torch.empty buffers are bitwise the same
+    w = WORKLOADS["prefill"]
+    d = make_inputs(w.T, w.C, seed=17, rows=w.rows, device=DEV)
+    cf = _coeffs_in(w.T, w.C, seed=18)
+    placed = mhc.post_pre_fused(d["x"], d["y"], cf, d["phi_next"], d["bias_next"], d["gamma_next"])
+    plain = {"x_out": torch.empty_like(d["x"]), "h": torch.empty_like(d["y"]),
+             "coeffs_next": torch.empty((w.T, 24), dtype=torch.float32, device=DEV)}
+    aligned = mhc.post_pre_fused(d["x"], d["y"], cf, d["phi_next"], d["bias_next"], d["gamma_next"], outs=plain)
+    torch.cuda.synchronize()
+    assert (placed["x_out"].data_ptr() - d["x"].data_ptr()) % 1024 == mhc.binding.PLACE_OFFSET
+    for k in ("x_out", "h", "coeffs_next"):
+        assert torch.equal(placed[k], aligned[k]), k
