@@ -291,9 +291,9 @@ int mhc_post_int8(const uint16_t* x, const int8_t* y_q, const float* y_scale, co
  * B = (sum_i |pre_i| sqrt(G_ii))^2), that difference of large fp32 terms is
  * not accurate enough; such tokens are listed in the workspace and their h
  * (and MXFP8 blocks) is recomputed after the pass, in binary64, from x'
- * recomputed from x, y and coeffs (the inputs): by the kernel's last
- * workgroup (staged launches, and persistent ones with MXFP8), or by a
- * second kernel always enqueued after a persistent launch without MXFP8.
+ * recomputed from x, y and coeffs (the inputs), within the same launch: by
+ * its last workgroup (staged launches, and persistent ones with MXFP8), or
+ * by its last reduce workgroup (persistent launches without MXFP8).
  * An exactly cancelling combination (g = 0) gives h = 0.
  *
  * Placement (performance only).  A workgroup reads x and writes x_out at the

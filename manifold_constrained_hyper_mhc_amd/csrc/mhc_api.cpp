@@ -283,18 +283,13 @@ mhc::SplitArgs split_args(const mhc::Plan& plan, void* ws, int64_t T, int64_t C,
   return a;
 }
 
-// One coefficients or fused call: a single persistent launch (a fused one
-// without the MXFP8 epilogue followed by the recomputation of the tokens it
-// listed; with it, the kernel's last workgroup recomputes them), or staged
+// One coefficients or fused call: a single persistent launch, or staged
 // launches of at most run.chunk_tiles tiles each, over consecutive tokens,
-// every pointer offset to the chunk's first token (their last workgroups
-// recompute the listed tokens themselves).
+// every pointer offset to the chunk's first token.  Each fused launch
+// recomputes the tokens it listed itself.
 int run_split(const mhc::Plan& run, int mode, const mhc::SplitArgs& a, hipStream_t s) {
   int rc;
-  if (run.lanes > 0) {
-    if ((rc = hip_status(mhc::launch_split(run, mode, a, s)))) return rc;
-    return mhc::mode_fused(mode) ? hip_status(mhc::launch_fix_flagged(a, mode, s)) : MHC_OK;
-  }
+  if (run.lanes > 0) return hip_status(mhc::launch_split(run, mode, a, s));
   const int64_t chunk = run.chunk_tiles * run.m;
   for (int64_t t0 = 0; t0 < a.T; t0 += chunk) {
     const int64_t n = a.T - t0 < chunk ? a.T - t0 : chunk;

@@ -63,7 +63,7 @@ constexpr int kCoeffsWords = 25;        // per token, coefficients only: project
 // the launch epoch (the low and high halves of one 64-bit word), the tagged
 // count of tokens whose fused pre needs the direct recomputation, then one
 // leave counter per possible tile (2^20 tokens / 32 tokens per tile).
-constexpr size_t kWsErr = 0, kWsTilesDone = 4, kWsTicket = 8, kWsEpoch = 12, kWsFixWord = 16;
+constexpr size_t kWsErr = 0, kWsTilesDone = 4, kWsTicket = 8, kWsEpoch = 12, kWsFixWord = 16, kWsRedDone = 24;
 constexpr size_t kWsDep = 256;
 constexpr int64_t kMaxTiles = (int64_t)(1 << 20) / 32;
 constexpr size_t kWsHeaderBytes = kWsDep + (size_t)kMaxTiles * 4;
@@ -161,6 +161,5 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_sinkhorn(float* coeffs, int64_t T, float eps, int iters, hipStream_t s);
 // After a persistent fused launch: the direct pre of the tokens it listed
 // (the count is read on the device, so it is always launched).
-hipError_t launch_fix_flagged(const SplitArgs& a, int mode, hipStream_t s);
 
 }  // namespace mhc

@@ -453,12 +453,11 @@ __device__ __forceinline__ void xprime8(const SplitArgs& a, int64_t t, int c, co
 }
 
 // The direct pre of the tokens a fused launch listed because their route
-// combination cancels (gram_rms_factor): run by the last workgroup of the
-// launch (NT threads: 256 in a staged launch, 512 in a persistent one with
-// the MXFP8 epilogue), once every other workgroup has left, or by
-// k_fix_flagged after any other persistent launch; either way the list and
-// the listed tokens' pre weights (written through to memory before the
-// tokens' q words) are complete.  Per token: x' recomputed from x, y and the post
+// combination cancels (gram_rms_factor): run once the list is complete (and
+// the listed tokens' pre weights, written through to memory before the
+// tokens' q words): by the last workgroup of a staged launch (NT = 256), and
+// of a persistent launch with the MXFP8 epilogue (NT = 512), or by the last
+// reduce workgroup of any other persistent launch (NT = 512).  Per token: x' recomputed from x, y and the post
 // coefficients (inputs only, so nothing another XCD wrote is read), g in
 // binary64, sum_c g^2 in binary64, then h and its MXFP8 blocks written; the
 // pre step left these tokens' rows unwritten (the sign of q0).  A launch
@@ -1438,6 +1437,32 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
         __syncthreads();  // the next unit's sums are in; this unit's are read
       }
+      // The last reduce workgroup to finish recomputes the listed tokens
+      // (bf16 modes; see the leave section for the MXFP8 ones): every token
+      // has been finalised, so the list is complete, and the stream
+      // workgroups, still running their last pre steps, leave the listed
+      // tokens' rows alone.  The arguments are read through the
+      // kernel-argument segment's address, made opaque (as in the leave
+      // section), so that the main loop's registers do not change.
+      if constexpr (!MX) {
+        if (tid == 0) {
+          uint32_t* rd = reinterpret_cast<uint32_t*>(a.fix_word + 1);
+          static_assert(kWsRedDone == kWsFixWord + 8, "reduce-done counter after the fix word");
+          uint32_t last = 0;
+          const uint32_t done = __hip_atomic_fetch_add(rd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (done == (uint32_t)nred - 1u) {
+            __hip_atomic_store(rd, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = 1;
+          }
+          s_last = last;
+        }
+        __syncthreads();
+        if (s_last != 0) {
+          const SplitArgs* ap = (const SplitArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+          asm volatile("" : "+s"(ap));
+          fix_flagged<YQ, false, kPersistThreads>(*ap, tag, reinterpret_cast<double*>(&red[0][0][0]));
+        }
+      }
     }
   } else {
     // ------------------------- stream workgroup -------------------------
@@ -2161,12 +2186,10 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   }
 
   // ---- leave: the last workgroup to finish advances the launch epoch ----
-  // The listed tokens of a fused launch are recomputed after every reduce
-  // workgroup has left (the list is then complete): in the MXFP8 modes by
-  // this workgroup, here; in the others by k_fix_flagged, launched after
-  // this kernel, which measured faster for them (the tail here changes the
-  // main loop's register allocation: MXFP8 prefill 161 -> 158 us, bf16
-  // prefill 268 -> 273 us).
+  // In the MXFP8 modes it then recomputes the listed tokens (every reduce
+  // workgroup has left, so the list is complete); the bf16 modes do that in
+  // their last reduce workgroup (the tail here changed the main loop's
+  // register allocation of those modes: prefill 268 -> 273 us).
   __syncthreads();
   if (tid == 0) {
     uint32_t last = 0;
@@ -2192,17 +2215,6 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       fix_flagged<YQ, MX, kPersistThreads>(*ap, tag, reinterpret_cast<double*>(&red[0][0][0]));
     }
   }
-}
-
-// The direct pre of the tokens a persistent fused launch without the MXFP8
-// epilogue listed (see fix_flagged), launched after it on the same stream;
-// its tag is the epoch the launch left.  Workgroup b takes the listed
-// tokens b, b + grid, ...
-template <bool YQ, bool MX>
-__global__ __launch_bounds__(256) void k_fix_flagged(const SplitArgs a) {
-  __shared__ double red[4];
-  const uint32_t tag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  fix_flagged<YQ, MX, 256>(a, tag, red, blockIdx.x, gridDim.x);
 }
 
 // ===========================================================================
@@ -2498,19 +2510,6 @@ hipError_t launch_pre(const uint16_t* x, int64_t xts, int64_t xrs, const float* 
   return hipGetLastError();
 }
 
-hipError_t launch_fix_flagged(const SplitArgs& a, int mode, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.T < 32 ? a.T : 32);
-  if (grid == 0) return hipSuccess;
-  const dim3 g(grid), b(256);
-  switch (mode) {
-    case kModeFused: k_fix_flagged<false, false><<<g, b, 0, s>>>(a); break;
-    case kModeFused | kModeYInt8: k_fix_flagged<true, false><<<g, b, 0, s>>>(a); break;
-    case kModeFusedMx:
-    case kModeFusedMx | kModeYInt8: return hipSuccess;  // the kernel's last workgroup did it
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_sinkhorn(float* cf, int64_t T, float eps, int iters, hipStream_t s) {
   const int64_t blocks = (T * 16 + 255) / 256;
