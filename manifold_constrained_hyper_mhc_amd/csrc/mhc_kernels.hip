@@ -1098,7 +1098,10 @@ struct IntC {
 };
 constexpr int kPersistThreads = 512;
 constexpr int kPersistTM = 32;
-constexpr int kPersistDepth = 6;  // iterations between the post and the pre step of a tile
+// Iterations between the post and the pre step of a tile: 7 (the x' of 7
+// tiles held in registers, 251-256 VGPRs with no spill at two waves per
+// SIMD), or 6 with the MXFP8 epilogue, which measured faster there.
+constexpr int persist_depth(int mode) { return mode_mx(mode) ? 6 : 7; }
 constexpr uint32_t kPersistSpinLimit = 1u << 18;
 constexpr int kPersistMaxS = 64;  // splits per row the reduce threads can gather
 constexpr int kCoeffsAhead = 3;   // coefficients-only pass: tiles of x held in registers ahead
@@ -1185,7 +1188,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   constexpr bool FUSED = mode_fused(MODE);
   constexpr bool YQ = mode_yq(MODE);
   constexpr bool MX = mode_mx(MODE);
-  constexpr int TM = kPersistTM, NV = kPartVals, D = kPersistDepth;
+  constexpr int TM = kPersistTM, NV = kPartVals, D = persist_depth(MODE);
+  static_assert(kRingK >= D + 1, "a ring slot is reused only after its tile was gathered");
   // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
   // [2][row block][token][route][16 chunks] x 16 B (chunk c of token t at
   // position c ^ (t % 16), so that the 16 tokens a wave reads at once hit
