@@ -391,8 +391,9 @@ def time_pre_broadcast(mhc, inp, packed, params, stream, args):
     [T, C]: coefficients and pre of x0 standing for all 4 routes.  HIP events
     around each call.  Algorithmic bytes 4C + 112 per token (x0 read once,
     h written, the coefficients written and their pre read back) + the
-    projection, bias and gamma once; the library reads x0 twice (the
-    coefficients kernel, then the pre kernel), so its traffic is 6C + 112."""
+    projection, bias and gamma once.  Where the persistent schedule runs
+    (prefill sizes) the library reads x0 once, in one pass; its two-pass
+    path (coefficients, then the pre kernel) reads it twice, 6C + 112."""
     import torch
 
     x0 = inp["x"][:, 0, :].contiguous()
@@ -422,7 +423,8 @@ def time_pre_broadcast(mhc, inp, packed, params, stream, args):
             "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "two_pass_bytes": two_pass, "two_pass_frac_of_peak": two_pass / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "note": "mhc_pre_broadcast_prepacked on a [T, C] first-layer input (coefficients + pre); "
-                    "algorithmic bytes read x0 once, the two kernels read it twice"}
+                    "algorithmic bytes read x0 once, as the one-pass schedule does (the two-pass path reads "
+                    "it twice: two_pass_*)"}
 
 
 def time_post_int8(mhc, inp, coeffs_in, stream, args):

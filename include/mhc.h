@@ -236,8 +236,18 @@ int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t 
  * token) instead of a [T][4][C] copy.  Writes coeffs [T][24] (pre, post,
  * res of this layer) and h [T][C] bf16.  Uses the workspace (see above);
  * the same bounds, alignment and aliasing rules as mhc_coeffs and mhc_pre.
- * Results are bitwise those of mhc_coeffs and mhc_pre on the explicit
- * [T][4][C] copy.
+ * From C = 3072 (or T <= 16 at C = 2048) the coefficients are computed on
+ * pseudo-routes: a split takes 512 consecutive channels of x0 against the
+ * projection summed over the routes and rounded to binary32, so they are
+ * not bitwise those of mhc_coeffs on the explicit [T][4][C] copy; both
+ * meet the same bounds against the plain definition.  Where the persistent
+ * schedule runs (C / 512 splits, at least four 32-token tiles per stream
+ * workgroup, MHC_SCHEDULE not "staged"), one launch computes both, each
+ * workgroup holding its x0 slices in registers until their coefficients
+ * are published (x0 is read once): h = bf16_rne((q * x0[c]) * gamma[c])
+ * with psum = ((pre0 + pre1) + pre2) + pre3 and q = psum / sqrt(psum^2 *
+ * sum_c x0^2 / C + rmsnorm_eps), all binary32.  Otherwise a pre launch
+ * (mhc_pre's arithmetic on g = psum * x0) follows the coefficients.
  * ------------------------------------------------------------------------- */
 int mhc_pre_broadcast(const uint16_t* x0, int64_t T, int64_t C, const float* phi, const float* bias,
                       const float* gamma, const mhc_params* p, float* coeffs, uint16_t* h, void* workspace,

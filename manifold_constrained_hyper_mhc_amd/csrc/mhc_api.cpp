@@ -125,8 +125,9 @@ int device_cus() {
 }
 
 // Which call a persistent launch serves: the fused pass, the coefficients
-// of a 4-route stream, or those of a broadcast stream on pseudo-routes.
-enum class Use { kFused, kCoeffs, kCoeffsPseudo };
+// of a 4-route stream, those of a broadcast stream on pseudo-routes, or
+// the one-pass coefficients and pre of a broadcast stream on pseudo-routes.
+enum class Use { kFused, kCoeffs, kCoeffsPseudo, kBcastFused };
 
 // The persistent kernel takes 16 to 64 splits per row (8 to 64 for the
 // coefficients of a broadcast stream on pseudo-routes); the fused pass and
@@ -140,7 +141,7 @@ enum class Use { kFused, kCoeffs, kCoeffsPseudo };
 void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   p.lanes = 0;
   if (!persistent_allowed()) return;
-  const bool pseudo = use == Use::kCoeffsPseudo;
+  const bool pseudo = use == Use::kCoeffsPseudo || use == Use::kBcastFused;
   if (p.m != 32 || p.s < (pseudo ? 8 : 16) || p.s > 64) return;
   const int cus = device_cus();
   const int reds = p.s <= 16 && use != Use::kCoeffs ? 64 : 32;
@@ -155,7 +156,7 @@ void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   // 33.0 vs 35.0 us fused), at C = 4096 (7 lanes) up to 24 (T = 768: 33.2 vs
   // 37.8 us), at C = 2048 (14 lanes) up to 64 (T = 2048: 39.4 vs 41.0 us);
   // above, the persistent one (T = 512 at C = 7168: 38.0 vs 39.8 us).
-  if (lanes < 1 || p.tiles < (pseudo ? 2 : 4) * (int64_t)lanes) return;
+  if (lanes < 1 || p.tiles < (use == Use::kCoeffsPseudo ? 2 : 4) * (int64_t)lanes) return;
   lanes = std::min(lanes, (cus - reds) / p.s);
   if (lanes < 1 || p.s * lanes + reds > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;
@@ -390,7 +391,11 @@ int coeffs_impl(const uint16_t* x, int64_t T, int64_t C, const float* phi, const
   return run_split(run, mhc::kModeCoeffs, a, s);
 }
 
-// Coefficients, then pre, of a [T][C] stream broadcast to the 4 routes.
+// Coefficients, then pre, of a [T][C] stream broadcast to the 4 routes:
+// where the persistent schedule runs, one pass on pseudo-routes
+// (kModeBcast: each stream workgroup keeps its x0 slices in registers until
+// their q words arrive, so x0 is read once); otherwise the coefficients
+// call, then a pre launch that reads x0 again.
 int pre_broadcast_impl(const uint16_t* x0, int64_t T, int64_t C, const float* phi, const void* phi_packed,
                        const float* bias, const float* gamma, const mhc_params* p, float* coeffs, uint16_t* h,
                        void* ws, size_t ws_bytes, void* stream) {
@@ -403,6 +408,35 @@ int pre_broadcast_impl(const uint16_t* x0, int64_t T, int64_t C, const float* ph
   const Span out[] = {{coeffs, (size_t)T * 24 * 4}, {h, (size_t)T * C * 2}};
   if ((rc = check_tensors(in, 4, out, 2))) return rc;
   if (ws != nullptr && overlaps(Span{ws, workspace_need(T, C)}, out[1])) return MHC_ERR_ALIAS;
+  const mhc::Plan pb = mhc::make_plan(T, C / 4);
+  if (bcast_pseudo(pb)) {
+    mhc::Plan run = pb;
+    choose_kernel(run, Use::kBcastFused);
+    if (run.lanes > 0) {
+      if ((rc = check_workspace(ws, ws_bytes, pb))) return rc;
+      const Span wsp{ws, pb.total};
+      for (const Span& o : out)
+        if (overlaps(wsp, o)) return MHC_ERR_ALIAS;
+      for (const Span& i : in)
+        if (overlaps(wsp, i)) return MHC_ERR_ALIAS;
+      hipStream_t s = static_cast<hipStream_t>(stream);
+      void* dst = static_cast<char*>(ws) + pb.off_phi;
+      if ((rc = hip_status(mhc::launch_pack_phi_sum(phi, phi_packed, (int)C, dst, s)))) return rc;
+      mhc::SplitArgs a = split_args(run, ws, T, C, p);
+      a.x = x0;
+      a.xts = C;
+      a.xrs = 128;
+      a.cs = 512;
+      a.prs = 128;
+      a.rms_c = (int)(C / 4);
+      a.phi_packed = static_cast<const uint32_t*>(dst);
+      a.bias = bias;
+      a.gamma = gamma;
+      a.coeffs_out = coeffs;
+      a.h = h;
+      return hip_status(mhc::launch_split(run, mhc::kModeFused | mhc::kModeBcast, a, s));
+    }
+  }
   if ((rc = coeffs_impl(x0, T, C, phi, phi_packed, bias, p, coeffs, ws, ws_bytes, stream, true))) return rc;
   return hip_status(
       mhc::launch_pre(x0, C, 0, coeffs, gamma, T, (int)C, p->rmsnorm_eps, h, static_cast<hipStream_t>(stream)));

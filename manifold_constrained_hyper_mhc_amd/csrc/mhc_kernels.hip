@@ -328,6 +328,10 @@ __device__ __forceinline__ float finalize_wave(const float* sums, float bias_lan
 // weight.  The Sinkhorn row and column sums are the same row-local DPP
 // moves, so the four rows run side by side.  sums: this lane's token.
 // publish(q, pre, cancels) of the fused modes runs before the Sinkhorn iterations.
+// BC: the stream is one [T][4C] row x0 broadcast to the routes, split into
+// pseudo-routes (sums[24..27] are its sum of squares in four parts), so
+// g = psum x0 with psum = ((pre0 + pre1) + pre2) + pre3, sum g^2 =
+// psum^2 ss, and every q word is psum r_h (no cancellation is possible).
 // bias: the bias vector, or this lane's two entries of it loaded beforehand
 // (LaneBias), so that the finalisation waits for no memory load.
 struct LaneBias {
@@ -337,7 +341,7 @@ __device__ __forceinline__ float bias_pw(const float* b, int kp) { return b[kp];
 __device__ __forceinline__ float bias_pw(const LaneBias& b, int) { return b.p; }
 __device__ __forceinline__ float bias_res(const float* b, int k) { return b[8 + k]; }
 __device__ __forceinline__ float bias_res(const LaneBias& b, int) { return b.r; }
-template <bool FUSED, class Bias, class Publish>
+template <bool FUSED, bool BC = false, class Bias, class Publish>
 __device__ __forceinline__ void finalize_rows(const float* sums, const Bias& bias, int C, const Scalars& sc,
                                               int lane, float& res, float& pp, Publish&& publish) {
   const int k = lane & 15, kp = lane & 7;
@@ -349,10 +353,17 @@ __device__ __forceinline__ void finalize_rows(const float* sums, const Bias& bia
   if constexpr (FUSED) {
     const int row0 = lane & 48;
     const float p[4] = {__shfl(pp, row0), __shfl(pp, row0 + 1), __shfl(pp, row0 + 2), __shfl(pp, row0 + 3)};
-    bool cancels;
-    const float rh = gram_rms_factor(sums + 24, p, C, sc.rmsnorm_eps, cancels);
-    const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
-    publish(q, p, cancels);
+    if constexpr (BC) {
+      const float psum = ((p[0] + p[1]) + p[2]) + p[3];
+      const float qb = psum / sqrtf(psum * psum * ss / (float)(kRoutes * C) + sc.rmsnorm_eps);
+      const float q[4] = {qb, qb, qb, qb};
+      publish(q, p, false);
+    } else {
+      bool cancels;
+      const float rh = gram_rms_factor(sums + 24, p, C, sc.rmsnorm_eps, cancels);
+      const float q[4] = {p[0] * rh, p[1] * rh, p[2] * rh, p[3] * rh};
+      publish(q, p, cancels);
+    }
   }
   const float l = r * sums[8 + k] + bias_res(bias, k);
   float v = expf(l);
@@ -1174,6 +1185,9 @@ __device__ __forceinline__ void lds_dma16_shared(const void* src, uint32_t base)
 // Buffer resource over [base, base + bytes): the hardware drops stores at
 // offsets past the end, so a store to a row past T needs no branch (raw
 // buffer, gfx9 resource word 3).
+// cache-policy operand of a buffer load with system scope (sc0 sc1), which
+// sees the system-scope stores of other workgroups
+constexpr int kCachePolicySystem = 1 | 16;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -1188,6 +1202,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   constexpr bool FUSED = mode_fused(MODE);
   constexpr bool YQ = mode_yq(MODE);
   constexpr bool MX = mode_mx(MODE);
+  constexpr bool BC = mode_bc(MODE);
+  static_assert(!BC || (FUSED && !MX && !YQ), "the broadcast pass is the bf16 fused pipeline without post");
   constexpr int TM = kPersistTM, NV = kPartVals, D = persist_depth(MODE);
   static_assert(kRingK >= D + 1, "a ring slot is reused only after its tile was gathered");
   // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
@@ -1208,7 +1224,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   __shared__ float red[FUSED ? 8 : 2][FUSED ? 16 : 8][FUSED ? NV : 16 * kCoeffsWords];
   __shared__ float cfs[FUSED ? TM : 1][20];
   __shared__ float qs[FUSED ? TM : 1][4];
-  __shared__ float gam[FUSED ? kCC : 1];
+  __shared__ float gam[FUSED ? (BC ? 4 * kCC : kCC) : 1];
   __shared__ uint32_t s_last;  // this workgroup left last
   float* finw = reinterpret_cast<float*>(&xslot[0][0][0]);  // reduce workgroups: [2][8][NV] or [TM][NV] sums
 
@@ -1387,14 +1403,29 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
         // the value loads stay behind the flag loads they depend on
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const float* vb = pf + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
-        float f[kPersistMaxS];
-#pragma unroll
-        for (int k = 0; k < kPersistMaxS; ++k)
-          f[k] = act && k < S ? __uint_as_float(load_sys32(vb + k * pstride)) : 0.0f;
         float acc = 0.0f;
+        if constexpr (BC) {
+          // (at most 32 splits) system-scope buffer loads, all issued
+          // before the first is waited for: past the S splits, and for
+          // threads without a word, the range check returns zeros
+          const __amdgpu_buffer_rsrc_t rs =
+              buffer_rsrc(pf + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV, (uint32_t)(S * pstride * 4));
+          float f[kPersistMaxS / 2];
 #pragma unroll
-        for (int k = 0; k < kPersistMaxS; ++k) acc += k < S ? f[k] : 0.0f;
+          for (int k = 0; k < kPersistMaxS / 2; ++k)
+            f[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rs, act ? (uint32_t)((k * pstride + v) * 4) : 0x7ffffff0u, 0, kCachePolicySystem));
+#pragma unroll
+          for (int k = 0; k < kPersistMaxS / 2; ++k) acc += f[k];
+        } else {
+          const float* vb = pf + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
+          float f[kPersistMaxS];
+#pragma unroll
+          for (int k = 0; k < kPersistMaxS; ++k)
+            f[k] = act && k < S ? __uint_as_float(load_sys32(vb + k * pstride)) : 0.0f;
+#pragma unroll
+          for (int k = 0; k < kPersistMaxS; ++k) acc += k < S ? f[k] : 0.0f;
+        }
         if (v >= 0 && v < 8 * NV) fin[v] = act ? acc : 0.0f;
       };
       if (j < nunits && wv >= 2) gather(j, finw);
@@ -1415,7 +1446,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           float res, pp;
           // every row of the tile is published ([R][TM][4] words): the
           // stream workgroups poll whole row blocks, padding rows included
-          finalize_rows<FUSED>(fin + ml * NV, lb, C, a.sc, lane, res, pp,
+          finalize_rows<FUSED, BC>(fin + ml * NV, lb, BC ? a.rms_c : C, a.sc, lane, res, pp,
                                [&](const float* q, const float* pw, bool cancels) __attribute__((always_inline)) {
                                  // a cancelling token: listed (and its pre weights written through)
                                  // before its q words, whose sign bit on q0 tells the pre step to
@@ -1448,7 +1479,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // tokens' rows alone.  The arguments are read through the
       // kernel-argument segment's address, made opaque (as in the leave
       // section), so that the main loop's registers do not change.
-      if constexpr (!MX) {
+      if constexpr (!MX && !BC) {
         if (tid == 0) {
           uint32_t* rd = reinterpret_cast<uint32_t*>(a.fix_word + 1);
           static_assert(kWsRedDone == kWsFixWord + 8, "reduce-done counter after the fix word");
@@ -1513,7 +1544,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     }
     // gamma slice: loaded now, stored to LDS after the prologue's wait
     // (a compiler wait for it here would also wait for the copies above)
-    const float gam_v = FUSED && tid < kCC ? a.gamma[c0 + tid] : 0.0f;
+    // (broadcast: the 512 channels of the split's four pseudo-routes)
+    const float gam_v = FUSED && (BC || tid < kCC) ? a.gamma[c0 + tid] : 0.0f;
     // block 4 fragment of this lane: its own column if < 8, else the zero fragment
     const int b4off = n16 < 8 ? 4 * kWave + g * 8 + n16 : -1;
 
@@ -1775,7 +1807,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         const int q = ks + 4 * k;
         const int64_t tok = (int64_t)t * TM + rb * 16 + q;
         const int64_t tc = tok < a.T ? tok : 0;
-        const uint16_t* src = a.x + tc * (int64_t)(4 * C) + (int64_t)jr * C + c0 + 8 * (p ^ q);
+        const uint16_t* src = BC ? a.x + tc * a.xts + (int64_t)jr * a.xrs + c0 + 8 * (p ^ q)
+                                 : a.x + tc * (int64_t)(4 * C) + (int64_t)jr * C + c0 + 8 * (p ^ q);
         lds_dma16(src, __builtin_amdgcn_readfirstlane(sb + (uint32_t)q * 1024u));
       }
     };
@@ -1784,6 +1817,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
     float4 ncf = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint64_t nq = 0;
     auto issue_y = [&](int i) __attribute__((always_inline)) {
+      if constexpr (BC) return;  // no post
       const int t = r + L * (i < niter ? i : 0);
       const int64_t tok = (int64_t)t * TM + m;
       const int64_t tc = tok < a.T ? tok : 0;
@@ -1868,7 +1902,24 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         issue_q(i + 1);
       }
       // pre step of tile t_{i-D}
-      if constexpr (doC) {
+      if constexpr (doC && BC) {
+        // broadcast: h of the split's four pseudo-routes, (q x') gamma at
+        // channels c0 + 128 jr + ch (q = psum r_h, the same in all 4 words)
+        const int64_t tokC0 = (int64_t)(r + L * (i - D)) * TM + rb * 16;
+        const uint32_t nC = (uint32_t)max((int64_t)0, min((int64_t)16, a.T - tokC0));
+        const float qb = qs[m][0];
+        const __amdgpu_buffer_rsrc_t rhb = buffer_rsrc(a.h + tokC0 * C, nC * (uint32_t)(2 * C));
+#pragma unroll
+        for (int jr = 0; jr < 4; ++jr) {
+          float hv[8];
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            hv[2 * qd] = (qb * bf16_lo(ring[0][jr][qd])) * gam[kCC * jr + ch + 2 * qd];
+            hv[2 * qd + 1] = (qb * bf16_hi(ring[0][jr][qd])) * gam[kCC * jr + ch + 2 * qd + 1];
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(pack8(hv), rhb, (n16 * C + cl + kCC * jr) * 2, 0, 0);
+        }
+      } else if constexpr (doC) {
         const int64_t tokC0 = (int64_t)(r + L * (i - D)) * TM + rb * 16;
         const uint32_t nC = (uint32_t)max((int64_t)0, min((int64_t)16, a.T - tokC0));
         const float q0 = qs[m][0], q1 = qs[m][1], q2 = qs[m][2], q3 = qs[m][3];
@@ -1941,7 +1992,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         u32x4_t xin[4];
 #pragma unroll
         for (int jr = 0; jr < 4; ++jr) xin[jr] = sp[(n16 * 4 + jr) * 16 + xpos];
-        if constexpr (FUSED) {
+        if constexpr (FUSED && !BC) {
           float pw[4], rs[16];
 #pragma unroll
           for (int k = 0; k < 4; ++k) pw[k] = cfs[m][k];
@@ -2059,7 +2110,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       if constexpr (FUSED) {
         const int ti = r + L * i;
         const float4 ccf = ncf;
-        if (gt < 16 * 5) {
+        if (!BC && gt < 16 * 5) {
           const bool ok = (int64_t)ti * TM + rb * 16 + gt / 5 < a.T;
           float* dd = &cfs[rb * 16 + gt / 5][4 * (gt % 5)];
           dd[0] = ok ? ccf.x : 0.0f;
@@ -2109,7 +2160,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_sched_barrier(0);
-      if (FUSED && tid < kCC) gam[tid] = gam_v;
+      if (FUSED && (BC || tid < kCC)) gam[tid] = gam_v;
       if (rb == 0) prepP(0, No{});
       __syncthreads();
       // step i: [row block 0: P(i)       | row block 1: M(i-1), prep P(i)]   barrier
@@ -2458,6 +2509,10 @@ hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStrea
       case kModeFusedMx: return launch_persist_mode<kModeFusedMx>(plan, a, s);
       case kModeFused | kModeYInt8: return launch_persist_mode<kModeFused | kModeYInt8>(plan, a, s);
       case kModeFusedMx | kModeYInt8: return launch_persist_mode<kModeFusedMx | kModeYInt8>(plan, a, s);
+      case kModeFused | kModeBcast:
+        // its reduce gathers at most kPersistMaxS / 2 splits
+        if (plan.s > kPersistMaxS / 2) return hipErrorInvalidConfiguration;
+        return launch_persist_mode<kModeFused | kModeBcast>(plan, a, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -787,9 +787,10 @@ def test_pre_broadcast_wide_ring_wraps():
 
 
 def skip_unless_schedule_bcast(T, C, schedule):
-    # the broadcast call's coefficients take the persistent kernel on
-    # pseudo-routes (C / 512 >= 8 splits, 192 / (C / 512) stream lanes per
-    # split) with two tiles per stream workgroup: at T = 2048 or more for
-    # these hidden sizes (16, 12, 10, 8 and 14 splits)
+    # the broadcast call takes the persistent kernel on pseudo-routes
+    # (C / 512 >= 8 splits, 192 / (C / 512) stream lanes per split): one pass
+    # for coefficients and h with four tiles per stream workgroup (here
+    # T = 2048 at C = 6144, 7168, 8192 and T = 4096 at C = 5120), else the
+    # coefficients pass with two (T = 2300 at C = 4096) and the pre kernel
     if schedule == "persistent" and T < 2048:
         pytest.skip(f"the broadcast call runs the staged schedule at T={T}, C={C}")
