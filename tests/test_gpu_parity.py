@@ -786,6 +786,24 @@ def test_pre_broadcast_wide_ring_wraps():
     assert_bf16_close(f64(h.index_select(0, idx)), rh, what="h")
 
 
+@pytest.mark.parametrize("C", [12288, 16384])
+def test_pre_broadcast_wide_hidden(C, schedule):
+    # 24 and 32 pseudo-route splits at T = 2048: the one-pass schedule with
+    # 32 reduce workgroups (9 and 7 stream lanes), whose reduce gathers at
+    # most 32 splits; sampled rows against the oracle on both schedules
+    T = 2048
+    d = make_inputs(T, C, seed=37, rows="outliers", device=DEV)
+    x0 = d["x"][:, 0, :].contiguous()
+    cf, h = mhc.pre_broadcast(x0, d["phi"], d["bias"], d["gamma"])
+    torch.cuda.synchronize()
+    rows = sample_rows(T, extra=(T - 1,))
+    idx = torch.from_numpy(rows).to(DEV)
+    rc, rh = O.pre_broadcast(f64(x0.index_select(0, idx)), f64(d["phi"]), f64(d["bias"]), f64(d["gamma"]),
+                             rmsnorm_eps=P.rmsnorm_eps, **kw())
+    assert_coeffs_close(f64(cf.index_select(0, idx)), rc)
+    assert_bf16_close(f64(h.index_select(0, idx)), rh, what="h")
+
+
 def skip_unless_schedule_bcast(T, C, schedule):
     # the broadcast call takes the persistent kernel on pseudo-routes
     # (C / 512 >= 8 splits, 192 / (C / 512) stream lanes per split): one pass
