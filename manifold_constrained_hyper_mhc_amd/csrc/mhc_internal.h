@@ -27,7 +27,7 @@ struct Plan {
   int d2 = 2;      // stage delay of the pre step (fused modes), > d1
   int s = 1;       // workgroups per row
   int lanes = 0;   // persistent kernel: stream workgroups per split (0: staged kernel)
-  int reds = 32;   // persistent kernel: reduce workgroups (32, or 64 at <= 16 splits)
+  int reds = 32;   // persistent kernel: reduce workgroups (32 to 64; see choose_kernel)
   int64_t tiles = 0;
   int64_t chunk_tiles = 0;  // staged kernel: tiles per launch (a longer call is a sequence of launches)
   // workspace layout (byte offsets)

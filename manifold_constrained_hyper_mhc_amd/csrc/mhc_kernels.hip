@@ -2495,7 +2495,11 @@ static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream
 
 template <int MODE>
 static hipError_t launch_persist_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
-  if (p.reds != 32 && !(p.reds == 64 && p.s <= 16)) return hipErrorInvalidConfiguration;
+  if constexpr (mode_bc(MODE)) {
+    if (p.reds < 32 || p.reds > 64) return hipErrorInvalidConfiguration;
+  } else {
+    if (p.reds != 32 && !(p.reds == 64 && p.s <= 16)) return hipErrorInvalidConfiguration;
+  }
   const dim3 grid((unsigned)(p.s * p.lanes + p.reds)), block(kPersistThreads);
   k_persist<MODE><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
