@@ -1087,13 +1087,15 @@ __global__ __launch_bounds__(256, RUN <= 8 && !TK ? 4 : 2) void k_split(const Sp
 //     The coefficients-only mode has neither post nor x' ring: its stream
 //     workgroups keep x in registers three tiles ahead (whole-line loads,
 //     turned into the operand layout through an LDS stage) and run both
-//     row blocks in step.
-//   * 32 "reduce" workgroups gather the S partial rows of 8 tokens at a
-//     time (a whole tile in the coefficients-only mode), finalise their
+//     row blocks in step.  The broadcast mode (kModeBcast) is the fused
+//     pipeline without post on the pseudo-routes of a [T][C] input x0: x'
+//     is x0, and the pre step writes the four pseudo-routes' channels of h.
+//   * 32 to 64 "reduce" workgroups gather the S partial rows of 8 tokens at
+//     a time (a whole tile in the coefficients-only mode), finalise their
 //     coefficients (four tokens per wave, one per 16-lane row) and publish
 //     q_i = pre'_i * r_h.
 // Stream workgroups wait for q words published by reduce workgroups, which
-// wait for partials of stream workgroups, so the launch needs all S*L + 32
+// wait for partials of stream workgroups, so the launch needs all of its
 // workgroups resident together (the host sizes L from the CU count; every
 // wait is bounded and sets the workspace error word on expiry).  Nothing is
 // read back from x_out: the pre step uses the x' registers, so the HBM
