@@ -100,18 +100,42 @@ __global__ __launch_bounds__(256) void k_pack_phi_sum(const float* __restrict__ 
   float va[8], vb[8];  // route sums of logit n16 and of logit 16 + n16 % 8, rows 32q + 8g + e
 #pragma unroll
   for (int e = 0; e < 8; ++e) va[e] = vb[e] = 0.0f;
+  // every load of the four routes first (one memory round trip), then the
+  // sums in route order
+  u32x4_t fr[PACKED ? 4 : 1][6];
+  float pr[PACKED ? 1 : 4][2][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (PACKED) {
+      const u32x4_t* f = pk + ((int64_t)j * (C / 32) + q) * (kPackBlocks * kWave);
+      fr[j][0] = f[0 * kWave + lane];
+      fr[j][1] = f[1 * kWave + lane];
+      fr[j][2] = f[2 * kWave + lane];
+      fr[j][3] = f[3 * kWave + lo16];
+      fr[j][4] = f[3 * kWave + lo16 + 8];
+      fr[j][5] = f[4 * kWave + lo16];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float* row = phi + ((int64_t)j * C + q * 32 + g * 8 + e) * kCoeffs;
+        pr[j][0][e] = row[n16];
+        pr[j][1][e] = row[16 + (n16 & 7)];
+      }
+    }
+  }
+  // (keeps the compiler from moving the loads between the sums below)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float ra[8], rb[8];
     if constexpr (PACKED) {
-      const u32x4_t* f = pk + ((int64_t)j * (C / 32) + q) * (kPackBlocks * kWave);
       float h0[8], m0[8], l0[8], h1[8], m1[8], l1[8];
-      unpack8(f[0 * kWave + lane], h0);
-      unpack8(f[1 * kWave + lane], m0);
-      unpack8(f[2 * kWave + lane], l0);
-      unpack8(f[3 * kWave + lo16], h1);
-      unpack8(f[3 * kWave + lo16 + 8], m1);
-      unpack8(f[4 * kWave + lo16], l1);
+      unpack8(fr[j][0], h0);
+      unpack8(fr[j][1], m0);
+      unpack8(fr[j][2], l0);
+      unpack8(fr[j][3], h1);
+      unpack8(fr[j][4], m1);
+      unpack8(fr[j][5], l1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ra[e] = (h0[e] + m0[e]) + l0[e];
@@ -120,9 +144,8 @@ __global__ __launch_bounds__(256) void k_pack_phi_sum(const float* __restrict__ 
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float* row = phi + ((int64_t)j * C + q * 32 + g * 8 + e) * kCoeffs;
-        ra[e] = row[n16];
-        rb[e] = row[16 + (n16 & 7)];
+        ra[e] = pr[j][0][e];
+        rb[e] = pr[j][1][e];
       }
     }
 #pragma unroll
