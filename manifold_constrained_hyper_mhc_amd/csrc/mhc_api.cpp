@@ -133,7 +133,8 @@ enum class Use { kFused, kCoeffs, kCoeffsPseudo, kBcastFused };
 // broadcast stream on pseudo-routes); the fused pass and the coefficients
 // of a 4-route stream take it for the same shapes.  Its reduce workgroups:
 // 32, or 64 at <= 16 splits for the fused pass and the broadcast
-// coefficients; the one-pass broadcast pre takes 64 at <= 12 splits, 48 at
+// coefficients, and the CUs the stream lanes leave at 17-24 splits for the
+// fused pass; the one-pass broadcast pre takes 64 at <= 12 splits, 48 at
 // 13-16, else 32.  At so few splits the stream workgroups' tiles
 // are short, and the reduce workgroups, which take one unit at a time and
 // wait for its flags and then its values, set the pace at 32; the
@@ -166,7 +167,11 @@ void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   lanes = std::min(lanes, (cus - reds) / p.s);
   if (lanes < 1 || p.s * lanes + reds > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;
-  p.reds = reds;
+  // the fused pass at 17-24 splits (9 to 13 stream lanes, whose tiles come
+  // fast) also takes the CUs its stream lanes leave for more reduce
+  // workgroups: C = 3072, T = 8192: 137-141 us with 40 against 150-153 with
+  // 32; at 40-64 splits the same measured 2-4% slower
+  p.reds = use == Use::kFused && p.s > 16 && p.s <= 24 ? std::max(reds, std::min(64, cus - p.s * lanes)) : reds;
 }
 
 int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {

@@ -2520,11 +2520,10 @@ static hipError_t launch_split_mode(const Plan& p, const SplitArgs& a, hipStream
 
 template <int MODE>
 static hipError_t launch_persist_mode(const Plan& p, const SplitArgs& a, hipStream_t s) {
-  if constexpr (mode_bc(MODE)) {
-    if (p.reds < 32 || p.reds > 64) return hipErrorInvalidConfiguration;
-  } else {
-    if (p.reds != 32 && !(p.reds == 64 && p.s <= 16)) return hipErrorInvalidConfiguration;
-  }
+  // 32 to 64 reduce workgroups; the coefficients-only mode's rings are
+  // whole multiples of its count (32, or 64 at <= 16 splits)
+  if (p.reds < 32 || p.reds > 64) return hipErrorInvalidConfiguration;
+  if (!mode_fused(MODE) && p.reds != 32 && !(p.reds == 64 && p.s <= 16)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(p.s * p.lanes + p.reds)), block(kPersistThreads);
   k_persist<MODE><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
