@@ -134,8 +134,7 @@ enum class Use { kFused, kCoeffs, kCoeffsPseudo, kBcastFused };
 // of a 4-route stream take it for the same shapes.  Its reduce workgroups:
 // 32, or 64 at <= 16 splits for the fused pass and the broadcast
 // coefficients, and the CUs the stream lanes leave at 17-24 splits for the
-// fused pass; the one-pass broadcast pre takes 64 at <= 12 splits, 48 at
-// 13-16, else 32.  At so few splits the stream workgroups' tiles
+// fused pass; the one-pass broadcast pre takes 48 at <= 9 splits, else 32.  At so few splits the stream workgroups' tiles
 // are short, and the reduce workgroups, which take one unit at a time and
 // wait for its flags and then its values, set the pace at 32; the
 // coefficients of a 4-route stream run faster with the two extra stream
@@ -147,10 +146,10 @@ void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   if (p.m != 32 || p.s < (pseudo ? 8 : 16) || p.s > 64) return;
   const int cus = device_cus();
   // (the broadcast pass balances its stream lanes against its reduce
-  // workgroups: at 14 splits, 48 reduce workgroups gave 72 us against 79
-  // with 64 and 96 with 32 (T = 8192); at 8 splits 64 gave 60 us against 72
-  // with 48)
-  const int reds = use == Use::kBcastFused ? (p.s <= 12 ? 64 : (p.s <= 16 ? 48 : 32))
+  // workgroups, T = 8192: at 8 splits 48 reduce workgroups gave 48-49 us
+  // against 59 with 32 and 50 with 64; at 10 splits 32 and 48 both 58 us;
+  // at 12-16 splits 32 was the fastest, 66 us against 75 with 48 at 14)
+  const int reds = use == Use::kBcastFused ? (p.s <= 9 ? 48 : 32)
                                            : (p.s <= 16 && use != Use::kCoeffs ? 64 : 32);
   // the lane count that decides the schedule: with 32 reduce workgroups
   // outside a broadcast stream, so that both calls take the same one

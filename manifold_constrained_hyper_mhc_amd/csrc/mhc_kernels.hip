@@ -1114,9 +1114,9 @@ __global__ __launch_bounds__(256, RUN <= 8 && !TK ? 4 : 2) void k_split(const Sp
 //     pipeline without post on the pseudo-routes of a [T][C] input x0: x'
 //     is x0, and the pre step writes the four pseudo-routes' channels of h.
 //   * 32 to 64 "reduce" workgroups gather the S partial rows of 8 tokens at
-//     a time (a whole tile in the coefficients-only mode), finalise their
-//     coefficients (four tokens per wave, one per 16-lane row) and publish
-//     q_i = pre'_i * r_h.
+//     a time (16 in the broadcast mode, a whole tile in the coefficients-only
+//     mode), finalise their coefficients (four tokens per wave, one per
+//     16-lane row) and publish q_i = pre'_i * r_h.
 // Stream workgroups wait for q words published by reduce workgroups, which
 // wait for partials of stream workgroups, so the launch needs all of its
 // workgroups resident together (the host sizes L from the CU count; every
@@ -1398,6 +1398,106 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         finalize_tile(t);
         __syncthreads();  // this tile's sums are read
       }
+    } else if constexpr (BC) {
+      // The broadcast pass (bf16 h, no listed tokens): units of 16 tokens,
+      // one row block, released by one flag per split.  Waves 4-7 gather
+      // unit u + nred (thread v sums the words v and v + 256, and wave 4
+      // also v + 512, of the unit's 16 NV over the S splits, with
+      // system-scope buffer loads all issued before the first is waited
+      // for; past the S splits the buffer's range check returns zeros) while
+      // waves 0-3 finalise unit u, four tokens per wave.
+      const int R = kRingK * L;
+      const float* pf = reinterpret_cast<const float*>(a.partials);
+      const int nunits = tiles * 2;
+      const int v = tid - 256;
+      auto flags_in = [&](const uint64_t* fb) __attribute__((always_inline)) {
+        const uint64_t f = lane < S ? tagged_load(fb + 2 * lane) : 0;
+        return __builtin_amdgcn_ballot_w64(lane < S && (uint32_t)(f >> 32) != want) == 0;
+      };
+      auto gather = [&](int u, float* fin, auto kMax) __attribute__((always_inline)) {
+        constexpr int KM = decltype(kMax)::value;  // splits the loads cover (>= S)
+        const int tu = u >> 1;
+        want = ring_tag(tag, (uint32_t)(tu / R));
+        const uint64_t* fb = a.pflag + (int64_t)(tu % R) * S * 2 + (u & 1);
+        if (!flags_in(fb)) {
+          uint32_t it = 0;
+          do {
+            __builtin_amdgcn_s_sleep(1);
+            if (++it > kPersistSpinLimit || ((it & 15u) == 0u && error_seen(a.err))) {
+              __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          } while (!flags_in(fb));
+        }
+        // the value loads stay behind the flag loads they depend on
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc(pf + (int64_t)(tu % R) * S * pstride + (u & 1) * 16 * NV, (uint32_t)(S * pstride * 4));
+        float f0[KM], f1[KM];
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+          f0[k] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)((k * pstride + v) * 4), 0, kCachePolicySystem));
+          f1[k] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)((k * pstride + v + 256) * 4), 0, kCachePolicySystem));
+        }
+        float s2 = 0.0f;
+        if (wv == 4) {
+          const bool has2 = v + 512 < 16 * NV;
+          float f2[KM];
+#pragma unroll
+          for (int k = 0; k < KM; ++k)
+            f2[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rs, has2 ? (uint32_t)((k * pstride + v + 512) * 4) : 0x7ffffff0u, 0, kCachePolicySystem));
+#pragma unroll
+          for (int k = 0; k < KM; ++k) s2 += f2[k];
+          if (has2) fin[v + 512] = s2;
+        }
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+          s0 += f0[k];
+          s1 += f1[k];
+        }
+        fin[v] = s0;
+        fin[v + 256] = s1;
+      };
+      auto gather_unit = [&](int u, float* fin) __attribute__((always_inline)) {
+        if (S <= 16) {
+          gather(u, fin, IntC<16>{});
+        } else {
+          gather(u, fin, IntC<kPersistMaxS / 2>{});
+        }
+      };
+      if (j < nunits && wv >= 4) gather_unit(j, finw);
+      const LaneBias lb = wv < 4 ? LaneBias{a.bias[lane & 7], a.bias[8 + (lane & 15)]} : LaneBias{0.0f, 0.0f};
+      __syncthreads();
+      int k = 0;
+      for (int u = j; u < nunits; u += nred, ++k) {
+        float* fin = finw + (k & 1) * (16 * NV);  // this unit's sums
+        if (wv < 4) {
+          // token 4 wave + r of the unit on lanes 16r .. 16r + 15
+          const int ml = 4 * wv + (lane >> 4), kk = lane & 15;
+          const int tu = u >> 1;
+          const int64_t tok = (int64_t)tu * TM + (u & 1) * 16 + ml;
+          const int64_t ptok = (int64_t)(tu % R) * TM + (u & 1) * 16 + ml;  // ring slot of the q words
+          const uint32_t qtag = ring_tag(tag, (uint32_t)(tu / R));
+          float res, pp;
+          finalize_rows<true, true>(fin + ml * NV, lb, a.rms_c, a.sc, lane, res, pp,
+                                    [&](const float* q, const float*, bool) __attribute__((always_inline)) {
+                                      if (kk < 4)
+                                        tagged_store(a.publish + ptok * 4 + kk,
+                                                     kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], qtag);
+                                    });
+          if (tok < a.T) {
+            a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
+            if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
+          }
+        } else if (u + nred < nunits) {
+          gather_unit(u + nred, finw + ((k + 1) & 1) * (16 * NV));
+        }
+        __syncthreads();  // the next unit's sums are in; this unit's are read
+      }
     } else {
       // The fused pass's partial values are plain binary32 words, released
       // per (tile, split, row block) by a tagged flag that the stream
@@ -1428,29 +1528,14 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         }
         // the value loads stay behind the flag loads they depend on
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const float* vb = pf + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
+        float f[kPersistMaxS];
+#pragma unroll
+        for (int k = 0; k < kPersistMaxS; ++k)
+          f[k] = act && k < S ? __uint_as_float(load_sys32(vb + k * pstride)) : 0.0f;
         float acc = 0.0f;
-        if constexpr (BC) {
-          // (at most 32 splits) system-scope buffer loads, all issued
-          // before the first is waited for: past the S splits, and for
-          // threads without a word, the range check returns zeros
-          const __amdgpu_buffer_rsrc_t rs =
-              buffer_rsrc(pf + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV, (uint32_t)(S * pstride * 4));
-          float f[kPersistMaxS / 2];
 #pragma unroll
-          for (int k = 0; k < kPersistMaxS / 2; ++k)
-            f[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                rs, act ? (uint32_t)((k * pstride + v) * 4) : 0x7ffffff0u, 0, kCachePolicySystem));
-#pragma unroll
-          for (int k = 0; k < kPersistMaxS / 2; ++k) acc += f[k];
-        } else {
-          const float* vb = pf + (int64_t)(tu % R) * S * pstride + (u & 3) * 8 * NV + (act ? v : 0);
-          float f[kPersistMaxS];
-#pragma unroll
-          for (int k = 0; k < kPersistMaxS; ++k)
-            f[k] = act && k < S ? __uint_as_float(load_sys32(vb + k * pstride)) : 0.0f;
-#pragma unroll
-          for (int k = 0; k < kPersistMaxS; ++k) acc += k < S ? f[k] : 0.0f;
-        }
+        for (int k = 0; k < kPersistMaxS; ++k) acc += k < S ? f[k] : 0.0f;
         if (v >= 0 && v < 8 * NV) fin[v] = act ? acc : 0.0f;
       };
       if (j < nunits && wv >= 2) gather(j, finw);
@@ -1471,7 +1556,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           float res, pp;
           // every row of the tile is published ([R][TM][4] words): the
           // stream workgroups poll whole row blocks, padding rows included
-          finalize_rows<FUSED, BC>(fin + ml * NV, lb, BC ? a.rms_c : C, a.sc, lane, res, pp,
+          finalize_rows<FUSED>(fin + ml * NV, lb, C, a.sc, lane, res, pp,
                                [&](const float* q, const float* pw, bool cancels) __attribute__((always_inline)) {
                                  // a cancelling token: listed (and its pre weights written through)
                                  // before its q words, whose sign bit on q0 tells the pre step to
@@ -1504,7 +1589,7 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
       // tokens' rows alone.  The arguments are read through the
       // kernel-argument segment's address, made opaque (as in the leave
       // section), so that the main loop's registers do not change.
-      if constexpr (!MX && !BC) {
+      if constexpr (!MX) {
         if (tid == 0) {
           uint32_t* rd = reinterpret_cast<uint32_t*>(a.fix_word + 1);
           static_assert(kWsRedDone == kWsFixWord + 8, "reduce-done counter after the fix word");
