@@ -124,17 +124,19 @@ int device_cus() {
   return cache[dev];
 }
 
-// Which call a persistent launch serves: the fused pass, the coefficients
-// of a 4-route stream, those of a broadcast stream on pseudo-routes, or
-// the one-pass coefficients and pre of a broadcast stream on pseudo-routes.
-enum class Use { kFused, kCoeffs, kCoeffsPseudo, kBcastFused };
+// Which call a persistent launch serves: the fused pass (8-token reduce
+// units, or 16-token units: kModeUnit16), the coefficients of a 4-route
+// stream, those of a broadcast stream on pseudo-routes, or the one-pass
+// coefficients and pre of a broadcast stream on pseudo-routes.
+enum class Use { kFused, kFused16, kCoeffs, kCoeffsPseudo, kBcastFused };
 
 // The persistent kernel takes 16 to 64 splits per row (8 to 64 for a
 // broadcast stream on pseudo-routes); the fused pass and the coefficients
 // of a 4-route stream take it for the same shapes.  Its reduce workgroups:
-// 32, or 64 at <= 16 splits for the fused pass and the broadcast
-// coefficients, and the CUs the stream lanes leave at 17-24 splits for the
-// fused pass; the one-pass broadcast pre takes 48 at <= 9 splits, else 32.  At so few splits the stream workgroups' tiles
+// 32, or 64 at <= 16 splits for the fused pass with 8-token units and the
+// broadcast coefficients, and the CUs the stream lanes leave at 17-24
+// splits for the fused pass; the one-pass broadcast pre takes 48 at <= 9
+// splits, else 32.  At so few splits the stream workgroups' tiles
 // are short, and the reduce workgroups, which take one unit at a time and
 // wait for its flags and then its values, set the pace at 32; the
 // coefficients of a 4-route stream run faster with the two extra stream
@@ -150,7 +152,7 @@ void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   // against 59 with 32 and 50 with 64; at 10 splits 32 and 48 both 58 us;
   // at 12-16 splits 32 was the fastest, 66 us against 75 with 48 at 14)
   const int reds = use == Use::kBcastFused ? (p.s <= 9 ? 48 : 32)
-                                           : (p.s <= 16 && use != Use::kCoeffs ? 64 : 32);
+                                           : (p.s <= 16 && (use == Use::kFused || use == Use::kCoeffsPseudo) ? 64 : 32);
   // the lane count that decides the schedule: with 32 reduce workgroups
   // outside a broadcast stream, so that both calls take the same one
   int lanes = (cus - (pseudo ? reds : 32)) / p.s;
@@ -170,7 +172,9 @@ void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   // fast) also takes the CUs its stream lanes leave for more reduce
   // workgroups: C = 3072, T = 8192: 137-141 us with 40 against 150-153 with
   // 32; at 40-64 splits the same measured 2-4% slower
-  p.reds = use == Use::kFused && p.s > 16 && p.s <= 24 ? std::max(reds, std::min(64, cus - p.s * lanes)) : reds;
+  p.reds = (use == Use::kFused || use == Use::kFused16) && p.s > 16 && p.s <= 24
+               ? std::max(reds, std::min(64, cus - p.s * lanes))
+               : reds;
 }
 
 int check_workspace(const void* ws, size_t bytes, const mhc::Plan& plan) {
@@ -553,7 +557,7 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   }
 
   mhc::Plan run = plan;
-  choose_kernel(run);
+  choose_kernel(run, !yq && !mx && plan.s <= 32 ? Use::kFused16 : Use::kFused);
   mhc::SplitArgs a = split_args(run, ws, T, C, p);
   if (err_word != nullptr) a.err = err_word;
   const void* packed = phi_packed;
@@ -579,7 +583,12 @@ int fused_impl(const YIn& y, const uint16_t* x, const float* coeffs, const float
   a.scale_mfma = mfma_scales ? 1 : 0;
   // deferred Sinkhorn: the res slots get exp(logits), mhc_sinkhorn finishes them
   if (flags & MHC_FLAG_DEFER_SINKHORN) a.sc.sinkhorn_iters = 0;
-  const int mode = (mx ? mhc::kModeFusedMx : mhc::kModeFused) | (yq ? mhc::kModeYInt8 : 0);
+  // 16-token reduce units where the persistent kernel runs at <= 32 splits
+  // (bf16 y and h): there the stream lanes' tiles come fast enough for the
+  // reduce's throughput to matter
+  const bool unit16 = run.lanes > 0 && run.s <= 32 && !yq && !mx;
+  const int mode = (mx ? mhc::kModeFusedMx : mhc::kModeFused) | (yq ? mhc::kModeYInt8 : 0) |
+                   (unit16 ? mhc::kModeUnit16 : 0);
   // (tokens whose route combination cancels get their pre recomputed directly)
   return run_split(run, mode, a, s);
 }

@@ -141,11 +141,15 @@ struct SplitArgs {
 // binary32 scale per token.  kModeBcast is a flag on kModeFused (persistent
 // kernel only): the coefficients and pre of a [T][C] stream broadcast to the
 // 4 routes, on pseudo-routes, in one pass (no post, no x_out; x holds x0).
-enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2, kModeYInt8 = 4, kModeBcast = 8 };
+// kModeUnit16 is a flag on kModeFused (persistent kernel only, at most 32
+// splits): the reduce workgroups take 16-token units, as the broadcast pass
+// does.
+enum SplitMode { kModeCoeffs = 0, kModeFused = 1, kModeFusedMx = 2, kModeYInt8 = 4, kModeBcast = 8, kModeUnit16 = 16 };
 constexpr bool mode_fused(int m) { return (m & 3) == kModeFused || (m & 3) == kModeFusedMx; }
 constexpr bool mode_mx(int m) { return (m & 3) == kModeFusedMx; }
 constexpr bool mode_yq(int m) { return (m & kModeYInt8) != 0; }
 constexpr bool mode_bc(int m) { return (m & kModeBcast) != 0; }
+constexpr bool mode_u16(int m) { return (m & (kModeBcast | kModeUnit16)) != 0; }
 
 hipError_t launch_pack_phi(const float* phi, int C, void* out, hipStream_t s);
 // Packed route-summed projection of C rows, Phi[c] = ((phi[c] + phi[C+c]) +

@@ -496,7 +496,9 @@ __device__ __forceinline__ void xprime8(const SplitArgs& a, int64_t t, int c, co
 // binary64, sum_c g^2 in binary64, then h and its MXFP8 blocks written; the
 // pre step left these tokens' rows unwritten (the sign of q0).  A launch
 // with no listed token only reads the count.
-template <bool YQ, bool MX, int NT>
+// (COPY: a separate instantiation for a second caller, so that the
+// compiler's inlining of the first does not depend on it)
+template <bool YQ, bool MX, int NT, int COPY = 0>
 __device__ void fix_flagged(const SplitArgs& a, uint32_t tag, double* red, uint32_t first = 0, uint32_t stride = 1) {
   const int tid = threadIdx.x;
   const uint64_t w = __hip_atomic_load(a.fix_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -1228,7 +1230,9 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
   constexpr bool YQ = mode_yq(MODE);
   constexpr bool MX = mode_mx(MODE);
   constexpr bool BC = mode_bc(MODE);
+  constexpr bool U16 = mode_u16(MODE);  // 16-token reduce units
   static_assert(!BC || (FUSED && !MX && !YQ), "the broadcast pass is the bf16 fused pipeline without post");
+  static_assert(!U16 || (FUSED && !YQ && !MX), "16-token reduce units: the bf16 fused modes");
   constexpr int TM = kPersistTM, NV = kPartVals, D = persist_depth(MODE);
   static_assert(kRingK >= D + 1, "a ring slot is reused only after its tile was gathered");
   // LDS: projection slice [4 routes][4 steps][kPhiFrag] x 16 B; x slots
@@ -1398,8 +1402,8 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
         finalize_tile(t);
         __syncthreads();  // this tile's sums are read
       }
-    } else if constexpr (BC) {
-      // The broadcast pass (bf16 h, no listed tokens): units of 16 tokens,
+    } else if constexpr (U16) {
+      // 16-token units (the broadcast pass, and kModeUnit16 at few splits):
       // one row block, released by one flag per split.  Waves 4-7 gather
       // unit u + nred (thread v sums the words v and v + 256, and wave 4
       // also v + 512, of the unit's 16 NV over the S splits, with
@@ -1483,12 +1487,22 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           const int64_t ptok = (int64_t)(tu % R) * TM + (u & 1) * 16 + ml;  // ring slot of the q words
           const uint32_t qtag = ring_tag(tag, (uint32_t)(tu / R));
           float res, pp;
-          finalize_rows<true, true>(fin + ml * NV, lb, a.rms_c, a.sc, lane, res, pp,
-                                    [&](const float* q, const float*, bool) __attribute__((always_inline)) {
+          finalize_rows<true, BC>(fin + ml * NV, lb, BC ? a.rms_c : C, a.sc, lane, res, pp,
+                                  [&](const float* q, const float* pw, bool cancels) __attribute__((always_inline)) {
+                                    // (as in the 8-token units below: a cancelling token is
+                                    // listed before its q words, whose sign bit on q0 marks it)
+                                    if (cancels && tok < a.T) {
                                       if (kk < 4)
-                                        tagged_store(a.publish + ptok * 4 + kk,
-                                                     kk == 0 ? q[0] : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3], qtag);
-                                    });
+                                        store_sys32(a.coeffs_out + tok * kCoeffs + kk,
+                                                    __float_as_uint(kk == 0 ? pw[0] : kk == 1 ? pw[1] : kk == 2 ? pw[2] : pw[3]));
+                                      if (kk == 0) flag_for_fix(a, tag, tok);
+                                      __builtin_amdgcn_s_waitcnt(0);
+                                    }
+                                    if (kk < 4)
+                                      tagged_store(a.publish + ptok * 4 + kk,
+                                                   kk == 0 ? (cancels ? -q[0] : q[0]) : kk == 1 ? q[1] : kk == 2 ? q[2] : q[3],
+                                                   qtag);
+                                  });
           if (tok < a.T) {
             a.coeffs_out[tok * kCoeffs + 8 + kk] = res;
             if (kk < 8) a.coeffs_out[tok * kCoeffs + kk] = pp;
@@ -1497,6 +1511,26 @@ __global__ __launch_bounds__(kPersistThreads, 1) void k_persist(const SplitArgs 
           gather_unit(u + nred, finw + ((k + 1) & 1) * (16 * NV));
         }
         __syncthreads();  // the next unit's sums are in; this unit's are read
+      }
+      // the last reduce workgroup recomputes the listed tokens (bf16 h; as
+      // in the 8-token units below)
+      if constexpr (!MX && !BC) {
+        if (tid == 0) {
+          uint32_t* rd = reinterpret_cast<uint32_t*>(a.fix_word + 1);
+          uint32_t last = 0;
+          const uint32_t done = __hip_atomic_fetch_add(rd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (done == (uint32_t)nred - 1u) {
+            __hip_atomic_store(rd, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = 1;
+          }
+          s_last = last;
+        }
+        __syncthreads();
+        if (s_last != 0) {
+          const SplitArgs* ap = (const SplitArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+          asm volatile("" : "+s"(ap));
+          fix_flagged<YQ, false, kPersistThreads, 1>(*ap, tag, reinterpret_cast<double*>(&red[0][0][0]));
+        }
       }
     } else {
       // The fused pass's partial values are plain binary32 words, released
@@ -2622,10 +2656,13 @@ hipError_t launch_split(const Plan& plan, int mode, const SplitArgs& a, hipStrea
       case kModeFusedMx: return launch_persist_mode<kModeFusedMx>(plan, a, s);
       case kModeFused | kModeYInt8: return launch_persist_mode<kModeFused | kModeYInt8>(plan, a, s);
       case kModeFusedMx | kModeYInt8: return launch_persist_mode<kModeFusedMx | kModeYInt8>(plan, a, s);
+      // (16-token reduce units gather at most kPersistMaxS / 2 splits)
       case kModeFused | kModeBcast:
-        // its reduce gathers at most kPersistMaxS / 2 splits
         if (plan.s > kPersistMaxS / 2) return hipErrorInvalidConfiguration;
         return launch_persist_mode<kModeFused | kModeBcast>(plan, a, s);
+      case kModeFused | kModeUnit16:
+        if (plan.s > kPersistMaxS / 2) return hipErrorInvalidConfiguration;
+        return launch_persist_mode<kModeFused | kModeUnit16>(plan, a, s);
       default: return hipErrorInvalidValue;
     }
   }
