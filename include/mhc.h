@@ -241,7 +241,7 @@ int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t 
  * projection summed over the routes and rounded to binary32, so they are
  * not bitwise those of mhc_coeffs on the explicit [T][4][C] copy; both
  * meet the same bounds against the plain definition.  Where the persistent
- * schedule runs (C / 512 splits, at least four 32-token tiles per stream
+ * schedule runs (C / 512 splits, at least two 32-token tiles per stream
  * workgroup, MHC_SCHEDULE not "staged"), one launch computes both, each
  * workgroup holding its x0 slices in registers until their coefficients
  * are published (x0 is read once): h = bf16_rne((q * x0[c]) * gamma[c])

@@ -104,7 +104,7 @@ bool plan_fits(const mhc::Plan& p) {
 // Persistent kernel: one 512-thread workgroup per CU, S*L stream workgroups
 // plus 32 or 64 reduce workgroups, all resident.  It runs when 16 <= S <= 64
 // (8 <= S for the coefficients of a broadcast stream) and each stream
-// workgroup gets at least four tiles (two: broadcast coefficients), unless the environment
+// workgroup gets at least four tiles (two for a broadcast stream), unless the environment
 // variable MHC_SCHEDULE is "staged" (read on every call); otherwise the
 // staged kernel runs.
 bool persistent_allowed() {
@@ -164,7 +164,9 @@ void choose_kernel(mhc::Plan& p, Use use = Use::kFused) {
   // 33.0 vs 35.0 us fused), at C = 4096 (7 lanes) up to 24 (T = 768: 33.2 vs
   // 37.8 us), at C = 2048 (14 lanes) up to 64 (T = 2048: 39.4 vs 41.0 us);
   // above, the persistent one (T = 512 at C = 7168: 38.0 vs 39.8 us).
-  if (lanes < 1 || p.tiles < (use == Use::kCoeffsPseudo ? 2 : 4) * (int64_t)lanes) return;
+  // (the broadcast pre's one pass takes over from its two passes at two
+  // tiles per stream workgroup: at C = 7168, T = 1536 29.7 against 34.5 us)
+  if (lanes < 1 || p.tiles < (use == Use::kCoeffsPseudo || use == Use::kBcastFused ? 2 : 4) * (int64_t)lanes) return;
   lanes = std::min(lanes, (cus - reds) / p.s);
   if (lanes < 1 || p.s * lanes + reds > mhc::kPersistMaxBlocks) return;
   p.lanes = lanes;

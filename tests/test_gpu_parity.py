@@ -732,7 +732,8 @@ def test_pack_phi_layout(C):
 
 
 @pytest.mark.parametrize("T,C", [(37, 3072), (300, 7168), (2048, 7168), (2300, 4096), (16, 2048), (37, 1024),
-                                 (2048, 8192), (2048, 6144), (4096, 5120), (2050, 7168), (4001, 6144)])
+                                 (2048, 8192), (2048, 6144), (4096, 5120), (2050, 7168), (4001, 6144),
+                                 (900, 7168), (1600, 4096)])
 def test_pre_broadcast(T, C, schedule):
     # First-layer pre of a [T, C] input standing for all 4 routes, against the
     # oracle's plain definition (coefficients and pre of the replicated
@@ -806,10 +807,14 @@ def test_pre_broadcast_wide_hidden(C, schedule):
 
 def skip_unless_schedule_bcast(T, C, schedule):
     # the broadcast call takes the persistent kernel on pseudo-routes
-    # (C / 512 >= 8 splits): one pass for coefficients and h with four tiles
-    # per stream workgroup (here T = 2048 at C = 6144, 7168, 8192, T = 4096
-    # at C = 5120, and the ragged T = 2050 at C = 7168, whose last tile has
-    # an empty row block, and T = 4001 at C = 6144), else the coefficients
-    # pass with two (T = 2300 at C = 4096) and the pre kernel
-    if schedule == "persistent" and T < 2048:
+    # (C / 512 >= 8 splits): one pass for coefficients and h with two tiles
+    # per stream workgroup (here T = 2048 at C = 6144, 7168, 8192, T = 2300
+    # at C = 4096, T = 4096 at C = 5120, and the ragged T = 2050 at C = 7168,
+    # whose last tile has an empty row block, and T = 4001 at C = 6144),
+    # else the coefficients pass with two tiles per stream workgroup of its
+    # own, more lanes (T = 900 at C = 7168, T = 1600 at C = 4096), and the
+    # pre kernel
+    # (every case here from T = 900 runs one of the two; the smaller ones
+    # run the staged kernel)
+    if schedule == "persistent" and T < 800:
         pytest.skip(f"the broadcast call runs the staged schedule at T={T}, C={C}")
