@@ -241,10 +241,11 @@ int mhc_pre(const uint16_t* x, const float* coeffs, const float* gamma, int64_t 
  * projection summed over the routes and rounded to binary32, so they are
  * not bitwise those of mhc_coeffs on the explicit [T][4][C] copy; both
  * meet the same bounds against the plain definition.  Where the persistent
- * schedule runs (C / 512 splits, at least two 32-token tiles per stream
- * workgroup, MHC_SCHEDULE not "staged"), one launch computes both, each
- * workgroup holding its x0 slices in registers until their coefficients
- * are published (x0 is read once): h = bf16_rne((q * x0[c]) * gamma[c])
+ * schedule runs (8 to 32 splits of 512 channels, so 4096 <= C, at least
+ * two 32-token tiles per stream workgroup, MHC_SCHEDULE not "staged"), one
+ * launch computes both, each workgroup holding its x0 slices in registers
+ * until their coefficients are published (x0 is read once):
+ * h = bf16_rne((q * x0[c]) * gamma[c])
  * with psum = ((pre0 + pre1) + pre2) + pre3 and q = psum / sqrt(psum^2 *
  * sum_c x0^2 / C + rmsnorm_eps), all binary32.  Otherwise a pre launch
  * (mhc_pre's arithmetic on g = psum * x0) follows the coefficients.
